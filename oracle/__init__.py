@@ -1,0 +1,158 @@
+"""Oracle: plain fp64 CPU reference for HyenaND's gated N-D linear convolution.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the GPU library ``dimensional_fft_long_amd`` and never imports it.
+
+What it computes (explainer "Native multi-dimensional subquadratic operators via
+input-dependent long convolutions", section "HyenaND: native-space implicit
+global kernel", output equation for y[i]; gist.science summary of the same
+paper, section "Methodology", item "Boundary handling")::
+
+    y[b,c,i] = sum_j phi_c(x[b,c,j]) * x[b,c,j] * K_c[i-j],   i, j in the grid,
+    phi_c(v) = 1 / (1 + exp(-(alpha_c v + beta_c))),
+
+zero outside the grid (non-circular), K_c on offsets [-(n-1), n-1] per axis with
+offset 0 at index n-1, one kernel per channel shared over the batch.
+
+Routes (all fp64, in ``oracle.c``):
+  * ``direct``        -- O1, the sum written out, every output.
+  * ``direct_points`` -- O1 at chosen outputs (for grids too big for O2).
+  * ``fftconv``       -- O2, explicit zero padding to 2n, textbook radix-2 FFT.
+  * ``kernel_spectrum`` -- the full DFT of the wrap-placed kernel.
+
+Inputs are numpy arrays: x fp32 [B,C,*dims] (bf16 data widened exactly to fp32
+by the caller), alpha/beta fp32 [C], K fp32 [C,*(2*dims-1)].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc -O2 -fopenmp."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-D_GNU_SOURCE", "-fopenmp", "-fPIC", "-shared",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.oracle_gate.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
+        lib.oracle_direct.argtypes = [P, P, P, P, P, I, I, I, P]
+        lib.oracle_direct_points.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
+        lib.oracle_kernel_spectrum.argtypes = [P, I, I, P, P, P]
+        lib.oracle_fftconv_pairs.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
+        lib.oracle_num_threads.argtypes = []
+        for f in ("oracle_gate", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
+                  "oracle_fftconv_pairs", "oracle_num_threads"):
+            getattr(lib, f).restype = I
+        _lib = lib
+    return _lib
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def _dims_of(x: np.ndarray, d: int):
+    dims = np.ascontiguousarray(np.asarray(x.shape[2:], dtype=np.int64))
+    if dims.size != d:
+        raise ValueError("x must be [B, C, *dims]")
+    return dims
+
+
+def gate(x, alpha: float, beta: float) -> np.ndarray:
+    """u = phi(x) * x, phi the logistic of alpha*x + beta, in fp64."""
+    x = _f32(x)
+    u = np.empty(x.shape, dtype=np.float64)
+    _check(_load().oracle_gate(_ptr(x), x.size, float(alpha), float(beta), _ptr(u)), "gate")
+    return u
+
+
+def direct(x, alpha, beta, K) -> np.ndarray:
+    """O1: every output of the gated linear convolution, fp64 [B, C, *dims]."""
+    x, alpha, beta, K = _f32(x), _f32(alpha), _f32(beta), _f32(K)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    y = np.empty(x.shape, dtype=np.float64)
+    _check(_load().oracle_direct(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(y), B, C, d, _ptr(dims)),
+           "direct")
+    return y
+
+
+def direct_points(x, alpha, beta, K, points) -> np.ndarray:
+    """O1 at chosen outputs; ``points`` is int [P, 2+d] rows (b, c, i_0..i_{d-1})."""
+    x, alpha, beta, K = _f32(x), _f32(alpha), _f32(beta), _f32(K)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    pts = np.ascontiguousarray(np.asarray(points, dtype=np.int64).reshape(-1, 2 + d))
+    out = np.empty(pts.shape[0], dtype=np.float64)
+    _check(_load().oracle_direct_points(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), B, C, d, _ptr(dims),
+                                        pts.shape[0], _ptr(pts), _ptr(out)), "direct_points")
+    return out
+
+
+def fftconv(x, alpha, beta, K, pairs=None) -> np.ndarray:
+    """O2 for the listed pair indices (b*C + c); all pairs when ``pairs`` is None.
+
+    Returns fp64 [len(pairs), *dims] (or [B, C, *dims] for all pairs).
+    """
+    x, alpha, beta, K = _f32(x), _f32(alpha), _f32(beta), _f32(K)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    allp = pairs is None
+    pr = np.arange(B * C, dtype=np.int64) if allp else np.ascontiguousarray(np.asarray(pairs, dtype=np.int64))
+    y = np.empty((pr.size,) + tuple(x.shape[2:]), dtype=np.float64)
+    _check(_load().oracle_fftconv_pairs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), B, C, d, _ptr(dims),
+                                        pr.size, _ptr(pr), _ptr(y)), "fftconv")
+    return y.reshape(x.shape) if allp else y
+
+
+def kernel_spectrum(K, dims) -> np.ndarray:
+    """Full DFT (complex128 [C, *2*dims]) of each channel's wrap-placed kernel."""
+    K = _f32(K)
+    d = len(dims)
+    dd = np.ascontiguousarray(np.asarray(dims, dtype=np.int64))
+    C = K.shape[0]
+    shape = (C,) + tuple(2 * int(n) for n in dims)
+    re = np.empty(shape, dtype=np.float64)
+    im = np.empty(shape, dtype=np.float64)
+    _check(_load().oracle_kernel_spectrum(_ptr(K), C, d, _ptr(dd), _ptr(re), _ptr(im)), "kernel_spectrum")
+    return re + 1j * im
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(_load().oracle_num_threads())
