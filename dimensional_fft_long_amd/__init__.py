@@ -1,0 +1,205 @@
+"""Python binding of ``libhyenand.so``, the MI355X gated N-D FFT convolution.
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current HIP stream.  The
+library must be built (``dimensional_fft_long_amd.build.build()``); the first
+call raises if it is missing.
+
+The operation (explainer "Native multi-dimensional subquadratic operators via
+input-dependent long convolutions", section "HyenaND: native-space implicit
+global kernel", output equation y[i]; gist.science summary, "Methodology",
+"Boundary handling")::
+
+    y[b,c,i] = sum_j sigmoid(alpha_c x[b,c,j] + beta_c) x[b,c,j] K_c[i-j]
+
+zero outside the grid.  Entry points mirror ``include/hyenand.h``:
+
+* ``kernel_spectrum(K, dims)``        -> K_hat (once per parameter set)
+* ``fftconv_fwd(x, alpha, beta, K_hat)`` -> y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhyenand.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+
+EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_bytes", "hyenand_kernel_spectrum",
+           "hyenand_fftconv_workspace_bytes", "hyenand_fftconv_workspace_min_bytes", "hyenand_fftconv_fwd",
+           "hyenand_fftconv_fwd_traced")
+
+_lib = None
+
+
+def get_lib() -> ctypes.CDLL:
+    """Load ``libhyenand.so`` (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run dimensional_fft_long_amd.build.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.hyenand_status_string.argtypes = [I]
+    lib.hyenand_status_string.restype = ctypes.c_char_p
+    lib.hyenand_version.argtypes = []
+    lib.hyenand_version.restype = I
+    lib.hyenand_kernel_spectrum_bytes.argtypes = [I, I, P]
+    lib.hyenand_kernel_spectrum_bytes.restype = SZ
+    lib.hyenand_kernel_spectrum.argtypes = [P, P, I, I, P, P]
+    lib.hyenand_kernel_spectrum.restype = I
+    lib.hyenand_fftconv_workspace_bytes.argtypes = [I, I, I, P, I]
+    lib.hyenand_fftconv_workspace_bytes.restype = SZ
+    lib.hyenand_fftconv_workspace_min_bytes.argtypes = [I, I, I, P, I]
+    lib.hyenand_fftconv_workspace_min_bytes.restype = SZ
+    lib.hyenand_fftconv_fwd.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_fftconv_fwd.restype = I
+    lib.hyenand_fftconv_fwd_traced.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I, ctypes.POINTER(I)]
+    lib.hyenand_fftconv_fwd_traced.restype = I
+    _lib = lib
+    return lib
+
+
+_P = ctypes.c_void_p
+
+
+class HyenandError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {get_lib().hyenand_status_string(code).decode()} ({code})")
+        self.code = code
+
+
+def _dims_arr(dims):
+    arr = (ctypes.c_int64 * len(dims))(*[int(v) for v in dims])
+    return arr
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"x must be float32 or bfloat16, got {t}")
+
+
+def spectrum_bytes(C: int, dims) -> int:
+    return int(get_lib().hyenand_kernel_spectrum_bytes(C, len(dims), _dims_arr(dims)))
+
+
+def workspace_bytes(B: int, C: int, dims, dtype=torch.float32, minimum: bool = False) -> int:
+    lib = get_lib()
+    f = lib.hyenand_fftconv_workspace_min_bytes if minimum else lib.hyenand_fftconv_workspace_bytes
+    return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype)))
+
+
+def kernel_spectrum(K: torch.Tensor, dims=None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """K: fp32 device tensor [C, 2n_0-1, ..., 2n_{d-1}-1] -> K_hat (complex64 flat [C, ksz])."""
+    if dims is None:
+        dims = tuple((s + 1) // 2 for s in K.shape[1:])
+    dims = tuple(int(v) for v in dims)
+    C = int(K.shape[0])
+    if K.dtype != torch.float32 or not K.is_cuda or not K.is_contiguous():
+        raise TypeError("K must be a contiguous float32 device tensor")
+    if tuple(K.shape[1:]) != tuple(2 * n - 1 for n in dims):
+        raise ValueError("K must be [C, 2n-1, ...]")
+    nbytes = spectrum_bytes(C, dims)
+    if nbytes == 0 and C > 0:
+        raise HyenandError(ERR_UNSUPPORTED, "kernel_spectrum")
+    if out is None:
+        out = torch.empty(nbytes // 8, dtype=torch.complex64, device=K.device).view(C, -1) if C else \
+            torch.empty(0, dtype=torch.complex64, device=K.device)
+    rc = get_lib().hyenand_kernel_spectrum(_P(K.data_ptr()), _P(out.data_ptr()), C, len(dims), _dims_arr(dims),
+                                     _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "kernel_spectrum")
+    return out
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(B, C, dims, dtype, device):
+    """The workspace is sized once per shape and reused (allocated on first use)."""
+    nbytes = workspace_bytes(B, C, dims, dtype)
+    key = (str(device), nbytes)
+    buf = _ws_cache.get(key)
+    if buf is None:
+        buf = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf, nbytes
+
+
+def fftconv_fwd(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, K_hat: torch.Tensor,
+                y: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Gated N-D linear convolution; x [B, C, *dims] fp32 or bf16 on the device."""
+    if not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous device tensor")
+    dt = _dtype_code(x.dtype)
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    for t, nm in ((alpha, "alpha"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
+    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
+    if K_hat.numel() * 8 < spectrum_bytes(C, dims):
+        raise ValueError("K_hat is smaller than the spectrum of this shape")
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = get_lib().hyenand_fftconv_fwd(_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()),
+                                 _P(y.data_ptr()), B, C, len(dims), _dims_arr(dims), dt,
+                                 _P(workspace.data_ptr()), ws_bytes, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd")
+    return y
+
+
+PASS_NAMES = {1: ("conv1d",), 2: ("row_fwd", "col_out", "row_inv"),
+              3: ("row_fwd", "col_mid_fwd", "col_out", "col_mid_inv", "row_inv")}
+
+
+def fftconv_fwd_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None) -> int:
+    """fftconv_fwd recording ``events`` (torch.cuda.Event list, timing enabled)
+    before each kernel launch and after the last; returns the launch count."""
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    n = ctypes.c_int(0)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = get_lib().hyenand_fftconv_fwd_traced(
+        _P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
+        B, C, len(dims), _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()), ws_bytes,
+        _stream(stream), arr, len(events), ctypes.byref(n))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd_traced")
+    return int(n.value)
+
+
+class HyenaConvolutionFunction(torch.autograd.Function):
+    """Forward-only autograd wrapper in the shape the explainer's "Concrete
+    implementation pattern (PyTorch)" gives: forward(ctx, input, kernel
+    params, preallocated FFT workspace).  The backward pass is not provided."""
+
+    @staticmethod
+    def forward(ctx, x, alpha, beta, K_hat, workspace=None):
+        return fftconv_fwd(x, alpha, beta, K_hat, workspace=workspace)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        raise NotImplementedError("backward of the gated FFT convolution is not implemented")

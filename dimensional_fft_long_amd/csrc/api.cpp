@@ -1,0 +1,139 @@
+// api.cpp -- the C ABI declared in include/hyenand.h: argument validation,
+// workspace sizing, chunking over channels, launch and error mapping.
+#include <hip/hip_runtime.h>
+
+#include "../../include/hyenand.h"
+#include "launch.h"
+#include "plan.h"
+
+using namespace hyenand;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hyenand_status_string(int s)
+{
+    switch (s) {
+    case HYENAND_OK: return "ok";
+    case HYENAND_ERR_INVALID_ARG: return "invalid argument";
+    case HYENAND_ERR_UNSUPPORTED: return "unsupported shape";
+    case HYENAND_ERR_WORKSPACE: return "workspace too small";
+    case HYENAND_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int hyenand_version(void) { return 100; }
+
+size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims)
+{
+    Geom g;
+    if (C < 0 || !make_geom(d, dims, &g)) return 0;
+    return (size_t)C * (size_t)g.ksz * 8u;
+}
+
+int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream)
+{
+    if (C < 0) return HYENAND_ERR_INVALID_ARG;
+    if (d < 1 || d > 3 || !dims) return d < 1 || d > 3 ? HYENAND_ERR_UNSUPPORTED : HYENAND_ERR_INVALID_ARG;
+    Geom g;
+    if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
+    if (C == 0) return HYENAND_OK;
+    if (!K || !K_hat) return HYENAND_ERR_INVALID_ARG;
+    if (!aligned(K, 4) || !aligned(K_hat, 8)) return HYENAND_ERR_INVALID_ARG;
+    ConvArgs a{};
+    a.K = K;
+    a.khat = static_cast<const float2*>(K_hat);
+    a.g = g;
+    a.B = 1;
+    a.C = C;
+    a.c0 = 0;
+    a.nch = C;
+    hipError_t e = launch_spectrum(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HYENAND_OK : HYENAND_ERR_HIP;
+}
+
+size_t hyenand_fftconv_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype)
+{
+    Geom g;
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
+    return recommended_workspace(g, B, C);
+}
+
+size_t hyenand_fftconv_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype)
+{
+    Geom g;
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
+    return (size_t)B * (size_t)g.wsp * 8u;
+}
+
+static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y, int B,
+                            int C, int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                            void* stream, LaunchTrace* trace)
+{
+    if (B < 0 || C < 0) return HYENAND_ERR_INVALID_ARG;
+    if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
+    if (d < 1 || d > 3) return HYENAND_ERR_UNSUPPORTED;
+    if (!dims) return HYENAND_ERR_INVALID_ARG;
+    Geom g;
+    if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
+    if (B == 0 || C == 0) return HYENAND_OK;
+    const size_t es = dtype == HYENAND_BF16 ? 2 : 4;
+    if (!x || !y || !alpha || !beta || !K_hat) return HYENAND_ERR_INVALID_ARG;
+    if (!aligned(x, es) || !aligned(y, es) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(K_hat, 8))
+        return HYENAND_ERR_INVALID_ARG;
+    int per = C;
+    if (g.wsp > 0) {
+        if (!workspace) return HYENAND_ERR_WORKSPACE;
+        if (!aligned(workspace, 8)) return HYENAND_ERR_INVALID_ARG;
+        per = chunk_channels(g, B, C, workspace_bytes);
+        if (per < 1) return HYENAND_ERR_WORKSPACE;
+    }
+    ConvArgs a{};
+    a.x = x;
+    a.y = y;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.khat = static_cast<const float2*>(K_hat);
+    a.ws = static_cast<float2*>(workspace);
+    a.g = g;
+    a.B = B;
+    a.C = C;
+    a.bf16 = dtype == HYENAND_BF16;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int c0 = 0; c0 < C; c0 += per) {
+        a.c0 = c0;
+        a.nch = (C - c0) < per ? (C - c0) : per;
+        if (launch_forward_chunk(a, st, trace) != hipSuccess) return HYENAND_ERR_HIP;
+    }
+    if (trace) trace->mark(st);
+    return HYENAND_OK;
+}
+
+int hyenand_fftconv_fwd(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y, int B,
+                        int C, int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    return fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes, stream,
+                            nullptr);
+}
+
+int hyenand_fftconv_fwd_traced(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y,
+                               int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                               int* n_launches)
+{
+    if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
+    LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
+    const int rc = fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes,
+                                    stream, &tr);
+    if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,560 @@
+// conv_bodies.h -- workgroup bodies of the gated N-D FFT convolution kernels.
+//
+// What is computed (explainer "Native multi-dimensional subquadratic operators
+// via input-dependent long convolutions", section "HyenaND: native-space
+// implicit global kernel": y[i] = sum_j phi(x[j]) x[j] K[i-j], evaluated as
+// FFT -> pointwise product with the kernel spectrum -> inverse FFT; gist.science
+// summary of the same paper, "Methodology", "Boundary handling": zero padding
+// to twice the grid, output cropped back):
+//
+//   u      = sigmoid(alpha_c x + beta_c) * x                          (gate)
+//   U      = FFT_N(pad(u))            N = 2n on every axis             (forward)
+//   Y      = U * Khat_c                                               (product)
+//   y      = crop(IFFT_N(Y)) / prod N                                 (inverse)
+//
+// Pass structure (layouts in plan.h):
+//   row_fwd   gate + real FFT of the innermost axis, two rows packed as one
+//             complex line (u_a + i u_b); separated into two half spectra.
+//   col_mid   forward / inverse FFT along the middle axis (3-D only).
+//   col_out   forward FFT along the outermost axis, product with the kernel
+//             spectrum, inverse FFT -- in one workgroup, per line tile, for
+//             every batch entry of a channel.
+//   row_inv   inverse real FFT of the innermost axis, crop, cast, store y.
+//   conv1d    all of the above for d = 1 (one line per signal).
+//   spec_*    the kernel spectrum (forward transforms only, full inputs).
+//
+// Every body is a function of (execution context, workgroup index, arguments,
+// LDS tile); the device kernels in hyenand_kernels.hip wrap them.
+#pragma once
+
+#include "fft_core.h"
+#include "plan.h"
+
+namespace hyenand {
+
+// ------------------------------------------------------------- element I/O
+__host__ __device__ inline float bf16_to_f32(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+
+// Round to nearest even; NaN stays NaN.
+__host__ __device__ inline uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__host__ __device__ inline float load_x(const ConvArgs& a, long long i)
+{
+    return a.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[i]) : static_cast<const float*>(a.x)[i];
+}
+
+__host__ __device__ inline void store_y(const ConvArgs& a, long long i, float v)
+{
+    if (a.bf16) static_cast<uint16_t*>(a.y)[i] = f32_to_bf16(v);
+    else static_cast<float*>(a.y)[i] = v;
+}
+
+// The content gate: u = phi(x) x with phi(x) = 1 / (1 + exp(-(alpha x + beta))).
+__host__ __device__ inline float gate(float x, float al, float be)
+{
+    return x / (1.0f + expf(-(al * x + be)));
+}
+
+// Workspace offset of row r (r = j_out * n_mid + j_mid) inside one pair.
+__host__ __device__ inline long long row_ws(const Geom& g, int r)
+{
+    return ((long long)(r / g.n_mid) * g.N_mid + (r % g.n_mid)) * g.S;
+}
+
+// --------------------------------------------------------------- row_fwd
+// NP line pairs per workgroup; line pair h = (pair slot q, rows 2i and 2i+1).
+template <int L, class Ctx>
+__host__ __device__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, n = L / 2, S = L / 2;
+    const Geom& g = a.g;
+    const int hp = g.n_out * g.n_mid / 2;
+    const int H = a.nch * a.B * hp;
+    const int h0 = bid * NP;
+    const int tid = ctx.tid();
+    for (int idx = tid; idx < NP * n; idx += NT) {
+        const int lp = idx / n, m = idx % n;
+        const int h = h0 + lp;
+        float2 z = make_float2(0.f, 0.f);
+        if (h < H) {
+            const int q = h / hp, r = (h % hp) * 2;
+            const int c = a.c0 + q / a.B, b = q % a.B;
+            const long long xo = ((long long)b * a.C + c) * g.vox + (long long)r * n + m;
+            const float al = a.alpha[c], be = a.beta[c];
+            z.x = gate(load_x(a, xo), al, be);
+            z.y = gate(load_x(a, xo + n), al, be);
+        }
+        T[m * LP + lp] = z;
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, false, true, false>(ctx, T);
+    // Separate the two rows: with Z = FFT(u_a + i u_b),
+    //   2 U_a[k] = Z[k] + conj Z[L-k],   2 U_b[k] = -i (Z[k] - conj Z[L-k]).
+    // The factor 2 is folded into the kernel spectrum.
+    for (int idx = tid; idx < NP * S; idx += NT) {
+        const int lp = idx / S, k = idx % S;
+        const int h = h0 + lp;
+        if (h >= H) continue;
+        const int q = h / hp, r = (h % hp) * 2;
+        float2* wa = a.ws + (long long)q * g.wsp + row_ws(g, r);
+        float2* wb = a.ws + (long long)q * g.wsp + row_ws(g, r + 1);
+        const float2 Z = T[k * LP + lp];
+        float2 oa, ob;
+        if (k == 0) {
+            const float2 ZN = T[S * LP + lp];
+            oa = make_float2(2.f * Z.x, 2.f * ZN.x);
+            ob = make_float2(2.f * Z.y, 2.f * ZN.y);
+        } else {
+            const float2 Zm = T[(L - k) * LP + lp];
+            oa = make_float2(Z.x + Zm.x, Z.y - Zm.y);
+            ob = make_float2(Z.y + Zm.y, Zm.x - Z.x);
+        }
+        wa[k] = oa;
+        wb[k] = ob;
+    }
+}
+
+// --------------------------------------------------------------- row_inv
+template <int L, class Ctx>
+__host__ __device__ void row_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, n = L / 2, S = L / 2;
+    const Geom& g = a.g;
+    const int hp = g.n_out * g.n_mid / 2;
+    const int H = a.nch * a.B * hp;
+    const int h0 = bid * NP;
+    const int tid = ctx.tid();
+    // Rebuild Z = Y_a + i Y_b over the full length from the two half spectra
+    // (Hermitian extension), slot 0 holding (bin 0, bin L/2).
+    for (int idx = tid; idx < NP * S; idx += NT) {
+        const int lp = idx / S, k = idx % S;
+        const int h = h0 + lp;
+        float2 ya = make_float2(0.f, 0.f), yb = ya;
+        if (h < H) {
+            const int q = h / hp, r = (h % hp) * 2;
+            ya = a.ws[(long long)q * g.wsp + row_ws(g, r) + k];
+            yb = a.ws[(long long)q * g.wsp + row_ws(g, r + 1) + k];
+        }
+        if (k == 0) {
+            T[lp] = make_float2(ya.x, yb.x);
+            T[S * LP + lp] = make_float2(ya.y, yb.y);
+        } else {
+            T[k * LP + lp] = make_float2(ya.x - yb.y, ya.y + yb.x);
+            T[(L - k) * LP + lp] = make_float2(ya.x + yb.y, yb.x - ya.y);
+        }
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
+    for (int idx = tid; idx < NP * n; idx += NT) {
+        const int lp = idx / n, m = idx % n;
+        const int h = h0 + lp;
+        if (h >= H) continue;
+        const int q = h / hp, r = (h % hp) * 2;
+        const int c = a.c0 + q / a.B, b = q % a.B;
+        const long long yo = ((long long)b * a.C + c) * g.vox + (long long)r * n + m;
+        const float2 z = T[m * LP + lp];
+        store_y(a, yo, z.x);
+        store_y(a, yo + n, z.y);
+    }
+}
+
+// --------------------------------------------------------------- col_mid
+// FFT along the middle axis of a 3-D grid, TW adjacent lines per workgroup.
+// Forward: n_mid non-zero inputs -> N_mid outputs.  Inverse: N_mid inputs ->
+// the n_mid outputs that are kept.
+template <int L, bool INV, class Ctx>
+__host__ __device__ void col_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = col_tw(L), NT = kThreads, n = L / 2;
+    const Geom& g = a.g;
+    const int lines = g.n_out * g.S;
+    const int tpp = (lines + TW - 1) / TW;
+    const int q = bid / tpp, lam0 = (bid % tpp) * TW;
+    float2* base = a.ws + (long long)q * g.wsp;
+    const int tid = ctx.tid();
+    constexpr int PIN = INV ? L : n;
+    for (int idx = tid; idx < PIN * TW; idx += NT) {
+        const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
+        float2 z = make_float2(0.f, 0.f);
+        if (lam < lines) z = base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S];
+        T[pos * TW + l] = z;
+    }
+    ctx.sync();
+    tile_fft<L, TW, TW, NT, INV, !INV, INV>(ctx, T);
+    constexpr int POUT = INV ? n : L;
+    for (int idx = tid; idx < POUT * TW; idx += NT) {
+        const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
+        if (lam < lines) base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S] = T[pos * TW + l];
+    }
+}
+
+// Rows of the middle axis handled together by one out-axis workgroup: with
+// NR = 2 the rows {rp, N_mid - rp} (and {0, N_mid/2} for rp = 0), so that the
+// slot-0 line of k_mid and its mirror -k_mid are in the same tile.
+struct OutTile {
+    int c_local, t, rows[2];
+    bool self_mirror;
+};
+
+template <int NR, int TW>
+__host__ __device__ inline OutTile out_tile(const Geom& g, int bid)
+{
+    OutTile o;
+    const int ct = (g.S + TW - 1) / TW;
+    const int nrp = NR == 1 ? 1 : g.N_mid / 2;
+    const int tpc = nrp * ct;
+    o.c_local = bid / tpc;
+    const int rem = bid % tpc;
+    const int rp = rem / ct;
+    o.t = rem % ct;
+    if (NR == 1) {
+        o.rows[0] = 0; o.rows[1] = 0; o.self_mirror = true;
+    } else {
+        o.rows[0] = rp;
+        o.rows[1] = rp == 0 ? g.N_mid / 2 : g.N_mid - rp;
+        o.self_mirror = rp == 0;
+    }
+    return o;
+}
+
+// Product of the out-axis spectra with the kernel spectrum, in place in the
+// tile (element (pos, row*TW + col) at pos*NL + row*TW + col).  Lines with
+// k_in = 0 carry Z = A + iB (packed bins 0 and N_in/2) and need the mirror
+// element (-k_out, -k_mid):  W = Z Sv + conj(Z(-k)) Dv.
+template <int L, int NR, int TW, class Ctx>
+__host__ __device__ inline void out_product(const Ctx& ctx, const Geom& g, const OutTile& o,
+                                            const float2* kc, float2* T)
+{
+    constexpr int NL = NR * TW, NT = kThreads;
+    const long long PS = (long long)g.N_mid * g.S;
+    const int tid = ctx.tid();
+    for (int idx = tid; idx < L * NL; idx += NT) {
+        const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
+        const int k = o.t * TW + col;
+        if (k >= g.S || k == 0) continue;
+        T[pos * NL + l] = cmul(T[pos * NL + l], kc[pos * PS + (long long)o.rows[row] * g.S + k]);
+    }
+    if (o.t == 0) {
+        const int njobs = o.self_mirror ? NR * (L / 2 + 1) : L;
+        for (int job = tid; job < njobs; job += NT) {
+            int ra, rb, pa, pb;
+            if (o.self_mirror) {
+                ra = job / (L / 2 + 1); rb = ra;
+                pa = job % (L / 2 + 1); pb = (L - pa) % L;
+            } else {
+                ra = 0; rb = 1; pa = job; pb = (L - job) % L;
+            }
+            const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
+            const float2 Za = T[ea], Zb = T[eb];
+            const float2 Sa = kc[pa * PS + (long long)o.rows[ra] * g.S];
+            const float2 Sb = kc[pb * PS + (long long)o.rows[rb] * g.S];
+            const float2 Da = kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]];
+            const float2 Db = kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]];
+            const float2 Wa = cadd(cmul(Za, Sa), cmul(cconj(Zb), Da));
+            const float2 Wb = cadd(cmul(Zb, Sb), cmul(cconj(Za), Db));
+            T[ea] = Wa;
+            if (eb != ea) T[eb] = Wb;
+        }
+    }
+}
+
+// --------------------------------------------------------------- col_out
+// Out axis: forward FFT (n_out inputs), product, inverse FFT (n_out kept), for
+// every batch entry of the channel; the kernel spectrum tile is re-read from
+// cache for each b.
+template <int L, int NR, class Ctx>
+__host__ __device__ void col_out_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = NR == 1 ? col_tw(L) : mul3_tw(L);
+    constexpr int NL = NR * TW, NT = kThreads, n = L / 2;
+    const Geom& g = a.g;
+    const OutTile o = out_tile<NR, TW>(g, bid);
+    const long long PS = (long long)g.N_mid * g.S;
+    const float2* kc = a.khat + (long long)(a.c0 + o.c_local) * g.ksz;
+    const int tid = ctx.tid();
+    for (int b = 0; b < a.B; ++b) {
+        float2* base = a.ws + ((long long)o.c_local * a.B + b) * g.wsp;
+        for (int idx = tid; idx < n * NL; idx += NT) {
+            const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
+            const int k = o.t * TW + col;
+            float2 z = make_float2(0.f, 0.f);
+            if (k < g.S) z = base[pos * PS + (long long)o.rows[row] * g.S + k];
+            T[pos * NL + l] = z;
+        }
+        ctx.sync();
+        tile_fft<L, NL, NL, NT, false, true, false>(ctx, T);
+        out_product<L, NR, TW>(ctx, g, o, kc, T);
+        ctx.sync();
+        tile_fft<L, NL, NL, NT, true, false, true>(ctx, T);
+        for (int idx = tid; idx < n * NL; idx += NT) {
+            const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
+            const int k = o.t * TW + col;
+            if (k < g.S) base[pos * PS + (long long)o.rows[row] * g.S + k] = T[pos * NL + l];
+        }
+        ctx.sync();
+    }
+}
+
+// ---------------------------------------------------------------- conv1d
+// d = 1: the two signals of a line belong to consecutive pair slots (possibly
+// different channels), so the product is applied to the separated half spectra.
+template <int L, class Ctx>
+__host__ __device__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, n = L / 2, S = L / 2;
+    const Geom& g = a.g;
+    const int P = a.nch * a.B;
+    const int H = (P + 1) / 2;
+    const int h0 = bid * NP;
+    const int tid = ctx.tid();
+    for (int idx = tid; idx < NP * n; idx += NT) {
+        const int lp = idx / n, m = idx % n;
+        const int h = h0 + lp;
+        float2 z = make_float2(0.f, 0.f);
+        if (h < H) {
+            const int qa = 2 * h, qb = 2 * h + 1;
+            const int ca = a.c0 + qa / a.B, ba = qa % a.B;
+            z.x = gate(load_x(a, ((long long)ba * a.C + ca) * g.vox + m), a.alpha[ca], a.beta[ca]);
+            if (qb < P) {
+                const int cb = a.c0 + qb / a.B, bb = qb % a.B;
+                z.y = gate(load_x(a, ((long long)bb * a.C + cb) * g.vox + m), a.alpha[cb], a.beta[cb]);
+            }
+        }
+        T[m * LP + lp] = z;
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, false, true, false>(ctx, T);
+    for (int idx = tid; idx < NP * S; idx += NT) {
+        const int lp = idx / S, k = idx % S;
+        const int h = h0 + lp;
+        if (h >= H) continue;
+        const int qa = 2 * h, qb = 2 * h + 1;
+        const bool vb = qb < P;
+        const float2* ka = a.khat + (long long)(a.c0 + qa / a.B) * g.ksz;
+        const float2* kb = a.khat + (long long)(a.c0 + (vb ? qb : qa) / a.B) * g.ksz;
+        if (k == 0) {
+            const float2 Z0 = T[lp], ZS = T[S * LP + lp];
+            const float2 Xa = make_float2(2.f * Z0.x, 2.f * ZS.x), Xb = make_float2(2.f * Z0.y, 2.f * ZS.y);
+            const float2 Wa = cadd(cmul(Xa, ka[0]), cmul(cconj(Xa), ka[S]));
+            float2 Wb = cadd(cmul(Xb, kb[0]), cmul(cconj(Xb), kb[S]));
+            if (!vb) Wb = make_float2(0.f, 0.f);
+            T[lp] = make_float2(Wa.x, Wb.x);
+            T[S * LP + lp] = make_float2(Wa.y, Wb.y);
+        } else {
+            const float2 Z = T[k * LP + lp], Zm = T[(L - k) * LP + lp];
+            const float2 Xa = make_float2(Z.x + Zm.x, Z.y - Zm.y), Xb = make_float2(Z.y + Zm.y, Zm.x - Z.x);
+            const float2 Ya = cmul(Xa, ka[k]);
+            float2 Yb = cmul(Xb, kb[k]);
+            if (!vb) Yb = make_float2(0.f, 0.f);
+            T[k * LP + lp] = make_float2(Ya.x - Yb.y, Ya.y + Yb.x);
+            T[(L - k) * LP + lp] = make_float2(Ya.x + Yb.y, Yb.x - Ya.y);
+        }
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
+    for (int idx = tid; idx < NP * n; idx += NT) {
+        const int lp = idx / n, m = idx % n;
+        const int h = h0 + lp;
+        if (h >= H) continue;
+        const int qa = 2 * h, qb = 2 * h + 1;
+        const float2 z = T[m * LP + lp];
+        const int ca = a.c0 + qa / a.B, ba = qa % a.B;
+        store_y(a, ((long long)ba * a.C + ca) * g.vox + m, z.x);
+        if (qb < P) {
+            const int cb = a.c0 + qb / a.B, bb = qb % a.B;
+            store_y(a, ((long long)bb * a.C + cb) * g.vox + m, z.y);
+        }
+    }
+}
+
+// ======================================================== kernel spectrum
+// Wrap placement: offset delta of an axis with grid n and padded length N sits
+// at index delta mod N; index n is never reached and stays zero.
+constexpr int kEmpty = 1 << 30;
+__host__ __device__ inline int unwrap(int m, int n, int N)
+{
+    if (N == 1) return 0;
+    if (m < n) return m;
+    if (m == n) return kEmpty;
+    return m - N;
+}
+
+__host__ __device__ inline float kernel_at(const ConvArgs& a, int c, int m_out, int m_mid, int t)
+{
+    const Geom& g = a.g;
+    const int d0 = unwrap(m_out, g.n_out, g.N_out), d1 = unwrap(m_mid, g.n_mid, g.N_mid),
+              d2 = unwrap(t, g.n_in, g.N_in);
+    if (d0 == kEmpty || d1 == kEmpty || d2 == kEmpty) return 0.f;
+    const long long kl = (long long)g.ke_out * g.ke_mid * g.ke_in;
+    return a.K[(long long)c * kl +
+               ((long long)(d0 + g.n_out - 1) * g.ke_mid + (d1 + g.n_mid - 1)) * g.ke_in + (d2 + g.n_in - 1)];
+}
+
+// Rows of the innermost axis, every row of the padded (out, mid) grid, paired
+// within a channel (d >= 2) or across channels (d = 1).  Writes the packed
+// half spectrum (true DFT values) into the main block; for d = 1 this is the
+// final spectrum and is scaled and split here.
+template <int L, class Ctx>
+__host__ __device__ void spec_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, S = L / 2;
+    const Geom& g = a.g;
+    const bool one_d = g.d == 1;
+    const int rc = g.N_out * g.N_mid;
+    const int hp = one_d ? 1 : rc / 2;
+    const int H = one_d ? (a.C + 1) / 2 : a.C * hp;
+    const int h0 = bid * NP;
+    const int tid = ctx.tid();
+    float2* khat = const_cast<float2*>(a.khat);
+    for (int idx = tid; idx < NP * L; idx += NT) {
+        const int lp = idx / L, t = idx % L;
+        const int h = h0 + lp;
+        float2 z = make_float2(0.f, 0.f);
+        if (h < H) {
+            if (one_d) {
+                z.x = kernel_at(a, 2 * h, 0, 0, t);
+                if (2 * h + 1 < a.C) z.y = kernel_at(a, 2 * h + 1, 0, 0, t);
+            } else {
+                const int c = h / hp, r = (h % hp) * 2;
+                z.x = kernel_at(a, c, r / g.N_mid, r % g.N_mid, t);
+                z.y = kernel_at(a, c, (r + 1) / g.N_mid, (r + 1) % g.N_mid, t);
+            }
+        }
+        T[t * LP + lp] = z;
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, false, false, false>(ctx, T);
+    const float gsc = 1.0f / (2.0f * (float)g.N_in);  // only used for d = 1
+    for (int idx = tid; idx < NP * S; idx += NT) {
+        const int lp = idx / S, k = idx % S;
+        const int h = h0 + lp;
+        if (h >= H) continue;
+        const float2 Z = T[k * LP + lp];
+        float2 Xa, Xb;
+        if (k == 0) {
+            const float2 ZN = T[S * LP + lp];
+            Xa = make_float2(Z.x, ZN.x);
+            Xb = make_float2(Z.y, ZN.y);
+        } else {
+            const float2 Zm = T[(L - k) * LP + lp];
+            Xa = make_float2(0.5f * (Z.x + Zm.x), 0.5f * (Z.y - Zm.y));
+            Xb = make_float2(0.5f * (Z.y + Zm.y), 0.5f * (Zm.x - Z.x));
+        }
+        if (one_d) {
+            for (int s = 0; s < 2; ++s) {
+                const int c = 2 * h + s;
+                if (c >= a.C) break;
+                const float2 X = s ? Xb : Xa;
+                float2* kc = khat + (long long)c * g.ksz;
+                if (k == 0) {
+                    kc[0] = make_float2(0.5f * (X.x + X.y) * gsc, 0.f);
+                    kc[S] = make_float2(0.5f * (X.x - X.y) * gsc, 0.f);
+                } else {
+                    kc[k] = cscale(X, gsc);
+                }
+            }
+        } else {
+            const int c = h / hp, r = (h % hp) * 2;
+            float2* kc = khat + (long long)c * g.ksz;
+            kc[(long long)r * S + k] = Xa;
+            kc[(long long)(r + 1) * S + k] = Xb;
+        }
+    }
+}
+
+// Full forward FFT along the middle axis of the main block (3-D), in place.
+template <int L, class Ctx>
+__host__ __device__ void spec_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = col_tw(L), NT = kThreads;
+    const Geom& g = a.g;
+    const int lines = g.N_out * g.S;
+    const int tpc = (lines + TW - 1) / TW;
+    const int c = bid / tpc, lam0 = (bid % tpc) * TW;
+    float2* base = const_cast<float2*>(a.khat) + (long long)c * g.ksz;
+    const int tid = ctx.tid();
+    for (int idx = tid; idx < L * TW; idx += NT) {
+        const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
+        float2 z = make_float2(0.f, 0.f);
+        if (lam < lines) z = base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S];
+        T[pos * TW + l] = z;
+    }
+    ctx.sync();
+    tile_fft<L, TW, TW, NT, false, false, false>(ctx, T);
+    for (int idx = tid; idx < L * TW; idx += NT) {
+        const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
+        if (lam < lines) base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S] = T[pos * TW + l];
+    }
+}
+
+// Full forward FFT along the out axis, then scale by g = 1/(2 prod N) and, for
+// the k_in = 0 lines, split Z = A + iB into Sv = (A+B)/2 g (main slot 0) and
+// Dv = (A-B)/2 g (dblk), with A = (Z + conj Z(-k))/2, B = (Z - conj Z(-k))/(2i).
+template <int L, int NR, class Ctx>
+__host__ __device__ void spec_out_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = NR == 1 ? col_tw(L) : mul3_tw(L);
+    constexpr int NL = NR * TW, NT = kThreads;
+    const Geom& g = a.g;
+    const OutTile o = out_tile<NR, TW>(g, bid);
+    const long long PS = (long long)g.N_mid * g.S;
+    float2* kc = const_cast<float2*>(a.khat) + (long long)o.c_local * g.ksz;
+    const float gsc = 1.0f / (2.0f * (float)g.N_out * (float)g.N_mid * (float)g.N_in);
+    const int tid = ctx.tid();
+    for (int idx = tid; idx < L * NL; idx += NT) {
+        const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
+        const int k = o.t * TW + col;
+        float2 z = make_float2(0.f, 0.f);
+        if (k < g.S) z = kc[pos * PS + (long long)o.rows[row] * g.S + k];
+        T[pos * NL + l] = z;
+    }
+    ctx.sync();
+    tile_fft<L, NL, NL, NT, false, false, false>(ctx, T);
+    for (int idx = tid; idx < L * NL; idx += NT) {
+        const int pos = idx / NL, l = idx % NL, col = l % TW;
+        const int k = o.t * TW + col;
+        if (k >= g.S || k == 0) continue;
+        T[pos * NL + l] = cscale(T[pos * NL + l], gsc);
+    }
+    if (o.t == 0) {
+        const int njobs = o.self_mirror ? NR * (L / 2 + 1) : L;
+        for (int job = tid; job < njobs; job += NT) {
+            int ra, rb, pa, pb;
+            if (o.self_mirror) {
+                ra = job / (L / 2 + 1); rb = ra;
+                pa = job % (L / 2 + 1); pb = (L - pa) % L;
+            } else {
+                ra = 0; rb = 1; pa = job; pb = (L - job) % L;
+            }
+            const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
+            const float2 Za = T[ea], Zb = T[eb];
+            // A = (Z + conj Zm)/2, B = (Z - conj Zm)/(2i); S = (A+B)/2 g, D = (A-B)/2 g.
+            const float2 Aa = cscale(cadd(Za, cconj(Zb)), 0.5f);
+            const float2 Va = csub(Za, cconj(Zb));
+            const float2 Ba = make_float2(0.5f * Va.y, -0.5f * Va.x);
+            const float2 Ab = cscale(cadd(Zb, cconj(Za)), 0.5f);
+            const float2 Vb = csub(Zb, cconj(Za));
+            const float2 Bb = make_float2(0.5f * Vb.y, -0.5f * Vb.x);
+            T[ea] = cscale(cadd(Aa, Ba), 0.5f * gsc);
+            kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]] = cscale(csub(Aa, Ba), 0.5f * gsc);
+            if (eb != ea) {
+                T[eb] = cscale(cadd(Ab, Bb), 0.5f * gsc);
+                kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]] = cscale(csub(Ab, Bb), 0.5f * gsc);
+            }
+        }
+    }
+    ctx.sync();
+    for (int idx = tid; idx < L * NL; idx += NT) {
+        const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
+        const int k = o.t * TW + col;
+        if (k < g.S) kc[pos * PS + (long long)o.rows[row] * g.S + k] = T[pos * NL + l];
+    }
+}
+
+}  // namespace hyenand

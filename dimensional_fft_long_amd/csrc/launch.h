@@ -1,0 +1,32 @@
+// launch.h -- host-side launchers of the convolution and spectrum kernels.
+// Each launcher validates nothing (the C ABI does) and returns hipSuccess or
+// the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+
+namespace hyenand {
+
+// Optional event trace: event ev[count] is recorded on the stream before each
+// kernel launch (and once more at the end of a call) while count < n.
+struct LaunchTrace {
+    hipEvent_t* ev;
+    int n;
+    int count;
+    __host__ void mark(hipStream_t st)
+    {
+        if (count < n) hipEventRecord(ev[count], st);
+        ++count;
+    }
+};
+
+// Gate + forward transforms + product + inverse transforms for the channels
+// [a.c0, a.c0 + a.nch) of every batch entry.
+hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace = nullptr);
+
+// Kernel spectrum of all channels into a.khat (in place, no workspace).
+hipError_t launch_spectrum(const ConvArgs& a, hipStream_t stream);
+
+}  // namespace hyenand

@@ -1,0 +1,123 @@
+// plan.h -- geometry, layouts and tiling of the gated N-D FFT convolution.
+//
+// No device code.  Shared by the C ABI (validation, workspace sizing, launch
+// grids) and the kernel bodies (argument struct).
+//
+// Axis naming.  A d-dimensional grid [n_0 .. n_{d-1}] is handled as
+// (out, mid, in):  d = 3 -> (n_0, n_1, n_2);  d = 2 -> (n_0, 1, n_1);
+// d = 1 -> (1, 1, n_0).  Every present axis is zero-padded to N = 2n (the
+// non-circular boundary of the gist.science summary, "Methodology",
+// "Boundary handling"); absent axes keep N = 1.
+//
+// Frequency layout.  The innermost axis is real: its spectrum has N_in/2 + 1
+// bins, of which bins 0 and N_in/2 are real.  Rows are stored with S = N_in/2
+// complex slots; slot 0 packs (bin 0, bin N_in/2) as (re, im).  After the outer
+// axes are transformed, slot 0 of every line holds Z = A + iB with A, B the
+// (Hermitian) spectra of those two real planes; the product step separates
+// them with the mirror bin -k.
+//
+// Kernel spectrum layout (per channel, complex64):
+//   main[k_out][k_mid][k_in], k_in in [0, S):  Khat(k) * g for k_in >= 1;
+//        slot k_in = 0 holds Sv = (Khat(k, 0) + Khat(k, N_in/2)) / 2 * g
+//   dblk[k_out][k_mid]:                        Dv = (Khat(k, 0) - Khat(k, N_in/2)) / 2 * g
+// with g = 1 / (2 prod N) and Khat the true DFT of the wrap-placed kernel.
+// The product step for slot-0 lines is then W(k) = Z(k) Sv(k) + conj(Z(-k)) Dv(k).
+//
+// Workspace layout (per (b,c) pair, complex64): [n_out][N_mid][S].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hyenand {
+
+struct Geom {
+    int d;
+    int n_out, n_mid, n_in;
+    int N_out, N_mid, N_in;
+    int S;                 // N_in / 2
+    long long vox;         // voxels per (b,c): n_out * n_mid * n_in
+    long long wsp;         // workspace complex per pair: n_out * N_mid * S (0 for d = 1)
+    long long kmain;       // main block complex per channel: N_out * N_mid * S
+    long long ksz;         // kmain + N_out * N_mid
+    int ke_out, ke_mid, ke_in;  // kernel extents 2n-1 (1 for absent axes)
+};
+
+inline bool is_pow2(long long v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Returns false for an unsupported shape: d in {1,2,3}, every n a power of two in [2, 1024].
+inline bool make_geom(int d, const int64_t* dims, Geom* g)
+{
+    if (d < 1 || d > 3 || !dims) return false;
+    for (int a = 0; a < d; ++a)
+        if (dims[a] < 2 || dims[a] > 1024 || !is_pow2(dims[a])) return false;
+    g->d = d;
+    if (d == 3) { g->n_out = (int)dims[0]; g->n_mid = (int)dims[1]; g->n_in = (int)dims[2]; }
+    else if (d == 2) { g->n_out = (int)dims[0]; g->n_mid = 1; g->n_in = (int)dims[1]; }
+    else { g->n_out = 1; g->n_mid = 1; g->n_in = (int)dims[0]; }
+    g->N_out = d >= 2 ? 2 * g->n_out : 1;
+    g->N_mid = d >= 3 ? 2 * g->n_mid : 1;
+    g->N_in = 2 * g->n_in;
+    g->S = g->n_in;
+    g->vox = (long long)g->n_out * g->n_mid * g->n_in;
+    g->wsp = d >= 2 ? (long long)g->n_out * g->N_mid * g->S : 0;
+    g->kmain = (long long)g->N_out * g->N_mid * g->S;
+    g->ksz = g->kmain + (long long)g->N_out * g->N_mid;
+    g->ke_out = 2 * g->n_out - 1;
+    g->ke_mid = 2 * g->n_mid - 1;
+    g->ke_in = 2 * g->n_in - 1;
+    return true;
+}
+
+// Arguments shared by every kernel of one call (passed by value).
+struct ConvArgs {
+    const void* x;          // [B][C][vox], fp32 or bf16
+    void* y;                // same layout and dtype as x
+    const float* alpha;     // [C]
+    const float* beta;      // [C]
+    const float2* khat;     // [C][ksz] (kernel spectrum) -- written by the spectrum kernels
+    float2* ws;             // workspace, [pairs in chunk][wsp]
+    const float* K;         // spectrum input: [C][ke_out][ke_mid][ke_in] fp32
+    Geom g;
+    int B, C;
+    int c0;                 // first channel of this chunk
+    int nch;                // channels in this chunk (pairs = nch * B, channel-major)
+    int bf16;               // I/O dtype: 0 fp32, 1 bf16
+};
+
+// ---------------------------------------------------------------- tiling
+// Row kernels: NP line pairs of length L per workgroup, tile L x (NP+1).
+constexpr int row_np(int L) { return L >= 4096 ? 1 : (4096 / L < 2 ? 2 : 4096 / L); }
+// Column kernels along the middle axis / the out axis of a 2-D grid:
+// TW adjacent lines, tile L x TW (<= 64 KiB).
+constexpr int col_tw(int L) { return 8192 / L > 16 ? 16 : (8192 / L < 1 ? 1 : 8192 / L); }
+// Out-axis kernel of a 3-D grid: two mirrored k_mid rows x TW lines.
+constexpr int mul3_tw(int L) { return 4096 / L > 16 ? 16 : (4096 / L < 1 ? 1 : 4096 / L); }
+
+constexpr int kThreads = 256;
+
+// Recommended workspace: whole channels (all B pairs of a channel are processed
+// together), about 64 MiB so that it stays resident in the 256 MiB last-level
+// cache between passes, at least one channel.
+inline int chunk_channels(const Geom& g, int B, int C, size_t ws_bytes_available)
+{
+    const size_t per_ch = (size_t)B * (size_t)g.wsp * 8u;
+    if (per_ch == 0) return C;
+    size_t n = ws_bytes_available / per_ch;
+    if (n > (size_t)C) n = (size_t)C;
+    return (int)n;
+}
+
+inline size_t recommended_workspace(const Geom& g, int B, int C)
+{
+    const size_t per_ch = (size_t)B * (size_t)g.wsp * 8u;
+    if (per_ch == 0) return 0;
+    const size_t target = (size_t)64 << 20;
+    size_t n = target / per_ch;
+    if (n < 1) n = 1;
+    if (n > (size_t)C) n = (size_t)C;
+    return n * per_ch;
+}
+
+}  // namespace hyenand

@@ -1,0 +1,136 @@
+/*
+ * hyenand.h -- C ABI of the gated N-D FFT convolution (HyenaND hot path) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (explainer "Native multi-dimensional subquadratic operators via
+ * input-dependent long convolutions", section "HyenaND: native-space implicit
+ * global kernel", output equation for y[i]):
+ *
+ *     y[b,c,i] = sum_{j in G} phi_c(x[b,c,j]) * x[b,c,j] * K_c[i - j],   i in G,
+ *     phi_c(v) = 1 / (1 + exp(-(alpha_c * v + beta_c))),
+ *
+ * over a native d-dimensional grid G = [0,n_0) x ... x [0,n_{d-1}), with the
+ * non-circular boundary of the gist.science summary of the same paper
+ * ("Methodology", "Boundary handling": every axis zero-padded to 2 n before the
+ * FFT, the output cropped back to G).  The kernel is depthwise (one K_c per
+ * channel, shared by the batch).  The evaluation route is the FFT convolution
+ * path of the explainer's "Implementation" item: forward FFT, pointwise product
+ * with the kernel spectrum, inverse FFT.
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are device pointers owned by the caller (e.g. torch
+ *     tensors).  The library allocates nothing and keeps no state between calls.
+ *   - Layouts are row-major with the last grid axis contiguous:
+ *       x, y   [B][C][dims[0]]..[dims[d-1]]     dtype HYENAND_F32 or HYENAND_BF16
+ *       alpha, beta [C]                          fp32
+ *       K      [C][2*dims[0]-1]..[2*dims[d-1]-1] fp32, offset 0 of each axis at
+ *              index dims[a]-1 (K holds K_c[delta] for delta_a in [-(n_a-1), n_a-1])
+ *       K_hat  library-defined complex64 layout, size from
+ *              hyenand_kernel_spectrum_bytes (see below)
+ *   - Supported shapes: d in {1, 2, 3}; every dims[a] a power of two in
+ *     [2, 1024].  Other shapes return HYENAND_ERR_UNSUPPORTED.
+ *   - Pointers must be aligned to their element size (x, y: 4 bytes for fp32,
+ *     2 for bf16; alpha, beta, K: 4; K_hat, workspace: 8).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *     stream) and return once the kernels are enqueued.  Concurrent calls need
+ *     distinct workspaces and outputs.  y must not alias x, K_hat or workspace.
+ *   - Argument errors are detected before anything is enqueued.  A failed
+ *     launch returns HYENAND_ERR_HIP.  No exception or abort crosses the ABI.
+ *   - B == 0 or C == 0 is a valid empty call: HYENAND_OK, nothing enqueued.
+ */
+#ifndef HYENAND_H
+#define HYENAND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of every entry point. */
+#define HYENAND_OK 0
+#define HYENAND_ERR_INVALID_ARG 1 /* null pointer, negative count, bad dtype, misaligned pointer */
+#define HYENAND_ERR_UNSUPPORTED 2 /* shape outside the supported set                            */
+#define HYENAND_ERR_WORKSPACE 3   /* workspace smaller than the minimum for the call             */
+#define HYENAND_ERR_HIP 4         /* a kernel launch failed                                      */
+
+/* I/O element types of x and y (the FFT arithmetic is always fp32). */
+#define HYENAND_F32 0
+#define HYENAND_BF16 1
+
+/* Static description of a return code. */
+const char* hyenand_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int hyenand_version(void);
+
+/*
+ * Bytes of the kernel spectrum K_hat for C channels of a grid `dims`.  0 for an
+ * unsupported shape.  Layout, per channel (complex64 = two fp32, real first),
+ * with N_a = 2 n_a and (out, mid, in) = the grid axes (3-D), (axis 0, -, axis 1)
+ * (2-D) or (-, -, axis 0) (1-D), absent axes of length 1, S = N_in / 2:
+ *   main[k_out][k_mid][k_in], k_in in [0, S):  g * Khat(k)                     (k_in >= 1)
+ *                              k_in = 0:       g * (Khat(k,0) + Khat(k,S)) / 2
+ *   then dblk[k_out][k_mid]:                   g * (Khat(k,0) - Khat(k,S)) / 2
+ * where Khat is the DFT over the padded grid of the kernel placed at offset
+ * delta -> index delta mod N_a, and g = 1 / (2 * prod_a N_a).
+ */
+size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims);
+
+/*
+ * Kernel spectrum precompute (once per parameter set; not part of the timed
+ * forward): wrap-place each K_c into the zero-padded grid, real N-D FFT, fold
+ * the normalisation.  K: device fp32 [C][2n-1 ...]; K_hat: device, at least
+ * hyenand_kernel_spectrum_bytes(C, d, dims) bytes, fully overwritten.
+ * Errors: INVALID_ARG (null pointer with C > 0, C < 0, misalignment),
+ * UNSUPPORTED (shape), HIP (launch).
+ */
+int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream);
+
+/*
+ * Workspace bytes recommended for hyenand_fftconv_fwd: whole channels (all B
+ * batch entries of a channel are processed together) up to about 64 MiB.  The
+ * minimum accepted is one channel, B * n_0 * (prod of the middle padded axes) *
+ * S * 8 bytes (0 for d = 1); a larger workspace processes more channels per
+ * pass.  0 for d = 1, for an empty call, or for an unsupported shape.
+ */
+size_t hyenand_fftconv_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype);
+
+/* Minimum workspace bytes (one channel); 0 when none is needed. */
+size_t hyenand_fftconv_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype);
+
+/*
+ * Forward gated convolution:  y = crop(IFFT(FFT(pad(phi(x) * x)) * Khat)).
+ * x, y: device [B][C][dims], dtype `dtype` (bf16 is widened exactly to fp32 on
+ * load and rounded to nearest even on store).  phi_alpha, phi_beta: device fp32
+ * [C].  K_hat: from hyenand_kernel_spectrum for the same C, d, dims.
+ * workspace: device scratch of workspace_bytes >= the minimum (unused and may be
+ * NULL for d = 1); its contents on entry and exit are unspecified.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (too small), HIP.
+ */
+int hyenand_fftconv_fwd(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat, void* y,
+                        int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * hyenand_fftconv_fwd with a launch trace, for measurement.  Arguments and
+ * errors as hyenand_fftconv_fwd, plus: events[k] (caller-created hipEvent_t,
+ * cast to void*) is recorded on `stream` before the k-th kernel launch of the
+ * call and once more after the last launch, for k < n_events (extra launches
+ * are not recorded).  The kernels of one channel chunk run in this order:
+ * d = 1: conv1d;  d = 2: row_fwd, col_out, row_inv;  d = 3: row_fwd,
+ * col_mid_fwd, col_out, col_mid_inv, row_inv.  *n_launches (may be NULL)
+ * receives the number of launches.  n_events < 0, or events NULL with
+ * n_events > 0, is INVALID_ARG.
+ */
+int hyenand_fftconv_fwd_traced(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                               void* y, int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                               int* n_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYENAND_H */

@@ -1,0 +1,118 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+rejects bad arguments before anything is launched (no GPU needed: every call
+here returns from argument validation or a size query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hyenand.h")
+
+
+@pytest.fixture(scope="module")
+def H():
+    import dimensional_fft_long_amd as H
+
+    if not os.path.exists(H.LIB_PATH):
+        from dimensional_fft_long_amd import build
+
+        build.build()
+    H.get_lib()
+    return H
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(hyenand_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(H):
+    names = _declared()
+    assert "hyenand_fftconv_fwd" in names and "hyenand_kernel_spectrum" in names
+    lib = H.get_lib()
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    assert set(names) == set(H.EXPORTS)
+
+
+def _dims(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_status_strings_and_version(H):
+    lib = H.get_lib()
+    assert lib.hyenand_version() >= 100
+    seen = {lib.hyenand_status_string(c) for c in range(5)}
+    assert len(seen) == 5
+    assert lib.hyenand_status_string(99) == b"unknown status"
+
+
+def test_sizes(H):
+    lib = H.get_lib()
+    # 2-D 256x256, C=64: main N0*S = 512*256, dblk N0 = 512, complex64.
+    assert lib.hyenand_kernel_spectrum_bytes(64, 2, _dims(256, 256)) == 64 * (512 * 256 + 512) * 8
+    # 3-D 128^3: main 256*256*128, dblk 256*256.
+    assert lib.hyenand_kernel_spectrum_bytes(32, 3, _dims(128, 128, 128)) == 32 * (256 * 256 * 128 + 256 * 256) * 8
+    # 1-D 64: main 64, dblk 1.
+    assert lib.hyenand_kernel_spectrum_bytes(3, 1, _dims(64)) == 3 * 65 * 8
+    # Workspace per pair n0 * N_mid * S complex; minimum is one channel (all B).
+    assert lib.hyenand_fftconv_workspace_min_bytes(8, 64, 2, _dims(256, 256), 0) == 8 * 256 * 256 * 8
+    assert lib.hyenand_fftconv_workspace_min_bytes(1, 4, 3, _dims(512, 512, 512), 1) == 512 * 1024 * 512 * 8
+    rec = lib.hyenand_fftconv_workspace_bytes(8, 64, 2, _dims(256, 256), 0)
+    assert rec % (8 * 256 * 256 * 8) == 0 and 0 < rec <= 64 * 8 * 256 * 256 * 8
+    assert rec == lib.hyenand_fftconv_workspace_bytes(8, 64, 2, _dims(256, 256), 0)
+    assert lib.hyenand_fftconv_workspace_bytes(4, 4, 1, _dims(1024), 0) == 0  # 1-D needs none
+    # Unsupported shapes size to 0.
+    for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(2048)), (4, _dims(2, 2, 2, 2))]:
+        assert lib.hyenand_kernel_spectrum_bytes(2, d, dims) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+MISALIGNED = ctypes.c_void_p(0x10001)
+
+
+@pytest.mark.parametrize("d,dims,code", [
+    (0, (4,), 2), (4, (4, 4, 4, 4), 2), (2, (3, 4), 2), (2, (4, 1), 2), (2, (2048, 2), 2), (1, (6,), 2),
+])
+def test_fwd_rejects_shapes(H, d, dims, code):
+    lib = H.get_lib()
+    rc = lib.hyenand_fftconv_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, d, _dims(*dims), 0, FAKE, 1 << 30, None)
+    assert rc == code
+
+
+def test_fwd_rejects_arguments(H):
+    lib = H.get_lib()
+    dd = _dims(8, 8)
+    ws = 1 << 20
+    call = lambda x=FAKE, a=FAKE, b=FAKE, k=FAKE, y=FAKE, B=1, C=1, dt=0, w=FAKE, wb=ws: \
+        lib.hyenand_fftconv_fwd(x, a, b, k, y, B, C, 2, dd, dt, w, wb, None)
+    assert call(x=None) == 1
+    assert call(y=None) == 1
+    assert call(k=None) == 1
+    assert call(a=None) == 1
+    assert call(B=-1) == 1
+    assert call(C=-2) == 1
+    assert call(dt=7) == 1
+    assert call(x=MISALIGNED) == 1
+    assert call(k=MISALIGNED) == 1
+    assert call(w=None) == 3
+    assert call(wb=8 * 8 * 8 - 1) == 3          # one pair needs n0 * S * 8 = 512 bytes
+    assert call(w=MISALIGNED) == 1
+    # Empty calls succeed without touching anything.
+    assert call(x=None, y=None, B=0) == 0
+    assert call(x=None, y=None, C=0) == 0
+    # dims = NULL
+    assert lib.hyenand_fftconv_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 2, None, 0, FAKE, ws, None) == 1
+
+
+def test_spectrum_rejects_arguments(H):
+    lib = H.get_lib()
+    assert lib.hyenand_kernel_spectrum(FAKE, FAKE, -1, 2, _dims(8, 8), None) == 1
+    assert lib.hyenand_kernel_spectrum(None, FAKE, 2, 2, _dims(8, 8), None) == 1
+    assert lib.hyenand_kernel_spectrum(FAKE, None, 2, 2, _dims(8, 8), None) == 1
+    assert lib.hyenand_kernel_spectrum(FAKE, MISALIGNED, 2, 2, _dims(8, 8), None) == 1
+    assert lib.hyenand_kernel_spectrum(FAKE, FAKE, 2, 2, _dims(8, 12), None) == 2
+    assert lib.hyenand_kernel_spectrum(FAKE, FAKE, 2, 5, _dims(8, 8), None) == 2
+    assert lib.hyenand_kernel_spectrum(None, None, 0, 2, _dims(8, 8), None) == 0

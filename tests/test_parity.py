@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bar (element by element): max|y_gpu - y_ref| / max|y_ref| <= 1e-4 for fp32 I/O
+and <= 2e-2 for bf16 I/O (fp32 FFT arithmetic in both cases).  Small grids are
+compared in full against the direct sum; the five seeded workloads run at their
+full sizes in the launch configuration the benchmark uses and are compared on
+whole (b,c) slices against the FFT oracle and on sampled outputs against the
+direct sum.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def H():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dimensional_fft_long_amd as H
+
+    H.get_lib()
+    return H
+
+
+def _rel(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+def _gpu_run(H, w, workspace=None):
+    dev = torch.device("cuda:0")
+    x = w["x"].to(dev)
+    al = torch.from_numpy(w["alpha"]).to(dev)
+    be = torch.from_numpy(w["beta"]).to(dev)
+    kh = H.kernel_spectrum(w["K"].to(dev))
+    y = H.fftconv_fwd(x, al, be, kh, workspace=workspace)
+    torch.cuda.synchronize()
+    return y, kh
+
+
+SMALL = [
+    ((2,), 1, 1, "f32"), ((64,), 3, 3, "f32"), ((1024,), 2, 3, "f32"), ((256,), 1, 5, "bf16"),
+    ((2, 2), 1, 1, "f32"), ((4, 8), 2, 3, "f32"), ((8, 4), 1, 2, "f32"), ((32, 32), 1, 4, "f32"),
+    ((16, 64), 2, 2, "f32"), ((64, 16), 1, 3, "bf16"), ((2, 512), 1, 2, "f32"), ((512, 2), 1, 2, "f32"),
+    ((2, 2, 2), 1, 1, "f32"), ((4, 8, 16), 2, 3, "f32"), ((16, 4, 8), 1, 2, "f32"), ((8, 8, 8), 3, 1, "f32"),
+    ((2, 2, 64), 1, 2, "f32"), ((64, 2, 2), 1, 2, "f32"), ((8, 16, 8), 2, 3, "bf16"),
+]
+
+
+@pytest.mark.parametrize("dims,B,C,dtype", SMALL, ids=lambda v: str(v))
+def test_small_grids_match_direct_sum(H, dims, B, C, dtype):
+    w = synth.make(dims, B=B, C=C, dtype=dtype, seed=17 + sum(dims) + B + C)
+    y, _ = _gpu_run(H, w)
+    ref = oracle.direct(w["x"].float().numpy(), w["alpha"], w["beta"], w["K"].numpy())
+    got = y.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert _rel(got, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 1, 2), ((32, 64, 16), 1, 2)])
+def test_medium_grids_match_fft_oracle(H, dims, B, C):
+    w = synth.make(dims, B=B, C=C, dtype="f32", seed=5)
+    y, _ = _gpu_run(H, w)
+    ref = oracle.fftconv(w["x"].numpy(), w["alpha"], w["beta"], w["K"].numpy())
+    assert _rel(y.cpu().numpy(), ref) <= 1e-4
+
+
+@pytest.mark.parametrize("dims", [(16,), (64,), (8, 8), (4, 16), (32, 8), (4, 4, 4), (8, 4, 16), (2, 8, 4)])
+def test_kernel_spectrum_layout(H, dims):
+    """K_hat against the oracle's DFT of the wrap-placed kernel, in the library
+    layout: main slots k_in >= 1 hold g*Khat, slot 0 holds g*(Khat0 + KhatS)/2,
+    the trailing block g*(Khat0 - KhatS)/2, g = 1/(2 prod N)."""
+    C = 3
+    w = synth.make(dims, B=1, C=C, seed=3, dtype="f32")
+    kh = H.kernel_spectrum(w["K"].to("cuda")).cpu().numpy().reshape(C, -1)
+    d = len(dims)
+    no, nm, ni = (1, 1, dims[0]) if d == 1 else ((dims[0], 1, dims[1]) if d == 2 else dims)
+    No, Nm, Ni = (2 * no if d >= 2 else 1), (2 * nm if d == 3 else 1), 2 * ni
+    S = ni
+    full = oracle.kernel_spectrum(w["K"].numpy(), dims).reshape(C, No, Nm, Ni)
+    g = 1.0 / (2 * No * Nm * Ni)
+    main = kh[:, :No * Nm * S].reshape(C, No, Nm, S)
+    dblk = kh[:, No * Nm * S:].reshape(C, No, Nm)
+    scale = np.abs(full).max() * g
+    assert np.abs(main[..., 1:] - g * full[..., 1:S]).max() <= 1e-5 * scale
+    assert np.abs(main[..., 0] - g * (full[..., 0] + full[..., S]) / 2).max() <= 1e-5 * scale
+    assert np.abs(dblk - g * (full[..., 0] - full[..., S]) / 2).max() <= 1e-5 * scale
+
+
+def test_chunked_workspace_is_bitwise_identical(H):
+    dims, B, C = (64, 64), 3, 5
+    w = synth.make(dims, B=B, C=C, seed=9)
+    y_full, _ = _gpu_run(H, w)
+    small = torch.empty(H.workspace_bytes(B, C, dims, minimum=True), dtype=torch.uint8, device="cuda")
+    y_one, _ = _gpu_run(H, w, workspace=small)
+    assert torch.equal(y_full, y_one)
+
+
+def test_deterministic_and_workspace_poison_free(H):
+    dims, B, C = (32, 16, 8), 2, 3
+    w = synth.make(dims, B=B, C=C, seed=10)
+    dev = "cuda"
+    x, al, be = w["x"].to(dev), torch.from_numpy(w["alpha"]).to(dev), torch.from_numpy(w["beta"]).to(dev)
+    kh = H.kernel_spectrum(w["K"].to(dev))
+    nb = H.workspace_bytes(B, C, dims)
+    ws = torch.empty(nb // 4, dtype=torch.float32, device=dev)
+    outs = []
+    for fill in (0.0, float("nan"), float("inf"), 0.0):
+        ws.fill_(fill)
+        outs.append(H.fftconv_fwd(x, al, be, kh, workspace=ws.view(torch.uint8)).clone())
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_runs_on_a_side_stream(H):
+    dims, B, C = (32, 32), 2, 2
+    w = synth.make(dims, B=B, C=C, seed=12)
+    y0, _ = _gpu_run(H, w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y1, _ = _gpu_run(H, w)
+    s.synchronize()
+    assert torch.equal(y0, y1)
+
+
+def test_empty_batch(H):
+    x = torch.empty((0, 3, 8, 8), device="cuda")
+    al = torch.zeros(3, device="cuda")
+    kh = H.kernel_spectrum(torch.zeros((3, 15, 15), device="cuda"))
+    y = H.fftconv_fwd(x, al, al, kh)
+    assert y.shape == x.shape
+
+
+# ------------------------------------------------------------ full workloads
+
+def _full_workload(H, wl, o2_pairs, sample_pairs, per_pair):
+    dev = torch.device("cuda:0")
+    p = synth.draw_params(wl.dims, wl.C, wl.seed)
+    x_t = synth.draw_x(p.rng, wl.B, wl.C, wl.dims, wl.dtype)
+    K = synth.kernel_channels(wl.dims, p, device=dev)            # fp32 on the device
+    kh = H.kernel_spectrum(K)
+    x = x_t.to(dev)
+    al, be = torch.from_numpy(p.alpha).to(dev), torch.from_numpy(p.beta).to(dev)
+    y = H.fftconv_fwd(x, al, be, kh)
+    torch.cuda.synchronize()
+    del kh
+    K_h = K.cpu().numpy()
+    del K
+    x_h = x_t.float().numpy()
+    y_h = y.float().cpu().numpy().reshape((wl.B * wl.C,) + wl.dims)
+    ys = y_h.reshape((wl.B, wl.C) + wl.dims)
+    errs = []
+    scale = 0.0
+    if o2_pairs:
+        ref = oracle.fftconv(x_h, p.alpha, p.beta, K_h, pairs=o2_pairs)
+        scale = float(np.max(np.abs(ref)))
+        errs.append(float(np.max(np.abs(y_h[o2_pairs] - ref))))
+    pts = synth.sample_points(wl.dims, wl.B, wl.C, sample_pairs, per_pair, seed=wl.seed)
+    ref_pts = oracle.direct_points(x_h, p.alpha, p.beta, K_h, pts)
+    got_pts = np.array([ys[tuple(r)] for r in pts])
+    scale = max(scale, float(np.max(np.abs(ref_pts))))
+    errs.append(float(np.max(np.abs(got_pts - ref_pts))))
+    assert np.all(np.isfinite(y_h))
+    return max(errs) / scale
+
+
+def test_workload_2d_32(H):
+    wl = synth.WORKLOADS[0]
+    w = synth.make(wl)
+    y, _ = _gpu_run(H, w)
+    ref = oracle.direct(w["x"].numpy(), w["alpha"], w["beta"], w["K"].numpy())
+    assert _rel(y.cpu().numpy(), ref) <= TOL[wl.dtype]
+
+
+@pytest.mark.timeout(300)
+def test_workload_2d_256(H):
+    wl = synth.WORKLOADS[1]
+    P = wl.B * wl.C
+    err = _full_workload(H, wl, o2_pairs=[0, 77, P - 1], sample_pairs=[(0, 5), (7, 63), (3, 31)], per_pair=24)
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.timeout(300)
+def test_workload_2d_1024_bf16(H):
+    wl = synth.WORKLOADS[2]
+    P = wl.B * wl.C
+    err = _full_workload(H, wl, o2_pairs=[0, P - 1], sample_pairs=[(0, 64), (1, 127)], per_pair=8)
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.timeout(300)
+def test_workload_3d_128(H):
+    wl = synth.WORKLOADS[3]
+    err = _full_workload(H, wl, o2_pairs=[0], sample_pairs=[(0, 13), (0, 31)], per_pair=16)
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.timeout(600)
+def test_workload_3d_512_bf16(H):
+    wl = synth.WORKLOADS[4]
+    err = _full_workload(H, wl, o2_pairs=[], sample_pairs=[(0, 0), (0, 3)], per_pair=6)
+    assert err <= TOL[wl.dtype]
