@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the gated N-D FFT convolution forward on one MI355X.
+
+One step = one ``hyenand_fftconv_fwd`` over the whole synthetic batch (gate,
+forward transforms, product with the precomputed kernel spectrum, inverse
+transforms, crop, store), inputs resident in HBM.  Default workload: the 256x256
+image, B=8, C=64, fp32 I/O.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gvoxel·channels/s of gated N-D FFT conv fwd; % of HBM roofline (1 GPU)"
+UNIT = "Gvoxel·channels/s"
+HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+# fp32 vector peak without packed-FP32 instructions (the build disables them):
+# 256 CUs x 64 lanes x 2 flop (FMA) x 2.4 GHz.
+ALU_PEAK = 256 * 64 * 2 * 2.4e9
+DEFAULT_WORKLOAD = "2d_256x256_b8_c64_f32"
+
+
+def _geom(dims):
+    d = len(dims)
+    no, nm, ni = (1, 1, dims[0]) if d == 1 else ((dims[0], 1, dims[1]) if d == 2 else tuple(dims))
+    No, Nm, Ni = (2 * no if d >= 2 else 1), (2 * nm if d == 3 else 1), 2 * ni
+    return dict(no=no, nm=nm, ni=ni, No=No, Nm=Nm, Ni=Ni, S=ni, vox=no * nm * ni, wsp=no * Nm * ni if d >= 2 else 0,
+                ksz=No * Nm * ni + No * Nm)
+
+
+def _fft_flops(N, lines, prune):
+    """Nominal flops of `lines` complex length-N transforms: 5 N log2 N, less
+    2N for each pruned half (zero half input, or half output unused)."""
+    return lines * (5.0 * N * math.log2(N) - 2.0 * N * prune)
+
+
+def pass_model(name, dims, B_chunk_pairs, nch, es):
+    """(algorithmic bytes, nominal flops) of one launch of pass `name` over a
+    chunk of `B_chunk_pairs` (b,c) pairs covering `nch` channels."""
+    g = _geom(dims)
+    P = B_chunk_pairs
+    rows = g["no"] * g["nm"]
+    if name == "row_fwd":
+        by = P * g["vox"] * es + P * rows * g["S"] * 8
+        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 2 * 2 + P * g["vox"] * 5
+    elif name == "row_inv":
+        by = P * rows * g["S"] * 8 + P * g["vox"] * es
+        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 4
+    elif name == "col_mid_fwd" or name == "col_mid_inv":
+        by = P * (rows * g["S"] + g["no"] * g["Nm"] * g["S"]) * 8
+        fl = _fft_flops(g["Nm"], P * g["no"] * g["S"], 1)
+    elif name == "col_out":
+        by = 2 * P * g["wsp"] * 8 + nch * g["ksz"] * 8
+        lines = P * g["Nm"] * g["S"]
+        fl = 2 * _fft_flops(g["No"], lines, 1) + lines * g["No"] * 6
+    elif name == "conv1d":
+        by = 2 * P * g["vox"] * es + nch * g["ksz"] * 8
+        fl = 2 * _fft_flops(g["Ni"], P / 2, 1) + P * g["S"] * (6 + 4) + P * g["vox"] * 5
+    else:
+        raise KeyError(name)
+    return by, fl
+
+
+def _src_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dimensional_fft_long_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile(kernel_name):
+    """HBM bytes per launch of `kernel_name` from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("source_hash") != _src_hash():
+        return None
+    return rec.get("kernels", {}).get(kernel_name, {}).get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, max_seconds=20.0):
+    """The fp64 oracle (O2 FFT route, as written) on a bounded sample of the
+    same workload: consecutive (b,c) pairs until about `max_seconds` pass."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    p = synth.draw_params(wl.dims, wl.C, wl.seed)
+    x = synth.draw_x(p.rng, wl.B, wl.C, wl.dims, wl.dtype).float().numpy()
+    K = synth.kernel_channels(wl.dims, p).numpy()
+    done = 0
+    t_total = 0.0
+    batch = 1
+    while t_total < max_seconds and done < wl.B * wl.C:
+        pairs = np.arange(done, min(done + batch, wl.B * wl.C))
+        t0 = time.perf_counter()
+        oracle.fftconv(x, p.alpha, p.beta, K, pairs=pairs)
+        t_total += time.perf_counter() - t0
+        done += len(pairs)
+        batch = min(batch * 2, 64)
+    vox = done * wl.voxels
+    return {"value": vox / t_total / 1e9, "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {wl.B * wl.C} (b,c) pairs of {wl.name}, fp64 O2 (radix-2 FFT) route, "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "channel with no communication, but no multi-GPU run is part of it.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dimensional_fft_long_amd as H
+    import synth
+
+    wl = {w.name: w for w in synth.WORKLOADS}[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    es = 2 if wl.dtype == "bf16" else 4
+
+    # Inputs of record: seeded parameters and x on the host, kernel evaluated on the device.
+    p = synth.draw_params(wl.dims, wl.C, wl.seed)
+    x = synth.draw_x(p.rng, wl.B, wl.C, wl.dims, wl.dtype).to(dev)
+    K = synth.kernel_channels(wl.dims, p, device=dev)
+    al = torch.from_numpy(p.alpha).to(dev)
+    be = torch.from_numpy(p.beta).to(dev)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    kh = H.kernel_spectrum(K)
+    s1.record()
+    torch.cuda.synchronize()
+    spectrum_ms = s0.elapsed_time(s1)
+    del K
+    y = torch.empty_like(x)
+    ws_bytes = H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
+    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+
+    # Launch count per step, then one event slot before each launch and one at the end.
+    probe = [torch.cuda.Event(enable_timing=True) for _ in range(1)]
+    n_launch = H.fftconv_fwd_traced(x, al, be, kh, y, ws, probe)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(args.steps):
+        H.fftconv_fwd_traced(x, al, be, kh, y, ws, evs[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    names = H.PASS_NAMES[wl.d]
+    per_pass = {nm: [] for nm in names}
+    step_ms = []
+    for k in range(args.steps):
+        e = evs[k]
+        step_ms.append(e[0].elapsed_time(e[-1]))
+        for j in range(n_launch):
+            per_pass[names[j % len(names)]].append(e[j].elapsed_time(e[j + 1]))
+    dominant = max(per_pass, key=lambda nm: sum(per_pass[nm]))
+    dom_avg_s = sum(per_pass[dominant]) / len(per_pass[dominant]) / 1e3
+
+    chunks = n_launch // len(names)
+    nch = math.ceil(wl.C / chunks)
+    by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch, es)
+    hbm = {"bound": "hbm", "achieved": by / dom_avg_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    alu = {"bound": "alu", "achieved": fl / dom_avg_s / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s"}
+    for r in (hbm, alu):
+        r["frac"] = r["achieved"] / r["peak"]
+    roof = hbm if hbm["frac"] >= alu["frac"] else alu
+    kernel_symbol = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_col_out",
+                     "col_mid_fwd": "k_col_mid", "col_mid_inv": "k_col_mid", "conv1d": "k_conv1d"}[dominant]
+    roof.update({"kernel": f"{kernel_symbol} ({dominant})", "avg_us": dom_avg_s * 1e6,
+                 "traffic": _traffic_from_profile(dominant)})
+    roof["other_bound"] = {k: v for k, v in (alu if roof is hbm else hbm).items()}
+
+    g = _geom(wl.dims)
+    voxch = wl.B * wl.C * wl.voxels
+    value = voxch / (ms_per_step / 1e3) / 1e9
+    bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
+                   "C": wl.C, "io_dtype": "bf16" if wl.dtype == "bf16" else "fp32", "launches_per_step": n_launch},
+        "hbm_roofline_frac_of_metric": bytes_min / (ms_per_step / 1e3) / HBM_PEAK,
+        "bytes_min": bytes_min,
+        "step_ms_median": sorted(step_ms)[len(step_ms) // 2],
+        "per_kernel_us": {nm: 1e3 * sum(v) / len(v) for nm, v in per_pass.items()},
+        "spectrum_ms": spectrum_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -179,6 +179,10 @@ def fftconv_fwd_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None)
     before each kernel launch and after the last; returns the launch count."""
     B, C = int(x.shape[0]), int(x.shape[1])
     dims = tuple(int(v) for v in x.shape[2:])
+    st = torch.cuda.current_stream() if stream is None else stream
+    for e in events:
+        if e.cuda_event == 0:     # torch creates the HIP event on its first record
+            e.record(st)
     arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     n = ctypes.c_int(0)
     ws_bytes = workspace.numel() * workspace.element_size()

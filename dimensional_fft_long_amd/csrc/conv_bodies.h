@@ -33,10 +33,10 @@
 namespace hyenand {
 
 // ------------------------------------------------------------- element I/O
-__host__ __device__ inline float bf16_to_f32(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+__host__ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
 
 // Round to nearest even; NaN stays NaN.
-__host__ __device__ inline uint16_t f32_to_bf16(float f)
+__host__ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
     uint32_t u = __builtin_bit_cast(uint32_t, f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
@@ -44,52 +44,82 @@ __host__ __device__ inline uint16_t f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
-__host__ __device__ inline float load_x(const ConvArgs& a, long long i)
+// I/O element type is a template parameter so that element loops carry no
+// runtime branch (loads can then be issued back to back).
+template <bool BF16>
+__host__ __device__ __forceinline__ float load_x(const ConvArgs& a, long long i)
 {
-    return a.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[i]) : static_cast<const float*>(a.x)[i];
+    if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(a.x)[i]);
+    else return static_cast<const float*>(a.x)[i];
 }
 
-__host__ __device__ inline void store_y(const ConvArgs& a, long long i, float v)
+template <bool BF16>
+__host__ __device__ __forceinline__ void store_y(const ConvArgs& a, long long i, float v)
 {
-    if (a.bf16) static_cast<uint16_t*>(a.y)[i] = f32_to_bf16(v);
+    if constexpr (BF16) static_cast<uint16_t*>(a.y)[i] = f32_to_bf16(v);
     else static_cast<float*>(a.y)[i] = v;
 }
 
-// The content gate: u = phi(x) x with phi(x) = 1 / (1 + exp(-(alpha x + beta))).
-__host__ __device__ inline float gate(float x, float al, float be)
-{
-    return x / (1.0f + expf(-(al * x + be)));
-}
-
 // Workspace offset of row r (r = j_out * n_mid + j_mid) inside one pair.
-__host__ __device__ inline long long row_ws(const Geom& g, int r)
+__host__ __device__ __forceinline__ long long row_ws(const Geom& g, int r)
 {
     return ((long long)(r / g.n_mid) * g.N_mid + (r % g.n_mid)) * g.S;
 }
 
-// --------------------------------------------------------------- row_fwd
-// NP line pairs per workgroup; line pair h = (pair slot q, rows 2i and 2i+1).
-template <int L, class Ctx>
-__host__ __device__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+// Line pair h of a row workgroup (d >= 2): pair slot q = h / hp (channel-major
+// in the chunk: c = c0 + q / B, b = q % B) and rows r = 2 (h % hp), r + 1.
+template <int NP, int NT, class Ctx>
+__host__ __device__ __forceinline__ void row_meta(const Ctx& ctx, int bid, const ConvArgs& a, RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, n = L / 2, S = L / 2;
     const Geom& g = a.g;
     const int hp = g.n_out * g.n_mid / 2;
     const int H = a.nch * a.B * hp;
-    const int h0 = bid * NP;
-    const int tid = ctx.tid();
-    for (int idx = tid; idx < NP * n; idx += NT) {
-        const int lp = idx / n, m = idx % n;
-        const int h = h0 + lp;
-        float2 z = make_float2(0.f, 0.f);
-        if (h < H) {
+    for (int lp = ctx.tid(); lp < NP; lp += NT) {
+        const int h = bid * NP + lp;
+        RowMeta m{};
+        m.valid = h < H;
+        if (m.valid) {
             const int q = h / hp, r = (h % hp) * 2;
             const int c = a.c0 + q / a.B, b = q % a.B;
-            const long long xo = ((long long)b * a.C + c) * g.vox + (long long)r * n + m;
-            const float al = a.alpha[c], be = a.beta[c];
-            z.x = gate(load_x(a, xo), al, be);
-            z.y = gate(load_x(a, xo + n), al, be);
+            m.o0 = ((long long)b * a.C + c) * g.vox + (long long)r * g.n_in;
+            m.o1 = m.o0 + g.n_in;
+            m.w0 = (long long)q * g.wsp + row_ws(g, r);
+            m.w1 = (long long)q * g.wsp + row_ws(g, r + 1);
+            m.al0 = m.al1 = a.alpha[c];
+            m.be0 = m.be1 = a.beta[c];
+            m.valid1 = 1;
         }
+        M[lp] = m;
+    }
+}
+
+// --------------------------------------------------------------- row_fwd
+// NP line pairs per workgroup; gate, FFT of u_a + i u_b, separation.  Element
+// loops run ITER = NP*n/NT iterations per thread; every load of a loop is
+// issued before the first use (invalid tail lines read offset 0 and are zeroed).
+template <int L, bool BF16, class Ctx>
+__host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
+                                                      RowMeta* M)
+{
+    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), n = L / 2, S = L / 2;
+    constexpr int ITER = NP * n / NT;
+    static_assert(NP * n % NT == 0, "whole element loops");
+    const int tid = ctx.tid();
+    row_meta<NP, NT>(ctx, bid, a, M);
+    ctx.sync();
+    float xa[ITER], xb[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / n, m = idx % n;
+        xa[i] = load_x<BF16>(a, M[lp].o0 + m);
+        xb[i] = load_x<BF16>(a, M[lp].o1 + m);
+    }
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / n, m = idx % n;
+        const RowMeta& md = M[lp];
+        float2 z = make_float2(ctx.gate(xa[i], md.al0, md.be0), ctx.gate(xb[i], md.al1, md.be1));
+        if (!md.valid) z = make_float2(0.f, 0.f);
         T[m * LP + lp] = z;
     }
     ctx.sync();
@@ -97,122 +127,139 @@ __host__ __device__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a
     // Separate the two rows: with Z = FFT(u_a + i u_b),
     //   2 U_a[k] = Z[k] + conj Z[L-k],   2 U_b[k] = -i (Z[k] - conj Z[L-k]).
     // The factor 2 is folded into the kernel spectrum.
-    for (int idx = tid; idx < NP * S; idx += NT) {
-        const int lp = idx / S, k = idx % S;
-        const int h = h0 + lp;
-        if (h >= H) continue;
-        const int q = h / hp, r = (h % hp) * 2;
-        float2* wa = a.ws + (long long)q * g.wsp + row_ws(g, r);
-        float2* wb = a.ws + (long long)q * g.wsp + row_ws(g, r + 1);
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / S, k = idx % S;
+        const RowMeta& md = M[lp];
         const float2 Z = T[k * LP + lp];
+        const float2 Zm = T[(k == 0 ? S : L - k) * LP + lp];
         float2 oa, ob;
         if (k == 0) {
-            const float2 ZN = T[S * LP + lp];
-            oa = make_float2(2.f * Z.x, 2.f * ZN.x);
-            ob = make_float2(2.f * Z.y, 2.f * ZN.y);
+            oa = make_float2(2.f * Z.x, 2.f * Zm.x);
+            ob = make_float2(2.f * Z.y, 2.f * Zm.y);
         } else {
-            const float2 Zm = T[(L - k) * LP + lp];
             oa = make_float2(Z.x + Zm.x, Z.y - Zm.y);
             ob = make_float2(Z.y + Zm.y, Zm.x - Z.x);
         }
-        wa[k] = oa;
-        wb[k] = ob;
+        if (md.valid) {
+            a.ws[md.w0 + k] = oa;
+            a.ws[md.w1 + k] = ob;
+        }
     }
 }
 
 // --------------------------------------------------------------- row_inv
-template <int L, class Ctx>
-__host__ __device__ void row_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+template <int L, bool BF16, class Ctx>
+__host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
+                                                      RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, n = L / 2, S = L / 2;
-    const Geom& g = a.g;
-    const int hp = g.n_out * g.n_mid / 2;
-    const int H = a.nch * a.B * hp;
-    const int h0 = bid * NP;
+    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), n = L / 2, S = L / 2;
+    constexpr int ITER = NP * S / NT;
+    static_assert(NP * S % NT == 0, "whole element loops");
     const int tid = ctx.tid();
+    row_meta<NP, NT>(ctx, bid, a, M);
+    ctx.sync();
     // Rebuild Z = Y_a + i Y_b over the full length from the two half spectra
     // (Hermitian extension), slot 0 holding (bin 0, bin L/2).
-    for (int idx = tid; idx < NP * S; idx += NT) {
-        const int lp = idx / S, k = idx % S;
-        const int h = h0 + lp;
-        float2 ya = make_float2(0.f, 0.f), yb = ya;
-        if (h < H) {
-            const int q = h / hp, r = (h % hp) * 2;
-            ya = a.ws[(long long)q * g.wsp + row_ws(g, r) + k];
-            yb = a.ws[(long long)q * g.wsp + row_ws(g, r + 1) + k];
-        }
+    float2 ya[ITER], yb[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / S, k = idx % S;
+        ya[i] = a.ws[M[lp].w0 + k];
+        yb[i] = a.ws[M[lp].w1 + k];
+    }
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / S, k = idx % S;
         if (k == 0) {
-            T[lp] = make_float2(ya.x, yb.x);
-            T[S * LP + lp] = make_float2(ya.y, yb.y);
+            T[lp] = make_float2(ya[i].x, yb[i].x);
+            T[S * LP + lp] = make_float2(ya[i].y, yb[i].y);
         } else {
-            T[k * LP + lp] = make_float2(ya.x - yb.y, ya.y + yb.x);
-            T[(L - k) * LP + lp] = make_float2(ya.x + yb.y, yb.x - ya.y);
+            T[k * LP + lp] = make_float2(ya[i].x - yb[i].y, ya[i].y + yb[i].x);
+            T[(L - k) * LP + lp] = make_float2(ya[i].x + yb[i].y, yb[i].x - ya[i].y);
         }
     }
     ctx.sync();
     tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
-    for (int idx = tid; idx < NP * n; idx += NT) {
-        const int lp = idx / n, m = idx % n;
-        const int h = h0 + lp;
-        if (h >= H) continue;
-        const int q = h / hp, r = (h % hp) * 2;
-        const int c = a.c0 + q / a.B, b = q % a.B;
-        const long long yo = ((long long)b * a.C + c) * g.vox + (long long)r * n + m;
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / n, m = idx % n;
+        const RowMeta& md = M[lp];
         const float2 z = T[m * LP + lp];
-        store_y(a, yo, z.x);
-        store_y(a, yo + n, z.y);
+        if (md.valid) {
+            store_y<BF16>(a, md.o0 + m, z.x);
+            store_y<BF16>(a, md.o1 + m, z.y);
+        }
     }
 }
 
 // --------------------------------------------------------------- col_mid
 // FFT along the middle axis of a 3-D grid, TW adjacent lines per workgroup.
 // Forward: n_mid non-zero inputs -> N_mid outputs.  Inverse: N_mid inputs ->
-// the n_mid outputs that are kept.
+// the n_mid outputs that are kept.  The first pass reads the workspace and the
+// last pass writes it back (in place; every read precedes a barrier that
+// precedes every write).
 template <int L, bool INV, class Ctx>
-__host__ __device__ void col_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+__host__ __device__ __forceinline__ void col_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int TW = col_tw(L), NT = kThreads, n = L / 2;
+    constexpr int TW = col_tw(L), NT = col_nt(L);
     const Geom& g = a.g;
     const int lines = g.n_out * g.S;
     const int tpp = (lines + TW - 1) / TW;
     const int q = bid / tpp, lam0 = (bid % tpp) * TW;
     float2* base = a.ws + (long long)q * g.wsp;
-    const int tid = ctx.tid();
-    constexpr int PIN = INV ? L : n;
-    for (int idx = tid; idx < PIN * TW; idx += NT) {
-        const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
-        float2 z = make_float2(0.f, 0.f);
-        if (lam < lines) z = base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S];
-        T[pos * TW + l] = z;
-    }
-    ctx.sync();
-    tile_fft<L, TW, TW, NT, INV, !INV, INV>(ctx, T);
-    constexpr int POUT = INV ? n : L;
-    for (int idx = tid; idx < POUT * TW; idx += NT) {
-        const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
-        if (lam < lines) base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S] = T[pos * TW + l];
-    }
+    const int sl = ilog2(g.S);
+    auto off = [&](int pos, int l) -> long long {
+        const int lam = lam0 + l;
+        return ((long long)(lam >> sl) * g.N_mid + pos) * g.S + (lam & (g.S - 1));
+    };
+    auto ld = [&](int pos, int l) -> float2 {
+        const bool ok = lam0 + l < lines;
+        const float2 v = base[ok ? off(pos, l) : 0];
+        return ok ? v : make_float2(0.f, 0.f);
+    };
+    auto st = [&](int pos, int l, const float2& v) {
+        if (lam0 + l < lines) base[off(pos, l)] = v;
+    };
+    if constexpr (INV) inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st);
+    else fwd_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st);
 }
 
 // Rows of the middle axis handled together by one out-axis workgroup: with
 // NR = 2 the rows {rp, N_mid - rp} (and {0, N_mid/2} for rp = 0), so that the
 // slot-0 line of k_mid and its mirror -k_mid are in the same tile.
+//
+// Workgroup order: the B workgroups of one (channel, tile) read the same kernel
+// spectrum tile.  Consecutive workgroup ids are dispatched round-robin over the
+// eight XCDs, so those B workgroups get ids u0 + 8 b (same id mod 8, hence the
+// same XCD and L2) whenever the tile index u lies in a full group of eight.
 struct OutTile {
-    int c_local, t, rows[2];
+    int c_local, t, b, rows[2];
     bool self_mirror;
 };
 
 template <int NR, int TW>
-__host__ __device__ inline OutTile out_tile(const Geom& g, int bid)
+__host__ __device__ __forceinline__ OutTile out_tile(const Geom& g, int B, int nch, int bid)
 {
     OutTile o;
     const int ct = (g.S + TW - 1) / TW;
     const int nrp = NR == 1 ? 1 : g.N_mid / 2;
     const int tpc = nrp * ct;
-    o.c_local = bid / tpc;
-    const int rem = bid % tpc;
-    const int rp = rem / ct;
-    o.t = rem % ct;
+    const int U = nch * tpc, U8 = U & ~7;
+    int u;
+    if (bid < U8 * B) {
+        const int grp = bid / (8 * B), rem = bid % (8 * B);
+        o.b = rem / 8;
+        u = grp * 8 + rem % 8;
+    } else {
+        const int rem = bid - U8 * B;
+        u = U8 + rem / B;
+        o.b = rem % B;
+    }
+    o.c_local = u / tpc;
+    const int r2 = u % tpc;
+    const int rp = r2 / ct;
+    o.t = r2 % ct;
     if (NR == 1) {
         o.rows[0] = 0; o.rows[1] = 0; o.self_mirror = true;
     } else {
@@ -223,108 +270,130 @@ __host__ __device__ inline OutTile out_tile(const Geom& g, int bid)
     return o;
 }
 
-// Product of the out-axis spectra with the kernel spectrum, in place in the
-// tile (element (pos, row*TW + col) at pos*NL + row*TW + col).  Lines with
-// k_in = 0 carry Z = A + iB (packed bins 0 and N_in/2) and need the mirror
-// element (-k_out, -k_mid):  W = Z Sv + conj(Z(-k)) Dv.
-template <int L, int NR, int TW, class Ctx>
-__host__ __device__ inline void out_product(const Ctx& ctx, const Geom& g, const OutTile& o,
-                                            const float2* kc, float2* T)
+// Product for the lines with k_in = 0 (present in tile t = 0, column 0 of each
+// row), in place in T (element (pos, row*TW) at pos*NL + row*TW).  Those lines
+// carry Z = A + iB (packed bins 0 and N_in/2) and need the mirror element
+// (-k_out, -k_mid):  W = Z Sv + conj(Z(-k)) Dv.  Each job owns an element and
+// its mirror, so no two threads touch the same element.
+template <int L, int NR, int TW, int NT, class Ctx>
+__host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const Geom& g, const OutTile& o,
+                                                           const float2* kc, float2* T)
 {
-    constexpr int NL = NR * TW, NT = kThreads;
+    constexpr int NL = NR * TW;
     const long long PS = (long long)g.N_mid * g.S;
-    const int tid = ctx.tid();
-    for (int idx = tid; idx < L * NL; idx += NT) {
-        const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
-        const int k = o.t * TW + col;
-        if (k >= g.S || k == 0) continue;
-        T[pos * NL + l] = cmul(T[pos * NL + l], kc[pos * PS + (long long)o.rows[row] * g.S + k]);
-    }
-    if (o.t == 0) {
-        const int njobs = o.self_mirror ? NR * (L / 2 + 1) : L;
-        for (int job = tid; job < njobs; job += NT) {
-            int ra, rb, pa, pb;
-            if (o.self_mirror) {
-                ra = job / (L / 2 + 1); rb = ra;
-                pa = job % (L / 2 + 1); pb = (L - pa) % L;
-            } else {
-                ra = 0; rb = 1; pa = job; pb = (L - job) % L;
-            }
-            const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
-            const float2 Za = T[ea], Zb = T[eb];
-            const float2 Sa = kc[pa * PS + (long long)o.rows[ra] * g.S];
-            const float2 Sb = kc[pb * PS + (long long)o.rows[rb] * g.S];
-            const float2 Da = kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]];
-            const float2 Db = kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]];
-            const float2 Wa = cadd(cmul(Za, Sa), cmul(cconj(Zb), Da));
-            const float2 Wb = cadd(cmul(Zb, Sb), cmul(cconj(Za), Db));
-            T[ea] = Wa;
-            if (eb != ea) T[eb] = Wb;
+    const int njobs = o.self_mirror ? NR * (L / 2 + 1) : L;
+    for (int job = ctx.tid(); job < njobs; job += NT) {
+        int ra, rb, pa, pb;
+        if (o.self_mirror) {
+            ra = job / (L / 2 + 1); rb = ra;
+            pa = job % (L / 2 + 1); pb = (L - pa) % L;
+        } else {
+            ra = 0; rb = 1; pa = job; pb = (L - job) % L;
         }
+        const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
+        const float2 Za = T[ea], Zb = T[eb];
+        const float2 Sa = kc[pa * PS + (long long)o.rows[ra] * g.S];
+        const float2 Sb = kc[pb * PS + (long long)o.rows[rb] * g.S];
+        const float2 Da = kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]];
+        const float2 Db = kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]];
+        const float2 Wa = cadd(cmul(Za, Sa), cmul(cconj(Zb), Da));
+        const float2 Wb = cadd(cmul(Zb, Sb), cmul(cconj(Za), Db));
+        T[ea] = Wa;
+        if (eb != ea) T[eb] = Wb;
     }
 }
 
 // --------------------------------------------------------------- col_out
-// Out axis: forward FFT (n_out inputs), product, inverse FFT (n_out kept), for
-// every batch entry of the channel; the kernel spectrum tile is re-read from
-// cache for each b.
+// Out axis, one (channel, tile, batch entry) per workgroup: forward FFT whose
+// first pass reads the n_out rows of the workspace, product with the kernel
+// spectrum in registers (the forward's last pass leaves each thread holding
+// exactly the positions the inverse's first pass needs), inverse FFT whose
+// last pass writes the n_out kept rows back.
 template <int L, int NR, class Ctx>
-__host__ __device__ void col_out_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+__host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int TW = NR == 1 ? col_tw(L) : mul3_tw(L);
-    constexpr int NL = NR * TW, NT = kThreads, n = L / 2;
+    constexpr int TW = out_tw(L, NR);
+    constexpr int NL = NR * TW, NT = out_nt(L, NR);
+    constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
     const Geom& g = a.g;
-    const OutTile o = out_tile<NR, TW>(g, bid);
+    const OutTile o = out_tile<NR, TW>(g, a.B, a.nch, bid);
     const long long PS = (long long)g.N_mid * g.S;
     const float2* kc = a.khat + (long long)(a.c0 + o.c_local) * g.ksz;
-    const int tid = ctx.tid();
-    for (int b = 0; b < a.B; ++b) {
-        float2* base = a.ws + ((long long)o.c_local * a.B + b) * g.wsp;
-        for (int idx = tid; idx < n * NL; idx += NT) {
-            const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
-            const int k = o.t * TW + col;
-            float2 z = make_float2(0.f, 0.f);
-            if (k < g.S) z = base[pos * PS + (long long)o.rows[row] * g.S + k];
-            T[pos * NL + l] = z;
-        }
+    float2* base = a.ws + ((long long)o.c_local * a.B + o.b) * g.wsp;
+    const int k0 = o.t * TW;
+    auto loff = [&](int l) -> long long { return (long long)o.rows[l / TW] * g.S + k0 + l % TW; };
+    auto lvalid = [&](int l) { return k0 + l % TW < g.S; };
+    auto ld = [&](int pos, int l) -> float2 {
+        const bool ok = lvalid(l);
+        const float2 v = base[ok ? pos * PS + loff(l) : 0];
+        return ok ? v : make_float2(0.f, 0.f);
+    };
+    auto s = fwd_from_fn<L, NL, NT, true>(ctx, T, ld);
+    ctx.sync();  // every LDS read of the forward transform is done: T is free
+    if (o.t == 0) {
+        pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) {
+            if (l % TW == 0) T[pos * NL + l] = v;
+        });
         ctx.sync();
-        tile_fft<L, NL, NL, NT, false, true, false>(ctx, T);
-        out_product<L, NR, TW>(ctx, g, o, kc, T);
+        out_slot0_product<L, NR, TW, NT>(ctx, g, o, kc, T);
         ctx.sync();
-        tile_fft<L, NL, NL, NT, true, false, true>(ctx, T);
-        for (int idx = tid; idx < n * NL; idx += NT) {
-            const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
-            const int k = o.t * TW + col;
-            if (k < g.S) base[pos * PS + (long long)o.rows[row] * g.S + k] = T[pos * NL + l];
-        }
+        pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) {
+            if (l % TW == 0) v = T[pos * NL + l];
+        });
         ctx.sync();
     }
+    // Every thread loads all its kernel spectrum values before the first use:
+    // lines outside the grid read a valid address and multiply by 1, and the
+    // k_in = 0 lines (already final) multiply by 1.
+    pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) {
+        const bool ok = lvalid(l) && k0 + l % TW != 0;
+        const float2 kv = kc[ok ? pos * PS + loff(l) : 1];
+        v = cmul(v, ok ? kv : make_float2(1.f, 0.f));
+    });
+    inv_to_fn<L, NL, NT, true>(ctx, T, s, [&](int pos, int l, const float2& v) {
+        if (lvalid(l)) base[pos * PS + loff(l)] = v;
+    });
 }
 
 // ---------------------------------------------------------------- conv1d
 // d = 1: the two signals of a line belong to consecutive pair slots (possibly
 // different channels), so the product is applied to the separated half spectra.
-template <int L, class Ctx>
-__host__ __device__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+// RowMeta: w0 / w1 hold the kernel spectrum offsets of the two channels.
+template <int L, bool BF16, class Ctx>
+__host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
+                                                     RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, n = L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), n = L / 2, S = L / 2;
     const Geom& g = a.g;
     const int P = a.nch * a.B;
     const int H = (P + 1) / 2;
-    const int h0 = bid * NP;
     const int tid = ctx.tid();
+    for (int lp = tid; lp < NP; lp += NT) {
+        const int h = bid * NP + lp;
+        RowMeta m{};
+        m.valid = h < H;
+        if (m.valid) {
+            const int qa = 2 * h, qb = 2 * h + 1;
+            m.valid1 = qb < P;
+            const int ca = a.c0 + qa / a.B, ba = qa % a.B;
+            const int cb = m.valid1 ? a.c0 + qb / a.B : ca, bb = m.valid1 ? qb % a.B : ba;
+            m.o0 = ((long long)ba * a.C + ca) * g.vox;
+            m.o1 = ((long long)bb * a.C + cb) * g.vox;
+            m.w0 = (long long)ca * g.ksz;
+            m.w1 = (long long)cb * g.ksz;
+            m.al0 = a.alpha[ca]; m.be0 = a.beta[ca];
+            m.al1 = a.alpha[cb]; m.be1 = a.beta[cb];
+        }
+        M[lp] = m;
+    }
+    ctx.sync();
     for (int idx = tid; idx < NP * n; idx += NT) {
         const int lp = idx / n, m = idx % n;
-        const int h = h0 + lp;
+        const RowMeta& md = M[lp];
         float2 z = make_float2(0.f, 0.f);
-        if (h < H) {
-            const int qa = 2 * h, qb = 2 * h + 1;
-            const int ca = a.c0 + qa / a.B, ba = qa % a.B;
-            z.x = gate(load_x(a, ((long long)ba * a.C + ca) * g.vox + m), a.alpha[ca], a.beta[ca]);
-            if (qb < P) {
-                const int cb = a.c0 + qb / a.B, bb = qb % a.B;
-                z.y = gate(load_x(a, ((long long)bb * a.C + cb) * g.vox + m), a.alpha[cb], a.beta[cb]);
-            }
+        if (md.valid) {
+            z.x = ctx.gate(load_x<BF16>(a, md.o0 + m), md.al0, md.be0);
+            if (md.valid1) z.y = ctx.gate(load_x<BF16>(a, md.o1 + m), md.al1, md.be1);
         }
         T[m * LP + lp] = z;
     }
@@ -332,18 +401,16 @@ __host__ __device__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a,
     tile_fft<L, NP, LP, NT, false, true, false>(ctx, T);
     for (int idx = tid; idx < NP * S; idx += NT) {
         const int lp = idx / S, k = idx % S;
-        const int h = h0 + lp;
-        if (h >= H) continue;
-        const int qa = 2 * h, qb = 2 * h + 1;
-        const bool vb = qb < P;
-        const float2* ka = a.khat + (long long)(a.c0 + qa / a.B) * g.ksz;
-        const float2* kb = a.khat + (long long)(a.c0 + (vb ? qb : qa) / a.B) * g.ksz;
+        const RowMeta& md = M[lp];
+        if (!md.valid) continue;
+        const float2* ka = a.khat + md.w0;
+        const float2* kb = a.khat + md.w1;
         if (k == 0) {
             const float2 Z0 = T[lp], ZS = T[S * LP + lp];
             const float2 Xa = make_float2(2.f * Z0.x, 2.f * ZS.x), Xb = make_float2(2.f * Z0.y, 2.f * ZS.y);
             const float2 Wa = cadd(cmul(Xa, ka[0]), cmul(cconj(Xa), ka[S]));
             float2 Wb = cadd(cmul(Xb, kb[0]), cmul(cconj(Xb), kb[S]));
-            if (!vb) Wb = make_float2(0.f, 0.f);
+            if (!md.valid1) Wb = make_float2(0.f, 0.f);
             T[lp] = make_float2(Wa.x, Wb.x);
             T[S * LP + lp] = make_float2(Wa.y, Wb.y);
         } else {
@@ -351,7 +418,7 @@ __host__ __device__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a,
             const float2 Xa = make_float2(Z.x + Zm.x, Z.y - Zm.y), Xb = make_float2(Z.y + Zm.y, Zm.x - Z.x);
             const float2 Ya = cmul(Xa, ka[k]);
             float2 Yb = cmul(Xb, kb[k]);
-            if (!vb) Yb = make_float2(0.f, 0.f);
+            if (!md.valid1) Yb = make_float2(0.f, 0.f);
             T[k * LP + lp] = make_float2(Ya.x - Yb.y, Ya.y + Yb.x);
             T[(L - k) * LP + lp] = make_float2(Ya.x + Yb.y, Yb.x - Ya.y);
         }
@@ -360,16 +427,11 @@ __host__ __device__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a,
     tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
     for (int idx = tid; idx < NP * n; idx += NT) {
         const int lp = idx / n, m = idx % n;
-        const int h = h0 + lp;
-        if (h >= H) continue;
-        const int qa = 2 * h, qb = 2 * h + 1;
+        const RowMeta& md = M[lp];
+        if (!md.valid) continue;
         const float2 z = T[m * LP + lp];
-        const int ca = a.c0 + qa / a.B, ba = qa % a.B;
-        store_y(a, ((long long)ba * a.C + ca) * g.vox + m, z.x);
-        if (qb < P) {
-            const int cb = a.c0 + qb / a.B, bb = qb % a.B;
-            store_y(a, ((long long)bb * a.C + cb) * g.vox + m, z.y);
-        }
+        store_y<BF16>(a, md.o0 + m, z.x);
+        if (md.valid1) store_y<BF16>(a, md.o1 + m, z.y);
     }
 }
 
@@ -377,7 +439,7 @@ __host__ __device__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a,
 // Wrap placement: offset delta of an axis with grid n and padded length N sits
 // at index delta mod N; index n is never reached and stays zero.
 constexpr int kEmpty = 1 << 30;
-__host__ __device__ inline int unwrap(int m, int n, int N)
+__host__ __device__ __forceinline__ int unwrap(int m, int n, int N)
 {
     if (N == 1) return 0;
     if (m < n) return m;
@@ -385,7 +447,7 @@ __host__ __device__ inline int unwrap(int m, int n, int N)
     return m - N;
 }
 
-__host__ __device__ inline float kernel_at(const ConvArgs& a, int c, int m_out, int m_mid, int t)
+__host__ __device__ __forceinline__ float kernel_at(const ConvArgs& a, int c, int m_out, int m_mid, int t)
 {
     const Geom& g = a.g;
     const int d0 = unwrap(m_out, g.n_out, g.N_out), d1 = unwrap(m_mid, g.n_mid, g.N_mid),
@@ -401,9 +463,9 @@ __host__ __device__ inline float kernel_at(const ConvArgs& a, int c, int m_out, 
 // half spectrum (true DFT values) into the main block; for d = 1 this is the
 // final spectrum and is scaled and split here.
 template <int L, class Ctx>
-__host__ __device__ void spec_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+__host__ __device__ __forceinline__ void spec_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = kThreads, S = L / 2;
+    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), S = L / 2;
     const Geom& g = a.g;
     const bool one_d = g.d == 1;
     const int rc = g.N_out * g.N_mid;
@@ -470,9 +532,9 @@ __host__ __device__ void spec_row_body(const Ctx& ctx, int bid, const ConvArgs& 
 
 // Full forward FFT along the middle axis of the main block (3-D), in place.
 template <int L, class Ctx>
-__host__ __device__ void spec_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+__host__ __device__ __forceinline__ void spec_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int TW = col_tw(L), NT = kThreads;
+    constexpr int TW = col_tw(L), NT = col_nt(L);
     const Geom& g = a.g;
     const int lines = g.N_out * g.S;
     const int tpc = (lines + TW - 1) / TW;
@@ -497,12 +559,12 @@ __host__ __device__ void spec_mid_body(const Ctx& ctx, int bid, const ConvArgs& 
 // the k_in = 0 lines, split Z = A + iB into Sv = (A+B)/2 g (main slot 0) and
 // Dv = (A-B)/2 g (dblk), with A = (Z + conj Z(-k))/2, B = (Z - conj Z(-k))/(2i).
 template <int L, int NR, class Ctx>
-__host__ __device__ void spec_out_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+__host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int TW = NR == 1 ? col_tw(L) : mul3_tw(L);
-    constexpr int NL = NR * TW, NT = kThreads;
+    constexpr int TW = out_tw(L, NR);
+    constexpr int NL = NR * TW, NT = out_nt(L, NR);
     const Geom& g = a.g;
-    const OutTile o = out_tile<NR, TW>(g, bid);
+    const OutTile o = out_tile<NR, TW>(g, 1, a.C, bid);
     const long long PS = (long long)g.N_mid * g.S;
     float2* kc = const_cast<float2*>(a.khat) + (long long)o.c_local * g.ksz;
     const float gsc = 1.0f / (2.0f * (float)g.N_out * (float)g.N_mid * (float)g.N_in);

@@ -16,8 +16,9 @@
 // half its outputs (PIN / POUT below).
 //
 // The code is written against a small execution context `Ctx` that provides
-// the thread index, the workgroup barrier and the twiddle table; the device
-// context is in hyenand_kernels.hip.
+// the thread index (tid()), the workgroup barrier (sync()), the LDS twiddle
+// tables (twl, laid out by fill_twiddles, reversed-plan tables at kRevBase) and
+// the gate's exponential and reciprocal; the device context is in kernels.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,22 +27,22 @@
 namespace hyenand {
 
 // ----------------------------------------------------------------- complex
-__host__ __device__ inline float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
-__host__ __device__ inline float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
-__host__ __device__ inline float2 cmul(float2 a, float2 b)
+__host__ __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__host__ __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__host__ __device__ __forceinline__ float2 cmul(float2 a, float2 b)
 {
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
 // a * conj(w)
-__host__ __device__ inline float2 cmulc(float2 a, float2 w)
+__host__ __device__ __forceinline__ float2 cmulc(float2 a, float2 w)
 {
     return make_float2(a.x * w.x + a.y * w.y, a.y * w.x - a.x * w.y);
 }
-__host__ __device__ inline float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
-__host__ __device__ inline float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+__host__ __device__ __forceinline__ float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
+__host__ __device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
 // a * (-i) when !INV (forward sign), a * (+i) when INV
 template <bool INV>
-__host__ __device__ inline float2 mul_mi(float2 a)
+__host__ __device__ __forceinline__ float2 mul_mi(float2 a)
 {
     return INV ? make_float2(-a.y, a.x) : make_float2(a.y, -a.x);
 }
@@ -97,7 +98,7 @@ struct Dft;
 
 template <bool INV, bool PIN, bool POUT>
 struct Dft<2, INV, PIN, POUT> {
-    __host__ __device__ static inline void run(float2* v)
+    __host__ __device__ static __forceinline__ void run(float2* v)
     {
         if constexpr (PIN) {
             v[1] = v[0];
@@ -111,7 +112,7 @@ struct Dft<2, INV, PIN, POUT> {
 
 template <bool INV, bool PIN, bool POUT>
 struct Dft<4, INV, PIN, POUT> {
-    __host__ __device__ static inline void run(float2* v)
+    __host__ __device__ static __forceinline__ void run(float2* v)
     {
         float2 a0, a1, b0, b1;
         if constexpr (PIN) {
@@ -133,17 +134,17 @@ struct Dft<4, INV, PIN, POUT> {
 // X[2s] = DFT4(a)[s], X[2s+1] = DFT4(b)[s].
 template <bool INV, bool PIN, bool POUT>
 struct Dft<8, INV, PIN, POUT> {
-    __host__ __device__ static inline float2 w8_1(float2 a)
+    __host__ __device__ static __forceinline__ float2 w8_1(float2 a)
     {
         constexpr float h = 0.70710678118654752440f;
         return INV ? make_float2((a.x - a.y) * h, (a.x + a.y) * h) : make_float2((a.x + a.y) * h, (a.y - a.x) * h);
     }
-    __host__ __device__ static inline float2 w8_3(float2 a)
+    __host__ __device__ static __forceinline__ float2 w8_3(float2 a)
     {
         constexpr float h = 0.70710678118654752440f;
         return INV ? make_float2((-a.x - a.y) * h, (a.x - a.y) * h) : make_float2((a.y - a.x) * h, (-a.x - a.y) * h);
     }
-    __host__ __device__ static inline void run(float2* v)
+    __host__ __device__ static __forceinline__ void run(float2* v)
     {
         float2 a[4], b[4];
         if constexpr (PIN) {
@@ -191,80 +192,315 @@ __host__ __device__ constexpr int plan_passes(int L)
     return p;
 }
 
-// ------------------------------------------------------- one Stockham pass
-// Butterfly g in [0, NL * L / R): line l = g % NL, j = g / NL.  Inputs at
-// positions j + r L/R; twiddle W_{NS R}^{(j mod NS) r}; outputs at
-// (j / NS) NS R + (j mod NS) + r NS, where NS is the product of the radices of
-// the passes already done.  Two barriers: all reads of the pass complete
-// before any write, and all writes before the next pass reads.
-template <int L, int R, int NS, int NL, int LP, int NT, bool INV, bool PIN, bool POUT, class Ctx>
-__host__ __device__ inline void stockham_pass(const Ctx& ctx, float2* T)
+// ------------------------------------------------------------ pass pieces
+// Radix and stride of pass p of the forward plan (REV = false) or of the
+// reversed plan (REV = true, used by inverse transforms so that the positions
+// held after a forward transform are those read by the inverse's first pass).
+template <int L, bool REV>
+__host__ __device__ constexpr int pass_radix(int p)
 {
-    constexpr int NB = NL * (L / R);
-    constexpr int PER = (NB + NT - 1) / NT;
-    constexpr int RIN = PIN ? R / 2 : R;
-    constexpr int ROUT = POUT ? R / 2 : R;
-    constexpr int TWS = TW_N / (NS * R);
-    const int tid = ctx.tid();
-    float2 v[PER][R];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int g = tid + i * NT;
-        if ((NB % NT) == 0 || g < NB) {
-            const int l = g % NL, j = g / NL;
-#pragma unroll
-            for (int r = 0; r < RIN; ++r) v[i][r] = T[(j + r * (L / R)) * LP + l];
-        }
-    }
-    ctx.sync();
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int g = tid + i * NT;
-        if ((NB % NT) == 0 || g < NB) {
-            const int l = g % NL, j = g / NL;
-            if constexpr (NS > 1) {
-                const int k = j % NS;
-#pragma unroll
-                for (int r = 1; r < RIN; ++r) {
-                    const float2 w = ctx.tw(k * r * TWS);
-                    v[i][r] = INV ? cmulc(v[i][r], w) : cmul(v[i][r], w);
-                }
-            }
-            Dft<R, INV, PIN, POUT>::run(v[i]);
-            const int base = (j / NS) * NS * R + (j % NS);
-#pragma unroll
-            for (int r = 0; r < ROUT; ++r) T[(base + r * NS) * LP + l] = v[i][r];
-        }
-    }
-    ctx.sync();
+    return REV ? plan_radix(L, plan_passes(L) - 1 - p) : plan_radix(L, p);
 }
 
-template <int L, int P, int NPASS, int NS, int NL, int LP, int NT, bool INV, bool PIN, bool POUT>
-struct PassChain {
+template <int L, bool REV>
+__host__ __device__ constexpr int pass_ns(int p)
+{
+    int ns = 1;
+    for (int q = 0; q < p; ++q) ns *= pass_radix<L, REV>(q);
+    return ns;
+}
+
+// Twiddle tables staged in LDS, one per pass with NS > 1, laid out [k][r-1]
+// (k in [0, NS), r in [1, R)) so that the lanes of a wave, which differ in k,
+// read addresses R-1 apart (no bank conflicts) and a butterfly reads R-1
+// consecutive entries.  Entry (k, r) = W_{NS R}^{k r} = W_2048^{k r 2048/(NS R)}.
+// The forward-plan tables (F) come first, then the reversed-plan tables (R).
+template <int L, bool REV>
+__host__ __device__ constexpr int tw_local_off(int p)
+{
+    int off = 0;
+    for (int q = 1; q < p; ++q) off += pass_ns<L, REV>(q) * (pass_radix<L, REV>(q) - 1);
+    return off;
+}
+
+template <int L, bool REV>
+__host__ __device__ constexpr int tw_plan_size()
+{
+    return tw_local_off<L, REV>(plan_passes(L));
+}
+
+constexpr int kPlanF = 1, kPlanR = 2;
+
+template <int L, int PLANS>
+__host__ __device__ constexpr int tw_table_size()
+{
+    return ((PLANS & kPlanF) ? tw_plan_size<L, false>() : 0) + ((PLANS & kPlanR) ? tw_plan_size<L, true>() : 0);
+}
+
+template <int L, int PLANS>
+__host__ __device__ constexpr int tw_rev_base()
+{
+    return (PLANS & kPlanF) ? tw_plan_size<L, false>() : 0;
+}
+
+// The tables of the plans in PLANS as one array (compile time).
+template <int L, int PLANS>
+__host__ __device__ constexpr int tw_table_alloc()
+{
+    return tw_table_size<L, PLANS>() > 0 ? tw_table_size<L, PLANS>() : 1;
+}
+
+template <int L, int PLANS>
+struct PlanTwiddles {
+    float2 w[tw_table_alloc<L, PLANS>()];
+};
+
+template <int L, int PLANS>
+constexpr PlanTwiddles<L, PLANS> make_plan_twiddles()
+{
+    constexpr TwTable base = make_twiddles();
+    PlanTwiddles<L, PLANS> t{};
+    int off = 0;
+    for (int rev = 0; rev < 2; ++rev) {
+        if (!(PLANS & (rev ? kPlanR : kPlanF))) continue;
+        for (int p = 1; p < plan_passes(L); ++p) {
+            const int NS = rev ? pass_ns<L, true>(p) : pass_ns<L, false>(p);
+            const int R = rev ? pass_radix<L, true>(p) : pass_radix<L, false>(p);
+            for (int k = 0; k < NS; ++k)
+                for (int r = 1; r < R; ++r) t.w[off++] = base.w[k * r * (TW_N / (NS * R))];
+        }
+    }
+    return t;
+}
+
+// Registers of one Stockham pass over NL lines: butterfly g in [0, NL*L/R),
+// line l = g % NL, j = g / NL; thread t owns g = t + i*NT.
+//   inputs:  positions j + r*L/R
+//   outputs: positions (j/NS)*NS*R + (j%NS) + r*NS  (= j + r*L/R on the last pass)
+template <int L, int R, int NL, int NT>
+struct PassRegs {
+    static constexpr int NB = NL * (L / R);
+    static constexpr int PER = (NB + NT - 1) / NT;
+    float2 v[PER][R];
+};
+
+template <int NB, int NT>
+__host__ __device__ __forceinline__ bool bf_valid(int g)
+{
+    return (NB % NT) == 0 || g < NB;
+}
+
+// Inputs from the LDS tile T[pos*LP + line]; with PIN only r < R/2.
+template <int L, int R, int NL, int LP, int NT, bool PIN, class Ctx>
+__host__ __device__ __forceinline__ void pass_load_lds(const Ctx& ctx, const float2* T, PassRegs<L, R, NL, NT>& s)
+{
+    using PR = PassRegs<L, R, NL, NT>;
+    const int tid = ctx.tid();
+#pragma unroll
+    for (int i = 0; i < PR::PER; ++i) {
+        const int g = tid + i * NT;
+        if (bf_valid<PR::NB, NT>(g)) {
+            const int l = g % NL, j = g / NL;
+#pragma unroll
+            for (int r = 0; r < (PIN ? R / 2 : R); ++r) s.v[i][r] = T[(j + r * (L / R)) * LP + l];
+        }
+    }
+}
+
+// Inputs through an accessor f(pos, line) (global memory); with PIN only r < R/2.
+template <int L, int R, int NL, int NT, bool PIN, class Ctx, class F>
+__host__ __device__ __forceinline__ void pass_load_fn(const Ctx& ctx, const F& f, PassRegs<L, R, NL, NT>& s)
+{
+    using PR = PassRegs<L, R, NL, NT>;
+    const int tid = ctx.tid();
+#pragma unroll
+    for (int i = 0; i < PR::PER; ++i) {
+        const int g = tid + i * NT;
+        if (bf_valid<PR::NB, NT>(g)) {
+            const int l = g % NL, j = g / NL;
+#pragma unroll
+            for (int r = 0; r < (PIN ? R / 2 : R); ++r) s.v[i][r] = f(j + r * (L / R), l);
+        }
+    }
+}
+
+// Twiddle W_{NS R}^{(j mod NS) r} and radix-R DFT on every owned butterfly.
+// TOFF: offset of this pass's twiddle table in the context's LDS tables.
+template <int L, int R, int NS, int NL, int NT, bool INV, bool PIN, bool POUT, int TOFF, class Ctx>
+__host__ __device__ __forceinline__ void pass_compute(const Ctx& ctx, PassRegs<L, R, NL, NT>& s)
+{
+    using PR = PassRegs<L, R, NL, NT>;
+    const int tid = ctx.tid();
+#pragma unroll
+    for (int i = 0; i < PR::PER; ++i) {
+        const int g = tid + i * NT;
+        if (bf_valid<PR::NB, NT>(g)) {
+            const int j = g / NL;
+            if constexpr (NS > 1) {
+                const float2* tw = ctx.twl + TOFF + (j % NS) * (R - 1) - 1;
+#pragma unroll
+                for (int r = 1; r < (PIN ? R / 2 : R); ++r) {
+                    const float2 w = tw[r];
+                    s.v[i][r] = INV ? cmulc(s.v[i][r], w) : cmul(s.v[i][r], w);
+                }
+            }
+            Dft<R, INV, PIN, POUT>::run(s.v[i]);
+        }
+    }
+}
+
+// Outputs to the LDS tile; with POUT only r < R/2.
+template <int L, int R, int NS, int NL, int LP, int NT, bool POUT, class Ctx>
+__host__ __device__ __forceinline__ void pass_store_lds(const Ctx& ctx, float2* T, const PassRegs<L, R, NL, NT>& s)
+{
+    using PR = PassRegs<L, R, NL, NT>;
+    const int tid = ctx.tid();
+#pragma unroll
+    for (int i = 0; i < PR::PER; ++i) {
+        const int g = tid + i * NT;
+        if (bf_valid<PR::NB, NT>(g)) {
+            const int l = g % NL, j = g / NL;
+            const int base = (j / NS) * NS * R + (j % NS);
+#pragma unroll
+            for (int r = 0; r < (POUT ? R / 2 : R); ++r) T[(base + r * NS) * LP + l] = s.v[i][r];
+        }
+    }
+}
+
+// Visit every output of a last pass (positions j + r*L/R, natural order):
+// f(pos, line, value&); with POUT only r < R/2.
+template <int L, int R, int NL, int NT, bool POUT, class Ctx, class F>
+__host__ __device__ __forceinline__ void pass_visit(const Ctx& ctx, PassRegs<L, R, NL, NT>& s, const F& f)
+{
+    using PR = PassRegs<L, R, NL, NT>;
+    const int tid = ctx.tid();
+#pragma unroll
+    for (int i = 0; i < PR::PER; ++i) {
+        const int g = tid + i * NT;
+        if (bf_valid<PR::NB, NT>(g)) {
+            const int l = g % NL, j = g / NL;
+#pragma unroll
+            for (int r = 0; r < (POUT ? R / 2 : R); ++r) f(j + r * (L / R), l, s.v[i][r]);
+        }
+    }
+}
+
+// In-place LDS passes [P, PEND) of the (reversed) plan, two barriers each.
+template <int L, bool REV, int P, int PEND, int NL, int LP, int NT, bool INV>
+struct LdsPasses {
     template <class Ctx>
-    __host__ __device__ static inline void run(const Ctx& ctx, float2* T)
+    __host__ __device__ static __forceinline__ void run(const Ctx& ctx, float2* T)
     {
-        constexpr int R = plan_radix(L, P);
-        stockham_pass<L, R, NS, NL, LP, NT, INV, PIN && P == 0, POUT && P == NPASS - 1>(ctx, T);
-        PassChain<L, P + 1, NPASS, NS * R, NL, LP, NT, INV, PIN, POUT>::run(ctx, T);
+        if constexpr (P < PEND) {
+            constexpr int R = pass_radix<L, REV>(P), NS = pass_ns<L, REV>(P);
+            constexpr int TOFF = (REV ? Ctx::kRevBase : 0) + tw_local_off<L, REV>(P);
+            PassRegs<L, R, NL, NT> s;
+            pass_load_lds<L, R, NL, LP, NT, false>(ctx, T, s);
+            ctx.sync();
+            pass_compute<L, R, NS, NL, NT, INV, false, false, TOFF>(ctx, s);
+            pass_store_lds<L, R, NS, NL, LP, NT, false>(ctx, T, s);
+            ctx.sync();
+            LdsPasses<L, REV, P + 1, PEND, NL, LP, NT, INV>::run(ctx, T);
+        }
     }
 };
 
-template <int L, int NPASS, int NS, int NL, int LP, int NT, bool INV, bool PIN, bool POUT>
-struct PassChain<L, NPASS, NPASS, NS, NL, LP, NT, INV, PIN, POUT> {
-    template <class Ctx>
-    __host__ __device__ static inline void run(const Ctx&, float2*) {}
-};
-
-// Length-L FFT of the NL lines of tile T (element (pos, line) at pos*LP + line),
-// in place, natural order.  Unnormalised in both directions.  With PIN only
-// positions < L/2 are read on entry; with POUT only positions < L/2 are valid
-// on exit.  Ends with a barrier.
+// Length-L FFT of the NL lines of tile T (element (pos, line) at pos*LP +
+// line), in place, natural order, unnormalised.  With PIN only positions < L/2
+// are read on entry; with POUT only positions < L/2 are valid on exit.  The
+// caller has synchronised the tile; ends with a barrier.
 template <int L, int NL, int LP, int NT, bool INV, bool PIN, bool POUT, class Ctx>
-__host__ __device__ inline void tile_fft(const Ctx& ctx, float2* T)
+__host__ __device__ __forceinline__ void tile_fft(const Ctx& ctx, float2* T)
 {
     static_assert(L >= 2 && L <= TW_N && (L & (L - 1)) == 0, "power-of-two length up to 2048");
-    PassChain<L, 0, plan_passes(L), 1, NL, LP, NT, INV, PIN, POUT>::run(ctx, T);
+    constexpr int NP = plan_passes(L);
+    constexpr int R0 = pass_radix<L, false>(0);
+    PassRegs<L, R0, NL, NT> s;
+    pass_load_lds<L, R0, NL, LP, NT, PIN>(ctx, T, s);
+    ctx.sync();
+    pass_compute<L, R0, 1, NL, NT, INV, PIN, POUT && NP == 1, 0>(ctx, s);
+    pass_store_lds<L, R0, 1, NL, LP, NT, POUT && NP == 1>(ctx, T, s);
+    ctx.sync();
+    if constexpr (NP > 1) {
+        LdsPasses<L, false, 1, NP - 1, NL, LP, NT, INV>::run(ctx, T);
+        constexpr int RL = pass_radix<L, false>(NP - 1), NSL = pass_ns<L, false>(NP - 1);
+        PassRegs<L, RL, NL, NT> t;
+        pass_load_lds<L, RL, NL, LP, NT, false>(ctx, T, t);
+        ctx.sync();
+        pass_compute<L, RL, NSL, NL, NT, INV, false, POUT, tw_local_off<L, false>(NP - 1)>(ctx, t);
+        pass_store_lds<L, RL, NSL, NL, LP, NT, POUT>(ctx, T, t);
+        ctx.sync();
+    }
+}
+
+// Forward transform of NL lines whose first pass reads through f(pos, line)
+// (PIN: only positions < L/2 exist) and whose last pass is left in registers
+// (positions j + r*L/R_last).  The tile T is scratch; the caller must not
+// touch it before a barrier.
+template <int L, int NL, int NT, bool PIN, class Ctx, class F>
+__host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, const F& f)
+{
+    constexpr int NP = plan_passes(L);
+    constexpr int R0 = pass_radix<L, false>(0);
+    PassRegs<L, R0, NL, NT> s;
+    pass_load_fn<L, R0, NL, NT, PIN>(ctx, f, s);
+    pass_compute<L, R0, 1, NL, NT, false, PIN, false, 0>(ctx, s);
+    if constexpr (NP == 1) {
+        return s;
+    } else {
+        pass_store_lds<L, R0, 1, NL, NL, NT, false>(ctx, T, s);
+        ctx.sync();
+        LdsPasses<L, false, 1, NP - 1, NL, NL, NT, false>::run(ctx, T);
+        constexpr int RL = pass_radix<L, false>(NP - 1), NSL = pass_ns<L, false>(NP - 1);
+        PassRegs<L, RL, NL, NT> t;
+        pass_load_lds<L, RL, NL, NL, NT, false>(ctx, T, t);
+        pass_compute<L, RL, NSL, NL, NT, false, false, false, tw_local_off<L, false>(NP - 1)>(ctx, t);
+        return t;
+    }
+}
+
+// Inverse transform (reversed plan) whose first-pass inputs are the registers
+// `s` (positions j + r*L/R, as left by fwd_from_fn or by a load) and whose
+// last pass writes through g(pos, line, value) (POUT: positions < L/2 only).
+// The tile T must be free for writing (a barrier after its last read).
+template <int L, int NL, int NT, bool POUT, class Ctx, class S, class G>
+__host__ __device__ __forceinline__ void inv_to_fn(const Ctx& ctx, float2* T, S& s, const G& gfn)
+{
+    constexpr int NP = plan_passes(L);
+    constexpr int R0 = pass_radix<L, true>(0);
+    pass_compute<L, R0, 1, NL, NT, true, false, POUT && NP == 1, 0>(ctx, s);
+    if constexpr (NP == 1) {
+        pass_visit<L, R0, NL, NT, POUT>(ctx, s, [&](int pos, int l, float2& v) { gfn(pos, l, v); });
+    } else {
+        pass_store_lds<L, R0, 1, NL, NL, NT, false>(ctx, T, s);
+        ctx.sync();
+        LdsPasses<L, true, 1, NP - 1, NL, NL, NT, true>::run(ctx, T);
+        constexpr int RL = pass_radix<L, true>(NP - 1), NSL = pass_ns<L, true>(NP - 1);
+        PassRegs<L, RL, NL, NT> t;
+        pass_load_lds<L, RL, NL, NL, NT, false>(ctx, T, t);
+        pass_compute<L, RL, NSL, NL, NT, true, false, POUT, Ctx::kRevBase + tw_local_off<L, true>(NP - 1)>(ctx, t);
+        pass_visit<L, RL, NL, NT, POUT>(ctx, t, [&](int pos, int l, float2& v) { gfn(pos, l, v); });
+    }
+}
+
+// Forward transform from f (first pass) to g (last pass), full output.
+template <int L, int NL, int NT, bool PIN, class Ctx, class F, class G>
+__host__ __device__ __forceinline__ void fwd_fn_to_fn(const Ctx& ctx, float2* T, const F& f, const G& gfn)
+{
+    constexpr int NP = plan_passes(L);
+    auto s = fwd_from_fn<L, NL, NT, PIN>(ctx, T, f);
+    constexpr int RL = pass_radix<L, false>(NP - 1);
+    pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) { gfn(pos, l, v); });
+}
+
+// Inverse transform from f (first pass, all L positions) to g (last pass).
+template <int L, int NL, int NT, bool POUT, class Ctx, class F, class G>
+__host__ __device__ __forceinline__ void inv_fn_to_fn(const Ctx& ctx, float2* T, const F& f, const G& gfn)
+{
+    constexpr int R0 = pass_radix<L, true>(0);
+    PassRegs<L, R0, NL, NT> s;
+    pass_load_fn<L, R0, NL, NT, false>(ctx, f, s);
+    inv_to_fn<L, NL, NT, POUT>(ctx, T, s, gfn);
 }
 
 }  // namespace hyenand

@@ -9,69 +9,118 @@
 
 namespace hyenand {
 
-// W_2048^t, computed at compile time (fft_core.h) and placed in constant memory.
-__constant__ const TwTable g_twiddles = make_twiddles();
-
+// Device execution context of a kernel whose transforms have length L and use
+// the plans PLANS: the twiddle tables (fft_core.h) are staged in LDS at kernel
+// entry; the first barrier of every body precedes its first transform.
+template <int L, int PLANS>
 struct DevCtx {
+    static constexpr int kRevBase = tw_rev_base<L, PLANS>();
+    const float2* twl;
     __device__ int tid() const { return (int)threadIdx.x; }
     __device__ void sync() const { __syncthreads(); }
-    __device__ float2 tw(int t) const { return g_twiddles.w[t]; }
+    // phi(x) x = x / (1 + exp(-(alpha x + beta))) with the hardware exp2 and reciprocal.
+    __device__ float gate(float x, float al, float be) const
+    {
+        const float e = __builtin_amdgcn_exp2f(-(al * x + be) * 1.44269504088896341f);
+        return x * __builtin_amdgcn_rcpf(1.0f + e);
+    }
 };
 
-template <int L>
-__global__ __launch_bounds__(kThreads) void k_row_fwd(ConvArgs a)
+template <int L, int PLANS>
+constexpr int twl_size() { return tw_table_alloc<L, PLANS>(); }
+
+// Per-(length, plans) twiddle tables, built at compile time.
+template <int L, int PLANS>
+__constant__ const PlanTwiddles<L, PLANS> g_plan_tw = make_plan_twiddles<L, PLANS>();
+
+// Stage the tables in LDS: every load is issued before the first store.
+template <int L, int NT, int PLANS>
+__device__ __forceinline__ DevCtx<L, PLANS> make_ctx(float2* twl)
 {
-    __shared__ float2 T[L * (row_np(L) + 1)];
-    row_fwd_body<L>(DevCtx{}, (int)blockIdx.x, a, T);
+    constexpr int SZ = tw_table_size<L, PLANS>();
+    if constexpr (SZ > 0) {
+        constexpr int IT = (SZ + NT - 1) / NT;
+        const int tid = (int)threadIdx.x;
+        float2 v[IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = tid + i * NT;
+            v[i] = g_plan_tw<L, PLANS>.w[e < SZ ? e : SZ - 1];
+        }
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = tid + i * NT;
+            if (e < SZ) twl[e] = v[i];
+        }
+    }
+    return DevCtx<L, PLANS>{twl};
 }
 
-template <int L>
-__global__ __launch_bounds__(kThreads) void k_row_inv(ConvArgs a)
+template <int L, bool BF16>
+__global__ __launch_bounds__(row_nt(L)) void k_row_fwd(ConvArgs a)
 {
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * (row_np(L) + 1)];
-    row_inv_body<L>(DevCtx{}, (int)blockIdx.x, a, T);
+    __shared__ RowMeta M[row_np(L)];
+    row_fwd_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
-template <int L>
-__global__ __launch_bounds__(kThreads) void k_conv1d(ConvArgs a)
+template <int L, bool BF16>
+__global__ __launch_bounds__(row_nt(L)) void k_row_inv(ConvArgs a)
 {
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * (row_np(L) + 1)];
-    conv1d_body<L>(DevCtx{}, (int)blockIdx.x, a, T);
+    __shared__ RowMeta M[row_np(L)];
+    row_inv_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+}
+
+template <int L, bool BF16>
+__global__ __launch_bounds__(row_nt(L)) void k_conv1d(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * (row_np(L) + 1)];
+    __shared__ RowMeta M[row_np(L)];
+    conv1d_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
 template <int L, bool INV>
-__global__ __launch_bounds__(kThreads) void k_col_mid(ConvArgs a)
+__global__ __launch_bounds__(col_nt(L)) void k_col_mid(ConvArgs a)
 {
+    __shared__ float2 TWL[twl_size<L, (INV ? kPlanR : kPlanF)>()];
     __shared__ float2 T[L * col_tw(L)];
-    col_mid_body<L, INV>(DevCtx{}, (int)blockIdx.x, a, T);
+    col_mid_body<L, INV>(make_ctx<L, col_nt(L), (INV ? kPlanR : kPlanF)>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L, int NR>
-__global__ __launch_bounds__(kThreads) void k_col_out(ConvArgs a)
+__global__ __launch_bounds__(out_nt(L, NR)) void k_col_out(ConvArgs a)
 {
-    __shared__ float2 T[L * NR * (NR == 1 ? col_tw(L) : mul3_tw(L))];
-    col_out_body<L, NR>(DevCtx{}, (int)blockIdx.x, a, T);
+    __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
+    __shared__ float2 T[L * NR * out_tw(L, NR)];
+    col_out_body<L, NR>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L>
-__global__ __launch_bounds__(kThreads) void k_spec_row(ConvArgs a)
+__global__ __launch_bounds__(row_nt(L)) void k_spec_row(ConvArgs a)
 {
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * (row_np(L) + 1)];
-    spec_row_body<L>(DevCtx{}, (int)blockIdx.x, a, T);
+    spec_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L>
-__global__ __launch_bounds__(kThreads) void k_spec_mid(ConvArgs a)
+__global__ __launch_bounds__(col_nt(L)) void k_spec_mid(ConvArgs a)
 {
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * col_tw(L)];
-    spec_mid_body<L>(DevCtx{}, (int)blockIdx.x, a, T);
+    spec_mid_body<L>(make_ctx<L, col_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L, int NR>
-__global__ __launch_bounds__(kThreads) void k_spec_out(ConvArgs a)
+__global__ __launch_bounds__(out_nt(L, NR)) void k_spec_out(ConvArgs a)
 {
-    __shared__ float2 T[L * NR * (NR == 1 ? col_tw(L) : mul3_tw(L))];
-    spec_out_body<L, NR>(DevCtx{}, (int)blockIdx.x, a, T);
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * NR * out_tw(L, NR)];
+    spec_out_body<L, NR>(make_ctx<L, out_nt(L, NR), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
 static inline unsigned ceil_div(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
@@ -101,20 +150,21 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
-    const dim3 blk(kThreads);
     hipError_t e;
     if (g.d == 1) {
         return with_length(g.N_in, [&]<int L>() {
             const long long H = ((long long)a.nch * a.B + 1) / 2;
             mark();
-            hipLaunchKernelGGL(k_conv1d<L>, dim3(ceil_div(H, row_np(L))), blk, 0, st, a);
+            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_conv1d<L, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
             return last_error();
         });
     }
     const long long H = (long long)a.nch * a.B * (g.n_out * g.n_mid / 2);
     e = with_length(g.N_in, [&]<int L>() {
         mark();
-        hipLaunchKernelGGL(k_row_fwd<L>, dim3(ceil_div(H, row_np(L))), blk, 0, st, a);
+        if (a.bf16) hipLaunchKernelGGL((k_row_fwd<L, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_fwd<L, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
     if (e != hipSuccess) return e;
@@ -122,35 +172,36 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
         e = with_length(g.N_mid, [&]<int L>() {
             const long long grid = (long long)a.nch * a.B * ceil_div((long long)g.n_out * g.S, col_tw(L));
             mark();
-            hipLaunchKernelGGL((k_col_mid<L, false>), dim3((unsigned)grid), blk, 0, st, a);
+            hipLaunchKernelGGL((k_col_mid<L, false>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
         e = with_length(g.N_out, [&]<int L>() {
-            const long long grid = (long long)a.nch * (g.N_mid / 2) * ceil_div(g.S, mul3_tw(L));
+            const long long grid = (long long)a.nch * a.B * (g.N_mid / 2) * ceil_div(g.S, mul3_tw(L));
             mark();
-            hipLaunchKernelGGL((k_col_out<L, 2>), dim3((unsigned)grid), blk, 0, st, a);
+            hipLaunchKernelGGL((k_col_out<L, 2>), dim3((unsigned)grid), dim3(out_nt(L, 2)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
         e = with_length(g.N_mid, [&]<int L>() {
             const long long grid = (long long)a.nch * a.B * ceil_div((long long)g.n_out * g.S, col_tw(L));
             mark();
-            hipLaunchKernelGGL((k_col_mid<L, true>), dim3((unsigned)grid), blk, 0, st, a);
+            hipLaunchKernelGGL((k_col_mid<L, true>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
             return last_error();
         });
     } else {
         e = with_length(g.N_out, [&]<int L>() {
-            const long long grid = (long long)a.nch * ceil_div(g.S, col_tw(L));
+            const long long grid = (long long)a.nch * a.B * ceil_div(g.S, col_tw(L));
             mark();
-            hipLaunchKernelGGL((k_col_out<L, 1>), dim3((unsigned)grid), blk, 0, st, a);
+            hipLaunchKernelGGL((k_col_out<L, 1>), dim3((unsigned)grid), dim3(out_nt(L, 1)), 0, st, a);
             return last_error();
         });
     }
     if (e != hipSuccess) return e;
     return with_length(g.N_in, [&]<int L>() {
         mark();
-        hipLaunchKernelGGL(k_row_inv<L>, dim3(ceil_div(H, row_np(L))), blk, 0, st, a);
+        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_inv<L, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
 }
@@ -158,30 +209,29 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
 hipError_t launch_spectrum(const ConvArgs& a, hipStream_t st)
 {
     const Geom& g = a.g;
-    const dim3 blk(kThreads);
     hipError_t e;
     const long long H = g.d == 1 ? ((long long)a.C + 1) / 2 : (long long)a.C * (g.N_out * g.N_mid / 2);
     e = with_length(g.N_in, [&]<int L>() {
-        hipLaunchKernelGGL(k_spec_row<L>, dim3(ceil_div(H, row_np(L))), blk, 0, st, a);
+        hipLaunchKernelGGL(k_spec_row<L>, dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
     if (e != hipSuccess || g.d == 1) return e;
     if (g.d == 3) {
         e = with_length(g.N_mid, [&]<int L>() {
             const long long grid = (long long)a.C * ceil_div((long long)g.N_out * g.S, col_tw(L));
-            hipLaunchKernelGGL(k_spec_mid<L>, dim3((unsigned)grid), blk, 0, st, a);
+            hipLaunchKernelGGL(k_spec_mid<L>, dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
         return with_length(g.N_out, [&]<int L>() {
             const long long grid = (long long)a.C * (g.N_mid / 2) * ceil_div(g.S, mul3_tw(L));
-            hipLaunchKernelGGL((k_spec_out<L, 2>), dim3((unsigned)grid), blk, 0, st, a);
+            hipLaunchKernelGGL((k_spec_out<L, 2>), dim3((unsigned)grid), dim3(out_nt(L, 2)), 0, st, a);
             return last_error();
         });
     }
     return with_length(g.N_out, [&]<int L>() {
         const long long grid = (long long)a.C * ceil_div(g.S, col_tw(L));
-        hipLaunchKernelGGL((k_spec_out<L, 1>), dim3((unsigned)grid), blk, 0, st, a);
+        hipLaunchKernelGGL((k_spec_out<L, 1>), dim3((unsigned)grid), dim3(out_nt(L, 1)), 0, st, a);
         return last_error();
     });
 }

@@ -86,16 +86,32 @@ struct ConvArgs {
     int bf16;               // I/O dtype: 0 fp32, 1 bf16
 };
 
+// Per-line data of a row workgroup, computed once per line: element offsets of
+// the two signals of the line in x / y (o0, o1) and in the workspace or the
+// kernel spectrum (w0, w1), their gate parameters, and validity.
+struct RowMeta {
+    long long o0, o1, w0, w1;
+    float al0, be0, al1, be1;
+    int valid, valid1;
+};
+
 // ---------------------------------------------------------------- tiling
-// Row kernels: NP line pairs of length L per workgroup, tile L x (NP+1).
-constexpr int row_np(int L) { return L >= 4096 ? 1 : (4096 / L < 2 ? 2 : 4096 / L); }
+// Row kernels: NP line pairs of length L per workgroup (2 <= NP <= 64),
+// tile L x (NP+1).
+constexpr int row_np(int L) { return 4096 / L < 2 ? 2 : (4096 / L > 64 ? 64 : 4096 / L); }
 // Column kernels along the middle axis / the out axis of a 2-D grid:
 // TW adjacent lines, tile L x TW (<= 64 KiB).
 constexpr int col_tw(int L) { return 8192 / L > 16 ? 16 : (8192 / L < 1 ? 1 : 8192 / L); }
 // Out-axis kernel of a 3-D grid: two mirrored k_mid rows x TW lines.
 constexpr int mul3_tw(int L) { return 4096 / L > 16 ? 16 : (4096 / L < 1 ? 1 : 4096 / L); }
 
-constexpr int kThreads = 256;
+// Threads of a workgroup for a tile of `points` complex values: 16 points per
+// thread per pass (two radix-8 butterflies), between 64 and 1024 threads.
+constexpr int tile_threads(int points) { return points / 16 < 64 ? 64 : (points / 16 > 1024 ? 1024 : points / 16); }
+constexpr int row_nt(int L) { return tile_threads(L * row_np(L)); }
+constexpr int col_nt(int L) { return tile_threads(L * col_tw(L)); }
+constexpr int out_tw(int L, int NR) { return NR == 1 ? col_tw(L) : mul3_tw(L); }
+constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
 
 // Recommended workspace: whole channels (all B pairs of a channel are processed
 // together), about 64 MiB so that it stays resident in the 256 MiB last-level
