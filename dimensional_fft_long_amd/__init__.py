@@ -32,7 +32,7 @@ F32, BF16 = 0, 1
 
 EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_bytes", "hyenand_kernel_spectrum",
            "hyenand_fftconv_workspace_bytes", "hyenand_fftconv_workspace_min_bytes", "hyenand_fftconv_fwd",
-           "hyenand_fftconv_fwd_traced")
+           "hyenand_fftconv_fwd_traced", "hyenand_fftconv_launch_plan")
 
 _lib = None
 
@@ -62,6 +62,8 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_fwd.restype = I
     lib.hyenand_fftconv_fwd_traced.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I, ctypes.POINTER(I)]
     lib.hyenand_fftconv_fwd_traced.restype = I
+    lib.hyenand_fftconv_launch_plan.argtypes = [I, I, I, P, I, SZ, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.hyenand_fftconv_launch_plan.restype = I
     _lib = lib
     return lib
 
@@ -168,6 +170,16 @@ def fftconv_fwd(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, K_hat:
     if rc != OK:
         raise HyenandError(rc, "fftconv_fwd")
     return y
+
+
+def launch_plan(B: int, C: int, dims, dtype, workspace_bytes: int) -> dict:
+    """How a forward call with this workspace runs: kernel launches and channels per chunk."""
+    n, ch = ctypes.c_int(0), ctypes.c_int(0)
+    rc = get_lib().hyenand_fftconv_launch_plan(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype),
+                                               int(workspace_bytes), ctypes.byref(n), ctypes.byref(ch))
+    if rc != OK:
+        raise HyenandError(rc, "launch_plan")
+    return {"launches": n.value, "chunk_channels": ch.value}
 
 
 PASS_NAMES = {1: ("conv1d",), 2: ("row_fwd", "col_out", "row_inv"),

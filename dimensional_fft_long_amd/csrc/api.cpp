@@ -12,6 +12,28 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// How a forward call is split into channel chunks (the kernel chain runs once
+// per chunk).  Chunks are balanced so that the last one is not a sliver.
+struct CallPlan {
+    int per;        // channels per chunk
+    int chunks;
+    int launches;
+};
+
+CallPlan plan_call(const Geom& g, int B, int C, size_t ws_bytes)
+{
+    CallPlan cp{C, 1, 1};
+    if (g.d == 1) return cp;
+    int per = chunk_channels(g, B, C, ws_bytes);
+    if (per > C) per = C;
+    if (per < 1) per = 1;
+    const int chunks = (C + per - 1) / per;
+    cp.per = (C + chunks - 1) / chunks;
+    cp.chunks = (C + cp.per - 1) / cp.per;
+    cp.launches = cp.chunks * (g.d == 3 ? 5 : 3);
+    return cp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,13 +109,12 @@ static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta
     if (!x || !y || !alpha || !beta || !K_hat) return HYENAND_ERR_INVALID_ARG;
     if (!aligned(x, es) || !aligned(y, es) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(K_hat, 8))
         return HYENAND_ERR_INVALID_ARG;
-    int per = C;
     if (g.wsp > 0) {
         if (!workspace) return HYENAND_ERR_WORKSPACE;
         if (!aligned(workspace, 8)) return HYENAND_ERR_INVALID_ARG;
-        per = chunk_channels(g, B, C, workspace_bytes);
-        if (per < 1) return HYENAND_ERR_WORKSPACE;
+        if (chunk_channels(g, B, C, workspace_bytes) < 1) return HYENAND_ERR_WORKSPACE;
     }
+    const CallPlan cp = plan_call(g, B, C, workspace_bytes);
     ConvArgs a{};
     a.x = x;
     a.y = y;
@@ -106,9 +127,9 @@ static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta
     a.C = C;
     a.bf16 = dtype == HYENAND_BF16;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    for (int c0 = 0; c0 < C; c0 += per) {
+    for (int c0 = 0; c0 < C; c0 += cp.per) {
         a.c0 = c0;
-        a.nch = (C - c0) < per ? (C - c0) : per;
+        a.nch = (C - c0) < cp.per ? (C - c0) : cp.per;
         if (launch_forward_chunk(a, st, trace) != hipSuccess) return HYENAND_ERR_HIP;
     }
     if (trace) trace->mark(st);
@@ -121,6 +142,23 @@ int hyenand_fftconv_fwd(const void* x, const float* alpha, const float* beta, co
 {
     return fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes, stream,
                             nullptr);
+}
+
+int hyenand_fftconv_launch_plan(int B, int C, int d, const int64_t* dims, int dtype, size_t workspace_bytes,
+                                int* n_launches, int* chunk_channels_out)
+{
+    if (B < 0 || C < 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16)) return HYENAND_ERR_INVALID_ARG;
+    if (!dims) return d < 1 || d > 3 ? HYENAND_ERR_UNSUPPORTED : HYENAND_ERR_INVALID_ARG;
+    Geom g;
+    if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
+    CallPlan cp{0, 0, 0};
+    if (B > 0 && C > 0) {
+        if (g.wsp > 0 && chunk_channels(g, B, C, workspace_bytes) < 1) return HYENAND_ERR_WORKSPACE;
+        cp = plan_call(g, B, C, workspace_bytes);
+    }
+    if (n_launches) *n_launches = cp.launches;
+    if (chunk_channels_out) *chunk_channels_out = cp.per;
+    return HYENAND_OK;
 }
 
 int hyenand_fftconv_fwd_traced(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y,

@@ -114,8 +114,9 @@ constexpr int out_tw(int L, int NR) { return NR == 1 ? col_tw(L) : mul3_tw(L); }
 constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
 
 // Recommended workspace: whole channels (all B pairs of a channel are processed
-// together), about 64 MiB so that it stays resident in the 256 MiB last-level
-// cache between passes, at least one channel.
+// together), up to about 128 MiB, at least one channel.  Measured on MI355X
+// (256x256, B=8, C=64): 64 MiB chunks 0.47 ms, 128 MiB 0.44 ms, 256 MiB
+// 0.46 ms per call; larger chunks mean fewer launches and shorter tails.
 inline int chunk_channels(const Geom& g, int B, int C, size_t ws_bytes_available)
 {
     const size_t per_ch = (size_t)B * (size_t)g.wsp * 8u;
@@ -129,7 +130,7 @@ inline size_t recommended_workspace(const Geom& g, int B, int C)
 {
     const size_t per_ch = (size_t)B * (size_t)g.wsp * 8u;
     if (per_ch == 0) return 0;
-    const size_t target = (size_t)64 << 20;
+    const size_t target = (size_t)128 << 20;
     size_t n = target / per_ch;
     if (n < 1) n = 1;
     if (n > (size_t)C) n = (size_t)C;

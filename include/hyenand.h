@@ -90,10 +90,10 @@ int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int
 
 /*
  * Workspace bytes recommended for hyenand_fftconv_fwd: whole channels (all B
- * batch entries of a channel are processed together) up to about 64 MiB.  The
+ * batch entries of a channel are processed together) up to about 128 MiB.  The
  * minimum accepted is one channel, B * n_0 * (prod of the middle padded axes) *
  * S * 8 bytes (0 for d = 1); a larger workspace processes more channels per
- * pass.  0 for d = 1, for an empty call, or for an unsupported shape.
+ * kernel chain.  0 for d = 1, for an empty call, or for an unsupported shape.
  */
 size_t hyenand_fftconv_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype);
 
@@ -112,6 +112,15 @@ size_t hyenand_fftconv_workspace_min_bytes(int B, int C, int d, const int64_t* d
 int hyenand_fftconv_fwd(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat, void* y,
                         int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * How hyenand_fftconv_fwd would run with this workspace size: *n_launches
+ * kernel launches and *chunk_channels channels per chunk (chunks are balanced).
+ * Either output pointer may be NULL.  Errors as hyenand_fftconv_fwd's argument
+ * checks (no data pointers are examined).
+ */
+int hyenand_fftconv_launch_plan(int B, int C, int d, const int64_t* dims, int dtype, size_t workspace_bytes,
+                                int* n_launches, int* chunk_channels);
 
 /*
  * hyenand_fftconv_fwd with a launch trace, for measurement.  Arguments and

@@ -207,3 +207,29 @@ def test_workload_3d_512_bf16(H):
     wl = synth.WORKLOADS[4]
     err = _full_workload(H, wl, o2_pairs=[], sample_pairs=[(0, 0), (0, 3)], per_pair=6)
     assert err <= TOL[wl.dtype]
+
+
+# ------------------------------------------------------- channel chunking
+
+def test_launch_plan_and_balanced_chunks(H):
+    minb = H.workspace_bytes(8, 64, (256, 256), torch.float32, minimum=True)
+    assert H.launch_plan(8, 64, (256, 256), torch.float32, minb) == {"launches": 64 * 3, "chunk_channels": 1}
+    assert H.launch_plan(8, 64, (256, 256), torch.float32, 16 * minb) == {"launches": 4 * 3, "chunk_channels": 16}
+    # 64 channels with room for 30: three chunks of 22, 22, 20 rather than 30, 30, 4.
+    assert H.launch_plan(8, 64, (256, 256), torch.float32, 30 * minb) == {"launches": 3 * 3, "chunk_channels": 22}
+    assert H.launch_plan(1, 4, (8, 8, 8), torch.float32, 1 << 30)["launches"] == 5
+    assert H.launch_plan(2, 3, (256,), torch.float32, 0)["launches"] == 1
+
+
+@pytest.mark.parametrize("dims,B,C,dtype", [((32, 32), 2, 7, "f32"), ((64, 64, 64), 1, 5, "bf16")],
+                         ids=lambda v: str(v))
+def test_every_chunking_gives_the_same_output(H, dims, B, C, dtype):
+    w = synth.make(dims, B=B, C=C, dtype=dtype, seed=40 + C)
+    dt = w["x"].dtype
+    minb = H.workspace_bytes(B, C, dims, dt, minimum=True)
+    outs = []
+    for k in (1, 2, 3, C):
+        ws = torch.empty(k * minb, dtype=torch.uint8, device="cuda")
+        outs.append(_gpu_run(H, w, workspace=ws)[0])
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
