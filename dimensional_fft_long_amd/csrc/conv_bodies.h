@@ -30,6 +30,8 @@
 #include "fft_core.h"
 #include "plan.h"
 
+#include <type_traits>
+
 namespace hyenand {
 
 // ------------------------------------------------------------- element I/O
@@ -101,10 +103,11 @@ template <int L, bool BF16, class Ctx>
 __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), n = L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
     constexpr int ITER = NP * n / NT;
     static_assert(NP * n % NT == 0, "whole element loops");
     const int tid = ctx.tid();
+    ctx.stage();
     row_meta<NP, NT>(ctx, bid, a, M);
     ctx.sync();
     float xa[ITER], xb[ITER];
@@ -153,10 +156,11 @@ template <int L, bool BF16, class Ctx>
 __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), n = L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
     constexpr int ITER = NP * S / NT;
     static_assert(NP * S % NT == 0, "whole element loops");
     const int tid = ctx.tid();
+    ctx.stage();
     row_meta<NP, NT>(ctx, bid, a, M);
     ctx.sync();
     // Rebuild Z = Y_a + i Y_b over the full length from the two half spectra
@@ -221,18 +225,22 @@ __host__ __device__ __forceinline__ void col_mid_body(const Ctx& ctx, int bid, c
     auto st = [&](int pos, int l, const float2& v) {
         if (lam0 + l < lines) base[off(pos, l)] = v;
     };
-    if constexpr (INV) inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st);
-    else fwd_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st);
+    auto after_load = [&]() { ctx.stage(); };
+    if constexpr (INV) inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
+    else fwd_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
 }
 
 // Rows of the middle axis handled together by one out-axis workgroup: with
 // NR = 2 the rows {rp, N_mid - rp} (and {0, N_mid/2} for rp = 0), so that the
 // slot-0 line of k_mid and its mirror -k_mid are in the same tile.
 //
-// Workgroup order: the B workgroups of one (channel, tile) read the same kernel
-// spectrum tile.  Consecutive workgroup ids are dispatched round-robin over the
-// eight XCDs, so those B workgroups get ids u0 + 8 b (same id mod 8, hence the
-// same XCD and L2) whenever the tile index u lies in a full group of eight.
+// Workgroup order: consecutive workgroup ids are dispatched round-robin over
+// the eight XCDs, each with its own L2.  Work item w = u*B + b (u the tile
+// index, b the batch entry) goes to id (w mod W8/8)*8 + w / (W8/8) for the
+// first W8 = W & ~7 items, so XCD x runs the contiguous items
+// [x W8/8, (x+1) W8/8) in order: the B workgroups of a tile read the same
+// kernel spectrum tile and neighbouring tiles share the cache lines at the
+// edges of their row segments, both within one L2.
 struct OutTile {
     int c_local, t, b, rows[2];
     bool self_mirror;
@@ -245,17 +253,10 @@ __host__ __device__ __forceinline__ OutTile out_tile(const Geom& g, int B, int n
     const int ct = (g.S + TW - 1) / TW;
     const int nrp = NR == 1 ? 1 : g.N_mid / 2;
     const int tpc = nrp * ct;
-    const int U = nch * tpc, U8 = U & ~7;
-    int u;
-    if (bid < U8 * B) {
-        const int grp = bid / (8 * B), rem = bid % (8 * B);
-        o.b = rem / 8;
-        u = grp * 8 + rem % 8;
-    } else {
-        const int rem = bid - U8 * B;
-        u = U8 + rem / B;
-        o.b = rem % B;
-    }
+    const int W = nch * tpc * B, W8 = W & ~7;
+    const int w = bid < W8 ? (bid % 8) * (W8 / 8) + bid / 8 : bid;
+    const int u = w / B;
+    o.b = w % B;
     o.c_local = u / tpc;
     const int r2 = u % tpc;
     const int rp = r2 / ct;
@@ -304,6 +305,15 @@ __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const
 }
 
 // --------------------------------------------------------------- col_out
+// p advanced by a 32-bit byte offset (a lane offset added to a wave-uniform
+// base: the form global loads and stores take without 64-bit lane arithmetic).
+template <class T>
+__host__ __device__ __forceinline__ T* add_bytes(T* p, unsigned bytes)
+{
+    using Byte = std::conditional_t<std::is_const_v<T>, const char, char>;
+    return reinterpret_cast<T*>(reinterpret_cast<Byte*>(p) + bytes);
+}
+
 // Out axis, one (channel, tile, batch entry) per workgroup: forward FFT whose
 // first pass reads the n_out rows of the workspace, product with the kernel
 // spectrum in registers (the forward's last pass leaves each thread holding
@@ -321,14 +331,40 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, c
     const float2* kc = a.khat + (long long)(a.c0 + o.c_local) * g.ksz;
     float2* base = a.ws + ((long long)o.c_local * a.B + o.b) * g.wsp;
     const int k0 = o.t * TW;
-    auto loff = [&](int l) -> long long { return (long long)o.rows[l / TW] * g.S + k0 + l % TW; };
     auto lvalid = [&](int l) { return k0 + l % TW < g.S; };
-    auto ld = [&](int pos, int l) -> float2 {
+    // Element (pos = j + q, line l) of the workspace or of the kernel spectrum
+    // is at q*PS (wave-uniform, q a constant of the unrolled loops) plus the
+    // lane's byte offset 8*(j*PS + row*S + k0 + l%TW), which stays below 4 GiB
+    // (j < L/R for R >= 2 and one channel's spectrum is at most 4 GiB).
+    auto lane_bytes = [&](int j, int l) -> unsigned {
+        return 8u * ((unsigned)j * (unsigned)PS + (unsigned)o.rows[l / TW] * (unsigned)g.S + (unsigned)(k0 + l % TW));
+    };
+    auto at = [](auto* p, long long q_elems, unsigned bytes) { return add_bytes(p + q_elems, bytes); };
+    auto ld = [&](int j, int q, int l) -> float2 {
         const bool ok = lvalid(l);
-        const float2 v = base[ok ? pos * PS + loff(l) : 0];
+        const float2 v = *at(base, q * PS, ok ? lane_bytes(j, l) : 0u);
         return ok ? v : make_float2(0.f, 0.f);
     };
-    auto s = fwd_from_fn<L, NL, NT, true>(ctx, T, ld);
+    // Kernel spectrum values for the positions this thread multiplies (the
+    // forward's last pass: positions j + r*L/RL), loaded while the forward
+    // transform runs.
+    using PL = PassRegs<L, RL, NL, NT>;
+    float2 kv[PL::PER][RL];
+    bool kok[PL::PER];
+    const auto tw_staged = ctx.stage_load();  // oldest loads: waited for first
+    auto after_load = [&]() {
+        const int tid = ctx.tid();
+#pragma unroll
+        for (int i = 0; i < PL::PER; ++i) {
+            const int g = tid + i * NT, l = g % NL, j = g / NL;
+            kok[i] = bf_valid<PL::NB, NT>(g) && lvalid(l) && k0 + l % TW != 0;
+            const unsigned lb = kok[i] ? lane_bytes(j, l) : 8u;
+#pragma unroll
+            for (int r = 0; r < RL; ++r) kv[i][r] = *at(kc, (long long)r * (L / RL) * PS, lb);
+        }
+        ctx.stage_store(tw_staged);
+    };
+    auto s = fwd_from_fn<L, NL, NT, true>(ctx, T, ld, after_load);
     ctx.sync();  // every LDS read of the forward transform is done: T is free
     if (o.t == 0) {
         pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) {
@@ -342,16 +378,17 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, c
         });
         ctx.sync();
     }
-    // Every thread loads all its kernel spectrum values before the first use:
-    // lines outside the grid read a valid address and multiply by 1, and the
-    // k_in = 0 lines (already final) multiply by 1.
-    pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) {
-        const bool ok = lvalid(l) && k0 + l % TW != 0;
-        const float2 kv = kc[ok ? pos * PS + loff(l) : 1];
-        v = cmul(v, ok ? kv : make_float2(1.f, 0.f));
-    });
-    inv_to_fn<L, NL, NT, true>(ctx, T, s, [&](int pos, int l, const float2& v) {
-        if (lvalid(l)) base[pos * PS + loff(l)] = v;
+    // Lines outside the grid and the k_in = 0 lines (final already) keep their values.
+#pragma unroll
+    for (int i = 0; i < PL::PER; ++i) {
+#pragma unroll
+        for (int r = 0; r < RL; ++r) {
+            const float2 m = cmul(s.v[i][r], kv[i][r]);
+            s.v[i][r] = kok[i] ? m : s.v[i][r];
+        }
+    }
+    inv_to_fn<L, NL, NT, true>(ctx, T, s, [&](int j, int q, int l, const float2& v) {
+        if (lvalid(l)) *at(base, q * PS, lane_bytes(j, l)) = v;
     });
 }
 
@@ -363,11 +400,12 @@ template <int L, bool BF16, class Ctx>
 __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                      RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), n = L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
     const Geom& g = a.g;
     const int P = a.nch * a.B;
     const int H = (P + 1) / 2;
     const int tid = ctx.tid();
+    ctx.stage();
     for (int lp = tid; lp < NP; lp += NT) {
         const int h = bid * NP + lp;
         RowMeta m{};
@@ -465,7 +503,7 @@ __host__ __device__ __forceinline__ float kernel_at(const ConvArgs& a, int c, in
 template <int L, class Ctx>
 __host__ __device__ __forceinline__ void spec_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int NP = row_np(L), LP = NP + 1, NT = row_nt(L), S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), S = L / 2;
     const Geom& g = a.g;
     const bool one_d = g.d == 1;
     const int rc = g.N_out * g.N_mid;
@@ -473,6 +511,7 @@ __host__ __device__ __forceinline__ void spec_row_body(const Ctx& ctx, int bid, 
     const int H = one_d ? (a.C + 1) / 2 : a.C * hp;
     const int h0 = bid * NP;
     const int tid = ctx.tid();
+    ctx.stage();
     float2* khat = const_cast<float2*>(a.khat);
     for (int idx = tid; idx < NP * L; idx += NT) {
         const int lp = idx / L, t = idx % L;
@@ -541,6 +580,7 @@ __host__ __device__ __forceinline__ void spec_mid_body(const Ctx& ctx, int bid, 
     const int c = bid / tpc, lam0 = (bid % tpc) * TW;
     float2* base = const_cast<float2*>(a.khat) + (long long)c * g.ksz;
     const int tid = ctx.tid();
+    ctx.stage();
     for (int idx = tid; idx < L * TW; idx += NT) {
         const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
         float2 z = make_float2(0.f, 0.f);
@@ -569,6 +609,7 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
     float2* kc = const_cast<float2*>(a.khat) + (long long)o.c_local * g.ksz;
     const float gsc = 1.0f / (2.0f * (float)g.N_out * (float)g.N_mid * (float)g.N_in);
     const int tid = ctx.tid();
+    ctx.stage();
     for (int idx = tid; idx < L * NL; idx += NT) {
         const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
         const int k = o.t * TW + col;

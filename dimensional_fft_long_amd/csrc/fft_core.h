@@ -17,8 +17,9 @@
 //
 // The code is written against a small execution context `Ctx` that provides
 // the thread index (tid()), the workgroup barrier (sync()), the LDS twiddle
-// tables (twl, laid out by fill_twiddles, reversed-plan tables at kRevBase) and
-// the gate's exponential and reciprocal; the device context is in kernels.hip.
+// tables (twl, reversed-plan tables at kRevBase; stage() fills them and must
+// precede a barrier that precedes the first transform pass with twiddles) and
+// the gate (gate()); the device context is in kernels.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -307,7 +308,24 @@ __host__ __device__ __forceinline__ void pass_load_lds(const Ctx& ctx, const flo
     }
 }
 
-// Inputs through an accessor f(pos, line) (global memory); with PIN only r < R/2.
+// Global-memory accessors come in two forms: f(pos, line), or f(j, q, line)
+// with pos = j + q, where q = r*L/R is the same for every lane (a constant of
+// the unrolled loop) and j is the lane's own part.  The second form lets an
+// accessor fold q into a wave-uniform base address and keep one 32-bit lane
+// offset per butterfly instead of a 64-bit address per element.
+template <class F>
+__host__ __device__ constexpr bool split_accessor()
+{
+    return requires(const F& f) { f(0, 0, 0); };
+}
+
+template <class F>
+__host__ __device__ constexpr bool split_visitor()
+{
+    return requires(const F& f, float2& v) { f(0, 0, 0, v); };
+}
+
+// Inputs through an accessor (global memory); with PIN only r < R/2.
 template <int L, int R, int NL, int NT, bool PIN, class Ctx, class F>
 __host__ __device__ __forceinline__ void pass_load_fn(const Ctx& ctx, const F& f, PassRegs<L, R, NL, NT>& s)
 {
@@ -319,7 +337,10 @@ __host__ __device__ __forceinline__ void pass_load_fn(const Ctx& ctx, const F& f
         if (bf_valid<PR::NB, NT>(g)) {
             const int l = g % NL, j = g / NL;
 #pragma unroll
-            for (int r = 0; r < (PIN ? R / 2 : R); ++r) s.v[i][r] = f(j + r * (L / R), l);
+            for (int r = 0; r < (PIN ? R / 2 : R); ++r) {
+                if constexpr (split_accessor<F>()) s.v[i][r] = f(j, r * (L / R), l);
+                else s.v[i][r] = f(j + r * (L / R), l);
+            }
         }
     }
 }
@@ -368,7 +389,8 @@ __host__ __device__ __forceinline__ void pass_store_lds(const Ctx& ctx, float2* 
 }
 
 // Visit every output of a last pass (positions j + r*L/R, natural order):
-// f(pos, line, value&); with POUT only r < R/2.
+// f(pos, line, value&) or the split form f(j, q, line, value&); with POUT
+// only r < R/2.
 template <int L, int R, int NL, int NT, bool POUT, class Ctx, class F>
 __host__ __device__ __forceinline__ void pass_visit(const Ctx& ctx, PassRegs<L, R, NL, NT>& s, const F& f)
 {
@@ -380,7 +402,10 @@ __host__ __device__ __forceinline__ void pass_visit(const Ctx& ctx, PassRegs<L, 
         if (bf_valid<PR::NB, NT>(g)) {
             const int l = g % NL, j = g / NL;
 #pragma unroll
-            for (int r = 0; r < (POUT ? R / 2 : R); ++r) f(j + r * (L / R), l, s.v[i][r]);
+            for (int r = 0; r < (POUT ? R / 2 : R); ++r) {
+                if constexpr (split_visitor<F>()) f(j, r * (L / R), l, s.v[i][r]);
+                else f(j + r * (L / R), l, s.v[i][r]);
+            }
         }
     }
 }
@@ -435,15 +460,18 @@ __host__ __device__ __forceinline__ void tile_fft(const Ctx& ctx, float2* T)
 
 // Forward transform of NL lines whose first pass reads through f(pos, line)
 // (PIN: only positions < L/2 exist) and whose last pass is left in registers
-// (positions j + r*L/R_last).  The tile T is scratch; the caller must not
-// touch it before a barrier.
-template <int L, int NL, int NT, bool PIN, class Ctx, class F>
-__host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, const F& f)
+// (positions j + r*L/R_last).  `after_load()` runs once the first pass's loads
+// are issued and before they are used (a place to issue more independent
+// loads).  The tile T is scratch; the caller must not touch it before a
+// barrier.
+template <int L, int NL, int NT, bool PIN, class Ctx, class F, class H>
+__host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, const F& f, const H& after_load)
 {
     constexpr int NP = plan_passes(L);
     constexpr int R0 = pass_radix<L, false>(0);
     PassRegs<L, R0, NL, NT> s;
     pass_load_fn<L, R0, NL, NT, PIN>(ctx, f, s);
+    after_load();
     pass_compute<L, R0, 1, NL, NT, false, PIN, false, 0>(ctx, s);
     if constexpr (NP == 1) {
         return s;
@@ -470,7 +498,7 @@ __host__ __device__ __forceinline__ void inv_to_fn(const Ctx& ctx, float2* T, S&
     constexpr int R0 = pass_radix<L, true>(0);
     pass_compute<L, R0, 1, NL, NT, true, false, POUT && NP == 1, 0>(ctx, s);
     if constexpr (NP == 1) {
-        pass_visit<L, R0, NL, NT, POUT>(ctx, s, [&](int pos, int l, float2& v) { gfn(pos, l, v); });
+        pass_visit<L, R0, NL, NT, POUT>(ctx, s, gfn);
     } else {
         pass_store_lds<L, R0, 1, NL, NL, NT, false>(ctx, T, s);
         ctx.sync();
@@ -479,27 +507,30 @@ __host__ __device__ __forceinline__ void inv_to_fn(const Ctx& ctx, float2* T, S&
         PassRegs<L, RL, NL, NT> t;
         pass_load_lds<L, RL, NL, NL, NT, false>(ctx, T, t);
         pass_compute<L, RL, NSL, NL, NT, true, false, POUT, Ctx::kRevBase + tw_local_off<L, true>(NP - 1)>(ctx, t);
-        pass_visit<L, RL, NL, NT, POUT>(ctx, t, [&](int pos, int l, float2& v) { gfn(pos, l, v); });
+        pass_visit<L, RL, NL, NT, POUT>(ctx, t, gfn);
     }
 }
 
 // Forward transform from f (first pass) to g (last pass), full output.
-template <int L, int NL, int NT, bool PIN, class Ctx, class F, class G>
-__host__ __device__ __forceinline__ void fwd_fn_to_fn(const Ctx& ctx, float2* T, const F& f, const G& gfn)
+template <int L, int NL, int NT, bool PIN, class Ctx, class F, class G, class H>
+__host__ __device__ __forceinline__ void fwd_fn_to_fn(const Ctx& ctx, float2* T, const F& f, const G& gfn,
+                                                      const H& after_load)
 {
     constexpr int NP = plan_passes(L);
-    auto s = fwd_from_fn<L, NL, NT, PIN>(ctx, T, f);
+    auto s = fwd_from_fn<L, NL, NT, PIN>(ctx, T, f, after_load);
     constexpr int RL = pass_radix<L, false>(NP - 1);
-    pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) { gfn(pos, l, v); });
+    pass_visit<L, RL, NL, NT, false>(ctx, s, gfn);
 }
 
 // Inverse transform from f (first pass, all L positions) to g (last pass).
-template <int L, int NL, int NT, bool POUT, class Ctx, class F, class G>
-__host__ __device__ __forceinline__ void inv_fn_to_fn(const Ctx& ctx, float2* T, const F& f, const G& gfn)
+template <int L, int NL, int NT, bool POUT, class Ctx, class F, class G, class H>
+__host__ __device__ __forceinline__ void inv_fn_to_fn(const Ctx& ctx, float2* T, const F& f, const G& gfn,
+                                                      const H& after_load)
 {
     constexpr int R0 = pass_radix<L, true>(0);
     PassRegs<L, R0, NL, NT> s;
     pass_load_fn<L, R0, NL, NT, false>(ctx, f, s);
+    after_load();
     inv_to_fn<L, NL, NT, POUT>(ctx, T, s, gfn);
 }
 

@@ -9,13 +9,21 @@
 
 namespace hyenand {
 
-// Device execution context of a kernel whose transforms have length L and use
-// the plans PLANS: the twiddle tables (fft_core.h) are staged in LDS at kernel
-// entry; the first barrier of every body precedes its first transform.
 template <int L, int PLANS>
+constexpr int twl_size() { return tw_table_alloc<L, PLANS>(); }
+
+// Per-(length, plans) twiddle tables, built at compile time.
+template <int L, int PLANS>
+__constant__ const PlanTwiddles<L, PLANS> g_plan_tw = make_plan_twiddles<L, PLANS>();
+
+// Device execution context of a kernel of NT threads whose transforms have
+// length L and use the plans PLANS.  The bodies call stage() to copy the
+// twiddle tables (fft_core.h) into LDS before a barrier that precedes their
+// first transform pass with twiddles.
+template <int L, int NT, int PLANS>
 struct DevCtx {
     static constexpr int kRevBase = tw_rev_base<L, PLANS>();
-    const float2* twl;
+    float2* twl;
     __device__ int tid() const { return (int)threadIdx.x; }
     __device__ void sync() const { __syncthreads(); }
     // phi(x) x = x / (1 + exp(-(alpha x + beta))) with the hardware exp2 and reciprocal.
@@ -24,43 +32,51 @@ struct DevCtx {
         const float e = __builtin_amdgcn_exp2f(-(al * x + be) * 1.44269504088896341f);
         return x * __builtin_amdgcn_rcpf(1.0f + e);
     }
-};
-
-template <int L, int PLANS>
-constexpr int twl_size() { return tw_table_alloc<L, PLANS>(); }
-
-// Per-(length, plans) twiddle tables, built at compile time.
-template <int L, int PLANS>
-__constant__ const PlanTwiddles<L, PLANS> g_plan_tw = make_plan_twiddles<L, PLANS>();
-
-// Stage the tables in LDS: every load is issued before the first store.
-template <int L, int NT, int PLANS>
-__device__ __forceinline__ DevCtx<L, PLANS> make_ctx(float2* twl)
-{
-    constexpr int SZ = tw_table_size<L, PLANS>();
-    if constexpr (SZ > 0) {
-        constexpr int IT = (SZ + NT - 1) / NT;
-        const int tid = (int)threadIdx.x;
-        float2 v[IT];
+    // Two halves so that callers can issue other loads in between: every
+    // load of the copy is issued before the first store.
+    static constexpr int kTwSize = tw_table_size<L, PLANS>();
+    static constexpr int kTwIter = kTwSize > 0 ? (kTwSize + NT - 1) / NT : 1;
+    struct Staged {
+        float2 v[kTwIter];
+    };
+    __device__ Staged stage_load() const
+    {
+        Staged st;
+        if constexpr (kTwSize > 0) {
+            const int t0 = (int)threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < IT; ++i) {
-            const int e = tid + i * NT;
-            v[i] = g_plan_tw<L, PLANS>.w[e < SZ ? e : SZ - 1];
+            for (int i = 0; i < kTwIter; ++i) {
+                const int e = t0 + i * NT;
+                st.v[i] = g_plan_tw<L, PLANS>.w[e < kTwSize ? e : kTwSize - 1];
+            }
         }
+        return st;
+    }
+    __device__ void stage_store(const Staged& st) const
+    {
+        if constexpr (kTwSize > 0) {
+            const int t0 = (int)threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < IT; ++i) {
-            const int e = tid + i * NT;
-            if (e < SZ) twl[e] = v[i];
+            for (int i = 0; i < kTwIter; ++i) {
+                const int e = t0 + i * NT;
+                if (e < kTwSize) twl[e] = st.v[i];
+            }
         }
     }
-    return DevCtx<L, PLANS>{twl};
+    __device__ void stage() const { stage_store(stage_load()); }
+};
+
+template <int L, int NT, int PLANS>
+__device__ __forceinline__ DevCtx<L, NT, PLANS> make_ctx(float2* twl)
+{
+    return DevCtx<L, NT, PLANS>{twl};
 }
 
 template <int L, bool BF16>
 __global__ __launch_bounds__(row_nt(L)) void k_row_fwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * (row_np(L) + 1)];
+    __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
     row_fwd_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
@@ -69,7 +85,7 @@ template <int L, bool BF16>
 __global__ __launch_bounds__(row_nt(L)) void k_row_inv(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * (row_np(L) + 1)];
+    __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
     row_inv_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
@@ -78,7 +94,7 @@ template <int L, bool BF16>
 __global__ __launch_bounds__(row_nt(L)) void k_conv1d(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * (row_np(L) + 1)];
+    __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
     conv1d_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
@@ -103,7 +119,7 @@ template <int L>
 __global__ __launch_bounds__(row_nt(L)) void k_spec_row(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * (row_np(L) + 1)];
+    __shared__ float2 T[L * row_lp(L)];
     spec_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 

@@ -17,7 +17,7 @@ struct LaunchTrace {
     int count;
     __host__ void mark(hipStream_t st)
     {
-        if (count < n) hipEventRecord(ev[count], st);
+        if (count < n) (void)hipEventRecord(ev[count], st);
         ++count;
     }
 };

@@ -97,13 +97,17 @@ struct RowMeta {
 
 // ---------------------------------------------------------------- tiling
 // Row kernels: NP line pairs of length L per workgroup (2 <= NP <= 64),
-// tile L x (NP+1).
+// tile L x row_lp(L) (line stride padded so that the transposed accesses of the
+// load and store phases spread over the LDS banks).
 constexpr int row_np(int L) { return 4096 / L < 2 ? 2 : (4096 / L > 64 ? 64 : 4096 / L); }
+constexpr int row_lp(int L) { return row_np(L) + 1; }
 // Column kernels along the middle axis / the out axis of a 2-D grid:
-// TW adjacent lines, tile L x TW (<= 64 KiB).
-constexpr int col_tw(int L) { return 8192 / L > 16 ? 16 : (8192 / L < 1 ? 1 : 8192 / L); }
+// TW adjacent lines, tile L x TW of up to 128 KiB (gfx950 gives a workgroup
+// up to 160 KiB of LDS), so that even 2048-point lines read row segments of
+// 64 bytes; narrower tiles waste most of each fetched cache line.
+constexpr int col_tw(int L) { return 16384 / L > 16 ? 16 : (16384 / L < 1 ? 1 : 16384 / L); }
 // Out-axis kernel of a 3-D grid: two mirrored k_mid rows x TW lines.
-constexpr int mul3_tw(int L) { return 4096 / L > 16 ? 16 : (4096 / L < 1 ? 1 : 4096 / L); }
+constexpr int mul3_tw(int L) { return 8192 / L > 16 ? 16 : (8192 / L < 1 ? 1 : 8192 / L); }
 
 // Threads of a workgroup for a tile of `points` complex values: 16 points per
 // thread per pass (two radix-8 butterflies), between 64 and 1024 threads.
