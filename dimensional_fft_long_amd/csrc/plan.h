@@ -105,22 +105,26 @@ constexpr int row_lp(int L) { return row_np(L) + 1; }
 // TW adjacent lines, tile L x TW of up to 128 KiB (gfx950 gives a workgroup
 // up to 160 KiB of LDS), so that even 2048-point lines read row segments of
 // 64 bytes; narrower tiles waste most of each fetched cache line.
-constexpr int col_tw(int L) { return 16384 / L > 16 ? 16 : (16384 / L < 1 ? 1 : 16384 / L); }
+// 512-point lines take 8 (three workgroups per CU instead of two; neighbouring
+// tiles share their cache lines in L2, see the out-axis workgroup order).
+constexpr int col_tw(int L) { return L == 512 ? 8 : (16384 / L > 16 ? 16 : (16384 / L < 1 ? 1 : 16384 / L)); }
 // Out-axis kernel of a 3-D grid: two mirrored k_mid rows x TW lines.
 constexpr int mul3_tw(int L) { return 8192 / L > 16 ? 16 : (8192 / L < 1 ? 1 : 8192 / L); }
 
 // Threads of a workgroup for a tile of `points` complex values: 16 points per
 // thread per pass (two radix-8 butterflies), between 64 and 1024 threads.
+// The row kernels take 8 points per thread: twice the waves to hide HBM
+// latency (they are the memory-bound passes).
 constexpr int tile_threads(int points) { return points / 16 < 64 ? 64 : (points / 16 > 1024 ? 1024 : points / 16); }
-constexpr int row_nt(int L) { return tile_threads(L * row_np(L)); }
+constexpr int row_nt(int L) { return tile_threads(2 * L * row_np(L)); }
 constexpr int col_nt(int L) { return tile_threads(L * col_tw(L)); }
 constexpr int out_tw(int L, int NR) { return NR == 1 ? col_tw(L) : mul3_tw(L); }
 constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
 
 // Recommended workspace: whole channels (all B pairs of a channel are processed
-// together), up to about 128 MiB, at least one channel.  Measured on MI355X
-// (256x256, B=8, C=64): 64 MiB chunks 0.47 ms, 128 MiB 0.44 ms, 256 MiB
-// 0.46 ms per call; larger chunks mean fewer launches and shorter tails.
+// together), up to about 128 MiB, at least one channel.  Measured on MI355X:
+// for 256x256 (B=8, C=64) chunks of 96, 128 and 256 MiB give 0.421, 0.407 and
+// 0.410 ms per call; 128^3 and 1024^2 vary by under 5% from 128 MiB to 1 GiB.
 inline int chunk_channels(const Geom& g, int B, int C, size_t ws_bytes_available)
 {
     const size_t per_ch = (size_t)B * (size_t)g.wsp * 8u;
