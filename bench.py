@@ -80,9 +80,11 @@ def _src_hash():
     return h.hexdigest()[:16]
 
 
-def _traffic_from_profile(kernel_name):
+def _traffic_from_profile(kernel_name, workload, chunk_channels):
     """HBM bytes per launch of `kernel_name` from the committed rocprofv3 PMC
-    summary, if it was taken on the current kernel sources; else None."""
+    summary (FETCH_SIZE and WRITE_SIZE scaled by what they read for a copy of
+    known size), if it was taken on the current kernel sources and the same
+    workload; else None."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
@@ -90,7 +92,8 @@ def _traffic_from_profile(kernel_name):
         rec = json.load(open(path))
     except ValueError:
         return None
-    if rec.get("source_hash") != _src_hash():
+    if (rec.get("source_hash") != _src_hash() or rec.get("workload") != workload
+            or rec.get("chunk_channels") != chunk_channels):
         return None
     return rec.get("kernels", {}).get(kernel_name, {}).get("traffic_bytes_per_launch")
 
@@ -131,6 +134,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ws-mb", type=float, default=None,
                     help="workspace size in MiB (default: the library's recommendation)")
+    ap.add_argument("--copy-probe-mb", type=int, default=None,
+                    help="only run 5 device-to-device copies of this many MiB (a kernel of known HBM "
+                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
@@ -138,6 +144,16 @@ def main():
         return 2
 
     import torch
+
+    if args.copy_probe_mb is not None:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "copies": 5}))
+        return 0
 
     import dimensional_fft_long_amd as H
     import synth
@@ -216,7 +232,7 @@ def main():
     for r in (hbm, alu):
         r["frac"] = r["achieved"] / r["peak"]
     roof = hbm if hbm["frac"] >= alu["frac"] else alu
-    roof.update({"kernel": kernel_label, "avg_us": dom_s * 1e6, "traffic": _traffic_from_profile(dominant)})
+    roof.update({"kernel": kernel_label, "avg_us": dom_s * 1e6, "traffic": _traffic_from_profile(kernel_label, wl.name, nch)})
     roof["other_bound"] = {k: v for k, v in (alu if roof is hbm else hbm).items()}
 
     voxch = wl.B * wl.C * wl.voxels

@@ -458,20 +458,17 @@ __host__ __device__ __forceinline__ void tile_fft(const Ctx& ctx, float2* T)
     }
 }
 
-// Forward transform of NL lines whose first pass reads through f(pos, line)
-// (PIN: only positions < L/2 exist) and whose last pass is left in registers
-// (positions j + r*L/R_last).  `after_load()` runs once the first pass's loads
-// are issued and before they are used (a place to issue more independent
-// loads).  The tile T is scratch; the caller must not touch it before a
-// barrier.
-template <int L, int NL, int NT, bool PIN, class Ctx, class F, class H>
-__host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, const F& f, const H& after_load)
+// Forward transform of NL lines whose first-pass inputs are the registers `s`
+// (positions j + r*L/R0, as left by pass_load_fn; PIN: only positions < L/2
+// are non-zero) and whose last pass is left in registers (positions
+// j + r*L/R_last).  The tile T is scratch; the caller must not touch it
+// before a barrier.
+template <int L, int NL, int NT, bool PIN, class Ctx>
+__host__ __device__ __forceinline__ auto fwd_from_regs(const Ctx& ctx, float2* T,
+                                                       PassRegs<L, pass_radix<L, false>(0), NL, NT>& s)
 {
     constexpr int NP = plan_passes(L);
     constexpr int R0 = pass_radix<L, false>(0);
-    PassRegs<L, R0, NL, NT> s;
-    pass_load_fn<L, R0, NL, NT, PIN>(ctx, f, s);
-    after_load();
     pass_compute<L, R0, 1, NL, NT, false, PIN, false, 0>(ctx, s);
     if constexpr (NP == 1) {
         return s;
@@ -487,18 +484,31 @@ __host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, 
     }
 }
 
+// Forward transform whose first pass reads through the accessor f (see
+// pass_load_fn).  `after_load()` runs once the first pass's loads are issued
+// and before they are used (a place to issue more independent loads).
+template <int L, int NL, int NT, bool PIN, class Ctx, class F, class H>
+__host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, const F& f, const H& after_load)
+{
+    PassRegs<L, pass_radix<L, false>(0), NL, NT> s;
+    pass_load_fn<L, pass_radix<L, false>(0), NL, NT, PIN>(ctx, f, s);
+    after_load();
+    return fwd_from_regs<L, NL, NT, PIN>(ctx, T, s);
+}
+
 // Inverse transform (reversed plan) whose first-pass inputs are the registers
-// `s` (positions j + r*L/R, as left by fwd_from_fn or by a load) and whose
-// last pass writes through g(pos, line, value) (POUT: positions < L/2 only).
-// The tile T must be free for writing (a barrier after its last read).
-template <int L, int NL, int NT, bool POUT, class Ctx, class S, class G>
-__host__ __device__ __forceinline__ void inv_to_fn(const Ctx& ctx, float2* T, S& s, const G& gfn)
+// `s` (positions j + r*L/R, as left by fwd_from_fn or by a load); returns the
+// last pass's registers (positions j + r*L/R0 in natural order, R0 the
+// forward plan's first radix; POUT: only positions < L/2 are valid).  The
+// tile T must be free for writing (a barrier after its last read).
+template <int L, int NL, int NT, bool POUT, class Ctx, class S>
+__host__ __device__ __forceinline__ auto inv_to_regs(const Ctx& ctx, float2* T, S& s)
 {
     constexpr int NP = plan_passes(L);
     constexpr int R0 = pass_radix<L, true>(0);
     pass_compute<L, R0, 1, NL, NT, true, false, POUT && NP == 1, 0>(ctx, s);
     if constexpr (NP == 1) {
-        pass_visit<L, R0, NL, NT, POUT>(ctx, s, gfn);
+        return s;
     } else {
         pass_store_lds<L, R0, 1, NL, NL, NT, false>(ctx, T, s);
         ctx.sync();
@@ -507,8 +517,16 @@ __host__ __device__ __forceinline__ void inv_to_fn(const Ctx& ctx, float2* T, S&
         PassRegs<L, RL, NL, NT> t;
         pass_load_lds<L, RL, NL, NL, NT, false>(ctx, T, t);
         pass_compute<L, RL, NSL, NL, NT, true, false, POUT, Ctx::kRevBase + tw_local_off<L, true>(NP - 1)>(ctx, t);
-        pass_visit<L, RL, NL, NT, POUT>(ctx, t, gfn);
+        return t;
     }
+}
+
+// Inverse transform whose last pass writes through gfn (see pass_visit).
+template <int L, int NL, int NT, bool POUT, class Ctx, class S, class G>
+__host__ __device__ __forceinline__ void inv_to_fn(const Ctx& ctx, float2* T, S& s, const G& gfn)
+{
+    auto t = inv_to_regs<L, NL, NT, POUT>(ctx, T, s);
+    pass_visit<L, pass_radix<L, false>(0), NL, NT, POUT>(ctx, t, gfn);
 }
 
 // Forward transform from f (first pass) to g (last pass), full output.
