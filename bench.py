@@ -27,6 +27,7 @@ HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
 # fp32 vector peak without packed-FP32 instructions (the build disables them):
 # 256 CUs x 64 lanes x 2 flop (FMA) x 2.4 GHz.
 ALU_PEAK = 256 * 64 * 2 * 2.4e9
+SETTLE_S = 0.3               # untimed calls before the warmup steps (GPU clock ramp)
 DEFAULT_WORKLOAD = "2d_256x256_b8_c64_f32"
 
 
@@ -187,6 +188,16 @@ def main():
     probe = [torch.cuda.Event(enable_timing=True) for _ in range(1)]
     n_launch = H.fftconv_fwd_traced(x, al, be, kh, y, ws, probe)
     torch.cuda.synchronize()
+    # Clock settle (untimed): the GPU needs tens of milliseconds of load to
+    # reach its steady clock (256^2: the first ~20 ms of calls run ~10% slower),
+    # so calls repeat for at least SETTLE_S before the W warmup steps.
+    t0 = time.perf_counter()
+    settle_calls = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(8):
+            H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
+        settle_calls += 8
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
     torch.cuda.synchronize()
@@ -209,6 +220,16 @@ def main():
     for k in range(args.steps):
         H.fftconv_fwd_traced(x, al, be, kh, y, ws, evs[k])
     torch.cuda.synchronize()
+    # The interval between two events around a kernel also holds the
+    # processing of one event marker; measured here as the interval between
+    # two markers with nothing in between, then taken off each kernel's.
+    mk = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    st = torch.cuda.current_stream()
+    for k in range(args.steps):
+        mk[2 * k].record(st)
+        mk[2 * k + 1].record(st)
+    torch.cuda.synchronize()
+    marker_ms = sorted(mk[2 * k].elapsed_time(mk[2 * k + 1]) for k in range(args.steps))[args.steps // 2]
 
     plan = H.launch_plan(wl.B, wl.C, wl.dims, x.dtype, ws_bytes)
     g = _geom(wl.dims)
@@ -220,7 +241,7 @@ def main():
         e = evs[k]
         step_ms.append(e[0].elapsed_time(e[-1]))
         for j in range(n_launch):
-            per_pass[names[j % len(names)]].append(e[j].elapsed_time(e[j + 1]))
+            per_pass[names[j % len(names)]].append(e[j].elapsed_time(e[j + 1]) - marker_ms)
     dominant = max(per_pass, key=lambda nm: sum(per_pass[nm]))
     dom_s = sum(per_pass[dominant]) / len(per_pass[dominant]) / 1e3
     nch = plan["chunk_channels"]
@@ -257,6 +278,8 @@ def main():
         "bytes_min": bytes_min,
         "traced_step_ms_median": sorted(step_ms)[len(step_ms) // 2],
         "per_kernel_us": {nm: 1e3 * sum(v) / len(v) for nm, v in per_pass.items()},
+        "event_marker_us": 1e3 * marker_ms,
+        "settle_calls": settle_calls,
         "spectrum_ms": spectrum_ms,
         "roofline": roof,
     }

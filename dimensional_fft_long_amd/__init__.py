@@ -30,7 +30,8 @@ LIB_PATH = os.path.join(HERE, "libhyenand.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 
-EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_bytes", "hyenand_kernel_spectrum",
+EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_bytes",
+           "hyenand_kernel_spectrum_tile", "hyenand_kernel_spectrum",
            "hyenand_fftconv_workspace_bytes", "hyenand_fftconv_workspace_min_bytes", "hyenand_fftconv_fwd",
            "hyenand_fftconv_fwd_traced", "hyenand_fftconv_launch_plan")
 
@@ -52,6 +53,8 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_version.restype = I
     lib.hyenand_kernel_spectrum_bytes.argtypes = [I, I, P]
     lib.hyenand_kernel_spectrum_bytes.restype = SZ
+    lib.hyenand_kernel_spectrum_tile.argtypes = [I, P]
+    lib.hyenand_kernel_spectrum_tile.restype = I
     lib.hyenand_kernel_spectrum.argtypes = [P, P, I, I, P, P]
     lib.hyenand_kernel_spectrum.restype = I
     lib.hyenand_fftconv_workspace_bytes.argtypes = [I, I, I, P, I]
@@ -98,6 +101,11 @@ def _dtype_code(t: torch.dtype) -> int:
 
 def spectrum_bytes(C: int, dims) -> int:
     return int(get_lib().hyenand_kernel_spectrum_bytes(C, len(dims), _dims_arr(dims)))
+
+
+def spectrum_tile(dims) -> int:
+    """Slot tile T of the K_hat layout (see hyenand_kernel_spectrum_bytes)."""
+    return int(get_lib().hyenand_kernel_spectrum_tile(len(dims), _dims_arr(dims)))
 
 
 def workspace_bytes(B: int, C: int, dims, dtype=torch.float32, minimum: bool = False) -> int:

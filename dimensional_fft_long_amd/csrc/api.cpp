@@ -59,6 +59,13 @@ size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims)
     return (size_t)C * (size_t)g.ksz * 8u;
 }
 
+int hyenand_kernel_spectrum_tile(int d, const int64_t* dims)
+{
+    Geom g;
+    if (!make_geom(d, dims, &g)) return 0;
+    return g.lt;
+}
+
 int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream)
 {
     if (C < 0) return HYENAND_ERR_INVALID_ARG;

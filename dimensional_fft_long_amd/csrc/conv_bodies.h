@@ -62,11 +62,16 @@ __host__ __device__ __forceinline__ void store_y(const ConvArgs& a, long long i,
     else static_cast<float*>(a.y)[i] = v;
 }
 
-// Workspace offset of row r (r = j_out * n_mid + j_mid) inside one pair.
-__host__ __device__ __forceinline__ long long row_ws(const Geom& g, int r)
+// Workspace plane row of grid row r (r = j_out * n_mid + j_mid): the mid axis
+// is padded to N_mid in the workspace.
+__host__ __device__ __forceinline__ long long ws_row(const Geom& g, int r)
 {
-    return ((long long)(r / g.n_mid) * g.N_mid + (r % g.n_mid)) * g.S;
+    return (long long)(r / g.n_mid) * g.N_mid + (r % g.n_mid);
 }
+
+// Rows of one pair's workspace plane and the stride between its slot tiles.
+__host__ __device__ __forceinline__ long long ws_rows(const Geom& g) { return (long long)g.n_out * g.N_mid; }
+__host__ __device__ __forceinline__ long long ws_tile_stride(const Geom& g) { return ws_rows(g) * g.lt; }
 
 // Line pair h of a row workgroup (d >= 2): pair slot q = h / hp (channel-major
 // in the chunk: c = c0 + q / B, b = q % B) and rows r = 2 (h % hp), r + 1.
@@ -85,8 +90,8 @@ __host__ __device__ __forceinline__ void row_meta(const Ctx& ctx, int bid, const
             const int c = a.c0 + q / a.B, b = q % a.B;
             m.o0 = ((long long)b * a.C + c) * g.vox + (long long)r * g.n_in;
             m.o1 = m.o0 + g.n_in;
-            m.w0 = (long long)q * g.wsp + row_ws(g, r);
-            m.w1 = (long long)q * g.wsp + row_ws(g, r + 1);
+            m.w0 = (long long)q * g.wsp + ws_row(g, r) * g.lt;
+            m.w1 = (long long)q * g.wsp + ws_row(g, r + 1) * g.lt;
             m.al0 = m.al1 = a.alpha[c];
             m.be0 = m.be1 = a.beta[c];
             m.valid1 = 1;
@@ -130,9 +135,14 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
     // Separate the two rows: with Z = FFT(u_a + i u_b),
     //   2 U_a[k] = Z[k] + conj Z[L-k],   2 U_b[k] = -i (Z[k] - conj Z[L-k]).
     // The factor 2 is folded into the kernel spectrum.
+    // Lanes run over (slot in tile, line pair, slot tile) so that a wave's
+    // stores cover whole runs of the tile-major workspace.
+    const long long tstride = ws_tile_stride(a.g);
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT, lp = idx / S, k = idx % S;
+        const int idx = tid + i * NT, u = idx & (a.g.lt - 1), rest = idx >> a.g.lt_log;
+        const int lp = rest % NP, k = ((rest / NP) << a.g.lt_log) + u;
+        const long long wo = (long long)(k >> a.g.lt_log) * tstride + u;
         const RowMeta& md = M[lp];
         const float2 Z = T[k * LP + lp];
         const float2 Zm = T[(k == 0 ? S : L - k) * LP + lp];
@@ -145,8 +155,8 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
             ob = make_float2(Z.y + Zm.y, Zm.x - Z.x);
         }
         if (md.valid) {
-            a.ws[md.w0 + k] = oa;
-            a.ws[md.w1 + k] = ob;
+            a.ws[md.w0 + wo] = oa;
+            a.ws[md.w1 + wo] = ob;
         }
     }
 }
@@ -165,16 +175,27 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
     ctx.sync();
     // Rebuild Z = Y_a + i Y_b over the full length from the two half spectra
     // (Hermitian extension), slot 0 holding (bin 0, bin L/2).
+    // Lanes run over (slot in tile, line pair, slot tile): whole runs of the
+    // tile-major workspace per wave.
+    const long long tstride = ws_tile_stride(a.g);
+    auto slot = [&](int idx, int& lp) {
+        const int u = idx & (a.g.lt - 1), rest = idx >> a.g.lt_log;
+        lp = rest % NP;
+        return ((rest / NP) << a.g.lt_log) + u;
+    };
     float2 ya[ITER], yb[ITER];
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT, lp = idx / S, k = idx % S;
-        ya[i] = a.ws[M[lp].w0 + k];
-        yb[i] = a.ws[M[lp].w1 + k];
+        int lp;
+        const int k = slot(tid + i * NT, lp);
+        const long long wo = (long long)(k >> a.g.lt_log) * tstride + (k & (a.g.lt - 1));
+        ya[i] = a.ws[M[lp].w0 + wo];
+        yb[i] = a.ws[M[lp].w1 + wo];
     }
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT, lp = idx / S, k = idx % S;
+        int lp;
+        const int k = slot(tid + i * NT, lp);
         if (k == 0) {
             T[lp] = make_float2(ya[i].x, yb[i].x);
             T[S * LP + lp] = make_float2(ya[i].y, yb[i].y);
@@ -213,9 +234,10 @@ __host__ __device__ __forceinline__ void col_mid_body(const Ctx& ctx, int bid, c
     const int q = bid / tpp, lam0 = (bid % tpp) * TW;
     float2* base = a.ws + (long long)q * g.wsp;
     const int sl = ilog2(g.S);
+    const long long rows = ws_rows(g);
     auto off = [&](int pos, int l) -> long long {
         const int lam = lam0 + l;
-        return ((long long)(lam >> sl) * g.N_mid + pos) * g.S + (lam & (g.S - 1));
+        return tm_index(g, rows, (long long)(lam >> sl) * g.N_mid + pos, lam & (g.S - 1));
     };
     auto ld = [&](int pos, int l) -> float2 {
         const bool ok = lam0 + l < lines;
@@ -281,7 +303,7 @@ __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const
                                                            const float2* kc, float2* T)
 {
     constexpr int NL = NR * TW;
-    const long long PS = (long long)g.N_mid * g.S;
+    const long long PS = (long long)g.N_mid * g.lt;  // slot 0 of (k_out, k_mid): (k_out N_mid + k_mid) lt
     const int njobs = o.self_mirror ? NR * (L / 2 + 1) : L;
     for (int job = ctx.tid(); job < njobs; job += NT) {
         int ra, rb, pa, pb;
@@ -293,8 +315,8 @@ __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const
         }
         const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
         const float2 Za = T[ea], Zb = T[eb];
-        const float2 Sa = kc[pa * PS + (long long)o.rows[ra] * g.S];
-        const float2 Sb = kc[pb * PS + (long long)o.rows[rb] * g.S];
+        const float2 Sa = kc[pa * PS + (long long)o.rows[ra] * g.lt];
+        const float2 Sb = kc[pb * PS + (long long)o.rows[rb] * g.lt];
         const float2 Da = kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]];
         const float2 Db = kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]];
         const float2 Wa = cadd(cmul(Za, Sa), cmul(cconj(Zb), Da));
@@ -327,17 +349,22 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, c
     constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
     const Geom& g = a.g;
     const OutTile o = out_tile<NR, TW>(g, a.B, a.nch, bid);
-    const long long PS = (long long)g.N_mid * g.S;
+    // The tile's slots k0 + [0, TW) lie in one slot tile of the tile-major
+    // planes (the slot tile is a power of two, a multiple of TW or S < TW),
+    // whose rows are k_out * N_mid + k_mid: position stride PS = N_mid * lt,
+    // and the tile starts at slot k0 % lt of its slot tile.
+    const long long PS = (long long)g.N_mid * g.lt;
+    const int k0 = o.t * TW, u0 = k0 & (g.lt - 1);
     const float2* kc = a.khat + (long long)(a.c0 + o.c_local) * g.ksz;
-    float2* base = a.ws + ((long long)o.c_local * a.B + o.b) * g.wsp;
-    const int k0 = o.t * TW;
+    const float2* kt = kc + (long long)(k0 >> g.lt_log) * ((long long)g.N_out * g.N_mid * g.lt);
+    float2* base = a.ws + ((long long)o.c_local * a.B + o.b) * g.wsp + (long long)(k0 >> g.lt_log) * ws_tile_stride(g);
     auto lvalid = [&](int l) { return k0 + l % TW < g.S; };
     // Element (pos = j + q, line l) of the workspace or of the kernel spectrum
-    // is at q*PS (wave-uniform, q a constant of the unrolled loops) plus the
-    // lane's byte offset 8*(j*PS + row*S + k0 + l%TW), which stays below 4 GiB
-    // (j < L/R for R >= 2 and one channel's spectrum is at most 4 GiB).
+    // tile is at q*PS (wave-uniform, q a constant of the unrolled loops) plus
+    // the lane's byte offset 8*(j*PS + row*lt + u0 + l%TW), which stays below
+    // 4 GiB (j < L/R for R >= 2 and one channel's spectrum is at most 4 GiB).
     auto lane_bytes = [&](int j, int l) -> unsigned {
-        return 8u * ((unsigned)j * (unsigned)PS + (unsigned)o.rows[l / TW] * (unsigned)g.S + (unsigned)(k0 + l % TW));
+        return 8u * ((unsigned)j * (unsigned)PS + (unsigned)o.rows[l / TW] * (unsigned)g.lt + (unsigned)(u0 + l % TW));
     };
     auto at = [](auto* p, long long q_elems, unsigned bytes) { return add_bytes(p + q_elems, bytes); };
     auto ld = [&](int j, int q, int l) -> float2 {
@@ -360,7 +387,7 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, c
             kok[i] = bf_valid<PL::NB, NT>(g) && lvalid(l) && k0 + l % TW != 0;
             const unsigned lb = kok[i] ? lane_bytes(j, l) : 8u;
 #pragma unroll
-            for (int r = 0; r < RL; ++r) kv[i][r] = *at(kc, (long long)r * (L / RL) * PS, lb);
+            for (int r = 0; r < RL; ++r) kv[i][r] = *at(kt, (long long)r * (L / RL) * PS, lb);
         }
         ctx.stage_store(tw_staged);
     };
@@ -563,8 +590,8 @@ __host__ __device__ __forceinline__ void spec_row_body(const Ctx& ctx, int bid, 
         } else {
             const int c = h / hp, r = (h % hp) * 2;
             float2* kc = khat + (long long)c * g.ksz;
-            kc[(long long)r * S + k] = Xa;
-            kc[(long long)(r + 1) * S + k] = Xb;
+            kc[tm_index(g, rc, r, k)] = Xa;
+            kc[tm_index(g, rc, r + 1, k)] = Xb;
         }
     }
 }
@@ -579,19 +606,20 @@ __host__ __device__ __forceinline__ void spec_mid_body(const Ctx& ctx, int bid, 
     const int tpc = (lines + TW - 1) / TW;
     const int c = bid / tpc, lam0 = (bid % tpc) * TW;
     float2* base = const_cast<float2*>(a.khat) + (long long)c * g.ksz;
+    const long long rows = (long long)g.N_out * g.N_mid;
     const int tid = ctx.tid();
     ctx.stage();
     for (int idx = tid; idx < L * TW; idx += NT) {
         const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
         float2 z = make_float2(0.f, 0.f);
-        if (lam < lines) z = base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S];
+        if (lam < lines) z = base[tm_index(g, rows, (long long)(lam / g.S) * g.N_mid + pos, lam % g.S)];
         T[pos * TW + l] = z;
     }
     ctx.sync();
     tile_fft<L, TW, TW, NT, false, false, false>(ctx, T);
     for (int idx = tid; idx < L * TW; idx += NT) {
         const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
-        if (lam < lines) base[((long long)(lam / g.S) * g.N_mid + pos) * g.S + lam % g.S] = T[pos * TW + l];
+        if (lam < lines) base[tm_index(g, rows, (long long)(lam / g.S) * g.N_mid + pos, lam % g.S)] = T[pos * TW + l];
     }
 }
 
@@ -605,7 +633,7 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
     constexpr int NL = NR * TW, NT = out_nt(L, NR);
     const Geom& g = a.g;
     const OutTile o = out_tile<NR, TW>(g, 1, a.C, bid);
-    const long long PS = (long long)g.N_mid * g.S;
+    const long long rows = (long long)g.N_out * g.N_mid;
     float2* kc = const_cast<float2*>(a.khat) + (long long)o.c_local * g.ksz;
     const float gsc = 1.0f / (2.0f * (float)g.N_out * (float)g.N_mid * (float)g.N_in);
     const int tid = ctx.tid();
@@ -614,7 +642,7 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
         const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
         const int k = o.t * TW + col;
         float2 z = make_float2(0.f, 0.f);
-        if (k < g.S) z = kc[pos * PS + (long long)o.rows[row] * g.S + k];
+        if (k < g.S) z = kc[tm_index(g, rows, (long long)pos * g.N_mid + o.rows[row], k)];
         T[pos * NL + l] = z;
     }
     ctx.sync();
@@ -656,7 +684,7 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
     for (int idx = tid; idx < L * NL; idx += NT) {
         const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
         const int k = o.t * TW + col;
-        if (k < g.S) kc[pos * PS + (long long)o.rows[row] * g.S + k] = T[pos * NL + l];
+        if (k < g.S) kc[tm_index(g, rows, (long long)pos * g.N_mid + o.rows[row], k)] = T[pos * NL + l];
     }
 }
 

@@ -32,6 +32,32 @@
 
 namespace hyenand {
 
+// ---------------------------------------------------------------- tiling
+// Row kernels: NP line pairs of length L per workgroup (2 <= NP <= 64),
+// tile L x row_lp(L) (line stride padded so that the transposed accesses of the
+// load and store phases spread over the LDS banks).
+constexpr int row_np(int L) { return 4096 / L < 2 ? 2 : (4096 / L > 64 ? 64 : 4096 / L); }
+constexpr int row_lp(int L) { return row_np(L) + 1; }
+// Column kernels along the middle axis / the out axis of a 2-D grid:
+// TW adjacent lines, tile L x TW of up to 128 KiB (gfx950 gives a workgroup
+// up to 160 KiB of LDS), so that even 2048-point lines read row segments of
+// 64 bytes; narrower tiles waste most of each fetched cache line.
+// 512-point lines take 8 (three workgroups per CU instead of two; neighbouring
+// tiles share their cache lines in L2, see the out-axis workgroup order).
+constexpr int col_tw(int L) { return L == 512 ? 8 : (16384 / L > 16 ? 16 : (16384 / L < 1 ? 1 : 16384 / L)); }
+// Out-axis kernel of a 3-D grid: two mirrored k_mid rows x TW lines.
+constexpr int mul3_tw(int L) { return 8192 / L > 16 ? 16 : (8192 / L < 1 ? 1 : 8192 / L); }
+
+// Threads of a workgroup for a tile of `points` complex values: 16 points per
+// thread per pass (two radix-8 butterflies), between 64 and 1024 threads.
+// The row kernels take 8 points per thread: twice the waves to hide HBM
+// latency (they are the memory-bound passes).
+constexpr int tile_threads(int points) { return points / 16 < 64 ? 64 : (points / 16 > 1024 ? 1024 : points / 16); }
+constexpr int row_nt(int L) { return tile_threads(2 * L * row_np(L)); }
+constexpr int col_nt(int L) { return tile_threads(L * col_tw(L)); }
+constexpr int out_tw(int L, int NR) { return NR == 1 ? col_tw(L) : mul3_tw(L); }
+constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
+
 struct Geom {
     int d;
     int n_out, n_mid, n_in;
@@ -42,7 +68,30 @@ struct Geom {
     long long kmain;       // main block complex per channel: N_out * N_mid * S
     long long ksz;         // kmain + N_out * N_mid
     int ke_out, ke_mid, ke_in;  // kernel extents 2n-1 (1 for absent axes)
+    int lt, lt_log;        // slot tile of the tile-major planes (a power of two <= S)
 };
+
+// Slot tile of the kernel spectrum and the workspace: the out-axis kernel's
+// tile width (capped at S), so that each out-axis workgroup's block of a 2-D
+// plane is contiguous.  In 3-D the workgroup's two mirrored k_mid rows stay
+// apart whatever the tile; there tiles of 16 slots (128-byte runs) win on
+// MI355X (128^3: 1.97 -> 1.91 ms) but 8-slot tiles lose to plain rows (512^3:
+// 24.7 -> 26.0 ms), so narrower out-axis tiles keep one tile of S slots.
+constexpr int slot_tile(int d, int N_out, int S)
+{
+    int tw = S;
+    if (d == 2) tw = out_tw(N_out, 1);
+    if (d == 3 && out_tw(N_out, 2) >= 16) tw = out_tw(N_out, 2);
+    return tw < S ? tw : S;
+}
+
+// A plane of `rows` rows (row = k_out * N_mid + k_mid) x S slots stored
+// tile-major: slot tiles of lt consecutive slots, each holding every row,
+//   element (row, slot) at ((slot / lt) * rows + row) * lt + slot % lt.
+__host__ __device__ __forceinline__ long long tm_index(const Geom& g, long long rows, long long row, int slot)
+{
+    return ((long long)(slot >> g.lt_log) * rows + row) * g.lt + (slot & (g.lt - 1));
+}
 
 inline bool is_pow2(long long v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -67,6 +116,9 @@ inline bool make_geom(int d, const int64_t* dims, Geom* g)
     g->ke_out = 2 * g->n_out - 1;
     g->ke_mid = 2 * g->n_mid - 1;
     g->ke_in = 2 * g->n_in - 1;
+    g->lt = slot_tile(d, g->N_out, g->S);
+    g->lt_log = 0;
+    while ((1 << g->lt_log) < g->lt) ++g->lt_log;
     return true;
 }
 
@@ -94,32 +146,6 @@ struct RowMeta {
     float al0, be0, al1, be1;
     int valid, valid1;
 };
-
-// ---------------------------------------------------------------- tiling
-// Row kernels: NP line pairs of length L per workgroup (2 <= NP <= 64),
-// tile L x row_lp(L) (line stride padded so that the transposed accesses of the
-// load and store phases spread over the LDS banks).
-constexpr int row_np(int L) { return 4096 / L < 2 ? 2 : (4096 / L > 64 ? 64 : 4096 / L); }
-constexpr int row_lp(int L) { return row_np(L) + 1; }
-// Column kernels along the middle axis / the out axis of a 2-D grid:
-// TW adjacent lines, tile L x TW of up to 128 KiB (gfx950 gives a workgroup
-// up to 160 KiB of LDS), so that even 2048-point lines read row segments of
-// 64 bytes; narrower tiles waste most of each fetched cache line.
-// 512-point lines take 8 (three workgroups per CU instead of two; neighbouring
-// tiles share their cache lines in L2, see the out-axis workgroup order).
-constexpr int col_tw(int L) { return L == 512 ? 8 : (16384 / L > 16 ? 16 : (16384 / L < 1 ? 1 : 16384 / L)); }
-// Out-axis kernel of a 3-D grid: two mirrored k_mid rows x TW lines.
-constexpr int mul3_tw(int L) { return 8192 / L > 16 ? 16 : (8192 / L < 1 ? 1 : 8192 / L); }
-
-// Threads of a workgroup for a tile of `points` complex values: 16 points per
-// thread per pass (two radix-8 butterflies), between 64 and 1024 threads.
-// The row kernels take 8 points per thread: twice the waves to hide HBM
-// latency (they are the memory-bound passes).
-constexpr int tile_threads(int points) { return points / 16 < 64 ? 64 : (points / 16 > 1024 ? 1024 : points / 16); }
-constexpr int row_nt(int L) { return tile_threads(2 * L * row_np(L)); }
-constexpr int col_nt(int L) { return tile_threads(L * col_tw(L)); }
-constexpr int out_tw(int L, int NR) { return NR == 1 ? col_tw(L) : mul3_tw(L); }
-constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
 
 // Recommended workspace: whole channels (all B pairs of a channel are processed
 // together), up to about 128 MiB, at least one channel.  Measured on MI355X:

@@ -69,14 +69,26 @@ int hyenand_version(void);
  * Bytes of the kernel spectrum K_hat for C channels of a grid `dims`.  0 for an
  * unsupported shape.  Layout, per channel (complex64 = two fp32, real first),
  * with N_a = 2 n_a and (out, mid, in) = the grid axes (3-D), (axis 0, -, axis 1)
- * (2-D) or (-, -, axis 0) (1-D), absent axes of length 1, S = N_in / 2:
- *   main[k_out][k_mid][k_in], k_in in [0, S):  g * Khat(k)                     (k_in >= 1)
- *                              k_in = 0:       g * (Khat(k,0) + Khat(k,S)) / 2
- *   then dblk[k_out][k_mid]:                   g * (Khat(k,0) - Khat(k,S)) / 2
+ * (2-D) or (-, -, axis 0) (1-D), absent axes of length 1, S = N_in / 2, and
+ * T = hyenand_kernel_spectrum_tile(d, dims) (a power of two dividing S):
+ *   main, N_out * N_mid * S values, slot-tile-major: the value for
+ *     (k_out, k_mid, k_in) sits at ((k_in / T) * N_out * N_mid
+ *                                   + k_out * N_mid + k_mid) * T + k_in % T,
+ *     holding  g * Khat(k)                           for k_in >= 1,
+ *              g * (Khat(k,0) + Khat(k,S)) / 2       for k_in = 0;
+ *   then dblk[k_out][k_mid]:  g * (Khat(k,0) - Khat(k,S)) / 2,
  * where Khat is the DFT over the padded grid of the kernel placed at offset
- * delta -> index delta mod N_a, and g = 1 / (2 * prod_a N_a).
+ * delta -> index delta mod N_a, and g = 1 / (2 * prod_a N_a).  (For d = 1 the
+ * main block is simply [k_in].)  The slot tiles make each out-axis workgroup's
+ * block of the spectrum contiguous.
  */
 size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims);
+
+/*
+ * Slot tile T of the K_hat layout above for a grid `dims` (0 for an
+ * unsupported shape).
+ */
+int hyenand_kernel_spectrum_tile(int d, const int64_t* dims);
 
 /*
  * Kernel spectrum precompute (once per parameter set; not part of the timed

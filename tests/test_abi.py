@@ -67,6 +67,25 @@ def test_sizes(H):
     # Unsupported shapes size to 0.
     for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(2048)), (4, _dims(2, 2, 2, 2))]:
         assert lib.hyenand_kernel_spectrum_bytes(2, d, dims) == 0
+        assert lib.hyenand_kernel_spectrum_tile(d, dims) == 0
+
+
+def test_spectrum_slot_tile(H):
+    """The K_hat slot tile: the out-axis workgroup's tile width capped at S, a
+    power of two dividing S (1-D: the whole row)."""
+    lib = H.get_lib()
+    assert lib.hyenand_kernel_spectrum_tile(2, _dims(256, 256)) == 8       # 512-point out lines: 8-line tiles
+    assert lib.hyenand_kernel_spectrum_tile(2, _dims(1024, 1024)) == 8     # 2048-point: 16384 / 2048
+    assert lib.hyenand_kernel_spectrum_tile(2, _dims(512, 4)) == 4         # capped at S = 4
+    assert lib.hyenand_kernel_spectrum_tile(3, _dims(128, 128, 128)) == 16  # 256-point, two mirrored rows
+    assert lib.hyenand_kernel_spectrum_tile(3, _dims(512, 512, 512)) == 512  # 8-slot out tiles: plain rows
+    assert lib.hyenand_kernel_spectrum_tile(1, _dims(64)) == 64
+    for d in (1, 2, 3):
+        for e in range(1, 11):
+            dims = _dims(*([2 ** e] * d))
+            t = lib.hyenand_kernel_spectrum_tile(d, dims)
+            S = 2 ** e
+            assert t >= 1 and S % t == 0 and t & (t - 1) == 0
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first

@@ -75,7 +75,8 @@ def test_medium_grids_match_fft_oracle(H, dims, B, C):
 def test_kernel_spectrum_layout(H, dims):
     """K_hat against the oracle's DFT of the wrap-placed kernel, in the library
     layout: main slots k_in >= 1 hold g*Khat, slot 0 holds g*(Khat0 + KhatS)/2,
-    the trailing block g*(Khat0 - KhatS)/2, g = 1/(2 prod N)."""
+    the trailing block g*(Khat0 - KhatS)/2, g = 1/(2 prod N); the main block is
+    slot-tile-major, [S/T][N_out][N_mid][T]."""
     C = 3
     w = synth.make(dims, B=1, C=C, seed=3, dtype="f32")
     kh = H.kernel_spectrum(w["K"].to("cuda")).cpu().numpy().reshape(C, -1)
@@ -85,7 +86,9 @@ def test_kernel_spectrum_layout(H, dims):
     S = ni
     full = oracle.kernel_spectrum(w["K"].numpy(), dims).reshape(C, No, Nm, Ni)
     g = 1.0 / (2 * No * Nm * Ni)
-    main = kh[:, :No * Nm * S].reshape(C, No, Nm, S)
+    T = H.spectrum_tile(dims)
+    assert T >= 1 and S % T == 0 and (T & (T - 1)) == 0
+    main = kh[:, :No * Nm * S].reshape(C, S // T, No, Nm, T).transpose(0, 2, 3, 1, 4).reshape(C, No, Nm, S)
     dblk = kh[:, No * Nm * S:].reshape(C, No, Nm)
     scale = np.abs(full).max() * g
     assert np.abs(main[..., 1:] - g * full[..., 1:S]).max() <= 1e-5 * scale
