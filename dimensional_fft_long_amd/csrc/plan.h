@@ -148,9 +148,11 @@ struct RowMeta {
 };
 
 // Recommended workspace: whole channels (all B pairs of a channel are processed
-// together), up to about 128 MiB, at least one channel.  Measured on MI355X:
-// for 256x256 (B=8, C=64) chunks of 96, 128 and 256 MiB give 0.421, 0.407 and
-// 0.410 ms per call; 128^3 and 1024^2 vary by under 5% from 128 MiB to 1 GiB.
+// together), up to about 256 MiB, at least one channel.  Measured on MI355X
+// (ms per call for 64 / 128 / 256 MiB): 256x256 B=8 C=64 0.363 / 0.324 /
+// 0.324; 1024^2 B=2 C=128 4.67 / 4.39 / 4.29; 128^3 B=1 C=32 2.15 / 1.90 /
+// 1.82.  Smaller chunks lose to launch tails; the workspace does not need to
+// fit in the 256 MB Infinity Cache.
 inline int chunk_channels(const Geom& g, int B, int C, size_t ws_bytes_available)
 {
     const size_t per_ch = (size_t)B * (size_t)g.wsp * 8u;
@@ -164,7 +166,7 @@ inline size_t recommended_workspace(const Geom& g, int B, int C)
 {
     const size_t per_ch = (size_t)B * (size_t)g.wsp * 8u;
     if (per_ch == 0) return 0;
-    const size_t target = (size_t)128 << 20;
+    const size_t target = (size_t)256 << 20;
     size_t n = target / per_ch;
     if (n < 1) n = 1;
     if (n > (size_t)C) n = (size_t)C;

@@ -102,7 +102,7 @@ int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int
 
 /*
  * Workspace bytes recommended for hyenand_fftconv_fwd: whole channels (all B
- * batch entries of a channel are processed together) up to about 128 MiB.  The
+ * batch entries of a channel are processed together) up to about 256 MiB.  The
  * minimum accepted is one channel, B * n_0 * (prod of the middle padded axes) *
  * S * 8 bytes (0 for d = 1); a larger workspace processes more channels per
  * kernel chain.  0 for d = 1, for an empty call, or for an unsupported shape.
