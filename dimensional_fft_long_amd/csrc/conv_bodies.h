@@ -338,87 +338,143 @@ __host__ __device__ __forceinline__ T* add_bytes(T* p, unsigned bytes)
     return reinterpret_cast<T*>(reinterpret_cast<Byte*>(p) + bytes);
 }
 
-// Out axis, one (channel, tile, batch entry) per workgroup: forward FFT whose
-// first pass reads the n_out rows of the workspace, product with the kernel
-// spectrum in registers (the forward's last pass leaves each thread holding
-// exactly the positions the inverse's first pass needs), inverse FFT whose
-// last pass writes the n_out kept rows back.
+// Work items of the out-axis kernel: (channel, tile, batch entry).
+template <int NR, int TW>
+__host__ __device__ __forceinline__ int out_items(const Geom& g, int B, int nch)
+{
+    const int ct = (g.S + TW - 1) / TW;
+    const int nrp = NR == 1 ? 1 : g.N_mid / 2;
+    return nch * nrp * ct * B;
+}
+
+// Addresses of one out-axis work item.  The tile's slots k0 + [0, TW) lie in
+// one slot tile of the tile-major planes (the slot tile is a power of two, a
+// multiple of TW or S < TW), whose rows are k_out * N_mid + k_mid; the tile
+// starts at slot u0 = k0 % lt of its slot tile.
+struct OutView {
+    OutTile o;
+    int k0, u0;
+    const float2* kc;  // the channel's kernel spectrum
+    const float2* kt;  // its slot tile
+    float2* base;      // the pair's workspace slot tile
+};
+
+template <int NR, int TW>
+__host__ __device__ __forceinline__ OutView out_view(const ConvArgs& a, int item)
+{
+    const Geom& g = a.g;
+    OutView v;
+    v.o = out_tile<NR, TW>(g, a.B, a.nch, item);
+    v.k0 = v.o.t * TW;
+    v.u0 = v.k0 & (g.lt - 1);
+    v.kc = a.khat + (long long)(a.c0 + v.o.c_local) * g.ksz;
+    v.kt = v.kc + (long long)(v.k0 >> g.lt_log) * ((long long)g.N_out * g.N_mid * g.lt);
+    v.base = a.ws + ((long long)v.o.c_local * a.B + v.o.b) * g.wsp + (long long)(v.k0 >> g.lt_log) * ws_tile_stride(g);
+    return v;
+}
+
+// Out axis: forward FFT whose first pass reads the n_out rows of the
+// workspace, product with the kernel spectrum in registers (the forward's last
+// pass leaves each thread holding exactly the positions the inverse's first
+// pass needs), inverse FFT whose last pass writes the n_out kept rows back.
+// Looping kernels (out_looped) run the items bid, bid + nblk, ... (nblk = the
+// grid, one workgroup per CU): no workgroup launch and tail per item, and the
+// item ids keep the XCD-blocked order of out_tile when nblk is a multiple of 8.
 template <int L, int NR, class Ctx>
-__host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+__host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, int nblk, const ConvArgs& a,
+                                                      float2* T)
 {
     constexpr int TW = out_tw(L, NR);
     constexpr int NL = NR * TW, NT = out_nt(L, NR);
+    constexpr int R0 = pass_radix<L, false>(0);
     constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
+    constexpr bool kLoop = out_looped(L, NR);
     const Geom& g = a.g;
-    const OutTile o = out_tile<NR, TW>(g, a.B, a.nch, bid);
-    // The tile's slots k0 + [0, TW) lie in one slot tile of the tile-major
-    // planes (the slot tile is a power of two, a multiple of TW or S < TW),
-    // whose rows are k_out * N_mid + k_mid: position stride PS = N_mid * lt,
-    // and the tile starts at slot k0 % lt of its slot tile.
+    const int W = out_items<NR, TW>(g, a.B, a.nch);
+    if (bid >= W) return;
+    const int tid = ctx.tid();
+    // Position stride of the planes; element (pos = j + q, line l) is at q*PS
+    // (wave-uniform, q a constant of the unrolled loops) plus the lane's byte
+    // offset 8*(j*PS + row*lt + u0 + l%TW), which stays below 4 GiB (j < L/R
+    // for R >= 2 and one channel's spectrum is at most 4 GiB).
     const long long PS = (long long)g.N_mid * g.lt;
-    const int k0 = o.t * TW, u0 = k0 & (g.lt - 1);
-    const float2* kc = a.khat + (long long)(a.c0 + o.c_local) * g.ksz;
-    const float2* kt = kc + (long long)(k0 >> g.lt_log) * ((long long)g.N_out * g.N_mid * g.lt);
-    float2* base = a.ws + ((long long)o.c_local * a.B + o.b) * g.wsp + (long long)(k0 >> g.lt_log) * ws_tile_stride(g);
-    auto lvalid = [&](int l) { return k0 + l % TW < g.S; };
-    // Element (pos = j + q, line l) of the workspace or of the kernel spectrum
-    // tile is at q*PS (wave-uniform, q a constant of the unrolled loops) plus
-    // the lane's byte offset 8*(j*PS + row*lt + u0 + l%TW), which stays below
-    // 4 GiB (j < L/R for R >= 2 and one channel's spectrum is at most 4 GiB).
-    auto lane_bytes = [&](int j, int l) -> unsigned {
-        return 8u * ((unsigned)j * (unsigned)PS + (unsigned)o.rows[l / TW] * (unsigned)g.lt + (unsigned)(u0 + l % TW));
+    auto lane_bytes = [&](const OutView& v, int j, int l) -> unsigned {
+        return 8u * ((unsigned)j * (unsigned)PS + (unsigned)v.o.rows[l / TW] * (unsigned)g.lt + (unsigned)(v.u0 + l % TW));
     };
     auto at = [](auto* p, long long q_elems, unsigned bytes) { return add_bytes(p + q_elems, bytes); };
-    auto ld = [&](int j, int q, int l) -> float2 {
-        const bool ok = lvalid(l);
-        const float2 v = *at(base, q * PS, ok ? lane_bytes(j, l) : 0u);
-        return ok ? v : make_float2(0.f, 0.f);
+    using P0 = PassRegs<L, R0, NL, NT>;
+    using PL = PassRegs<L, RL, NL, NT>;
+    auto load_cols = [&](const OutView& v, P0& s) {
+        pass_load_fn<L, R0, NL, NT, true>(ctx, [&](int j, int q, int l) -> float2 {
+            const bool ok = v.k0 + l % TW < g.S;
+            const float2 x = *at(v.base, q * PS, ok ? lane_bytes(v, j, l) : 0u);
+            return ok ? x : make_float2(0.f, 0.f);
+        }, s);
     };
     // Kernel spectrum values for the positions this thread multiplies (the
-    // forward's last pass: positions j + r*L/RL), loaded while the forward
-    // transform runs.
-    using PL = PassRegs<L, RL, NL, NT>;
+    // forward's last pass: positions j + r*L/RL); kok: a line inside the grid
+    // whose k_in is not 0 (the k_in = 0 lines take the mirror product).
     float2 kv[PL::PER][RL];
     bool kok[PL::PER];
-    const auto tw_staged = ctx.stage_load();  // oldest loads: waited for first
-    auto after_load = [&]() {
-        const int tid = ctx.tid();
+    auto load_kv = [&](const OutView& v) {
 #pragma unroll
         for (int i = 0; i < PL::PER; ++i) {
-            const int g = tid + i * NT, l = g % NL, j = g / NL;
-            kok[i] = bf_valid<PL::NB, NT>(g) && lvalid(l) && k0 + l % TW != 0;
-            const unsigned lb = kok[i] ? lane_bytes(j, l) : 8u;
+            const int gi = tid + i * NT, l = gi % NL, j = gi / NL;
+            kok[i] = bf_valid<PL::NB, NT>(gi) && v.k0 + l % TW < g.S && v.k0 + l % TW != 0;
+            const unsigned lb = kok[i] ? lane_bytes(v, j, l) : 8u;
 #pragma unroll
-            for (int r = 0; r < RL; ++r) kv[i][r] = *at(kt, (long long)r * (L / RL) * PS, lb);
+            for (int r = 0; r < RL; ++r) kv[i][r] = *at(v.kt, (long long)r * (L / RL) * PS, lb);
         }
-        ctx.stage_store(tw_staged);
     };
-    auto s = fwd_from_fn<L, NL, NT, true>(ctx, T, ld, after_load);
-    ctx.sync();  // every LDS read of the forward transform is done: T is free
-    if (o.t == 0) {
-        pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) {
-            if (l % TW == 0) T[pos * NL + l] = v;
-        });
-        ctx.sync();
-        out_slot0_product<L, NR, TW, NT>(ctx, g, o, kc, T);
-        ctx.sync();
-        pass_visit<L, RL, NL, NT, false>(ctx, s, [&](int pos, int l, float2& v) {
-            if (l % TW == 0) v = T[pos * NL + l];
-        });
-        ctx.sync();
-    }
-    // Lines outside the grid and the k_in = 0 lines (final already) keep their values.
+    // One item: forward from the loaded columns, product, inverse and store.
+    auto run_item = [&](const OutView& v, P0& s) {
+        auto t = fwd_from_regs<L, NL, NT, true>(ctx, T, s);
+        ctx.sync();  // every LDS read of the forward transform is done: T is free
+        if (v.o.t == 0) {
+            pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
+                if (l % TW == 0) T[pos * NL + l] = x;
+            });
+            ctx.sync();
+            out_slot0_product<L, NR, TW, NT>(ctx, g, v.o, v.kc, T);
+            ctx.sync();
+            pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
+                if (l % TW == 0) x = T[pos * NL + l];
+            });
+            ctx.sync();
+        }
+        // Lines outside the grid and the k_in = 0 lines (final already) keep their values.
 #pragma unroll
-    for (int i = 0; i < PL::PER; ++i) {
+        for (int i = 0; i < PL::PER; ++i) {
 #pragma unroll
-        for (int r = 0; r < RL; ++r) {
-            const float2 m = cmul(s.v[i][r], kv[i][r]);
-            s.v[i][r] = kok[i] ? m : s.v[i][r];
+            for (int r = 0; r < RL; ++r) {
+                const float2 m = cmul(t.v[i][r], kv[i][r]);
+                t.v[i][r] = kok[i] ? m : t.v[i][r];
+            }
+        }
+        inv_to_fn<L, NL, NT, true>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+            if (v.k0 + l % TW < g.S) *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
+        });
+    };
+    OutView v = out_view<NR, TW>(a, bid);
+    const auto tw_staged = ctx.stage_load();  // oldest loads: waited for first
+    P0 s;
+    load_cols(v, s);
+    load_kv(v);
+    ctx.stage_store(tw_staged);
+    if constexpr (!kLoop) {
+        run_item(v, s);
+    } else {
+        for (int item = bid;;) {
+            const int nxt = item + nblk;
+            run_item(v, s);
+            if (nxt >= W) break;
+            item = nxt;
+            v = out_view<NR, TW>(a, nxt);
+            load_cols(v, s);
+            load_kv(v);
+            ctx.sync();  // the inverse's last LDS reads are done: T is free
         }
     }
-    inv_to_fn<L, NL, NT, true>(ctx, T, s, [&](int j, int q, int l, const float2& v) {
-        if (lvalid(l)) *at(base, q * PS, lane_bytes(j, l)) = v;
-    });
 }
 
 // ---------------------------------------------------------------- conv1d

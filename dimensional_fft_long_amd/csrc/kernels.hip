@@ -112,7 +112,7 @@ __global__ __launch_bounds__(out_nt(L, NR)) void k_col_out(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
     __shared__ float2 T[L * NR * out_tw(L, NR)];
-    col_out_body<L, NR>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
+    col_out_body<L, NR>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, (int)gridDim.x, a, T);
 }
 
 template <int L>
@@ -140,6 +140,31 @@ __global__ __launch_bounds__(out_nt(L, NR)) void k_spec_out(ConvArgs a)
 }
 
 static inline unsigned ceil_div(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
+
+// Workgroups of `kernel` (nt threads) resident at once on the current device
+// (CUs x workgroups per CU), queried once per kernel instance; every device
+// the library runs on is taken to be alike.  0 if the query fails.
+template <class K>
+static unsigned resident_wgs(K kernel, int nt)
+{
+    static const unsigned n = [&]() -> unsigned {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess) return 0;
+        return (unsigned)(cus > 0 ? cus : 0) * (unsigned)(per_cu > 0 ? per_cu : 0);
+    }();
+    return n;
+}
+
+// Grid of an item-looping kernel: one workgroup per item up to the number
+// resident at once.
+template <class K>
+static unsigned loop_grid(K kernel, int nt, long long items)
+{
+    const unsigned r = resident_wgs(kernel, nt);
+    return r > 0 && items > (long long)r ? r : (unsigned)items;
+}
 
 // Calls F.template operator()<L>() for the runtime length L in {4, ..., 2048}.
 template <class F>
@@ -193,9 +218,10 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
         });
         if (e != hipSuccess) return e;
         e = with_length(g.N_out, [&]<int L>() {
-            const long long grid = (long long)a.nch * a.B * (g.N_mid / 2) * ceil_div(g.S, mul3_tw(L));
+            const long long items = out_items<2, out_tw(L, 2)>(g, a.B, a.nch);
+            const unsigned grid = out_looped(L, 2) ? loop_grid(k_col_out<L, 2>, out_nt(L, 2), items) : (unsigned)items;
             mark();
-            hipLaunchKernelGGL((k_col_out<L, 2>), dim3((unsigned)grid), dim3(out_nt(L, 2)), 0, st, a);
+            hipLaunchKernelGGL((k_col_out<L, 2>), dim3(grid), dim3(out_nt(L, 2)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
@@ -207,9 +233,10 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
         });
     } else {
         e = with_length(g.N_out, [&]<int L>() {
-            const long long grid = (long long)a.nch * a.B * ceil_div(g.S, col_tw(L));
+            const long long items = out_items<1, out_tw(L, 1)>(g, a.B, a.nch);
+            const unsigned grid = out_looped(L, 1) ? loop_grid(k_col_out<L, 1>, out_nt(L, 1), items) : (unsigned)items;
             mark();
-            hipLaunchKernelGGL((k_col_out<L, 1>), dim3((unsigned)grid), dim3(out_nt(L, 1)), 0, st, a);
+            hipLaunchKernelGGL((k_col_out<L, 1>), dim3(grid), dim3(out_nt(L, 1)), 0, st, a);
             return last_error();
         });
     }

@@ -57,6 +57,12 @@ constexpr int row_nt(int L) { return tile_threads(2 * L * row_np(L)); }
 constexpr int col_nt(int L) { return tile_threads(L * col_tw(L)); }
 constexpr int out_tw(int L, int NR) { return NR == 1 ? col_tw(L) : mul3_tw(L); }
 constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
+// 2-D out-axis tiles above 80 KiB leave room for one workgroup per CU: such
+// kernels run one workgroup per CU that loops over the work items (1024^2:
+// 4.29 -> 4.08 ms per call).  The 3-D kernel of the same tile size lost with
+// the loop (512^3: 24.8 -> 29.2 ms), and smaller tiles rely on several
+// workgroups per CU; those run one item per workgroup.
+constexpr bool out_looped(int L, int NR) { return NR == 1 && (long long)L * NR * out_tw(L, NR) * 8 > 80 * 1024; }
 
 struct Geom {
     int d;
