@@ -20,6 +20,16 @@ Routes (all fp64, in ``oracle.c``):
   * ``direct_points`` -- O1 at chosen outputs (for grids too big for O2).
   * ``fftconv``       -- O2, explicit zero padding to 2n, textbook radix-2 FFT.
   * ``kernel_spectrum`` -- the full DFT of the wrap-placed kernel.
+  * ``bwd_direct`` / ``bwd_points`` / ``bwd_fft`` -- the backward (vector-Jacobian
+    product, explainer section "Implementation and operation patterns", item
+    "Concrete implementation pattern (PyTorch)": gradients of the input and of
+    the kernel parameters): O1 written out (all, or chosen points) and O2 by
+    FFTs.  Given dy = dLoss/dy::
+
+        du[j]    = sum_i dy[i] K[i-j]
+        dx[j]    = du[j] (s + alpha x s (1-s)),   s = sigmoid(alpha x + beta)
+        dalpha_c = sum_{b,j} du x^2 s (1-s),   dbeta_c = sum_{b,j} du x s (1-s)
+        dK_c[l]  = sum_b sum_j dy[j+l] u[j]     (l over K's offsets)
 
 Inputs are numpy arrays: x fp32 [B,C,*dims] (bf16 data widened exactly to fp32
 by the caller), alpha/beta fp32 [C], K fp32 [C,*(2*dims-1)].
@@ -63,8 +73,12 @@ def _load():
         lib.oracle_kernel_spectrum.argtypes = [P, I, I, P, P, P]
         lib.oracle_fftconv_pairs.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_bwd_direct.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, P]
+        lib.oracle_bwd_direct_points.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, I64, P, P]
+        lib.oracle_bwd_fft.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, P, P, P]
         for f in ("oracle_gate", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
-                  "oracle_fftconv_pairs", "oracle_num_threads"):
+                  "oracle_fftconv_pairs", "oracle_num_threads", "oracle_bwd_direct", "oracle_bwd_direct_points",
+                  "oracle_bwd_fft"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -151,6 +165,62 @@ def kernel_spectrum(K, dims) -> np.ndarray:
     im = np.empty(shape, dtype=np.float64)
     _check(_load().oracle_kernel_spectrum(_ptr(K), C, d, _ptr(dd), _ptr(re), _ptr(im)), "kernel_spectrum")
     return re + 1j * im
+
+
+def bwd_direct(x, alpha, beta, K, dy):
+    """O1 backward: (dx [B,C,*dims], dalpha [C], dbeta [C], dK [C,*(2*dims-1)]), fp64."""
+    x, alpha, beta, K, dy = _f32(x), _f32(alpha), _f32(beta), _f32(K), _f32(dy)
+    if dy.shape != x.shape:
+        raise ValueError("dy must have the shape of x")
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    dx = np.empty(x.shape, dtype=np.float64)
+    da = np.empty(C, dtype=np.float64)
+    db = np.empty(C, dtype=np.float64)
+    dK = np.empty(K.shape, dtype=np.float64)
+    _check(_load().oracle_bwd_direct(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(dy), B, C, d, _ptr(dims),
+                                     _ptr(dx), _ptr(da), _ptr(db), _ptr(dK)), "bwd_direct")
+    return dx, da, db, dK
+
+
+def bwd_points(x, alpha, beta, K, dy, x_points=None, k_points=None):
+    """O1 backward at chosen points: dx at rows (b, c, j_0..) and dK at rows (c, e_0..)
+    (e the index into K's extents).  Returns (dx values, dK values), fp64."""
+    x, alpha, beta, K, dy = _f32(x), _f32(alpha), _f32(beta), _f32(K), _f32(dy)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    xp = np.ascontiguousarray(np.asarray([] if x_points is None else x_points, dtype=np.int64).reshape(-1, 2 + d))
+    kp = np.ascontiguousarray(np.asarray([] if k_points is None else k_points, dtype=np.int64).reshape(-1, 1 + d))
+    ox = np.empty(max(xp.shape[0], 1), dtype=np.float64)
+    ok = np.empty(max(kp.shape[0], 1), dtype=np.float64)
+    _check(_load().oracle_bwd_direct_points(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(dy), B, C, d,
+                                            _ptr(dims), xp.shape[0], _ptr(xp), _ptr(ox), kp.shape[0], _ptr(kp),
+                                            _ptr(ok)), "bwd_points")
+    return ox[:xp.shape[0]], ok[:kp.shape[0]]
+
+
+def bwd_fft(x, alpha, beta, K, dy, chans=None):
+    """O2 backward for the listed channels (all when None), every batch entry.
+
+    Returns (dx [B, len(chans), *dims], dalpha [len], dbeta [len], dK [len, *(2*dims-1)]), fp64.
+    """
+    x, alpha, beta, K, dy = _f32(x), _f32(alpha), _f32(beta), _f32(K), _f32(dy)
+    if dy.shape != x.shape:
+        raise ValueError("dy must have the shape of x")
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    ch = np.arange(C, dtype=np.int64) if chans is None else np.ascontiguousarray(np.asarray(chans, dtype=np.int64))
+    n = ch.size
+    dx = np.empty((n, B) + tuple(x.shape[2:]), dtype=np.float64)
+    da = np.empty(n, dtype=np.float64)
+    db = np.empty(n, dtype=np.float64)
+    dK = np.empty((n,) + tuple(K.shape[1:]), dtype=np.float64)
+    _check(_load().oracle_bwd_fft(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(dy), B, C, d, _ptr(dims),
+                                  n, _ptr(ch), _ptr(dx), _ptr(da), _ptr(db), _ptr(dK)), "bwd_fft")
+    return np.ascontiguousarray(dx.swapaxes(0, 1)), da, db, dK
 
 
 def num_threads() -> int:

@@ -32,6 +32,9 @@
  *   O2  oracle_fftconv_pairs: explicit zero padding to N_a = 2 n_a, textbook
  *       radix-2 complex FFT (bit reversal + butterflies, fp64 twiddles from
  *       cos/sin), row-column over the axes, product, inverse, crop.
+ * and the same two routes for the backward (the gradients of the input, the
+ * gate parameters and the kernel; see the backward section below):
+ *   O1  oracle_bwd_direct / oracle_bwd_direct_points,  O2  oracle_bwd_fft.
  *
  * Layouts: x  [B][C][n_0..n_{d-1}] fp32 (bf16 inputs are widened exactly by the
  * caller), K [C][2n_0-1 .. 2n_{d-1}-1] fp32, alpha/beta [C] fp32, outputs fp64.
@@ -367,6 +370,273 @@ int oracle_fftconv_pairs(const float *x, const float *alpha, const float *beta, 
                     ys[(j0 * g.n[1] + j1) * g.n[2] + j2] = ur[(j0 * g.N[1] + j1) * g.N[2] + j2] * scale;
     }
     free(ur); free(ui); free(kr); free(ki);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward: the vector-Jacobian product of the output equation.             */
+/* ------------------------------------------------------------------------- */
+/*
+ * [EXPL] section "Implementation and operation patterns", item "Concrete
+ * implementation pattern (PyTorch)": the layer is an autograd function whose
+ * backward recomputes the forward FFTs from the saved input and kernel
+ * parameters (gradient checkpointing) and returns the gradients of the input
+ * and of the kernel parameters.  With dy = dLoss/dy, the chain rule through
+ * y[i] = sum_j u[j] K[i-j] and u = x s, s = sigma(alpha x + beta), gives
+ *
+ *   du[j]     = sum_{i in G} dy[i] K[i-j]                  (correlation with K)
+ *   dx[j]     = du[j] (s + alpha x s (1-s))
+ *   dalpha_c  = sum_{b,j} du[j] x^2 s (1-s)
+ *   dbeta_c   = sum_{b,j} du[j] x s (1-s)
+ *   dK_c[dl]  = sum_b sum_{j in G, j+dl in G} dy[j+dl] u[j]   (dl on K's offsets)
+ *
+ * Layouts as above; dy like x; dx fp64 [B][C][L]; dalpha, dbeta fp64 [C];
+ * dK fp64 [C][KL].
+ */
+
+static inline double sigm(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/* dx, and this pair's terms of dalpha and dbeta, from du. */
+static void gate_vjp(const float *xs, const double *du, int64_t L, double alpha, double beta,
+                     double *dx, double *da, double *db)
+{
+    double sa = 0.0, sb = 0.0;
+    for (int64_t j = 0; j < L; ++j) {
+        const double x = (double)xs[j], s = sigm(alpha * x + beta), ds = s * (1.0 - s);
+        dx[j] = du[j] * (s + alpha * x * ds);
+        sa += du[j] * x * x * ds;
+        sb += du[j] * x * ds;
+    }
+    *da += sa;
+    *db += sb;
+}
+
+/* O1 of the backward: every sum above written out. */
+int oracle_bwd_direct(const float *x, const float *alpha, const float *beta, const float *K, const float *dy,
+                      int B, int C, int d, const int64_t *dims,
+                      double *dx, double *dalpha, double *dbeta, double *dK)
+{
+    geom_t g;
+    if (!x || !alpha || !beta || !K || !dy || !dx || !dalpha || !dbeta || !dK || B < 0 || C < 0) return ORC_EINVAL;
+    if (geom_init(&g, d, dims)) return ORC_EINVAL;
+    const size_t n = (size_t)(g.L ? g.L : 1);
+    double *u = (double *)malloc(sizeof(double) * n), *du = (double *)malloc(sizeof(double) * n);
+    if (!u || !du) { free(u); free(du); return ORC_ENOMEM; }
+    for (int c = 0; c < C; ++c) {
+        const float *Kc = K + (int64_t)c * g.KL;
+        double *dKc = dK + (int64_t)c * g.KL;
+        for (int64_t m = 0; m < g.KL; ++m) dKc[m] = 0.0;
+        dalpha[c] = 0.0;
+        dbeta[c] = 0.0;
+        for (int b = 0; b < B; ++b) {
+            const int64_t p = (int64_t)b * C + c;
+            const float *xs = x + p * g.L, *dys = dy + p * g.L;
+            for (int64_t j = 0; j < g.L; ++j) u[j] = gate((double)xs[j], alpha[c], beta[c]);
+#pragma omp parallel for schedule(static)
+            for (int64_t j = 0; j < g.L; ++j) {
+                const int64_t j2 = j % g.n[2], j1 = (j / g.n[2]) % g.n[1], j0 = j / (g.n[1] * g.n[2]);
+                double acc = 0.0;
+                for (int64_t i = 0; i < g.L; ++i) {
+                    const int64_t i2 = i % g.n[2], i1 = (i / g.n[2]) % g.n[1], i0 = i / (g.n[1] * g.n[2]);
+                    acc += (double)dys[i] * kval(Kc, &g, i0 - j0, i1 - j1, i2 - j2);
+                }
+                du[j] = acc;
+            }
+            gate_vjp(xs, du, g.L, alpha[c], beta[c], dx + p * g.L, &dalpha[c], &dbeta[c]);
+#pragma omp parallel for schedule(static)
+            for (int64_t m = 0; m < g.KL; ++m) {
+                const int64_t e2 = m % g.ke[2], e1 = (m / g.ke[2]) % g.ke[1], e0 = m / (g.ke[1] * g.ke[2]);
+                const int64_t l0 = e0 - (g.n[0] - 1), l1 = e1 - (g.n[1] - 1), l2 = e2 - (g.n[2] - 1);
+                double acc = 0.0;
+                for (int64_t j0 = 0; j0 < g.n[0]; ++j0) {
+                    const int64_t i0 = j0 + l0;
+                    if (i0 < 0 || i0 >= g.n[0]) continue;
+                    for (int64_t j1 = 0; j1 < g.n[1]; ++j1) {
+                        const int64_t i1 = j1 + l1;
+                        if (i1 < 0 || i1 >= g.n[1]) continue;
+                        for (int64_t j2 = 0; j2 < g.n[2]; ++j2) {
+                            const int64_t i2 = j2 + l2;
+                            if (i2 < 0 || i2 >= g.n[2]) continue;
+                            acc += (double)dys[(i0 * g.n[1] + i1) * g.n[2] + i2] * u[(j0 * g.n[1] + j1) * g.n[2] + j2];
+                        }
+                    }
+                }
+                dKc[m] += acc;
+            }
+        }
+    }
+    free(u);
+    free(du);
+    return ORC_OK;
+}
+
+/*
+ * O1 of the backward at chosen points.  xpts [nx][2+d] (b, c, j..) -> dx_out;
+ * kpts [nk][1+d] (c, e..) with e the index into K's extents -> dK_out.
+ */
+int oracle_bwd_direct_points(const float *x, const float *alpha, const float *beta, const float *K,
+                             const float *dy, int B, int C, int d, const int64_t *dims,
+                             int64_t nx, const int64_t *xpts, double *dx_out,
+                             int64_t nk, const int64_t *kpts, double *dK_out)
+{
+    geom_t g;
+    if (!x || !alpha || !beta || !K || !dy || nx < 0 || nk < 0) return ORC_EINVAL;
+    if ((nx && (!xpts || !dx_out)) || (nk && (!kpts || !dK_out))) return ORC_EINVAL;
+    if (geom_init(&g, d, dims)) return ORC_EINVAL;
+    for (int64_t q = 0; q < nx; ++q) {
+        const int64_t *pt = xpts + q * (2 + d);
+        if (pt[0] < 0 || pt[0] >= B || pt[1] < 0 || pt[1] >= C) return ORC_EINVAL;
+        for (int a = 0; a < d; ++a)
+            if (pt[2 + a] < 0 || pt[2 + a] >= dims[a]) return ORC_EINVAL;
+    }
+    for (int64_t q = 0; q < nk; ++q) {
+        const int64_t *pt = kpts + q * (1 + d);
+        if (pt[0] < 0 || pt[0] >= C) return ORC_EINVAL;
+        for (int a = 0; a < d; ++a)
+            if (pt[1 + a] < 0 || pt[1 + a] >= 2 * dims[a] - 1) return ORC_EINVAL;
+    }
+    for (int64_t q = 0; q < nx; ++q) {
+        const int64_t *pt = xpts + q * (2 + d);
+        const int64_t c = pt[1], p = pt[0] * C + c;
+        int64_t jj[3] = {0, 0, 0};
+        for (int a = 0; a < d; ++a) jj[3 - d + a] = pt[2 + a];
+        const float *dys = dy + p * g.L, *Kc = K + c * g.KL;
+        double du = 0.0;
+#pragma omp parallel for reduction(+ : du) schedule(static)
+        for (int64_t i0 = 0; i0 < g.n[0]; ++i0)
+            for (int64_t i1 = 0; i1 < g.n[1]; ++i1)
+                for (int64_t i2 = 0; i2 < g.n[2]; ++i2)
+                    du += (double)dys[(i0 * g.n[1] + i1) * g.n[2] + i2] * kval(Kc, &g, i0 - jj[0], i1 - jj[1], i2 - jj[2]);
+        const double xv = (double)x[p * g.L + (jj[0] * g.n[1] + jj[1]) * g.n[2] + jj[2]];
+        const double s = sigm(alpha[c] * xv + beta[c]);
+        dx_out[q] = du * (s + alpha[c] * xv * s * (1.0 - s));
+    }
+    for (int64_t q = 0; q < nk; ++q) {
+        const int64_t *pt = kpts + q * (1 + d);
+        const int64_t c = pt[0];
+        int64_t l[3] = {0, 0, 0};
+        for (int a = 0; a < d; ++a) l[3 - d + a] = pt[1 + a] - (dims[a] - 1);
+        double acc = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t p = b * C + c;
+            const float *xs = x + p * g.L, *dys = dy + p * g.L;
+#pragma omp parallel for reduction(+ : acc) schedule(static)
+            for (int64_t j0 = 0; j0 < g.n[0]; ++j0) {
+                const int64_t i0 = j0 + l[0];
+                if (i0 < 0 || i0 >= g.n[0]) continue;
+                for (int64_t j1 = 0; j1 < g.n[1]; ++j1) {
+                    const int64_t i1 = j1 + l[1];
+                    if (i1 < 0 || i1 >= g.n[1]) continue;
+                    for (int64_t j2 = 0; j2 < g.n[2]; ++j2) {
+                        const int64_t i2 = j2 + l[2];
+                        if (i2 < 0 || i2 >= g.n[2]) continue;
+                        acc += (double)dys[(i0 * g.n[1] + i1) * g.n[2] + i2] *
+                               gate((double)xs[(j0 * g.n[1] + j1) * g.n[2] + j2], alpha[c], beta[c]);
+                    }
+                }
+            }
+        }
+        dK_out[q] = acc;
+    }
+    return ORC_OK;
+}
+
+/* Zero-padded copy of one (b,c) signal into the N-grid (re only; im zeroed). */
+static void pad_into(const double *v, const geom_t *g, double *re, double *im)
+{
+    memset(re, 0, sizeof(double) * (size_t)g->NL);
+    memset(im, 0, sizeof(double) * (size_t)g->NL);
+    for (int64_t j0 = 0; j0 < g->n[0]; ++j0)
+        for (int64_t j1 = 0; j1 < g->n[1]; ++j1)
+            for (int64_t j2 = 0; j2 < g->n[2]; ++j2)
+                re[(j0 * g->N[1] + j1) * g->N[2] + j2] = v[(j0 * g->n[1] + j1) * g->n[2] + j2];
+}
+
+/*
+ * O2 of the backward for the listed channels (every batch entry of each):
+ * zero padding to N = 2n, the textbook FFT of fft_nd, and
+ *   du = crop(IFFT(FFT(pad dy) conj(FFT(wrap K)))) / prod N
+ *   dK[dl] = IFFT(sum_b FFT(pad dy_b) conj(FFT(pad u_b)))[dl mod N] / prod N
+ * (a correlation is a product with the conjugate spectrum; with N = 2n the
+ * lags used never wrap).  Outputs: dx [nch][B][L], dalpha/dbeta [nch],
+ * dK [nch][KL], in the order of `chans`.
+ */
+int oracle_bwd_fft(const float *x, const float *alpha, const float *beta, const float *K, const float *dy,
+                   int B, int C, int d, const int64_t *dims, int64_t nch, const int64_t *chans,
+                   double *dx, double *dalpha, double *dbeta, double *dK)
+{
+    geom_t g;
+    if (!x || !alpha || !beta || !K || !dy || !chans || !dx || !dalpha || !dbeta || !dK || nch < 0) return ORC_EINVAL;
+    if (geom_init(&g, d, dims)) return ORC_EINVAL;
+    for (int a = 0; a < 3; ++a)
+        if (!is_pow2(g.N[a])) return ORC_EINVAL;
+    for (int64_t q = 0; q < nch; ++q)
+        if (chans[q] < 0 || chans[q] >= C) return ORC_EINVAL;
+    const size_t bytes = sizeof(double) * (size_t)g.NL;
+    double *buf[10];
+    int fail = 0;
+    for (int k = 0; k < 10; ++k) {
+        buf[k] = (double *)malloc(bytes);
+        if (!buf[k]) fail = 1;
+    }
+    double *v = (double *)malloc(sizeof(double) * (size_t)g.L);
+    if (fail || !v) {
+        for (int k = 0; k < 10; ++k) free(buf[k]);
+        free(v);
+        return ORC_ENOMEM;
+    }
+    double *kr = buf[0], *ki = buf[1], *pr = buf[2], *pi = buf[3], *yr = buf[4], *yi = buf[5];
+    double *ur = buf[6], *ui = buf[7], *tr = buf[8], *ti = buf[9];
+    const double scale = 1.0 / (double)g.NL;
+    int rc = ORC_OK;
+    for (int64_t q = 0; q < nch && rc == ORC_OK; ++q) {
+        const int64_t c = chans[q];
+        memset(kr, 0, bytes);
+        memset(ki, 0, bytes);
+        wrap_place(K + c * g.KL, &g, kr);
+        if ((rc = fft_nd(kr, ki, g.N, -1))) break;
+        memset(pr, 0, bytes);
+        memset(pi, 0, bytes);
+        dalpha[q] = 0.0;
+        dbeta[q] = 0.0;
+        for (int64_t b = 0; b < B && rc == ORC_OK; ++b) {
+            const int64_t p = b * C + c;
+            const float *xs = x + p * g.L, *dys = dy + p * g.L;
+            for (int64_t j = 0; j < g.L; ++j) v[j] = (double)dys[j];
+            pad_into(v, &g, yr, yi);
+            if ((rc = fft_nd(yr, yi, g.N, -1))) break;
+            for (int64_t j = 0; j < g.L; ++j) v[j] = gate((double)xs[j], alpha[c], beta[c]);
+            pad_into(v, &g, ur, ui);
+            if ((rc = fft_nd(ur, ui, g.N, -1))) break;
+            for (int64_t m = 0; m < g.NL; ++m) {
+                /* P += DY conj(U);  T = DY conj(Khat) */
+                pr[m] += yr[m] * ur[m] + yi[m] * ui[m];
+                pi[m] += yi[m] * ur[m] - yr[m] * ui[m];
+                tr[m] = yr[m] * kr[m] + yi[m] * ki[m];
+                ti[m] = yi[m] * kr[m] - yr[m] * ki[m];
+            }
+            if ((rc = fft_nd(tr, ti, g.N, +1))) break;
+            for (int64_t j0 = 0; j0 < g.n[0]; ++j0)
+                for (int64_t j1 = 0; j1 < g.n[1]; ++j1)
+                    for (int64_t j2 = 0; j2 < g.n[2]; ++j2)
+                        v[(j0 * g.n[1] + j1) * g.n[2] + j2] = tr[(j0 * g.N[1] + j1) * g.N[2] + j2] * scale;
+            gate_vjp(xs, v, g.L, alpha[c], beta[c], dx + (q * B + b) * g.L, &dalpha[q], &dbeta[q]);
+        }
+        if (rc) break;
+        if ((rc = fft_nd(pr, pi, g.N, +1))) break;
+        double *dKc = dK + q * g.KL;
+        for (int64_t a0 = 0; a0 < g.ke[0]; ++a0)
+            for (int64_t a1 = 0; a1 < g.ke[1]; ++a1)
+                for (int64_t a2 = 0; a2 < g.ke[2]; ++a2) {
+                    const int64_t d0 = a0 - (g.n[0] - 1), d1 = a1 - (g.n[1] - 1), d2 = a2 - (g.n[2] - 1);
+                    const int64_t m0 = (d0 % g.N[0] + g.N[0]) % g.N[0];
+                    const int64_t m1 = (d1 % g.N[1] + g.N[1]) % g.N[1];
+                    const int64_t m2 = (d2 % g.N[2] + g.N[2]) % g.N[2];
+                    dKc[(a0 * g.ke[1] + a1) * g.ke[2] + a2] = pr[(m0 * g.N[1] + m1) * g.N[2] + m2] * scale;
+                }
+    }
+    for (int k = 0; k < 10; ++k) free(buf[k]);
+    free(v);
     return rc;
 }
 
