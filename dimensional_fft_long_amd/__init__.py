@@ -16,6 +16,10 @@ zero outside the grid.  Entry points mirror ``include/hyenand.h``:
 
 * ``kernel_spectrum(K, dims)``        -> K_hat (once per parameter set)
 * ``fftconv_fwd(x, alpha, beta, K_hat)`` -> y
+* ``fftconv_bwd(x, alpha, beta, K_hat, dy)`` -> (dx, dalpha, dbeta, dK): the
+  backward, recomputing the forward transforms (explainer, "Implementation and
+  operation patterns", "Concrete implementation pattern (PyTorch)")
+* ``HyenaConvolutionFunction`` -- the autograd wrapper of that pattern
 """
 from __future__ import annotations
 
@@ -33,7 +37,9 @@ F32, BF16 = 0, 1
 EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_bytes",
            "hyenand_kernel_spectrum_tile", "hyenand_kernel_spectrum",
            "hyenand_fftconv_workspace_bytes", "hyenand_fftconv_workspace_min_bytes", "hyenand_fftconv_fwd",
-           "hyenand_fftconv_fwd_traced", "hyenand_fftconv_launch_plan")
+           "hyenand_fftconv_fwd_traced", "hyenand_fftconv_launch_plan", "hyenand_fftconv_bwd",
+           "hyenand_fftconv_bwd_workspace_bytes", "hyenand_fftconv_bwd_workspace_min_bytes",
+           "hyenand_fftconv_bwd_traced")
 
 _lib = None
 
@@ -67,6 +73,15 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_fwd_traced.restype = I
     lib.hyenand_fftconv_launch_plan.argtypes = [I, I, I, P, I, SZ, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.hyenand_fftconv_launch_plan.restype = I
+    lib.hyenand_fftconv_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_fftconv_bwd.restype = I
+    lib.hyenand_fftconv_bwd_traced.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I,
+                                               ctypes.POINTER(I)]
+    lib.hyenand_fftconv_bwd_traced.restype = I
+    lib.hyenand_fftconv_bwd_workspace_bytes.argtypes = [I, I, I, P, I, I]
+    lib.hyenand_fftconv_bwd_workspace_bytes.restype = SZ
+    lib.hyenand_fftconv_bwd_workspace_min_bytes.argtypes = [I, I, I, P, I, I]
+    lib.hyenand_fftconv_bwd_workspace_min_bytes.restype = SZ
     _lib = lib
     return lib
 
@@ -215,15 +230,110 @@ def fftconv_fwd_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None)
     return int(n.value)
 
 
+def bwd_workspace_bytes(B: int, C: int, dims, dtype=torch.float32, with_dK: bool = True,
+                        minimum: bool = False) -> int:
+    lib = get_lib()
+    f = lib.hyenand_fftconv_bwd_workspace_min_bytes if minimum else lib.hyenand_fftconv_bwd_workspace_bytes
+    return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype), int(bool(with_dK))))
+
+
+def _bwd_workspace(B, C, dims, dtype, with_dK, device):
+    nbytes = bwd_workspace_bytes(B, C, dims, dtype, with_dK)
+    key = ("bwd", str(device), nbytes)
+    buf = _ws_cache.get(key)
+    if buf is None:
+        buf = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf, nbytes
+
+
+def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace):
+    if not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous device tensor")
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_cuda or not dy.is_contiguous():
+        raise TypeError("dy must be a contiguous device tensor with the shape and dtype of x")
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    for t, nm in ((alpha, "alpha"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
+    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
+    if K_hat.numel() * 8 < spectrum_bytes(C, dims):
+        raise ValueError("K_hat is smaller than the spectrum of this shape")
+    dx = torch.empty_like(x) if dx is None else dx
+    dalpha = torch.empty(C, dtype=torch.float32, device=x.device) if dalpha is None else dalpha
+    dbeta = torch.empty(C, dtype=torch.float32, device=x.device) if dbeta is None else dbeta
+    if with_dK and dK is None:
+        dK = torch.empty((C,) + tuple(2 * n - 1 for n in dims), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace, ws_bytes = _bwd_workspace(B, C, dims, x.dtype, dK is not None, x.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(dy.data_ptr()),
+            _P(dx.data_ptr()), _P(dalpha.data_ptr()), _P(dbeta.data_ptr()),
+            _P(dK.data_ptr()) if dK is not None else None, B, C, len(dims), _dims_arr(dims),
+            _dtype_code(x.dtype), _P(workspace.data_ptr()), ws_bytes]
+    return args, (dx, dalpha, dbeta, dK)
+
+
+def fftconv_bwd(x, alpha, beta, K_hat, dy, dx=None, dalpha=None, dbeta=None, dK=None, with_dK: bool = True,
+                workspace=None, stream=None):
+    """Backward of fftconv_fwd for the output gradient dy.
+
+    Returns (dx [B, C, *dims] in x's dtype, dalpha [C], dbeta [C], dK [C, *(2*dims-1)] or None)."""
+    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace)
+    rc = get_lib().hyenand_fftconv_bwd(*args, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_bwd")
+    return outs
+
+
+BWD_PASS_NAMES = {
+    (1, False): ("conv1d_bwd", "gate_reduce"),
+    (1, True): ("conv1d_bwd", "gate_reduce", "corr1d", "dk_row"),
+    (2, False): ("row_fwd_dy", "col_out_bwd", "row_inv_bwd", "gate_reduce"),
+    (2, True): ("row_fwd_dy", "row_fwd_u", "col_out_bwd", "row_inv_bwd", "gate_reduce", "dk_row"),
+    (3, False): ("row_fwd_dy", "col_mid_fwd_dy", "col_out_bwd", "col_mid_inv", "row_inv_bwd", "gate_reduce"),
+    (3, True): ("row_fwd_dy", "row_fwd_u", "col_mid_fwd_dy", "col_mid_fwd_u", "col_out_bwd", "col_mid_inv",
+                "row_inv_bwd", "gate_reduce", "mid_inv_dk", "dk_row"),
+}
+
+
+def fftconv_bwd_traced(x, alpha, beta, K_hat, dy, outs, workspace, events, stream=None) -> int:
+    """fftconv_bwd into ``outs`` = (dx, dalpha, dbeta, dK or None), recording
+    ``events`` before each kernel launch and after the last; returns the launch count."""
+    dx, dalpha, dbeta, dK = outs
+    args, _ = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, dK is not None, workspace)
+    st = torch.cuda.current_stream() if stream is None else stream
+    for e in events:
+        if e.cuda_event == 0:
+            e.record(st)
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    n = ctypes.c_int(0)
+    rc = get_lib().hyenand_fftconv_bwd_traced(*args, _stream(stream), arr, len(events), ctypes.byref(n))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_bwd_traced")
+    return int(n.value)
+
+
 class HyenaConvolutionFunction(torch.autograd.Function):
-    """Forward-only autograd wrapper in the shape the explainer's "Concrete
-    implementation pattern (PyTorch)" gives: forward(ctx, input, kernel
-    params, preallocated FFT workspace).  The backward pass is not provided."""
+    """Autograd wrapper in the shape of the explainer's "Concrete implementation
+    pattern (PyTorch)": the forward keeps only the input and the kernel
+    parameters (alpha, beta and the kernel spectrum computed from K), the
+    backward recomputes the transforms and returns the gradients of x, alpha,
+    beta and K.  The FFT workspaces are preallocated per shape and reused."""
 
     @staticmethod
-    def forward(ctx, x, alpha, beta, K_hat, workspace=None):
-        return fftconv_fwd(x, alpha, beta, K_hat, workspace=workspace)
+    def forward(ctx, x, alpha, beta, K):
+        dims = tuple(int(v) for v in x.shape[2:])
+        K_hat = kernel_spectrum(K.contiguous(), dims)
+        ctx.save_for_backward(x, alpha, beta, K_hat)
+        ctx.needs_dK = ctx.needs_input_grad[3]
+        return fftconv_fwd(x, alpha, beta, K_hat)
 
     @staticmethod
     def backward(ctx, grad_out):
-        raise NotImplementedError("backward of the gated FFT convolution is not implemented")
+        x, alpha, beta, K_hat = ctx.saved_tensors
+        dx, da, db, dK = fftconv_bwd(x, alpha, beta, K_hat, grad_out.contiguous(), with_dK=ctx.needs_dK)
+        return dx, da, db, dK

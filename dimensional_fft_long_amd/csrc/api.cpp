@@ -181,4 +181,105 @@ int hyenand_fftconv_fwd_traced(const void* x, const float* alpha, const float* b
     return rc;
 }
 
+// ------------------------------------------------------------------ backward
+size_t hyenand_fftconv_bwd_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
+{
+    Geom g;
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
+    return recommended_bwd_workspace(g, B, C, with_dK != 0);
+}
+
+size_t hyenand_fftconv_bwd_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
+{
+    Geom g;
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
+    return bwd_channel_bytes(g, B, with_dK != 0);
+}
+
+static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta, const void* K_hat, const void* dy,
+                            void* dx, float* dalpha, float* dbeta, float* dK, int B, int C, int d,
+                            const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                            LaunchTrace* trace)
+{
+    if (B < 0 || C < 0) return HYENAND_ERR_INVALID_ARG;
+    if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
+    if (d < 1 || d > 3) return HYENAND_ERR_UNSUPPORTED;
+    if (!dims) return HYENAND_ERR_INVALID_ARG;
+    Geom g;
+    if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
+    if (C == 0) return HYENAND_OK;
+    if (!dalpha || !dbeta || !aligned(dalpha, 4) || !aligned(dbeta, 4) || (dK && !aligned(dK, 4)))
+        return HYENAND_ERR_INVALID_ARG;
+    const bool dk = dK != nullptr;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (B == 0) {
+        // Sums over an empty batch.
+        const long long kl = (long long)g.ke_out * g.ke_mid * g.ke_in;
+        if (launch_zero(dalpha, C, st) != hipSuccess || launch_zero(dbeta, C, st) != hipSuccess ||
+            (dk && launch_zero(dK, (long long)C * kl, st) != hipSuccess))
+            return HYENAND_ERR_HIP;
+        if (trace) trace->mark(st);
+        return HYENAND_OK;
+    }
+    const size_t es = dtype == HYENAND_BF16 ? 2 : 4;
+    if (!x || !alpha || !beta || !K_hat || !dy || !dx) return HYENAND_ERR_INVALID_ARG;
+    if (!aligned(x, es) || !aligned(dy, es) || !aligned(dx, es) || !aligned(alpha, 4) || !aligned(beta, 4) ||
+        !aligned(K_hat, 8))
+        return HYENAND_ERR_INVALID_ARG;
+    if (!workspace) return HYENAND_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return HYENAND_ERR_INVALID_ARG;
+    int per = bwd_chunk_channels(g, B, C, dk, workspace_bytes);
+    if (per < 1) return HYENAND_ERR_WORKSPACE;
+    const int chunks = (C + per - 1) / per;
+    per = (C + chunks - 1) / chunks;  // balanced chunks
+    ConvArgs a{};
+    a.x = x;
+    a.y = dx;
+    a.dy = dy;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.khat = static_cast<const float2*>(K_hat);
+    a.dalpha = dalpha;
+    a.dbeta = dbeta;
+    a.dK = dK;
+    a.g = g;
+    a.B = B;
+    a.C = C;
+    a.bf16 = dtype == HYENAND_BF16;
+    float2* w = static_cast<float2*>(workspace);
+    const long long plane = (long long)per * B * g.wsp;
+    a.ws = w;
+    a.ws_u = dk ? w + plane : nullptr;
+    a.dkw = dk ? w + plane * 2 : nullptr;
+    a.part = w + plane * (dk ? 2 : 1) + (dk ? (g.d == 1 ? (long long)per * B * g.S : (long long)per * g.kmain) : 0);
+    for (int c0 = 0; c0 < C; c0 += per) {
+        a.c0 = c0;
+        a.nch = (C - c0) < per ? (C - c0) : per;
+        if (launch_backward_chunk(a, dk, st, trace) != hipSuccess) return HYENAND_ERR_HIP;
+    }
+    if (trace) trace->mark(st);
+    return HYENAND_OK;
+}
+
+int hyenand_fftconv_bwd(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                        const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C, int d,
+                        const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
+                            workspace, workspace_bytes, stream, nullptr);
+}
+
+int hyenand_fftconv_bwd_traced(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                               const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C,
+                               int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events, int n_events, int* n_launches)
+{
+    if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
+    LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
+    const int rc = fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
+                                    workspace, workspace_bytes, stream, &tr);
+    if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
+    return rc;
+}
+
 }  // extern "C"

@@ -57,6 +57,14 @@ __host__ __device__ __forceinline__ float load_x(const ConvArgs& a, long long i)
     else return __builtin_nontemporal_load(static_cast<const float*>(a.x) + i);
 }
 
+// Same for another input of the I/O dtype (the output gradient of the backward).
+template <bool BF16>
+__host__ __device__ __forceinline__ float load_in(const void* p, long long i)
+{
+    if constexpr (BF16) return bf16_to_f32(__builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i));
+    else return __builtin_nontemporal_load(static_cast<const float*>(p) + i);
+}
+
 template <bool BF16>
 __host__ __device__ __forceinline__ void store_y(const ConvArgs& a, long long i, float v)
 {
@@ -106,7 +114,8 @@ __host__ __device__ __forceinline__ void row_meta(const Ctx& ctx, int bid, const
 // NP line pairs per workgroup; gate, FFT of u_a + i u_b, separation.  Element
 // loops run ITER = NP*n/NT iterations per thread; every load of a loop is
 // issued before the first use (invalid tail lines read offset 0 and are zeroed).
-template <int L, bool BF16, class Ctx>
+// GATE = false transforms x as it is (the backward's output gradient).
+template <int L, bool BF16, bool GATE, class Ctx>
 __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
@@ -128,7 +137,8 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
     for (int i = 0; i < ITER; ++i) {
         const int idx = tid + i * NT, lp = idx / n, m = idx % n;
         const RowMeta& md = M[lp];
-        float2 z = make_float2(ctx.gate(xa[i], md.al0, md.be0), ctx.gate(xb[i], md.al1, md.be1));
+        float2 z = GATE ? make_float2(ctx.gate(xa[i], md.al0, md.be0), ctx.gate(xb[i], md.al1, md.be1))
+                        : make_float2(xa[i], xb[i]);
         if (!md.valid) z = make_float2(0.f, 0.f);
         T[m * LP + lp] = z;
     }
@@ -163,8 +173,82 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
     }
 }
 
+// ------------------------------------------------------- backward epilogue
+// Gradient of the gate u = x s, s = sigmoid(alpha x + beta), for one element:
+// returns dx = du (s + alpha x s (1-s)) and sets the element's terms of
+// dalpha and dbeta, du x s (1-s) * (x, 1).
+template <class Ctx>
+__host__ __device__ __forceinline__ float gate_vjp(const Ctx& ctx, float du, float x, float al, float be,
+                                                   float2& terms)
+{
+    const float s = ctx.sigmoid(al * x + be);
+    const float t = du * x * s * (1.0f - s);
+    terms = make_float2(t * x, t);
+    return du * s + al * t;
+}
+
+// Backward epilogue of a row workgroup whose inverse transform left du in T
+// (line pair lp: du_a + i du_b at T[m*LP + lp], m < n): dx stored through
+// store_y (y holds dx), and each line pair's sums of the dalpha and dbeta
+// terms, taken in a fixed order (an LDS tree over the n elements of each
+// line), written to part: one float2 per line pair for d >= 2 (both rows
+// belong to one (b, c) pair), one per signal for d = 1 (part[2h], part[2h+1]).
+// xa, xb: the x values of the thread's elements, loaded before the transform.
+template <int L, bool BF16, int ITER, class Ctx>
+__host__ __device__ __forceinline__ void bwd_epilogue(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
+                                                      const RowMeta* M, const float* xa, const float* xb)
+{
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2;
+    const int tid = ctx.tid();
+    float2 ea[ITER], eb[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / n, m = idx % n;
+        const RowMeta& md = M[lp];
+        const float2 z = T[m * LP + lp];
+        ea[i] = make_float2(0.f, 0.f);
+        eb[i] = make_float2(0.f, 0.f);
+        if (md.valid) {
+            store_y<BF16>(a, md.o0 + m, gate_vjp(ctx, z.x, xa[i], md.al0, md.be0, ea[i]));
+            if (md.valid1) store_y<BF16>(a, md.o1 + m, gate_vjp(ctx, z.y, xb[i], md.al1, md.be1, eb[i]));
+        }
+    }
+    ctx.sync();  // every read of du in T is done
+    float2* Ea = T;
+    float2* Eb = T + NP * n;
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT;
+        Ea[idx] = ea[i];
+        Eb[idx] = eb[i];
+    }
+    ctx.sync();
+    for (int h = n / 2; h >= 1; h /= 2) {
+        for (int e = tid; e < 2 * NP * h; e += NT) {
+            const int half = e / (NP * h), r = e % (NP * h), lp = r / h, m = r % h;
+            float2* E = half ? Eb : Ea;
+            E[lp * n + m] = cadd(E[lp * n + m], E[lp * n + m + h]);
+        }
+        ctx.sync();
+    }
+    for (int lp = tid; lp < NP; lp += NT) {
+        const RowMeta& md = M[lp];
+        if (!md.valid) continue;
+        const long long h = (long long)bid * NP + lp;
+        if (a.g.d == 1) {
+            a.part[2 * h] = Ea[lp * n];
+            if (md.valid1) a.part[2 * h + 1] = Eb[lp * n];
+        } else {
+            a.part[h] = cadd(Ea[lp * n], Eb[lp * n]);
+        }
+    }
+}
+
 // --------------------------------------------------------------- row_inv
-template <int L, bool BF16, class Ctx>
+// BWD: the inverse transforms carry du; the epilogue computes dx and the
+// partial sums of dalpha and dbeta (x is read again: the forward saves no
+// intermediate, the explainer's gradient-checkpointing pattern).
+template <int L, bool BF16, bool BWD, class Ctx>
 __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
@@ -206,16 +290,29 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
             T[(L - k) * LP + lp] = make_float2(ya[i].x + yb[i].y, yb[i].x - ya[i].y);
         }
     }
+    float xa[BWD ? ITER : 1], xb[BWD ? ITER : 1];
+    if constexpr (BWD) {
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / n, m = idx % n;
+            xa[i] = load_x<BF16>(a, M[lp].o0 + m);
+            xb[i] = load_x<BF16>(a, M[lp].o1 + m);
+        }
+    }
     ctx.sync();
     tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
+    if constexpr (BWD) {
+        bwd_epilogue<L, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
+    } else {
 #pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT, lp = idx / n, m = idx % n;
-        const RowMeta& md = M[lp];
-        const float2 z = T[m * LP + lp];
-        if (md.valid) {
-            store_y<BF16>(a, md.o0 + m, z.x);
-            store_y<BF16>(a, md.o1 + m, z.y);
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / n, m = idx % n;
+            const RowMeta& md = M[lp];
+            const float2 z = T[m * LP + lp];
+            if (md.valid) {
+                store_y<BF16>(a, md.o0 + m, z.x);
+                store_y<BF16>(a, md.o1 + m, z.y);
+            }
         }
     }
 }
@@ -300,7 +397,9 @@ __host__ __device__ __forceinline__ OutTile out_tile(const Geom& g, int B, int n
 // carry Z = A + iB (packed bins 0 and N_in/2) and need the mirror element
 // (-k_out, -k_mid):  W = Z Sv + conj(Z(-k)) Dv.  Each job owns an element and
 // its mirror, so no two threads touch the same element.
-template <int L, int NR, int TW, int NT, class Ctx>
+// CONJ multiplies by the conjugate spectrum (the backward's correlation with
+// K): Sv, Dv of a real kernel conjugate like the spectrum itself.
+template <int L, int NR, int TW, int NT, bool CONJ = false, class Ctx>
 __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const Geom& g, const OutTile& o,
                                                            const float2* kc, float2* T)
 {
@@ -317,10 +416,11 @@ __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const
         }
         const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
         const float2 Za = T[ea], Zb = T[eb];
-        const float2 Sa = kc[pa * PS + (long long)o.rows[ra] * g.lt];
-        const float2 Sb = kc[pb * PS + (long long)o.rows[rb] * g.lt];
-        const float2 Da = kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]];
-        const float2 Db = kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]];
+        auto kv = [](float2 v) { return CONJ ? cconj(v) : v; };
+        const float2 Sa = kv(kc[pa * PS + (long long)o.rows[ra] * g.lt]);
+        const float2 Sb = kv(kc[pb * PS + (long long)o.rows[rb] * g.lt]);
+        const float2 Da = kv(kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]]);
+        const float2 Db = kv(kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]]);
         const float2 Wa = cadd(cmul(Za, Sa), cmul(cconj(Zb), Da));
         const float2 Wb = cadd(cmul(Zb, Sb), cmul(cconj(Za), Db));
         T[ea] = Wa;
@@ -477,11 +577,172 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     }
 }
 
+// Kernel-gradient product for the k_in = 0 lines of tile 0: T holds, in
+// column 0 of each row block, the forward out-axis transform Zd of the output
+// gradient and, in column 1, Zu of the gated input (both packed: Z = A + iB,
+// A and B the spectra of the bin-0 and bin-N_in/2 planes).  Writes to column
+// 2 the packed product  P = A_d conj(A_u) + i B_d conj(B_u),  with
+// A = (Z(k) + conj Z(-k))/2 and B = (Z(k) - conj Z(-k))/(2i); the mirror
+// element takes P(-k) = conj(A_d) A_u + i conj(B_d) B_u (A and B Hermitian).
+template <int L, int NR, int TW, int NT, class Ctx>
+__host__ __device__ __forceinline__ void out_slot0_corr(const Ctx& ctx, const OutTile& o, float2* T)
+{
+    constexpr int NL = NR * TW;
+    const int njobs = o.self_mirror ? NR * (L / 2 + 1) : L;
+    for (int job = ctx.tid(); job < njobs; job += NT) {
+        int ra, rb, pa, pb;
+        if (o.self_mirror) {
+            ra = job / (L / 2 + 1); rb = ra;
+            pa = job % (L / 2 + 1); pb = (L - pa) % L;
+        } else {
+            ra = 0; rb = 1; pa = job; pb = (L - job) % L;
+        }
+        const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
+        const float2 Da = T[ea], Db = T[eb], Ua = T[ea + 1], Ub = T[eb + 1];
+        const float2 Ad = cscale(cadd(Da, cconj(Db)), 0.5f), Au = cscale(cadd(Ua, cconj(Ub)), 0.5f);
+        const float2 vd = csub(Da, cconj(Db)), vu = csub(Ua, cconj(Ub));
+        const float2 Bd = make_float2(0.5f * vd.y, -0.5f * vd.x), Bu = make_float2(0.5f * vu.y, -0.5f * vu.x);
+        const float2 pA = cmulc(Ad, Au), pB = cmulc(Bd, Bu);
+        T[ea + 2] = make_float2(pA.x - pB.y, pA.y + pB.x);
+        if (eb != ea) {
+            const float2 qA = cmulc(Au, Ad), qB = cmulc(Bu, Bd);  // conj(A_d) A_u, conj(B_d) B_u
+            T[eb + 2] = make_float2(qA.x - qB.y, qA.y + qB.x);
+        }
+    }
+}
+
+// Backward out axis, one (channel, tile) per workgroup, looping over the B
+// batch entries (the kernel spectrum tile is read once per workgroup):
+//   DY_b = forward out-axis FFT of the output-gradient columns,
+//   du_b = pruned inverse of DY_b conj(Khat), written back in place,
+// and with DK also
+//   U_b  = forward out-axis FFT of the gated-input columns,
+//   P   += DY_b conj(U_b)   (registers; k_in = 0 lines through out_slot0_corr)
+// followed by the full inverse of P (all N_out positions: the kernel gradient
+// lives on every offset) into the kernel-gradient planes dkw.
+template <int L, int NR, bool DK, class Ctx>
+__host__ __device__ __forceinline__ void col_out_bwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = out_tw(L, NR);
+    constexpr int NL = NR * TW, NT = out_nt(L, NR);
+    constexpr int R0 = pass_radix<L, false>(0);
+    constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
+    static_assert(TW >= 3, "the k_in = 0 staging uses three columns per row block");
+    const Geom& g = a.g;
+    const int tid = ctx.tid();
+    const OutTile o = out_tile<NR, TW>(g, 1, a.nch, bid);
+    const int k0 = o.t * TW, u0 = k0 & (g.lt - 1);
+    const long long tile = k0 >> g.lt_log;
+    // Position stride of the planes (workspace, kernel spectrum and dkw alike);
+    // lane offsets as in col_out_body.
+    const long long PS = (long long)g.N_mid * g.lt;
+    const float2* kc = a.khat + (long long)(a.c0 + o.c_local) * g.ksz;
+    const float2* kt = kc + tile * ((long long)g.N_out * g.N_mid * g.lt);
+    auto lane_bytes = [&](int j, int l) -> unsigned {
+        return 8u * ((unsigned)j * (unsigned)PS + (unsigned)o.rows[l / TW] * (unsigned)g.lt + (unsigned)(u0 + l % TW));
+    };
+    auto at = [](auto* p, long long q_elems, unsigned bytes) { return add_bytes(p + q_elems, bytes); };
+    auto lvalid = [&](int l) { return k0 + l % TW < g.S; };
+    using P0 = PassRegs<L, R0, NL, NT>;
+    using PL = PassRegs<L, RL, NL, NT>;
+    auto load_cols = [&](const float2* base, P0& s) {
+        pass_load_fn<L, R0, NL, NT, true>(ctx, [&](int j, int q, int l) -> float2 {
+            const bool ok = lvalid(l);
+            const float2 x = *at(base, q * PS, ok ? lane_bytes(j, l) : 0u);
+            return ok ? x : make_float2(0.f, 0.f);
+        }, s);
+    };
+    float2 kv[PL::PER][RL];
+    bool kok[PL::PER];
+    const auto tw_staged = ctx.stage_load();
+#pragma unroll
+    for (int i = 0; i < PL::PER; ++i) {
+        const int gi = tid + i * NT, l = gi % NL, j = gi / NL;
+        kok[i] = bf_valid<PL::NB, NT>(gi) && lvalid(l) && k0 + l % TW != 0;
+        const unsigned lb = kok[i] ? lane_bytes(j, l) : 8u;
+#pragma unroll
+        for (int r = 0; r < RL; ++r) kv[i][r] = *at(kt, (long long)r * (L / RL) * PS, lb);
+    }
+    ctx.stage_store(tw_staged);
+    PL P;
+    if constexpr (DK) {
+#pragma unroll
+        for (int i = 0; i < PL::PER; ++i)
+#pragma unroll
+            for (int r = 0; r < RL; ++r) P.v[i][r] = make_float2(0.f, 0.f);
+    }
+    for (int b = 0; b < a.B; ++b) {
+        const long long poff = ((long long)o.c_local * a.B + b) * g.wsp + tile * ws_tile_stride(g);
+        float2* bdy = a.ws + poff;
+        P0 s;
+        load_cols(bdy, s);
+        PL t = fwd_from_regs<L, NL, NT, true>(ctx, T, s);
+        ctx.sync();  // every LDS read of the transform is done: T is free
+        PL tu;
+        if constexpr (DK) {
+            P0 s2;
+            load_cols(a.ws_u + poff, s2);
+            tu = fwd_from_regs<L, NL, NT, true>(ctx, T, s2);
+            ctx.sync();
+        }
+        if (o.t == 0) {
+            pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
+                if (l % TW == 0) T[pos * NL + l] = x;
+            });
+            if constexpr (DK) {
+                pass_visit<L, RL, NL, NT, false>(ctx, tu, [&](int pos, int l, float2& x) {
+                    if (l % TW == 0) T[pos * NL + l + 1] = x;
+                });
+                ctx.sync();
+                out_slot0_corr<L, NR, TW, NT>(ctx, o, T);
+            }
+            ctx.sync();
+            out_slot0_product<L, NR, TW, NT, true>(ctx, g, o, kc, T);
+            ctx.sync();
+            pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
+                if (l % TW == 0) x = T[pos * NL + l];
+            });
+            if constexpr (DK) {
+                pass_visit<L, RL, NL, NT, false>(ctx, P, [&](int pos, int l, float2& x) {
+                    if (l % TW == 0) x = cadd(x, T[pos * NL + l + 2]);
+                });
+            }
+            ctx.sync();
+        }
+        // Lines outside the grid and the k_in = 0 lines (done above) keep their values.
+#pragma unroll
+        for (int i = 0; i < PL::PER; ++i) {
+#pragma unroll
+            for (int r = 0; r < RL; ++r) {
+                if constexpr (DK) {
+                    const float2 pc = cadd(P.v[i][r], cmulc(t.v[i][r], tu.v[i][r]));
+                    P.v[i][r] = kok[i] ? pc : P.v[i][r];
+                }
+                const float2 m = cmulc(t.v[i][r], kv[i][r]);
+                t.v[i][r] = kok[i] ? m : t.v[i][r];
+            }
+        }
+        inv_to_fn<L, NL, NT, true>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+            if (lvalid(l)) *at(bdy, q * PS, lane_bytes(j, l)) = x;
+        });
+        ctx.sync();  // the inverse's last LDS reads are done: T is free
+    }
+    if constexpr (DK) {
+        float2* dk = a.dkw + (long long)o.c_local * g.kmain + tile * ((long long)g.N_out * g.N_mid * g.lt);
+        inv_to_fn<L, NL, NT, false>(ctx, T, P, [&](int j, int q, int l, const float2& x) {
+            if (lvalid(l)) *at(dk, q * PS, lane_bytes(j, l)) = x;
+        });
+    }
+}
+
 // ---------------------------------------------------------------- conv1d
 // d = 1: the two signals of a line belong to consecutive pair slots (possibly
 // different channels), so the product is applied to the separated half spectra.
 // RowMeta: w0 / w1 hold the kernel spectrum offsets of the two channels.
-template <int L, bool BF16, class Ctx>
+// BWD: the line carries the output gradients dy (no gate), the product takes
+// the conjugate spectrum (a correlation with K), and the backward epilogue
+// turns du into dx and the dalpha / dbeta partial sums.
+template <int L, bool BF16, bool BWD, class Ctx>
 __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                      RowMeta* M)
 {
@@ -510,13 +771,27 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
         M[lp] = m;
     }
     ctx.sync();
-    for (int idx = tid; idx < NP * n; idx += NT) {
-        const int lp = idx / n, m = idx % n;
+    constexpr int ITER = NP * n / NT;
+    static_assert(NP * n % NT == 0, "whole element loops");
+    float xa[BWD ? ITER : 1], xb[BWD ? ITER : 1];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / n, m = idx % n;
         const RowMeta& md = M[lp];
         float2 z = make_float2(0.f, 0.f);
         if (md.valid) {
-            z.x = ctx.gate(load_x<BF16>(a, md.o0 + m), md.al0, md.be0);
-            if (md.valid1) z.y = ctx.gate(load_x<BF16>(a, md.o1 + m), md.al1, md.be1);
+            if constexpr (BWD) {
+                xa[i] = load_x<BF16>(a, md.o0 + m);
+                xb[i] = md.valid1 ? load_x<BF16>(a, md.o1 + m) : 0.f;
+                z.x = load_in<BF16>(a.dy, md.o0 + m);
+                if (md.valid1) z.y = load_in<BF16>(a.dy, md.o1 + m);
+            } else {
+                z.x = ctx.gate(load_x<BF16>(a, md.o0 + m), md.al0, md.be0);
+                if (md.valid1) z.y = ctx.gate(load_x<BF16>(a, md.o1 + m), md.al1, md.be1);
+            }
+        } else if constexpr (BWD) {
+            xa[i] = 0.f;
+            xb[i] = 0.f;
         }
         T[m * LP + lp] = z;
     }
@@ -528,19 +803,21 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
         if (!md.valid) continue;
         const float2* ka = a.khat + md.w0;
         const float2* kb = a.khat + md.w1;
+        // the spectrum value, conjugated for the backward
+        auto kv = [](const float2* p, int i) { const float2 v = p[i]; return BWD ? cconj(v) : v; };
         if (k == 0) {
             const float2 Z0 = T[lp], ZS = T[S * LP + lp];
             const float2 Xa = make_float2(2.f * Z0.x, 2.f * ZS.x), Xb = make_float2(2.f * Z0.y, 2.f * ZS.y);
-            const float2 Wa = cadd(cmul(Xa, ka[0]), cmul(cconj(Xa), ka[S]));
-            float2 Wb = cadd(cmul(Xb, kb[0]), cmul(cconj(Xb), kb[S]));
+            const float2 Wa = cadd(cmul(Xa, kv(ka, 0)), cmul(cconj(Xa), kv(ka, S)));
+            float2 Wb = cadd(cmul(Xb, kv(kb, 0)), cmul(cconj(Xb), kv(kb, S)));
             if (!md.valid1) Wb = make_float2(0.f, 0.f);
             T[lp] = make_float2(Wa.x, Wb.x);
             T[S * LP + lp] = make_float2(Wa.y, Wb.y);
         } else {
             const float2 Z = T[k * LP + lp], Zm = T[(L - k) * LP + lp];
             const float2 Xa = make_float2(Z.x + Zm.x, Z.y - Zm.y), Xb = make_float2(Z.y + Zm.y, Zm.x - Z.x);
-            const float2 Ya = cmul(Xa, ka[k]);
-            float2 Yb = cmul(Xb, kb[k]);
+            const float2 Ya = cmul(Xa, kv(ka, k));
+            float2 Yb = cmul(Xb, kv(kb, k));
             if (!md.valid1) Yb = make_float2(0.f, 0.f);
             T[k * LP + lp] = make_float2(Ya.x - Yb.y, Ya.y + Yb.x);
             T[(L - k) * LP + lp] = make_float2(Ya.x + Yb.y, Yb.x - Ya.y);
@@ -548,13 +825,17 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
     }
     ctx.sync();
     tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
-    for (int idx = tid; idx < NP * n; idx += NT) {
-        const int lp = idx / n, m = idx % n;
-        const RowMeta& md = M[lp];
-        if (!md.valid) continue;
-        const float2 z = T[m * LP + lp];
-        store_y<BF16>(a, md.o0 + m, z.x);
-        if (md.valid1) store_y<BF16>(a, md.o1 + m, z.y);
+    if constexpr (BWD) {
+        bwd_epilogue<L, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
+    } else {
+        for (int idx = tid; idx < NP * n; idx += NT) {
+            const int lp = idx / n, m = idx % n;
+            const RowMeta& md = M[lp];
+            if (!md.valid) continue;
+            const float2 z = T[m * LP + lp];
+            store_y<BF16>(a, md.o0 + m, z.x);
+            if (md.valid1) store_y<BF16>(a, md.o1 + m, z.y);
+        }
     }
 }
 
@@ -654,16 +935,18 @@ __host__ __device__ __forceinline__ void spec_row_body(const Ctx& ctx, int bid, 
     }
 }
 
-// Full forward FFT along the middle axis of the main block (3-D), in place.
-template <int L, class Ctx>
-__host__ __device__ __forceinline__ void spec_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+// Full FFT (forward, or inverse with INV) along the middle axis of 3-D planes
+// of N_out * N_mid * S values in the tile-major layout of the kernel
+// spectrum's main block, in place; plane p starts at planes + p * pstride.
+template <int L, bool INV, class Ctx>
+__host__ __device__ __forceinline__ void plane_mid_body(const Ctx& ctx, int bid, const Geom& g, float2* planes,
+                                                        long long pstride, float2* T)
 {
     constexpr int TW = col_tw(L), NT = col_nt(L);
-    const Geom& g = a.g;
     const int lines = g.N_out * g.S;
     const int tpc = (lines + TW - 1) / TW;
     const int c = bid / tpc, lam0 = (bid % tpc) * TW;
-    float2* base = const_cast<float2*>(a.khat) + (long long)c * g.ksz;
+    float2* base = planes + (long long)c * pstride;
     const long long rows = (long long)g.N_out * g.N_mid;
     const int tid = ctx.tid();
     ctx.stage();
@@ -674,11 +957,18 @@ __host__ __device__ __forceinline__ void spec_mid_body(const Ctx& ctx, int bid, 
         T[pos * TW + l] = z;
     }
     ctx.sync();
-    tile_fft<L, TW, TW, NT, false, false, false>(ctx, T);
+    tile_fft<L, TW, TW, NT, INV, false, false>(ctx, T);
     for (int idx = tid; idx < L * TW; idx += NT) {
         const int pos = idx / TW, l = idx % TW, lam = lam0 + l;
         if (lam < lines) base[tm_index(g, rows, (long long)(lam / g.S) * g.N_mid + pos, lam % g.S)] = T[pos * TW + l];
     }
+}
+
+// Forward middle-axis FFT of the kernel spectrum's main block (3-D).
+template <int L, class Ctx>
+__host__ __device__ __forceinline__ void spec_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    plane_mid_body<L, false>(ctx, bid, a.g, const_cast<float2*>(a.khat), a.g.ksz, T);
 }
 
 // Full forward FFT along the out axis, then scale by g = 1/(2 prod N) and, for
@@ -743,6 +1033,181 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
         const int pos = idx / NL, l = idx % NL, row = l / TW, col = l % TW;
         const int k = o.t * TW + col;
         if (k < g.S) kc[tm_index(g, rows, (long long)pos * g.N_mid + o.rows[row], k)] = T[pos * NL + l];
+    }
+}
+
+// ======================================================== backward tails
+// dalpha, dbeta of the chunk's channel `bid`: the sum of its B * pair_lines
+// partial sums, in a fixed order (strided per thread, then an LDS tree), in
+// fp64.  R: LDS scratch of 2 * NT doubles.
+template <int NT, class Ctx>
+__host__ __device__ __forceinline__ void gate_reduce_body(const Ctx& ctx, int bid, const ConvArgs& a, double* R)
+{
+    const int per = a.B * pair_lines(a.g);
+    const float2* p = a.part + (long long)bid * per;
+    const int tid = ctx.tid();
+    double sa = 0.0, sb = 0.0;
+    for (int e = tid; e < per; e += NT) {
+        const float2 v = p[e];
+        sa += (double)v.x;
+        sb += (double)v.y;
+    }
+    R[tid] = sa;
+    R[NT + tid] = sb;
+    ctx.sync();
+    for (int h = NT / 2; h >= 1; h /= 2) {
+        if (tid < h) {
+            R[tid] += R[tid + h];
+            R[NT + tid] += R[NT + tid + h];
+        }
+        ctx.sync();
+    }
+    if (tid == 0) {
+        a.dalpha[a.c0 + bid] = (float)R[0];
+        a.dbeta[a.c0 + bid] = (float)R[NT];
+    }
+}
+
+// d = 1 kernel gradient, first step: the line u_q + i dy_q of pair q (gated
+// input and output gradient of one signal) -> FFT -> separated 2U, 2DY ->
+// P_q = 2DY conj(2U) on the S slots (slot 0 packs the real bins 0 and S) into
+// dkw[q][S].
+template <int L, bool BF16, class Ctx>
+__host__ __device__ __forceinline__ void corr1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
+                                                     RowMeta* M)
+{
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
+    const Geom& g = a.g;
+    const int P = a.nch * a.B;
+    const int tid = ctx.tid();
+    ctx.stage();
+    for (int lp = tid; lp < NP; lp += NT) {
+        const int q = bid * NP + lp;
+        RowMeta m{};
+        m.valid = q < P;
+        if (m.valid) {
+            const int c = a.c0 + q / a.B, b = q % a.B;
+            m.o0 = ((long long)b * a.C + c) * g.vox;
+            m.w0 = (long long)q * S;
+            m.al0 = a.alpha[c];
+            m.be0 = a.beta[c];
+        }
+        M[lp] = m;
+    }
+    ctx.sync();
+    for (int idx = tid; idx < NP * n; idx += NT) {
+        const int lp = idx / n, m = idx % n;
+        const RowMeta& md = M[lp];
+        float2 z = make_float2(0.f, 0.f);
+        if (md.valid)
+            z = make_float2(ctx.gate(load_x<BF16>(a, md.o0 + m), md.al0, md.be0), load_in<BF16>(a.dy, md.o0 + m));
+        T[m * LP + lp] = z;
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, false, true, false>(ctx, T);
+    for (int idx = tid; idx < NP * S; idx += NT) {
+        const int lp = idx / S, k = idx % S;
+        const RowMeta& md = M[lp];
+        if (!md.valid) continue;
+        const float2 Z = T[k * LP + lp];
+        float2 p;
+        if (k == 0) {
+            const float2 ZS = T[S * LP + lp];
+            p = make_float2(4.f * Z.x * Z.y, 4.f * ZS.x * ZS.y);
+        } else {
+            const float2 Zm = T[(L - k) * LP + lp];
+            const float2 ou = make_float2(Z.x + Zm.x, Z.y - Zm.y), od = make_float2(Z.y + Zm.y, Zm.x - Z.x);
+            p = cmulc(od, ou);
+        }
+        a.dkw[md.w0 + k] = p;
+    }
+}
+
+// Kernel gradient, last step: inverse real FFT of the innermost axis over the
+// full length (every offset is kept), scaled by 1 / (4 prod N) (the planes
+// hold 4 DY conj(U) summed over the batch) and written to dK at the offsets
+// delta = unwrap(index); the wrap slot n of every axis carries nothing.
+// d >= 2: rows r, r+1 of a channel's dkw plane (N_out * N_mid rows, after the
+// outer inverse transforms); d = 1: the line pairs channels 2h, 2h+1 of the
+// chunk, each summing its B per-pair spectra.
+template <int L, class Ctx>
+__host__ __device__ __forceinline__ void dk_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
+                                                     RowMeta* M)
+{
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), S = L / 2;
+    const Geom& g = a.g;
+    const bool one_d = g.d == 1;
+    const int rc = g.N_out * g.N_mid;
+    const int hp = one_d ? 1 : rc / 2;
+    const int H = one_d ? (a.nch + 1) / 2 : a.nch * hp;
+    const int tid = ctx.tid();
+    ctx.stage();
+    for (int lp = tid; lp < NP; lp += NT) {
+        const int h = bid * NP + lp;
+        RowMeta m{};
+        m.valid = h < H;
+        if (m.valid) {
+            if (one_d) {
+                m.w0 = 2 * h;
+                m.w1 = 2 * h + 1;
+                m.valid1 = 2 * h + 1 < a.nch;
+            } else {
+                m.w0 = m.w1 = h / hp;
+                m.o0 = (h % hp) * 2;
+                m.o1 = m.o0 + 1;
+                m.valid1 = 1;
+            }
+        }
+        M[lp] = m;
+    }
+    ctx.sync();
+    for (int idx = tid; idx < NP * S; idx += NT) {
+        const int lp = idx / S, k = idx % S;
+        const RowMeta& md = M[lp];
+        float2 ya = make_float2(0.f, 0.f), yb = make_float2(0.f, 0.f);
+        if (md.valid) {
+            if (one_d) {
+                for (int b = 0; b < a.B; ++b) {
+                    ya = cadd(ya, a.dkw[((long long)md.w0 * a.B + b) * S + k]);
+                    if (md.valid1) yb = cadd(yb, a.dkw[((long long)md.w1 * a.B + b) * S + k]);
+                }
+            } else {
+                const float2* pl = a.dkw + md.w0 * g.kmain;
+                ya = pl[tm_index(g, rc, md.o0, k)];
+                yb = pl[tm_index(g, rc, md.o1, k)];
+            }
+        }
+        if (k == 0) {
+            T[lp] = make_float2(ya.x, yb.x);
+            T[S * LP + lp] = make_float2(ya.y, yb.y);
+        } else {
+            T[k * LP + lp] = make_float2(ya.x - yb.y, ya.y + yb.x);
+            T[(L - k) * LP + lp] = make_float2(ya.x + yb.y, yb.x - ya.y);
+        }
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
+    const float sc = 1.0f / (4.0f * (float)g.N_out * (float)g.N_mid * (float)g.N_in);
+    const long long kl = (long long)g.ke_out * g.ke_mid * g.ke_in;
+    for (int idx = tid; idx < NP * L; idx += NT) {
+        const int lp = idx / L, t = idx % L;
+        const RowMeta& md = M[lp];
+        const int d2 = unwrap(t, g.n_in, g.N_in);
+        if (!md.valid || d2 == kEmpty) continue;
+        const float2 z = T[t * LP + lp];
+        for (int s2 = 0; s2 < 2; ++s2) {
+            if (s2 == 1 && !md.valid1) break;
+            const long long c = s2 ? md.w1 : md.w0;
+            int d0 = 0, d1 = 0;
+            if (!one_d) {
+                const int row = (int)(s2 ? md.o1 : md.o0);
+                d0 = unwrap(row / g.N_mid, g.n_out, g.N_out);
+                d1 = unwrap(row % g.N_mid, g.n_mid, g.N_mid);
+                if (d0 == kEmpty || d1 == kEmpty) continue;
+            }
+            a.dK[(a.c0 + c) * kl + ((long long)(d0 + g.n_out - 1) * g.ke_mid + (d1 + g.n_mid - 1)) * g.ke_in +
+                 (d2 + g.n_in - 1)] = (s2 ? z.y : z.x) * sc;
+        }
     }
 }
 

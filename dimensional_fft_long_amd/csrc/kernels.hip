@@ -32,6 +32,10 @@ struct DevCtx {
         const float e = __builtin_amdgcn_exp2f(-(al * x + be) * 1.44269504088896341f);
         return x * __builtin_amdgcn_rcpf(1.0f + e);
     }
+    __device__ float sigmoid(float v) const
+    {
+        return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * 1.44269504088896341f));
+    }
     // Two halves so that callers can issue other loads in between: every
     // load of the copy is issued before the first store.
     static constexpr int kTwSize = tw_table_size<L, PLANS>();
@@ -72,31 +76,80 @@ __device__ __forceinline__ DevCtx<L, NT, PLANS> make_ctx(float2* twl)
     return DevCtx<L, NT, PLANS>{twl};
 }
 
-template <int L, bool BF16>
+template <int L, bool BF16, bool GATE>
 __global__ __launch_bounds__(row_nt(L)) void k_row_fwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
-    row_fwd_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+    row_fwd_body<L, BF16, GATE>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
-template <int L, bool BF16>
+template <int L, bool BF16, bool BWD>
 __global__ __launch_bounds__(row_nt(L)) void k_row_inv(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
-    row_inv_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+    row_inv_body<L, BF16, BWD>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
-template <int L, bool BF16>
+template <int L, bool BF16, bool BWD>
 __global__ __launch_bounds__(row_nt(L)) void k_conv1d(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
-    conv1d_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+    conv1d_body<L, BF16, BWD>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+}
+
+template <int L, int NR, bool DK>
+__global__ __launch_bounds__(out_nt(L, NR)) void k_col_out_bwd(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
+    __shared__ float2 T[L * NR * out_tw(L, NR)];
+    col_out_bwd_body<L, NR, DK>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
+}
+
+template <int L>
+__global__ __launch_bounds__(col_nt(L)) void k_plane_mid_inv(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * col_tw(L)];
+    plane_mid_body<L, true>(make_ctx<L, col_nt(L), kPlanF>(TWL), (int)blockIdx.x, a.g, a.dkw, a.g.kmain, T);
+}
+
+template <int L, bool BF16>
+__global__ __launch_bounds__(row_nt(L)) void k_corr1d(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * row_lp(L)];
+    __shared__ RowMeta M[row_np(L)];
+    corr1d_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+}
+
+template <int L>
+__global__ __launch_bounds__(row_nt(L)) void k_dk_row(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * row_lp(L)];
+    __shared__ RowMeta M[row_np(L)];
+    dk_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+}
+
+constexpr int kReduceNT = 256;
+
+__global__ __launch_bounds__(kReduceNT) void k_gate_reduce(ConvArgs a)
+{
+    __shared__ double R[2 * kReduceNT];
+    gate_reduce_body<kReduceNT>(make_ctx<4, kReduceNT, kPlanF>(nullptr), (int)blockIdx.x, a, R);
+}
+
+// Zero fill (the gradients of an empty batch), n floats.
+__global__ __launch_bounds__(256) void k_zero(float* p, long long n)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
 }
 
 template <int L, bool INV>
@@ -196,16 +249,16 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
         return with_length(g.N_in, [&]<int L>() {
             const long long H = ((long long)a.nch * a.B + 1) / 2;
             mark();
-            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-            else hipLaunchKernelGGL((k_conv1d<L, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_conv1d<L, false, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
             return last_error();
         });
     }
     const long long H = (long long)a.nch * a.B * (g.n_out * g.n_mid / 2);
     e = with_length(g.N_in, [&]<int L>() {
         mark();
-        if (a.bf16) hipLaunchKernelGGL((k_row_fwd<L, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        else hipLaunchKernelGGL((k_row_fwd<L, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        if (a.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_fwd<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
     if (e != hipSuccess) return e;
@@ -243,10 +296,114 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
     if (e != hipSuccess) return e;
     return with_length(g.N_in, [&]<int L>() {
         mark();
-        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        else hipLaunchKernelGGL((k_row_inv<L, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_inv<L, false, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
+}
+
+hipError_t launch_zero(float* p, long long n, hipStream_t st)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero, dim3(ceil_div(n, 256)), dim3(256), 0, st, p, n);
+    return last_error();
+}
+
+hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
+{
+    auto mark = [&]() { if (tr) tr->mark(st); };
+    const Geom& g = a.g;
+    hipError_t e;
+    auto reduce = [&]() {
+        mark();
+        hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)a.nch), dim3(kReduceNT), 0, st, a);
+        return last_error();
+    };
+    auto dk_rows = [&](long long lines) {
+        return with_length(g.N_in, [&]<int L>() {
+            mark();
+            hipLaunchKernelGGL(k_dk_row<L>, dim3(ceil_div(lines, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            return last_error();
+        });
+    };
+    if (g.d == 1) {
+        e = with_length(g.N_in, [&]<int L>() {
+            const long long H = ((long long)a.nch * a.B + 1) / 2;
+            mark();
+            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_conv1d<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            return last_error();
+        });
+        if (e != hipSuccess) return e;
+        if ((e = reduce()) != hipSuccess || !dk) return e;
+        e = with_length(g.N_in, [&]<int L>() {
+            mark();
+            const unsigned grid = ceil_div((long long)a.nch * a.B, row_np(L));
+            if (a.bf16) hipLaunchKernelGGL((k_corr1d<L, true>), dim3(grid), dim3(row_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_corr1d<L, false>), dim3(grid), dim3(row_nt(L)), 0, st, a);
+            return last_error();
+        });
+        if (e != hipSuccess) return e;
+        return dk_rows(((long long)a.nch + 1) / 2);
+    }
+    ConvArgs ady = a;  // the row pass reads the output gradient in place of x
+    ady.x = a.dy;
+    ConvArgs au = a;   // the gated input's planes
+    au.ws = a.ws_u;
+    const long long H = (long long)a.nch * a.B * (g.n_out * g.n_mid / 2);
+    e = with_length(g.N_in, [&]<int L>() {
+        mark();
+        if (ady.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, ady);
+        else hipLaunchKernelGGL((k_row_fwd<L, false, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, ady);
+        if (last_error() != hipSuccess || !dk) return last_error();
+        mark();
+        if (au.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, au);
+        else hipLaunchKernelGGL((k_row_fwd<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, au);
+        return last_error();
+    });
+    if (e != hipSuccess) return e;
+    auto col_mid = [&]<bool INV>(const ConvArgs& arg) {
+        return with_length(g.N_mid, [&]<int L>() {
+            const long long grid = (long long)arg.nch * arg.B * ceil_div((long long)g.n_out * g.S, col_tw(L));
+            mark();
+            hipLaunchKernelGGL((k_col_mid<L, INV>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, arg);
+            return last_error();
+        });
+    };
+    if (g.d == 3) {
+        if ((e = col_mid.template operator()<false>(a)) != hipSuccess) return e;
+        if (dk && (e = col_mid.template operator()<false>(au)) != hipSuccess) return e;
+    }
+    auto col_out = [&]<int NR>() {
+        return with_length(g.N_out, [&]<int L>() {
+            const long long grid = (long long)a.nch * (NR == 1 ? 1 : g.N_mid / 2) * ceil_div(g.S, out_tw(L, NR));
+            mark();
+            if (dk) hipLaunchKernelGGL((k_col_out_bwd<L, NR, true>), dim3((unsigned)grid), dim3(out_nt(L, NR)), 0, st, a);
+            else hipLaunchKernelGGL((k_col_out_bwd<L, NR, false>), dim3((unsigned)grid), dim3(out_nt(L, NR)), 0, st, a);
+            return last_error();
+        });
+    };
+    e = g.d == 3 ? col_out.template operator()<2>() : col_out.template operator()<1>();
+    if (e != hipSuccess) return e;
+    if (g.d == 3 && (e = col_mid.template operator()<true>(a)) != hipSuccess) return e;
+    e = with_length(g.N_in, [&]<int L>() {
+        mark();
+        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_inv<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        return last_error();
+    });
+    if (e != hipSuccess) return e;
+    if ((e = reduce()) != hipSuccess || !dk) return e;
+    if (g.d == 3) {
+        e = with_length(g.N_mid, [&]<int L>() {
+            const long long grid = (long long)a.nch * ceil_div((long long)g.N_out * g.S, col_tw(L));
+            mark();
+            hipLaunchKernelGGL(k_plane_mid_inv<L>, dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
+            return last_error();
+        });
+        if (e != hipSuccess) return e;
+    }
+    return dk_rows((long long)a.nch * (g.N_out * g.N_mid / 2));
 }
 
 hipError_t launch_spectrum(const ConvArgs& a, hipStream_t st)

@@ -26,6 +26,14 @@ struct LaunchTrace {
 // [a.c0, a.c0 + a.nch) of every batch entry.
 hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace = nullptr);
 
+// Backward for the channels [a.c0, a.c0 + a.nch): dx (into a.y), dalpha,
+// dbeta and, with dk, the kernel gradient a.dK, using the chunk workspace
+// a.ws (output-gradient planes), a.ws_u, a.dkw (with dk) and a.part.
+hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t stream, LaunchTrace* trace = nullptr);
+
+// Zero fill of n floats.
+hipError_t launch_zero(float* p, long long n, hipStream_t stream);
+
 // Kernel spectrum of all channels into a.khat (in place, no workspace).
 hipError_t launch_spectrum(const ConvArgs& a, hipStream_t stream);
 

@@ -142,6 +142,16 @@ struct ConvArgs {
     int c0;                 // first channel of this chunk
     int nch;                // channels in this chunk (pairs = nch * B, channel-major)
     int bf16;               // I/O dtype: 0 fp32, 1 bf16
+    // Backward only (y then holds dx):
+    const void* dy;         // [B][C][vox], dtype of x
+    float2* ws_u;           // gated-input planes, like ws (when dK is wanted)
+    float2* dkw;            // d >= 2: per chunk channel, N_out * N_mid * S kernel-gradient
+                            // spectrum (tile-major like K_hat's main block); d = 1: per
+                            // pair, S values
+    float2* part;           // per line pair (d >= 2) or per pair (d = 1): (dalpha, dbeta) terms
+    float* dalpha;          // [C]
+    float* dbeta;           // [C]
+    float* dK;              // [C][ke_out][ke_mid][ke_in]
 };
 
 // Per-line data of a row workgroup, computed once per line: element offsets of
@@ -174,6 +184,40 @@ inline size_t recommended_workspace(const Geom& g, int B, int C)
     if (per_ch == 0) return 0;
     const size_t target = (size_t)256 << 20;
     size_t n = target / per_ch;
+    if (n < 1) n = 1;
+    if (n > (size_t)C) n = (size_t)C;
+    return n * per_ch;
+}
+
+// Line pairs of one (b, c) pair in the row kernels (d >= 2), or 1 for d = 1
+// (where the backward keeps one partial sum per pair).
+__host__ __device__ __forceinline__ int pair_lines(const Geom& g) { return g.d == 1 ? 1 : g.n_out * g.n_mid / 2; }
+
+// Backward workspace per channel of a chunk (bytes): the planes of dy and, for
+// dK, of the gated input (B * wsp complex each), the kernel-gradient spectrum
+// (N_out N_mid S complex for d >= 2; B S for d = 1) and the partial sums of
+// dalpha and dbeta (B * pair_lines float2).
+inline size_t bwd_channel_bytes(const Geom& g, int B, bool dk)
+{
+    size_t v = (size_t)B * (size_t)g.wsp * (dk ? 2u : 1u);
+    if (dk) v += g.d == 1 ? (size_t)B * (size_t)g.S : (size_t)g.kmain;
+    v += (size_t)B * (size_t)pair_lines(g);
+    return v * 8u;
+}
+
+inline int bwd_chunk_channels(const Geom& g, int B, int C, bool dk, size_t ws_bytes_available)
+{
+    size_t n = ws_bytes_available / bwd_channel_bytes(g, B, dk);
+    if (n > (size_t)C) n = (size_t)C;
+    return (int)n;
+}
+
+// Recommended backward workspace: whole channels up to about 512 MiB (two
+// planes per pair instead of the forward's one).
+inline size_t recommended_bwd_workspace(const Geom& g, int B, int C, bool dk)
+{
+    const size_t per_ch = bwd_channel_bytes(g, B, dk);
+    size_t n = ((size_t)512 << 20) / per_ch;
     if (n < 1) n = 1;
     if (n > (size_t)C) n = (size_t)C;
     return n * per_ch;

@@ -150,6 +150,59 @@ int hyenand_fftconv_fwd_traced(const void* x, const float* phi_alpha, const floa
                                size_t workspace_bytes, void* stream, void* const* events, int n_events,
                                int* n_launches);
 
+/*
+ * Backward (vector-Jacobian product) of hyenand_fftconv_fwd.  The explainer's
+ * autograd pattern ("Implementation and operation patterns", item "Concrete
+ * implementation pattern (PyTorch)") saves only the input and the kernel
+ * parameters and recomputes the forward transforms in the backward; this call
+ * does exactly that.  With dy = dLoss/dy and u = s x, s = sigmoid(alpha x + beta):
+ *
+ *     du[j]    = sum_{i in G} dy[i] K[i - j]              (correlation with K)
+ *     dx[j]    = du[j] (s + alpha x s (1 - s))
+ *     dalpha_c = sum_{b,j} du x^2 s (1 - s),    dbeta_c = sum_{b,j} du x s (1 - s)
+ *     dK_c[l]  = sum_b sum_{j in G, j+l in G} dy[j+l] u[j]   for every offset l of K
+ *
+ * evaluated as conj(K_hat) products and Sum_b FFT(dy) conj(FFT(u)) on the same
+ * zero-padded grid.  x, dy, dx: device [B][C][dims] of `dtype`; dx is written.
+ * phi_alpha, phi_beta, K_hat: as for the forward.  dalpha, dbeta: device fp32
+ * [C], overwritten.  dK: device fp32 [C][2n-1 ...] (the layout of K),
+ * overwritten; NULL skips the kernel gradient (and its workspace).  dx must
+ * not alias x, dy, K_hat or the workspace.  The sums over the batch are taken
+ * in a fixed order (bit-identical results from call to call).  B == 0 with
+ * C > 0 writes zeros to dalpha, dbeta and dK.  workspace: device scratch of at
+ * least hyenand_fftconv_bwd_workspace_min_bytes (with_dK = dK != NULL);
+ * contents unspecified on entry and exit.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (too small or NULL), HIP.
+ */
+int hyenand_fftconv_bwd(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                        const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C, int d,
+                        const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward workspace bytes: recommended (whole channels up to about 512 MiB)
+ * and minimum (one channel).  Per channel: B * n_0 * (prod of the middle padded
+ * axes) * S complex for the output-gradient planes, the same again plus the
+ * kernel-gradient spectrum (N_out N_mid S complex, or B S for d = 1) when
+ * with_dK, and 8 bytes per line pair for the partial sums.  0 for an empty
+ * call or an unsupported shape.
+ */
+size_t hyenand_fftconv_bwd_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK);
+size_t hyenand_fftconv_bwd_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK);
+
+/*
+ * hyenand_fftconv_bwd with a launch trace (events as for
+ * hyenand_fftconv_fwd_traced).  Kernels of one channel chunk, in order:
+ * d = 1: conv1d_bwd, gate_reduce[, corr1d, dk_row];  d = 2: row_fwd(dy)
+ * [, row_fwd(u)], col_out_bwd, row_inv_bwd, gate_reduce[, dk_row];  d = 3:
+ * row_fwd(dy)[, row_fwd(u)], col_mid_fwd(dy)[, col_mid_fwd(u)], col_out_bwd,
+ * col_mid_inv, row_inv_bwd, gate_reduce[, mid_inv(dK), dk_row]  (bracketed:
+ * only with dK).
+ */
+int hyenand_fftconv_bwd_traced(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                               const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C,
+                               int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events, int n_events, int* n_launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -176,3 +176,28 @@ def sample_points(dims, B: int, C: int, pairs, per_pair: int, seed: int) -> np.n
         for _ in range(per_pair):
             rows.append([b, c] + [int(rng.integers(0, n)) for n in dims])
     return np.asarray(rows, dtype=np.int64)
+
+
+def draw_dy(dims, B: int, C: int, dtype: str, seed: int):
+    """Output gradient of the backward: dy ~ N(0,1) fp32 [B, C, *dims] from its
+    own stream, PCG64 seeded with [seed, 1] (x's stream is untouched); bf16 I/O
+    rounds to bf16 as draw_x does."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1]))
+    return draw_x(rng, B, C, dims, dtype)
+
+
+def sample_kernel_points(dims, chans, per_chan: int, seed: int) -> np.ndarray:
+    """Kernel-gradient coordinates to check one by one: for each listed channel
+    the 2^d corner offsets +-(n-1), offset 0, and ``per_chan`` seeded random
+    offsets.  Returns int64 [P, 1+d] rows (c, e_0..e_{d-1}), e the index into
+    K's extents 2n-1 (offset e - (n-1))."""
+    rng = np.random.Generator(np.random.PCG64([seed, 2]))
+    d = len(dims)
+    rows = []
+    for c in chans:
+        for corner in range(1 << d):
+            rows.append([c] + [(2 * dims[a] - 2) if (corner >> a) & 1 else 0 for a in range(d)])
+        rows.append([c] + [n - 1 for n in dims])
+        for _ in range(per_chan):
+            rows.append([c] + [int(rng.integers(0, 2 * n - 1)) for n in dims])
+    return np.asarray(rows, dtype=np.int64)

@@ -135,3 +135,39 @@ def test_spectrum_rejects_arguments(H):
     assert lib.hyenand_kernel_spectrum(FAKE, FAKE, 2, 2, _dims(8, 12), None) == 2
     assert lib.hyenand_kernel_spectrum(FAKE, FAKE, 2, 5, _dims(8, 8), None) == 2
     assert lib.hyenand_kernel_spectrum(None, None, 0, 2, _dims(8, 8), None) == 0
+
+
+def test_bwd_sizes(H):
+    lib = H.get_lib()
+    # 2-D 256x256, B=8: per channel two planes of B * n0 * S complex, the
+    # kernel-gradient spectrum N0 * S complex and one float2 per line pair.
+    plane = 8 * 256 * 256 * 8
+    per_ch = 2 * plane + 512 * 256 * 8 + 8 * 128 * 8
+    assert lib.hyenand_fftconv_bwd_workspace_min_bytes(8, 64, 2, _dims(256, 256), 0, 1) == per_ch
+    assert lib.hyenand_fftconv_bwd_workspace_min_bytes(8, 64, 2, _dims(256, 256), 0, 0) == plane + 8 * 128 * 8
+    rec = lib.hyenand_fftconv_bwd_workspace_bytes(8, 64, 2, _dims(256, 256), 0, 1)
+    assert rec % per_ch == 0 and per_ch <= rec <= 64 * per_ch
+    # 1-D: per pair S complex for the kernel gradient and one float2.
+    assert lib.hyenand_fftconv_bwd_workspace_min_bytes(4, 2, 1, _dims(64), 0, 1) == 4 * 64 * 8 + 4 * 8
+    assert lib.hyenand_fftconv_bwd_workspace_min_bytes(4, 2, 1, _dims(64), 0, 0) == 4 * 8
+    for d, dims in [(2, _dims(3, 4)), (1, _dims(2048))]:
+        assert lib.hyenand_fftconv_bwd_workspace_bytes(2, 2, d, dims, 0, 1) == 0
+
+
+def test_bwd_rejects_arguments(H):
+    lib = H.get_lib()
+    dd = _dims(8, 8)
+    ws = 1 << 20
+    call = lambda x=FAKE, a=FAKE, b=FAKE, k=FAKE, dy=FAKE, dx=FAKE, da=FAKE, db=FAKE, dK=FAKE, B=1, C=1, d=2, \
+        dims=dd, dt=0, w=FAKE, wb=ws: lib.hyenand_fftconv_bwd(x, a, b, k, dy, dx, da, db, dK, B, C, d, dims, dt,
+                                                              w, wb, None)
+    for kw in ("x", "a", "b", "k", "dy", "dx", "da", "db"):
+        assert call(**{kw: None}) == 1, kw
+    assert call(B=-1) == 1 and call(C=-1) == 1 and call(dt=3) == 1
+    assert call(x=MISALIGNED) == 1 and call(dy=MISALIGNED) == 1 and call(dx=MISALIGNED) == 1
+    assert call(k=MISALIGNED) == 1 and call(dK=MISALIGNED) == 1 and call(w=MISALIGNED) == 1
+    assert call(w=None) == 3
+    need = lib.hyenand_fftconv_bwd_workspace_min_bytes(1, 1, 2, dd, 0, 1)
+    assert call(wb=need - 1) == 3
+    assert call(d=2, dims=_dims(8, 6)) == 2 and call(d=0) == 2 and call(dims=None) == 1
+    assert call(x=None, dy=None, dx=None, C=0) == 0
