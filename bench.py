@@ -1,12 +1,15 @@
 #!/usr/bin/env python3
-"""Throughput of the gated N-D FFT convolution forward on one MI355X.
+"""Throughput of the gated N-D FFT convolution on one MI355X.
 
 One step = one ``hyenand_fftconv_fwd`` over the whole synthetic batch (gate,
 forward transforms, product with the precomputed kernel spectrum, inverse
 transforms, crop, store), inputs resident in HBM.  Default workload: the 256x256
-image, B=8, C=64, fp32 I/O.  Prints ONE JSON line.
+image, B=8, C=64, fp32 I/O.  With ``--pass bwd`` a step is one
+``hyenand_fftconv_bwd`` (dx, dalpha, dbeta and dK for a synthetic output
+gradient).  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME] [--pass fwd|bwd]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "Gvoxel·channels/s of gated N-D FFT conv fwd; % of HBM roofline (1 GPU)"
+METRIC_BWD = "Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK); % of HBM roofline (1 GPU)"
 UNIT = "Gvoxel·channels/s"
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
 # fp32 vector peak without packed-FP32 instructions (the build disables them):
@@ -36,7 +40,7 @@ def _geom(dims):
     no, nm, ni = (1, 1, dims[0]) if d == 1 else ((dims[0], 1, dims[1]) if d == 2 else tuple(dims))
     No, Nm, Ni = (2 * no if d >= 2 else 1), (2 * nm if d == 3 else 1), 2 * ni
     return dict(no=no, nm=nm, ni=ni, No=No, Nm=Nm, Ni=Ni, S=ni, vox=no * nm * ni, wsp=no * Nm * ni if d >= 2 else 0,
-                ksz=No * Nm * ni + No * Nm)
+                ksz=No * Nm * ni + No * Nm, kmain=No * Nm * ni, kl=(2 * no - 1) * (2 * nm - 1) * (2 * ni - 1))
 
 
 def _fft_flops(N, lines, prune):
@@ -67,9 +71,45 @@ def pass_model(name, dims, B_chunk_pairs, nch, es):
     elif name == "conv1d":
         by = 2 * P * g["vox"] * es + nch * g["ksz"] * 8
         fl = 2 * _fft_flops(g["Ni"], P / 2, 1) + P * g["S"] * (6 + 4) + P * g["vox"] * 5
+    # ---- backward passes (dK wanted)
+    elif name in ("row_fwd_dy", "row_fwd_u"):
+        by = P * g["vox"] * es + P * rows * g["S"] * 8
+        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 2 * 2 + (P * g["vox"] * 5 if name == "row_fwd_u" else 0)
+    elif name in ("col_mid_fwd_dy", "col_mid_fwd_u"):
+        return pass_model("col_mid_fwd", dims, P, nch, es)
+    elif name == "col_out_bwd":
+        # dy planes read and written, u planes read, K_hat read, kernel-gradient planes written
+        by = 3 * P * g["wsp"] * 8 + nch * g["ksz"] * 8 + nch * g["kmain"] * 8
+        lines = P * g["Nm"] * g["S"]
+        fl = 3 * _fft_flops(g["No"], lines, 1) + lines * g["No"] * (6 + 8) + _fft_flops(g["No"], nch * g["Nm"] * g["S"], 0)
+    elif name == "row_inv_bwd":
+        by = P * rows * g["S"] * 8 + 2 * P * g["vox"] * es + P * max(rows // 2, 1) * 8
+        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 4 + P * g["vox"] * 14
+    elif name == "gate_reduce":
+        by = P * max(rows // 2, 1) * 8
+        fl = P * max(rows // 2, 1) * 2
+    elif name == "mid_inv_dk":
+        by = 2 * nch * g["kmain"] * 8
+        fl = _fft_flops(g["Nm"], nch * g["No"] * g["S"], 0)
+    elif name == "dk_row":
+        by = (nch * g["kmain"] * 8 if len(dims) > 1 else P * g["S"] * 8) + nch * g["kl"] * 4
+        fl = _fft_flops(g["Ni"], nch * g["No"] * g["Nm"] / 2, 0) + nch * g["No"] * g["Nm"] * g["S"] * 4
+    elif name == "conv1d_bwd":
+        by = 3 * P * g["vox"] * es + nch * g["ksz"] * 8 + P * 8
+        fl = 2 * _fft_flops(g["Ni"], P / 2, 1) + P * g["S"] * (6 + 4) + P * g["vox"] * 14
+    elif name == "corr1d":
+        by = 2 * P * g["vox"] * es + P * g["S"] * 8
+        fl = _fft_flops(g["Ni"], P, 1) + P * g["S"] * 10 + P * g["vox"] * 5
     else:
         raise KeyError(name)
     return by, fl
+
+
+KERNEL_LABEL = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_col_out", "col_mid_fwd": "k_col_mid",
+                "col_mid_inv": "k_col_mid", "conv1d": "k_conv1d", "row_fwd_dy": "k_row_fwd", "row_fwd_u": "k_row_fwd",
+                "col_mid_fwd_dy": "k_col_mid", "col_mid_fwd_u": "k_col_mid", "col_out_bwd": "k_col_out_bwd",
+                "row_inv_bwd": "k_row_inv", "gate_reduce": "k_gate_reduce", "mid_inv_dk": "k_plane_mid_inv",
+                "dk_row": "k_dk_row", "conv1d_bwd": "k_conv1d", "corr1d": "k_corr1d"}
 
 
 def _src_hash():
@@ -126,12 +166,39 @@ def cpu_baseline(wl, max_seconds=20.0):
                       f"{t_total:.1f} s"}
 
 
+def cpu_baseline_bwd(wl, max_seconds=20.0):
+    """The fp64 oracle's backward (O2 FFT route, as written) on a bounded
+    sample of the same workload: whole channels (every batch entry) until
+    about `max_seconds` pass."""
+    import oracle
+    import synth
+
+    p = synth.draw_params(wl.dims, wl.C, wl.seed)
+    x = synth.draw_x(p.rng, wl.B, wl.C, wl.dims, wl.dtype).float().numpy()
+    dy = synth.draw_dy(wl.dims, wl.B, wl.C, wl.dtype, wl.seed).float().numpy()
+    done = 0
+    t_total = 0.0
+    while t_total < max_seconds and done < wl.C:
+        c = done
+        K = synth.kernel_channels(wl.dims, p, channels=[c]).numpy()
+        t0 = time.perf_counter()
+        oracle.bwd_fft(x[:, c:c + 1], p.alpha[c:c + 1], p.beta[c:c + 1], K, dy[:, c:c + 1])
+        t_total += time.perf_counter() - t0
+        done += 1
+    vox = done * wl.B * wl.voxels
+    return {"value": vox / t_total / 1e9, "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {wl.C} channels (all {wl.B} batch entries each) of {wl.name}, fp64 O2 backward "
+                      f"(radix-2 FFT) route, {t_total:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward with the kernel gradient")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ws-mb", type=float, default=None,
                     help="workspace size in MiB (default: the library's recommendation)")
@@ -178,15 +245,35 @@ def main():
     torch.cuda.synchronize()
     spectrum_ms = s0.elapsed_time(s1)
     del K
-    y = torch.empty_like(x)
-    ws_bytes = H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
-    if args.ws_mb is not None:
-        ws_bytes = max(H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
+    bwd = args.which == "bwd"
+    if bwd:
+        dy = synth.draw_dy(wl.dims, wl.B, wl.C, wl.dtype, wl.seed).to(dev)
+        outs = (torch.empty_like(x), torch.empty(wl.C, device=dev), torch.empty(wl.C, device=dev),
+                torch.empty((wl.C,) + tuple(2 * n - 1 for n in wl.dims), device=dev))
+        ws_bytes = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
+        if args.ws_mb is not None:
+            ws_bytes = max(H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
+    else:
+        y = torch.empty_like(x)
+        ws_bytes = H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
+        if args.ws_mb is not None:
+            ws_bytes = max(H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
     ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+
+    def call():
+        if bwd:
+            H.fftconv_bwd(x, al, be, kh, dy, *outs, workspace=ws)
+        else:
+            H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
+
+    def traced(events):
+        if bwd:
+            return H.fftconv_bwd_traced(x, al, be, kh, dy, outs, ws, events)
+        return H.fftconv_fwd_traced(x, al, be, kh, y, ws, events)
 
     # Launch count per step, then one event slot before each launch and one at the end.
     probe = [torch.cuda.Event(enable_timing=True) for _ in range(1)]
-    n_launch = H.fftconv_fwd_traced(x, al, be, kh, y, ws, probe)
+    n_launch = traced(probe)
     torch.cuda.synchronize()
     # Clock settle (untimed): the GPU needs tens of milliseconds of load to
     # reach its steady clock (256^2: the first ~20 ms of calls run ~10% slower),
@@ -195,11 +282,11 @@ def main():
     settle_calls = 0
     while time.perf_counter() - t0 < SETTLE_S:
         for _ in range(8):
-            H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
+            call()
         settle_calls += 8
         torch.cuda.synchronize()
     for _ in range(args.warmup):
-        H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
+        call()
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` plain calls, bracketed by synchronisations.
@@ -207,7 +294,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record()
     for _ in range(args.steps):
-        H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
+        call()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -218,7 +305,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
-        H.fftconv_fwd_traced(x, al, be, kh, y, ws, evs[k])
+        traced(evs[k])
     torch.cuda.synchronize()
     # The interval between two events around a kernel also holds the
     # processing of one event marker; measured here as the interval between
@@ -231,10 +318,19 @@ def main():
     torch.cuda.synchronize()
     marker_ms = sorted(mk[2 * k].elapsed_time(mk[2 * k + 1]) for k in range(args.steps))[args.steps // 2]
 
-    plan = H.launch_plan(wl.B, wl.C, wl.dims, x.dtype, ws_bytes)
     g = _geom(wl.dims)
-    bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8
-    names = H.PASS_NAMES[wl.d]
+    if bwd:
+        per_ch = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True)
+        nch = min(wl.C, ws_bytes // per_ch)
+        nch = -(-wl.C // -(-wl.C // nch))  # balanced chunks, as the library splits them
+        plan = {"chunk_channels": nch}
+        # x, dy and dx once, K_hat once, dK once (alpha, beta, dalpha, dbeta negligible)
+        bytes_min = 3 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8 + wl.C * g["kl"] * 4
+        names = H.BWD_PASS_NAMES[(wl.d, True)]
+    else:
+        plan = H.launch_plan(wl.B, wl.C, wl.dims, x.dtype, ws_bytes)
+        bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8
+        names = H.PASS_NAMES[wl.d]
     per_pass = {nm: [] for nm in names}
     step_ms = []
     for k in range(args.steps):
@@ -246,8 +342,7 @@ def main():
     dom_s = sum(per_pass[dominant]) / len(per_pass[dominant]) / 1e3
     nch = plan["chunk_channels"]
     by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch, es)
-    kernel_label = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_col_out",
-                    "col_mid_fwd": "k_col_mid", "col_mid_inv": "k_col_mid", "conv1d": "k_conv1d"}[dominant]
+    kernel_label = KERNEL_LABEL[dominant]
     hbm = {"bound": "hbm", "achieved": by / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     alu = {"bound": "alu", "achieved": fl / dom_s / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s"}
     for r in (hbm, alu):
@@ -259,7 +354,7 @@ def main():
     voxch = wl.B * wl.C * wl.voxels
     value = voxch / (ms_per_step / 1e3) / 1e9
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": value,
         "unit": UNIT,
         "n_gpus": 1,
@@ -271,7 +366,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
+        "config": {"workload": wl.name, "pass": args.which, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
                    "C": wl.C, "io_dtype": "bf16" if wl.dtype == "bf16" else "fp32", "launches_per_step": n_launch, "workspace_mib": ws_bytes / 2**20,
                    "chunk_channels": plan["chunk_channels"]},
         "hbm_roofline_frac_of_metric": bytes_min / (ms_per_step / 1e3) / HBM_PEAK,
@@ -284,7 +379,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline_bwd(wl) if bwd else cpu_baseline(wl)
     print(json.dumps(out), flush=True)
     return 0
 

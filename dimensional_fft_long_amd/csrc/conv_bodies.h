@@ -623,8 +623,8 @@ __host__ __device__ __forceinline__ void out_slot0_corr(const Ctx& ctx, const Ou
 template <int L, int NR, bool DK, class Ctx>
 __host__ __device__ __forceinline__ void col_out_bwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int TW = out_tw(L, NR);
-    constexpr int NL = NR * TW, NT = out_nt(L, NR);
+    constexpr int TW = bwd_tw(L, NR);
+    constexpr int NL = NR * TW, NT = bwd_nt(L, NR);
     constexpr int R0 = pass_radix<L, false>(0);
     constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
     static_assert(TW >= 3, "the k_in = 0 staging uses three columns per row block");
@@ -1038,22 +1038,43 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
 
 // ======================================================== backward tails
 // dalpha, dbeta of the chunk's channel `bid`: the sum of its B * pair_lines
-// partial sums, in a fixed order (strided per thread, then an LDS tree), in
-// fp64.  R: LDS scratch of 2 * NT doubles.
+// partial sums, in a fixed order (each thread sums a strided subset into
+// U independent fp64 accumulators, so that U loads are in flight at once;
+// then an LDS tree).  R: LDS scratch of 2 * NT doubles.
 template <int NT, class Ctx>
 __host__ __device__ __forceinline__ void gate_reduce_body(const Ctx& ctx, int bid, const ConvArgs& a, double* R)
 {
+    constexpr int U = 8;
     const int per = a.B * pair_lines(a.g);
     const float2* p = a.part + (long long)bid * per;
     const int tid = ctx.tid();
-    double sa = 0.0, sb = 0.0;
-    for (int e = tid; e < per; e += NT) {
-        const float2 v = p[e];
-        sa += (double)v.x;
-        sb += (double)v.y;
+    double sa[U], sb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) sa[u] = sb[u] = 0.0;
+    int e = tid;
+    for (; e + (U - 1) * NT < per; e += U * NT) {
+        float2 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = p[e + u * NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            sa[u] += (double)v[u].x;
+            sb[u] += (double)v[u].y;
+        }
     }
-    R[tid] = sa;
-    R[NT + tid] = sb;
+    for (int u = 0; e < per; e += NT, ++u) {
+        const float2 v = p[e];
+        sa[u] += (double)v.x;
+        sb[u] += (double)v.y;
+    }
+    double ta = 0.0, tb = 0.0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        ta += sa[u];
+        tb += sb[u];
+    }
+    R[tid] = ta;
+    R[NT + tid] = tb;
     ctx.sync();
     for (int h = NT / 2; h >= 1; h /= 2) {
         if (tid < h) {

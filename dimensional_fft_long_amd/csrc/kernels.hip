@@ -104,11 +104,11 @@ __global__ __launch_bounds__(row_nt(L)) void k_conv1d(ConvArgs a)
 }
 
 template <int L, int NR, bool DK>
-__global__ __launch_bounds__(out_nt(L, NR)) void k_col_out_bwd(ConvArgs a)
+__global__ __launch_bounds__(bwd_nt(L, NR)) void k_col_out_bwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
-    __shared__ float2 T[L * NR * out_tw(L, NR)];
-    col_out_bwd_body<L, NR, DK>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
+    __shared__ float2 T[L * NR * bwd_tw(L, NR)];
+    col_out_bwd_body<L, NR, DK>(make_ctx<L, bwd_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L>
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(row_nt(L)) void k_dk_row(ConvArgs a)
     dk_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
-constexpr int kReduceNT = 256;
+constexpr int kReduceNT = 1024;
 
 __global__ __launch_bounds__(kReduceNT) void k_gate_reduce(ConvArgs a)
 {
@@ -376,10 +376,10 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
     }
     auto col_out = [&]<int NR>() {
         return with_length(g.N_out, [&]<int L>() {
-            const long long grid = (long long)a.nch * (NR == 1 ? 1 : g.N_mid / 2) * ceil_div(g.S, out_tw(L, NR));
+            const long long grid = (long long)a.nch * (NR == 1 ? 1 : g.N_mid / 2) * ceil_div(g.S, bwd_tw(L, NR));
             mark();
-            if (dk) hipLaunchKernelGGL((k_col_out_bwd<L, NR, true>), dim3((unsigned)grid), dim3(out_nt(L, NR)), 0, st, a);
-            else hipLaunchKernelGGL((k_col_out_bwd<L, NR, false>), dim3((unsigned)grid), dim3(out_nt(L, NR)), 0, st, a);
+            if (dk) hipLaunchKernelGGL((k_col_out_bwd<L, NR, true>), dim3((unsigned)grid), dim3(bwd_nt(L, NR)), 0, st, a);
+            else hipLaunchKernelGGL((k_col_out_bwd<L, NR, false>), dim3((unsigned)grid), dim3(bwd_nt(L, NR)), 0, st, a);
             return last_error();
         });
     };

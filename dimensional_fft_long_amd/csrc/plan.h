@@ -62,6 +62,23 @@ constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)
 // 4.29 -> 4.08 ms per call).  The 3-D kernel of the same tile size lost with
 // the loop (512^3: 24.8 -> 29.2 ms), and smaller tiles rely on several
 // workgroups per CU; those run one item per workgroup.
+// Backward out-axis kernel: it holds four tile-sized register arrays (the
+// output-gradient and gated-input spectra, the kernel-gradient accumulator and
+// the kernel spectrum values), so its tile is capped at 64 KiB (4 x 128 KiB
+// would fill a CU's whole 512 KiB register file: 1024^2 22.8 -> 10.9 ms,
+// 512^3 104.6 -> 79.9 ms per call).  Points per thread per pass: 8 for 2-D
+// lines (256^2: 0.88 -> 0.80 ms against 16), 16 for the two-row 3-D tiles
+// (128^3: 6.7 against 7.8 ms with 8).
+constexpr int bwd_tw(int L, int NR)
+{
+    const int cap = 65536 / (8 * L * NR);
+    return out_tw(L, NR) < cap ? out_tw(L, NR) : (cap < 4 ? 4 : cap);
+}
+constexpr int bwd_nt(int L, int NR)
+{
+    const int t = L * NR * bwd_tw(L, NR) / (NR == 1 ? 8 : 16);
+    return t < 64 ? 64 : (t > 1024 ? 1024 : t);
+}
 constexpr bool out_looped(int L, int NR) { return NR == 1 && (long long)L * NR * out_tw(L, NR) * 8 > 80 * 1024; }
 
 struct Geom {
