@@ -20,6 +20,9 @@ Routes (all fp64, in ``oracle.c``):
   * ``direct_points`` -- O1 at chosen outputs (for grids too big for O2).
   * ``fftconv``       -- O2, explicit zero padding to 2n, textbook radix-2 FFT.
   * ``kernel_spectrum`` -- the full DFT of the wrap-placed kernel.
+  * ``direct_circ`` / ``fftconv_circ`` -- the circular mode (summary, "Boundary
+    handling": periodic grids, no padding): y[i] = sum_j u[j] K[(i-j) mod n]
+    with K stored [C, *dims], index m = offset mod n.
   * ``bwd_direct`` / ``bwd_points`` / ``bwd_fft`` -- the backward (vector-Jacobian
     product, explainer section "Implementation and operation patterns", item
     "Concrete implementation pattern (PyTorch)": gradients of the input and of
@@ -73,12 +76,14 @@ def _load():
         lib.oracle_kernel_spectrum.argtypes = [P, I, I, P, P, P]
         lib.oracle_fftconv_pairs.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_direct_circ.argtypes = [P, P, P, P, P, I, I, I, P]
+        lib.oracle_fftconv_circ_pairs.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
         lib.oracle_bwd_direct.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, P]
         lib.oracle_bwd_direct_points.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, I64, P, P]
         lib.oracle_bwd_fft.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, P, P, P]
         for f in ("oracle_gate", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
                   "oracle_fftconv_pairs", "oracle_num_threads", "oracle_bwd_direct", "oracle_bwd_direct_points",
-                  "oracle_bwd_fft"):
+                  "oracle_bwd_fft", "oracle_direct_circ", "oracle_fftconv_circ_pairs"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -165,6 +170,36 @@ def kernel_spectrum(K, dims) -> np.ndarray:
     im = np.empty(shape, dtype=np.float64)
     _check(_load().oracle_kernel_spectrum(_ptr(K), C, d, _ptr(dd), _ptr(re), _ptr(im)), "kernel_spectrum")
     return re + 1j * im
+
+
+def direct_circ(x, alpha, beta, K) -> np.ndarray:
+    """O1, circular mode: every output, fp64 [B, C, *dims]; K is [C, *dims] (index = offset mod n)."""
+    x, alpha, beta, K = _f32(x), _f32(alpha), _f32(beta), _f32(K)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    if tuple(K.shape) != (C,) + tuple(x.shape[2:]):
+        raise ValueError("the circular kernel is [C, *dims]")
+    y = np.empty(x.shape, dtype=np.float64)
+    _check(_load().oracle_direct_circ(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(y), B, C, d, _ptr(dims)),
+           "direct_circ")
+    return y
+
+
+def fftconv_circ(x, alpha, beta, K, pairs=None) -> np.ndarray:
+    """O2, circular mode (FFT of size n, no padding) for the listed pairs (all when None)."""
+    x, alpha, beta, K = _f32(x), _f32(alpha), _f32(beta), _f32(K)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    if tuple(K.shape) != (C,) + tuple(x.shape[2:]):
+        raise ValueError("the circular kernel is [C, *dims]")
+    allp = pairs is None
+    pr = np.arange(B * C, dtype=np.int64) if allp else np.ascontiguousarray(np.asarray(pairs, dtype=np.int64))
+    y = np.empty((pr.size,) + tuple(x.shape[2:]), dtype=np.float64)
+    _check(_load().oracle_fftconv_circ_pairs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), B, C, d, _ptr(dims),
+                                             pr.size, _ptr(pr), _ptr(y)), "fftconv_circ")
+    return y.reshape(x.shape) if allp else y
 
 
 def bwd_direct(x, alpha, beta, K, dy):

@@ -32,7 +32,9 @@
  *   O2  oracle_fftconv_pairs: explicit zero padding to N_a = 2 n_a, textbook
  *       radix-2 complex FFT (bit reversal + butterflies, fp64 twiddles from
  *       cos/sin), row-column over the axes, product, inverse, crop.
- * and the same two routes for the backward (the gradients of the input, the
+ * The circular mode of [SUMM] (periodic grids, no padding) has the same two
+ * routes: oracle_direct_circ and oracle_fftconv_circ_pairs.
+ * And the same two routes for the backward (the gradients of the input, the
  * gate parameters and the kernel; see the backward section below):
  *   O1  oracle_bwd_direct / oracle_bwd_direct_points,  O2  oracle_bwd_fft.
  *
@@ -368,6 +370,93 @@ int oracle_fftconv_pairs(const float *x, const float *alpha, const float *beta, 
             for (int64_t j1 = 0; j1 < g.n[1]; ++j1)
                 for (int64_t j2 = 0; j2 < g.n[2]; ++j2)
                     ys[(j0 * g.n[1] + j1) * g.n[2] + j2] = ur[(j0 * g.N[1] + j1) * g.N[2] + j2] * scale;
+    }
+    free(ur); free(ui); free(kr); free(ki);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Circular mode ([SUMM] "Boundary handling": circular convolutions for       */
+/* periodic physical systems, next to the zero-padded non-circular ones).     */
+/* ------------------------------------------------------------------------- */
+/*
+ * On a periodic grid the kernel lives on the offsets modulo n_a: K_c is stored
+ * [C][n_0]..[n_{d-1}] with index m_a = delta_a mod n_a (offset 0 at index 0),
+ * and
+ *     y[b,c,i] = sum_{j in G} u[b,c,j] K_c[(i - j) mod n],   u = phi(x) x.
+ * The FFT route needs no padding: N_a = n_a, y = IFFT(FFT(u) FFT(K)) / prod n.
+ */
+
+/* O1, circular: every output of every (b,c). */
+int oracle_direct_circ(const float *x, const float *alpha, const float *beta, const float *K,
+                       double *y, int B, int C, int d, const int64_t *dims)
+{
+    geom_t g;
+    if (!x || !alpha || !beta || !K || !y || B < 0 || C < 0) return ORC_EINVAL;
+    if (geom_init(&g, d, dims)) return ORC_EINVAL;
+    double *u = (double *)malloc(sizeof(double) * (size_t)(g.L ? g.L : 1));
+    if (!u) return ORC_ENOMEM;
+    for (int b = 0; b < B; ++b)
+        for (int c = 0; c < C; ++c) {
+            const int64_t p = (int64_t)b * C + c;
+            const float *xs = x + p * g.L;
+            for (int64_t j = 0; j < g.L; ++j) u[j] = gate((double)xs[j], alpha[c], beta[c]);
+            const float *Kc = K + (int64_t)c * g.L;
+            double *ys = y + p * g.L;
+#pragma omp parallel for schedule(static)
+            for (int64_t i = 0; i < g.L; ++i) {
+                const int64_t i2 = i % g.n[2], i1 = (i / g.n[2]) % g.n[1], i0 = i / (g.n[1] * g.n[2]);
+                double acc = 0.0;
+                for (int64_t j0 = 0; j0 < g.n[0]; ++j0)
+                    for (int64_t j1 = 0; j1 < g.n[1]; ++j1)
+                        for (int64_t j2 = 0; j2 < g.n[2]; ++j2) {
+                            const int64_t m0 = ((i0 - j0) % g.n[0] + g.n[0]) % g.n[0];
+                            const int64_t m1 = ((i1 - j1) % g.n[1] + g.n[1]) % g.n[1];
+                            const int64_t m2 = ((i2 - j2) % g.n[2] + g.n[2]) % g.n[2];
+                            acc += u[(j0 * g.n[1] + j1) * g.n[2] + j2] * (double)Kc[(m0 * g.n[1] + m1) * g.n[2] + m2];
+                        }
+                ys[i] = acc;
+            }
+        }
+    free(u);
+    return ORC_OK;
+}
+
+/* O2, circular, for the listed pairs: FFT of size n on every axis, product, inverse, / prod n. */
+int oracle_fftconv_circ_pairs(const float *x, const float *alpha, const float *beta, const float *K,
+                              int B, int C, int d, const int64_t *dims,
+                              int64_t npairs, const int64_t *pairs, double *y_out)
+{
+    geom_t g;
+    if (!x || !alpha || !beta || !K || !pairs || !y_out || npairs < 0) return ORC_EINVAL;
+    if (geom_init(&g, d, dims)) return ORC_EINVAL;
+    for (int a = 0; a < 3; ++a)
+        if (!is_pow2(g.n[a])) return ORC_EINVAL;
+    for (int64_t q = 0; q < npairs; ++q)
+        if (pairs[q] < 0 || pairs[q] >= (int64_t)B * C) return ORC_EINVAL;
+    const size_t bytes = sizeof(double) * (size_t)g.L;
+    double *ur = (double *)malloc(bytes), *ui = (double *)malloc(bytes);
+    double *kr = (double *)malloc(bytes), *ki = (double *)malloc(bytes);
+    if (!ur || !ui || !kr || !ki) { free(ur); free(ui); free(kr); free(ki); return ORC_ENOMEM; }
+    int64_t kc_cur = -1;
+    int rc = ORC_OK;
+    for (int64_t q = 0; q < npairs && rc == ORC_OK; ++q) {
+        const int64_t p = pairs[q], c = p % C;
+        if (c != kc_cur) {
+            for (int64_t m = 0; m < g.L; ++m) { kr[m] = (double)K[c * g.L + m]; ki[m] = 0.0; }
+            if ((rc = fft_nd(kr, ki, g.n, -1))) break;
+            kc_cur = c;
+        }
+        const float *xs = x + p * g.L;
+        for (int64_t j = 0; j < g.L; ++j) { ur[j] = gate((double)xs[j], alpha[c], beta[c]); ui[j] = 0.0; }
+        if ((rc = fft_nd(ur, ui, g.n, -1))) break;
+        for (int64_t m = 0; m < g.L; ++m) {
+            const double a = ur[m], b = ui[m];
+            ur[m] = a * kr[m] - b * ki[m];
+            ui[m] = a * ki[m] + b * kr[m];
+        }
+        if ((rc = fft_nd(ur, ui, g.n, +1))) break;
+        for (int64_t j = 0; j < g.L; ++j) y_out[q * g.L + j] = ur[j] / (double)g.L;
     }
     free(ur); free(ui); free(kr); free(ki);
     return rc;
