@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "Gvoxel·channels/s of gated N-D FFT conv fwd; % of HBM roofline (1 GPU)"
+METRIC_CIRC = "Gvoxel·channels/s of gated N-D FFT conv fwd, circular mode; % of HBM roofline (1 GPU)"
 METRIC_BWD = "Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK); % of HBM roofline (1 GPU)"
 UNIT = "Gvoxel·channels/s"
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
@@ -35,12 +36,17 @@ SETTLE_S = 0.3               # untimed calls before the warmup steps (GPU clock 
 DEFAULT_WORKLOAD = "2d_256x256_b8_c64_f32"
 
 
-def _geom(dims):
+def _geom(dims, circ=False):
+    """Grid, padded transform lengths (N = 2n, or N = n in circular mode) and
+    per-pair / per-channel sizes in complex values."""
     d = len(dims)
     no, nm, ni = (1, 1, dims[0]) if d == 1 else ((dims[0], 1, dims[1]) if d == 2 else tuple(dims))
-    No, Nm, Ni = (2 * no if d >= 2 else 1), (2 * nm if d == 3 else 1), 2 * ni
-    return dict(no=no, nm=nm, ni=ni, No=No, Nm=Nm, Ni=Ni, S=ni, vox=no * nm * ni, wsp=no * Nm * ni if d >= 2 else 0,
-                ksz=No * Nm * ni + No * Nm, kmain=No * Nm * ni, kl=(2 * no - 1) * (2 * nm - 1) * (2 * ni - 1))
+    f = 1 if circ else 2
+    No, Nm, Ni = (f * no if d >= 2 else 1), (f * nm if d == 3 else 1), f * ni
+    S = Ni // 2
+    return dict(no=no, nm=nm, ni=ni, No=No, Nm=Nm, Ni=Ni, S=S, vox=no * nm * ni, wsp=no * Nm * S if d >= 2 else 0,
+                ksz=No * Nm * S + No * Nm, kmain=No * Nm * S, kl=(2 * no - 1) * (2 * nm - 1) * (2 * ni - 1),
+                prune=0 if circ else 1)
 
 
 def _fft_flops(N, lines, prune):
@@ -49,28 +55,30 @@ def _fft_flops(N, lines, prune):
     return lines * (5.0 * N * math.log2(N) - 2.0 * N * prune)
 
 
-def pass_model(name, dims, B_chunk_pairs, nch, es):
+def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
     """(algorithmic bytes, nominal flops) of one launch of pass `name` over a
-    chunk of `B_chunk_pairs` (b,c) pairs covering `nch` channels."""
-    g = _geom(dims)
+    chunk of `B_chunk_pairs` (b,c) pairs covering `nch` channels (circular
+    mode: transforms of length n, nothing pruned)."""
+    g = _geom(dims, circ)
     P = B_chunk_pairs
     rows = g["no"] * g["nm"]
+    pr = g["prune"]
     if name == "row_fwd":
         by = P * g["vox"] * es + P * rows * g["S"] * 8
-        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 2 * 2 + P * g["vox"] * 5
+        fl = _fft_flops(g["Ni"], P * rows / 2, pr) + P * rows * g["S"] * 2 * 2 + P * g["vox"] * 5
     elif name == "row_inv":
         by = P * rows * g["S"] * 8 + P * g["vox"] * es
-        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 4
+        fl = _fft_flops(g["Ni"], P * rows / 2, pr) + P * rows * g["S"] * 4
     elif name == "col_mid_fwd" or name == "col_mid_inv":
         by = P * (rows * g["S"] + g["no"] * g["Nm"] * g["S"]) * 8
-        fl = _fft_flops(g["Nm"], P * g["no"] * g["S"], 1)
+        fl = _fft_flops(g["Nm"], P * g["no"] * g["S"], pr)
     elif name == "col_out":
         by = 2 * P * g["wsp"] * 8 + nch * g["ksz"] * 8
         lines = P * g["Nm"] * g["S"]
-        fl = 2 * _fft_flops(g["No"], lines, 1) + lines * g["No"] * 6
+        fl = 2 * _fft_flops(g["No"], lines, pr) + lines * g["No"] * 6
     elif name == "conv1d":
         by = 2 * P * g["vox"] * es + nch * g["ksz"] * 8
-        fl = 2 * _fft_flops(g["Ni"], P / 2, 1) + P * g["S"] * (6 + 4) + P * g["vox"] * 5
+        fl = 2 * _fft_flops(g["Ni"], P / 2, pr) + P * g["S"] * (6 + 4) + P * g["vox"] * 5
     # ---- backward passes (dK wanted)
     elif name in ("row_fwd_dy", "row_fwd_u"):
         by = P * g["vox"] * es + P * rows * g["S"] * 8
@@ -139,9 +147,10 @@ def _traffic_from_profile(kernel_name, workload, chunk_channels):
     return rec.get("kernels", {}).get(kernel_name, {}).get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, max_seconds=20.0):
-    """The fp64 oracle (O2 FFT route, as written) on a bounded sample of the
-    same workload: consecutive (b,c) pairs until about `max_seconds` pass."""
+def cpu_baseline(wl, circ=False, max_seconds=20.0):
+    """The fp64 oracle (O2 FFT route, as written; its circular route in
+    circular mode) on a bounded sample of the same workload: consecutive (b,c)
+    pairs until about `max_seconds` pass."""
     import numpy as np
 
     import oracle
@@ -149,20 +158,22 @@ def cpu_baseline(wl, max_seconds=20.0):
 
     p = synth.draw_params(wl.dims, wl.C, wl.seed)
     x = synth.draw_x(p.rng, wl.B, wl.C, wl.dims, wl.dtype).float().numpy()
-    K = synth.kernel_channels(wl.dims, p).numpy()
+    K = (synth.circular_kernel(wl.dims, p) if circ else synth.kernel_channels(wl.dims, p)).numpy()
+    route = oracle.fftconv_circ if circ else oracle.fftconv
     done = 0
     t_total = 0.0
     batch = 1
     while t_total < max_seconds and done < wl.B * wl.C:
         pairs = np.arange(done, min(done + batch, wl.B * wl.C))
         t0 = time.perf_counter()
-        oracle.fftconv(x, p.alpha, p.beta, K, pairs=pairs)
+        route(x, p.alpha, p.beta, K, pairs=pairs)
         t_total += time.perf_counter() - t0
         done += len(pairs)
         batch = min(batch * 2, 64)
     vox = done * wl.voxels
     return {"value": vox / t_total / 1e9, "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done} of {wl.B * wl.C} (b,c) pairs of {wl.name}, fp64 O2 (radix-2 FFT) route, "
+            "sample": f"{done} of {wl.B * wl.C} (b,c) pairs of {wl.name}, fp64 O2 (radix-2 FFT) route"
+                      f"{', circular' if circ else ''}, "
                       f"{t_total:.1f} s"}
 
 
@@ -199,6 +210,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward with the kernel gradient")
+    ap.add_argument("--boundary", choices=("padded", "circular"), default="padded",
+                    help="zero-padded non-circular convolution (default) or the circular mode (forward only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ws-mb", type=float, default=None,
                     help="workspace size in MiB (default: the library's recommendation)")
@@ -227,6 +240,10 @@ def main():
     import synth
 
     wl = {w.name: w for w in synth.WORKLOADS}[args.workload]
+    circ = args.boundary == "circular"
+    if circ and args.which == "bwd":
+        print("bench.py: the backward is built for the zero-padded mode only", file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     es = 2 if wl.dtype == "bf16" else 4
@@ -234,13 +251,13 @@ def main():
     # Inputs of record: seeded parameters and x on the host, kernel evaluated on the device.
     p = synth.draw_params(wl.dims, wl.C, wl.seed)
     x = synth.draw_x(p.rng, wl.B, wl.C, wl.dims, wl.dtype).to(dev)
-    K = synth.kernel_channels(wl.dims, p, device=dev)
+    K = synth.circular_kernel(wl.dims, p, device=dev) if circ else synth.kernel_channels(wl.dims, p, device=dev)
     al = torch.from_numpy(p.alpha).to(dev)
     be = torch.from_numpy(p.beta).to(dev)
     torch.cuda.synchronize()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record()
-    kh = H.kernel_spectrum(K)
+    kh = H.kernel_spectrum_circ(K) if circ else H.kernel_spectrum(K)
     s1.record()
     torch.cuda.synchronize()
     spectrum_ms = s0.elapsed_time(s1)
@@ -253,6 +270,11 @@ def main():
         ws_bytes = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
         if args.ws_mb is not None:
             ws_bytes = max(H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
+    elif circ:
+        y = torch.empty_like(x)
+        ws_bytes = H.circ_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
+        if args.ws_mb is not None:
+            ws_bytes = max(H.circ_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
     else:
         y = torch.empty_like(x)
         ws_bytes = H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
@@ -263,12 +285,16 @@ def main():
     def call():
         if bwd:
             H.fftconv_bwd(x, al, be, kh, dy, *outs, workspace=ws)
+        elif circ:
+            H.fftconv_fwd_circ(x, al, be, kh, y=y, workspace=ws)
         else:
             H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
 
     def traced(events):
         if bwd:
             return H.fftconv_bwd_traced(x, al, be, kh, dy, outs, ws, events)
+        if circ:
+            return H.fftconv_fwd_circ_traced(x, al, be, kh, y, ws, events)
         return H.fftconv_fwd_traced(x, al, be, kh, y, ws, events)
 
     # Launch count per step, then one event slot before each launch and one at the end.
@@ -318,7 +344,7 @@ def main():
     torch.cuda.synchronize()
     marker_ms = sorted(mk[2 * k].elapsed_time(mk[2 * k + 1]) for k in range(args.steps))[args.steps // 2]
 
-    g = _geom(wl.dims)
+    g = _geom(wl.dims, circ)
     if bwd:
         per_ch = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True)
         nch = min(wl.C, ws_bytes // per_ch)
@@ -328,7 +354,13 @@ def main():
         bytes_min = 3 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8 + wl.C * g["kl"] * 4
         names = H.BWD_PASS_NAMES[(wl.d, True)]
     else:
-        plan = H.launch_plan(wl.B, wl.C, wl.dims, x.dtype, ws_bytes)
+        per_ch = (H.circ_workspace_bytes if circ else H.workspace_bytes)(wl.B, wl.C, wl.dims, x.dtype, minimum=True)
+        if per_ch > 0:
+            nch = min(wl.C, ws_bytes // per_ch)
+            nch = -(-wl.C // -(-wl.C // nch))  # balanced chunks, as the library splits them
+        else:
+            nch = wl.C
+        plan = {"chunk_channels": nch}
         bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8
         names = H.PASS_NAMES[wl.d]
     per_pass = {nm: [] for nm in names}
@@ -341,20 +373,21 @@ def main():
     dominant = max(per_pass, key=lambda nm: sum(per_pass[nm]))
     dom_s = sum(per_pass[dominant]) / len(per_pass[dominant]) / 1e3
     nch = plan["chunk_channels"]
-    by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch, es)
+    by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch, es, circ)
     kernel_label = KERNEL_LABEL[dominant]
     hbm = {"bound": "hbm", "achieved": by / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     alu = {"bound": "alu", "achieved": fl / dom_s / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s"}
     for r in (hbm, alu):
         r["frac"] = r["achieved"] / r["peak"]
     roof = hbm if hbm["frac"] >= alu["frac"] else alu
-    roof.update({"kernel": kernel_label, "avg_us": dom_s * 1e6, "traffic": _traffic_from_profile(kernel_label, wl.name, nch)})
+    roof.update({"kernel": kernel_label, "avg_us": dom_s * 1e6,
+                 "traffic": None if circ else _traffic_from_profile(kernel_label, wl.name, nch)})
     roof["other_bound"] = {k: v for k, v in (alu if roof is hbm else hbm).items()}
 
     voxch = wl.B * wl.C * wl.voxels
     value = voxch / (ms_per_step / 1e3) / 1e9
     out = {
-        "metric": METRIC_BWD if bwd else METRIC,
+        "metric": METRIC_BWD if bwd else (METRIC_CIRC if circ else METRIC),
         "value": value,
         "unit": UNIT,
         "n_gpus": 1,
@@ -366,7 +399,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "pass": args.which, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
+        "config": {"workload": wl.name, "pass": args.which, "boundary": args.boundary, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
                    "C": wl.C, "io_dtype": "bf16" if wl.dtype == "bf16" else "fp32", "launches_per_step": n_launch, "workspace_mib": ws_bytes / 2**20,
                    "chunk_channels": plan["chunk_channels"]},
         "hbm_roofline_frac_of_metric": bytes_min / (ms_per_step / 1e3) / HBM_PEAK,
@@ -379,7 +412,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_bwd(wl) if bwd else cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline_bwd(wl) if bwd else cpu_baseline(wl, circ)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -20,6 +20,9 @@ zero outside the grid.  Entry points mirror ``include/hyenand.h``:
   backward, recomputing the forward transforms (explainer, "Implementation and
   operation patterns", "Concrete implementation pattern (PyTorch)")
 * ``HyenaConvolutionFunction`` -- the autograd wrapper of that pattern
+* ``kernel_spectrum_circ(K)`` / ``fftconv_fwd_circ(...)`` -- the circular mode
+  (gist.science summary, "Boundary handling": periodic grids, no padding; K is
+  [C, *dims] indexed by offset mod n)
 """
 from __future__ import annotations
 
@@ -39,7 +42,9 @@ EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_
            "hyenand_fftconv_workspace_bytes", "hyenand_fftconv_workspace_min_bytes", "hyenand_fftconv_fwd",
            "hyenand_fftconv_fwd_traced", "hyenand_fftconv_launch_plan", "hyenand_fftconv_bwd",
            "hyenand_fftconv_bwd_workspace_bytes", "hyenand_fftconv_bwd_workspace_min_bytes",
-           "hyenand_fftconv_bwd_traced")
+           "hyenand_fftconv_bwd_traced", "hyenand_kernel_spectrum_circ_bytes", "hyenand_kernel_spectrum_circ_tile",
+           "hyenand_kernel_spectrum_circ", "hyenand_fftconv_circ_workspace_bytes",
+           "hyenand_fftconv_circ_workspace_min_bytes", "hyenand_fftconv_fwd_circ", "hyenand_fftconv_fwd_circ_traced")
 
 _lib = None
 
@@ -82,6 +87,20 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_bwd_workspace_bytes.restype = SZ
     lib.hyenand_fftconv_bwd_workspace_min_bytes.argtypes = [I, I, I, P, I, I]
     lib.hyenand_fftconv_bwd_workspace_min_bytes.restype = SZ
+    lib.hyenand_kernel_spectrum_circ_bytes.argtypes = [I, I, P]
+    lib.hyenand_kernel_spectrum_circ_bytes.restype = SZ
+    lib.hyenand_kernel_spectrum_circ_tile.argtypes = [I, P]
+    lib.hyenand_kernel_spectrum_circ_tile.restype = I
+    lib.hyenand_kernel_spectrum_circ.argtypes = [P, P, I, I, P, P]
+    lib.hyenand_kernel_spectrum_circ.restype = I
+    lib.hyenand_fftconv_circ_workspace_bytes.argtypes = [I, I, I, P, I]
+    lib.hyenand_fftconv_circ_workspace_bytes.restype = SZ
+    lib.hyenand_fftconv_circ_workspace_min_bytes.argtypes = [I, I, I, P, I]
+    lib.hyenand_fftconv_circ_workspace_min_bytes.restype = SZ
+    lib.hyenand_fftconv_fwd_circ.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_fftconv_fwd_circ.restype = I
+    lib.hyenand_fftconv_fwd_circ_traced.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I, ctypes.POINTER(I)]
+    lib.hyenand_fftconv_fwd_circ_traced.restype = I
     _lib = lib
     return lib
 
@@ -337,3 +356,86 @@ class HyenaConvolutionFunction(torch.autograd.Function):
         x, alpha, beta, K_hat = ctx.saved_tensors
         dx, da, db, dK = fftconv_bwd(x, alpha, beta, K_hat, grad_out.contiguous(), with_dK=ctx.needs_dK)
         return dx, da, db, dK
+
+
+# ----------------------------------------------------------- circular mode
+
+def spectrum_circ_bytes(C: int, dims) -> int:
+    return int(get_lib().hyenand_kernel_spectrum_circ_bytes(C, len(dims), _dims_arr(dims)))
+
+
+def circ_workspace_bytes(B: int, C: int, dims, dtype=torch.float32, minimum: bool = False) -> int:
+    lib = get_lib()
+    f = lib.hyenand_fftconv_circ_workspace_min_bytes if minimum else lib.hyenand_fftconv_circ_workspace_bytes
+    return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype)))
+
+
+def kernel_spectrum_circ(K: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Circular mode: K fp32 device tensor [C, *dims] (index = offset mod n) -> K_hat (complex64 [C, ksz])."""
+    dims = tuple(int(v) for v in K.shape[1:])
+    C = int(K.shape[0])
+    if K.dtype != torch.float32 or not K.is_cuda or not K.is_contiguous():
+        raise TypeError("K must be a contiguous float32 device tensor")
+    nbytes = spectrum_circ_bytes(C, dims)
+    if nbytes == 0 and C > 0:
+        raise HyenandError(ERR_UNSUPPORTED, "kernel_spectrum_circ")
+    if out is None:
+        out = torch.empty(nbytes // 8, dtype=torch.complex64, device=K.device).view(C, -1) if C else \
+            torch.empty(0, dtype=torch.complex64, device=K.device)
+    rc = get_lib().hyenand_kernel_spectrum_circ(_P(K.data_ptr()), _P(out.data_ptr()), C, len(dims), _dims_arr(dims),
+                                                _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "kernel_spectrum_circ")
+    return out
+
+
+def _circ_args(x, alpha, beta, K_hat, y, workspace):
+    if not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous device tensor")
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    for t, nm in ((alpha, "alpha"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
+    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum_circ")
+    if K_hat.numel() * 8 < spectrum_circ_bytes(C, dims):
+        raise ValueError("K_hat is smaller than the circular spectrum of this shape")
+    y = torch.empty_like(x) if y is None else y
+    if workspace is None:
+        nbytes = circ_workspace_bytes(B, C, dims, x.dtype)
+        key = ("circ", str(x.device), nbytes)
+        workspace = _ws_cache.get(key)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
+            _ws_cache[key] = workspace
+        ws_bytes = nbytes
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
+            B, C, len(dims), _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()), ws_bytes]
+    return args, y
+
+
+def fftconv_fwd_circ(x, alpha, beta, K_hat, y=None, workspace=None, stream=None) -> torch.Tensor:
+    """Circular-mode gated N-D convolution (periodic grid, no padding); K_hat from kernel_spectrum_circ."""
+    args, y = _circ_args(x, alpha, beta, K_hat, y, workspace)
+    rc = get_lib().hyenand_fftconv_fwd_circ(*args, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd_circ")
+    return y
+
+
+def fftconv_fwd_circ_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None) -> int:
+    """fftconv_fwd_circ recording ``events`` before each kernel launch and after the last."""
+    args, y = _circ_args(x, alpha, beta, K_hat, y, workspace)
+    st = torch.cuda.current_stream() if stream is None else stream
+    for e in events:
+        if e.cuda_event == 0:
+            e.record(st)
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    n = ctypes.c_int(0)
+    rc = get_lib().hyenand_fftconv_fwd_circ_traced(*args, _stream(stream), arr, len(events), ctypes.byref(n))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd_circ_traced")
+    return int(n.value)

@@ -52,26 +52,32 @@ const char* hyenand_status_string(int s)
 
 int hyenand_version(void) { return 100; }
 
-size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims)
+static size_t spectrum_bytes(int C, int d, const int64_t* dims, bool circ)
 {
     Geom g;
-    if (C < 0 || !make_geom(d, dims, &g)) return 0;
+    if (C < 0 || !make_geom(d, dims, &g, circ)) return 0;
     return (size_t)C * (size_t)g.ksz * 8u;
 }
 
-int hyenand_kernel_spectrum_tile(int d, const int64_t* dims)
+static int spectrum_tile(int d, const int64_t* dims, bool circ)
 {
     Geom g;
-    if (!make_geom(d, dims, &g)) return 0;
+    if (!make_geom(d, dims, &g, circ)) return 0;
     return g.lt;
 }
 
-int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream)
+size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims) { return spectrum_bytes(C, d, dims, false); }
+int hyenand_kernel_spectrum_tile(int d, const int64_t* dims) { return spectrum_tile(d, dims, false); }
+size_t hyenand_kernel_spectrum_circ_bytes(int C, int d, const int64_t* dims) { return spectrum_bytes(C, d, dims, true); }
+int hyenand_kernel_spectrum_circ_tile(int d, const int64_t* dims) { return spectrum_tile(d, dims, true); }
+
+static int kernel_spectrum_impl(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream,
+                                bool circ)
 {
     if (C < 0) return HYENAND_ERR_INVALID_ARG;
     if (d < 1 || d > 3 || !dims) return d < 1 || d > 3 ? HYENAND_ERR_UNSUPPORTED : HYENAND_ERR_INVALID_ARG;
     Geom g;
-    if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
+    if (!make_geom(d, dims, &g, circ)) return HYENAND_ERR_UNSUPPORTED;
     if (C == 0) return HYENAND_OK;
     if (!K || !K_hat) return HYENAND_ERR_INVALID_ARG;
     if (!aligned(K, 4) || !aligned(K_hat, 8)) return HYENAND_ERR_INVALID_ARG;
@@ -87,30 +93,53 @@ int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int
     return e == hipSuccess ? HYENAND_OK : HYENAND_ERR_HIP;
 }
 
-size_t hyenand_fftconv_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype)
+int hyenand_kernel_spectrum(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream)
+{
+    return kernel_spectrum_impl(K, K_hat, C, d, dims, stream, false);
+}
+
+int hyenand_kernel_spectrum_circ(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream)
+{
+    return kernel_spectrum_impl(K, K_hat, C, d, dims, stream, true);
+}
+
+static size_t workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, bool circ, bool minimum)
 {
     Geom g;
-    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
-    return recommended_workspace(g, B, C);
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g, circ)) return 0;
+    return minimum ? (size_t)B * (size_t)g.wsp * 8u : recommended_workspace(g, B, C);
+}
+
+size_t hyenand_fftconv_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype)
+{
+    return workspace_bytes(B, C, d, dims, dtype, false, false);
 }
 
 size_t hyenand_fftconv_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype)
 {
-    Geom g;
-    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
-    return (size_t)B * (size_t)g.wsp * 8u;
+    return workspace_bytes(B, C, d, dims, dtype, false, true);
+}
+
+size_t hyenand_fftconv_circ_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype)
+{
+    return workspace_bytes(B, C, d, dims, dtype, true, false);
+}
+
+size_t hyenand_fftconv_circ_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype)
+{
+    return workspace_bytes(B, C, d, dims, dtype, true, true);
 }
 
 static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y, int B,
                             int C, int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
-                            void* stream, LaunchTrace* trace)
+                            void* stream, LaunchTrace* trace, bool circ)
 {
     if (B < 0 || C < 0) return HYENAND_ERR_INVALID_ARG;
     if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
     if (d < 1 || d > 3) return HYENAND_ERR_UNSUPPORTED;
     if (!dims) return HYENAND_ERR_INVALID_ARG;
     Geom g;
-    if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
+    if (!make_geom(d, dims, &g, circ)) return HYENAND_ERR_UNSUPPORTED;
     if (B == 0 || C == 0) return HYENAND_OK;
     const size_t es = dtype == HYENAND_BF16 ? 2 : 4;
     if (!x || !y || !alpha || !beta || !K_hat) return HYENAND_ERR_INVALID_ARG;
@@ -148,7 +177,15 @@ int hyenand_fftconv_fwd(const void* x, const float* alpha, const float* beta, co
                         void* stream)
 {
     return fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes, stream,
-                            nullptr);
+                            nullptr, false);
+}
+
+int hyenand_fftconv_fwd_circ(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y, int B,
+                             int C, int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream)
+{
+    return fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes, stream,
+                            nullptr, true);
 }
 
 int hyenand_fftconv_launch_plan(int B, int C, int d, const int64_t* dims, int dtype, size_t workspace_bytes,
@@ -176,7 +213,20 @@ int hyenand_fftconv_fwd_traced(const void* x, const float* alpha, const float* b
     if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
     LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
     const int rc = fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes,
-                                    stream, &tr);
+                                    stream, &tr, false);
+    if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
+    return rc;
+}
+
+int hyenand_fftconv_fwd_circ_traced(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y,
+                                    int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                                    int* n_launches)
+{
+    if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
+    LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
+    const int rc = fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes,
+                                    stream, &tr, true);
     if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
     return rc;
 }

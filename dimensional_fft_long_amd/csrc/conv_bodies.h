@@ -115,13 +115,14 @@ __host__ __device__ __forceinline__ void row_meta(const Ctx& ctx, int bid, const
 // loops run ITER = NP*n/NT iterations per thread; every load of a loop is
 // issued before the first use (invalid tail lines read offset 0 and are zeroed).
 // GATE = false transforms x as it is (the backward's output gradient).
-template <int L, bool BF16, bool GATE, class Ctx>
+// CIRC (circular mode): rows of n = L samples, nothing pruned.
+template <int L, bool BF16, bool GATE, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
-    constexpr int ITER = NP * n / NT;
-    static_assert(NP * n % NT == 0, "whole element loops");
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
+    constexpr int ITER = NP * n / NT, ITS = NP * S / NT;  // element loops over samples / slots
+    static_assert(NP * n % NT == 0 && NP * S % NT == 0, "whole element loops");
     const int tid = ctx.tid();
     ctx.stage();
     row_meta<NP, NT>(ctx, bid, a, M);
@@ -143,7 +144,7 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
         T[m * LP + lp] = z;
     }
     ctx.sync();
-    tile_fft<L, NP, LP, NT, false, true, false>(ctx, T);
+    tile_fft<L, NP, LP, NT, false, !CIRC, false>(ctx, T);
     // Separate the two rows: with Z = FFT(u_a + i u_b),
     //   2 U_a[k] = Z[k] + conj Z[L-k],   2 U_b[k] = -i (Z[k] - conj Z[L-k]).
     // The factor 2 is folded into the kernel spectrum.
@@ -151,7 +152,7 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
     // stores cover whole runs of the tile-major workspace.
     const long long tstride = ws_tile_stride(a.g);
 #pragma unroll
-    for (int i = 0; i < ITER; ++i) {
+    for (int i = 0; i < ITS; ++i) {
         const int idx = tid + i * NT, u = idx & (a.g.lt - 1), rest = idx >> a.g.lt_log;
         const int lp = rest % NP, k = ((rest / NP) << a.g.lt_log) + u;
         const long long wo = (long long)(k >> a.g.lt_log) * tstride + u;
@@ -248,13 +249,15 @@ __host__ __device__ __forceinline__ void bwd_epilogue(const Ctx& ctx, int bid, c
 // BWD: the inverse transforms carry du; the epilogue computes dx and the
 // partial sums of dalpha and dbeta (x is read again: the forward saves no
 // intermediate, the explainer's gradient-checkpointing pattern).
-template <int L, bool BF16, bool BWD, class Ctx>
+// CIRC (circular mode): every one of the L outputs is kept.
+template <int L, bool BF16, bool BWD, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
-    constexpr int ITER = NP * S / NT;
-    static_assert(NP * S % NT == 0, "whole element loops");
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
+    constexpr int ITER = NP * S / NT, ITO = NP * n / NT;
+    static_assert(NP * S % NT == 0 && NP * n % NT == 0, "whole element loops");
+    static_assert(!(BWD && CIRC), "the backward is built for the zero-padded mode");
     const int tid = ctx.tid();
     ctx.stage();
     row_meta<NP, NT>(ctx, bid, a, M);
@@ -300,12 +303,12 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
         }
     }
     ctx.sync();
-    tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
+    tile_fft<L, NP, LP, NT, true, false, !CIRC>(ctx, T);
     if constexpr (BWD) {
         bwd_epilogue<L, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
     } else {
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) {
+        for (int i = 0; i < ITO; ++i) {
             const int idx = tid + i * NT, lp = idx / n, m = idx % n;
             const RowMeta& md = M[lp];
             const float2 z = T[m * LP + lp];
@@ -323,7 +326,7 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
 // the n_mid outputs that are kept.  The first pass reads the workspace and the
 // last pass writes it back (in place; every read precedes a barrier that
 // precedes every write).
-template <int L, bool INV, class Ctx>
+template <int L, bool INV, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void col_mid_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
     constexpr int TW = col_tw(L), NT = col_nt(L);
@@ -347,8 +350,8 @@ __host__ __device__ __forceinline__ void col_mid_body(const Ctx& ctx, int bid, c
         if (lam0 + l < lines) base[off(pos, l)] = v;
     };
     auto after_load = [&]() { ctx.stage(); };
-    if constexpr (INV) inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
-    else fwd_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
+    if constexpr (INV) inv_fn_to_fn<L, TW, NT, !CIRC>(ctx, T, ld, st, after_load);
+    else fwd_fn_to_fn<L, TW, NT, !CIRC>(ctx, T, ld, st, after_load);
 }
 
 // Rows of the middle axis handled together by one out-axis workgroup: with
@@ -480,7 +483,8 @@ __host__ __device__ __forceinline__ OutView out_view(const ConvArgs& a, int item
 // Looping kernels (out_looped) run the items bid, bid + nblk, ... (nblk = the
 // grid, one workgroup per CU): no workgroup launch and tail per item, and the
 // item ids keep the XCD-blocked order of out_tile when nblk is a multiple of 8.
-template <int L, int NR, class Ctx>
+// CIRC (circular mode): all L positions are read and written.
+template <int L, int NR, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, int nblk, const ConvArgs& a,
                                                       float2* T)
 {
@@ -505,7 +509,7 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     using P0 = PassRegs<L, R0, NL, NT>;
     using PL = PassRegs<L, RL, NL, NT>;
     auto load_cols = [&](const OutView& v, P0& s) {
-        pass_load_fn<L, R0, NL, NT, true>(ctx, [&](int j, int q, int l) -> float2 {
+        pass_load_fn<L, R0, NL, NT, !CIRC>(ctx, [&](int j, int q, int l) -> float2 {
             const bool ok = v.k0 + l % TW < g.S;
             const float2 x = *at(v.base, q * PS, ok ? lane_bytes(v, j, l) : 0u);
             return ok ? x : make_float2(0.f, 0.f);
@@ -528,7 +532,7 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     };
     // One item: forward from the loaded columns, product, inverse and store.
     auto run_item = [&](const OutView& v, P0& s) {
-        auto t = fwd_from_regs<L, NL, NT, true>(ctx, T, s);
+        auto t = fwd_from_regs<L, NL, NT, !CIRC>(ctx, T, s);
         ctx.sync();  // every LDS read of the forward transform is done: T is free
         if (v.o.t == 0) {
             pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
@@ -551,7 +555,7 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
                 t.v[i][r] = kok[i] ? m : t.v[i][r];
             }
         }
-        inv_to_fn<L, NL, NT, true>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+        inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
             if (v.k0 + l % TW < g.S) *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
         });
     };
@@ -742,11 +746,13 @@ __host__ __device__ __forceinline__ void col_out_bwd_body(const Ctx& ctx, int bi
 // BWD: the line carries the output gradients dy (no gate), the product takes
 // the conjugate spectrum (a correlation with K), and the backward epilogue
 // turns du into dx and the dalpha / dbeta partial sums.
-template <int L, bool BF16, bool BWD, class Ctx>
+// CIRC (circular mode): lines of n = L samples, nothing pruned or cropped.
+template <int L, bool BF16, bool BWD, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                      RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
+    static_assert(!(BWD && CIRC), "the backward is built for the zero-padded mode");
     const Geom& g = a.g;
     const int P = a.nch * a.B;
     const int H = (P + 1) / 2;
@@ -796,7 +802,7 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
         T[m * LP + lp] = z;
     }
     ctx.sync();
-    tile_fft<L, NP, LP, NT, false, true, false>(ctx, T);
+    tile_fft<L, NP, LP, NT, false, !CIRC, false>(ctx, T);
     for (int idx = tid; idx < NP * S; idx += NT) {
         const int lp = idx / S, k = idx % S;
         const RowMeta& md = M[lp];
@@ -824,7 +830,7 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
         }
     }
     ctx.sync();
-    tile_fft<L, NP, LP, NT, true, false, true>(ctx, T);
+    tile_fft<L, NP, LP, NT, true, false, !CIRC>(ctx, T);
     if constexpr (BWD) {
         bwd_epilogue<L, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
     } else {
@@ -854,6 +860,8 @@ __host__ __device__ __forceinline__ int unwrap(int m, int n, int N)
 __host__ __device__ __forceinline__ float kernel_at(const ConvArgs& a, int c, int m_out, int m_mid, int t)
 {
     const Geom& g = a.g;
+    if (g.circ)  // periodic: the kernel is stored by offset mod n, which is the index itself
+        return a.K[(long long)c * g.ke_out * g.ke_mid * g.ke_in + ((long long)m_out * g.ke_mid + m_mid) * g.ke_in + t];
     const int d0 = unwrap(m_out, g.n_out, g.N_out), d1 = unwrap(m_mid, g.n_mid, g.N_mid),
               d2 = unwrap(t, g.n_in, g.N_in);
     if (d0 == kEmpty || d1 == kEmpty || d2 == kEmpty) return 0.f;

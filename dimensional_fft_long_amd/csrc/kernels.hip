@@ -76,31 +76,31 @@ __device__ __forceinline__ DevCtx<L, NT, PLANS> make_ctx(float2* twl)
     return DevCtx<L, NT, PLANS>{twl};
 }
 
-template <int L, bool BF16, bool GATE>
+template <int L, bool BF16, bool GATE, bool CIRC = false>
 __global__ __launch_bounds__(row_nt(L)) void k_row_fwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
-    row_fwd_body<L, BF16, GATE>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+    row_fwd_body<L, BF16, GATE, CIRC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
-template <int L, bool BF16, bool BWD>
+template <int L, bool BF16, bool BWD, bool CIRC = false>
 __global__ __launch_bounds__(row_nt(L)) void k_row_inv(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
-    row_inv_body<L, BF16, BWD>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+    row_inv_body<L, BF16, BWD, CIRC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
-template <int L, bool BF16, bool BWD>
+template <int L, bool BF16, bool BWD, bool CIRC = false>
 __global__ __launch_bounds__(row_nt(L)) void k_conv1d(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
-    conv1d_body<L, BF16, BWD>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+    conv1d_body<L, BF16, BWD, CIRC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
 template <int L, int NR, bool DK>
@@ -152,20 +152,20 @@ __global__ __launch_bounds__(256) void k_zero(float* p, long long n)
     if (i < n) p[i] = 0.f;
 }
 
-template <int L, bool INV>
+template <int L, bool INV, bool CIRC = false>
 __global__ __launch_bounds__(col_nt(L)) void k_col_mid(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (INV ? kPlanR : kPlanF)>()];
     __shared__ float2 T[L * col_tw(L)];
-    col_mid_body<L, INV>(make_ctx<L, col_nt(L), (INV ? kPlanR : kPlanF)>(TWL), (int)blockIdx.x, a, T);
+    col_mid_body<L, INV, CIRC>(make_ctx<L, col_nt(L), (INV ? kPlanR : kPlanF)>(TWL), (int)blockIdx.x, a, T);
 }
 
-template <int L, int NR>
+template <int L, int NR, bool CIRC = false>
 __global__ __launch_bounds__(out_nt(L, NR)) void k_col_out(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
     __shared__ float2 T[L * NR * out_tw(L, NR)];
-    col_out_body<L, NR>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, (int)gridDim.x, a, T);
+    col_out_body<L, NR, CIRC>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, (int)gridDim.x, a, T);
 }
 
 template <int L>
@@ -240,7 +240,8 @@ static hipError_t with_length(int L, F&& f)
 
 static hipError_t last_error() { return hipGetLastError(); }
 
-hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
+template <bool CIRC>
+static hipError_t forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
@@ -249,16 +250,16 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
         return with_length(g.N_in, [&]<int L>() {
             const long long H = ((long long)a.nch * a.B + 1) / 2;
             mark();
-            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-            else hipLaunchKernelGGL((k_conv1d<L, false, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true, false, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_conv1d<L, false, false, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
             return last_error();
         });
     }
     const long long H = (long long)a.nch * a.B * (g.n_out * g.n_mid / 2);
     e = with_length(g.N_in, [&]<int L>() {
         mark();
-        if (a.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        else hipLaunchKernelGGL((k_row_fwd<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        if (a.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_fwd<L, false, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
     if (e != hipSuccess) return e;
@@ -266,40 +267,45 @@ hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
         e = with_length(g.N_mid, [&]<int L>() {
             const long long grid = (long long)a.nch * a.B * ceil_div((long long)g.n_out * g.S, col_tw(L));
             mark();
-            hipLaunchKernelGGL((k_col_mid<L, false>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
+            hipLaunchKernelGGL((k_col_mid<L, false, CIRC>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
         e = with_length(g.N_out, [&]<int L>() {
             const long long items = out_items<2, out_tw(L, 2)>(g, a.B, a.nch);
-            const unsigned grid = out_looped(L, 2) ? loop_grid(k_col_out<L, 2>, out_nt(L, 2), items) : (unsigned)items;
+            const unsigned grid = out_looped(L, 2) ? loop_grid(k_col_out<L, 2, CIRC>, out_nt(L, 2), items) : (unsigned)items;
             mark();
-            hipLaunchKernelGGL((k_col_out<L, 2>), dim3(grid), dim3(out_nt(L, 2)), 0, st, a);
+            hipLaunchKernelGGL((k_col_out<L, 2, CIRC>), dim3(grid), dim3(out_nt(L, 2)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
         e = with_length(g.N_mid, [&]<int L>() {
             const long long grid = (long long)a.nch * a.B * ceil_div((long long)g.n_out * g.S, col_tw(L));
             mark();
-            hipLaunchKernelGGL((k_col_mid<L, true>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
+            hipLaunchKernelGGL((k_col_mid<L, true, CIRC>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
             return last_error();
         });
     } else {
         e = with_length(g.N_out, [&]<int L>() {
             const long long items = out_items<1, out_tw(L, 1)>(g, a.B, a.nch);
-            const unsigned grid = out_looped(L, 1) ? loop_grid(k_col_out<L, 1>, out_nt(L, 1), items) : (unsigned)items;
+            const unsigned grid = out_looped(L, 1) ? loop_grid(k_col_out<L, 1, CIRC>, out_nt(L, 1), items) : (unsigned)items;
             mark();
-            hipLaunchKernelGGL((k_col_out<L, 1>), dim3(grid), dim3(out_nt(L, 1)), 0, st, a);
+            hipLaunchKernelGGL((k_col_out<L, 1, CIRC>), dim3(grid), dim3(out_nt(L, 1)), 0, st, a);
             return last_error();
         });
     }
     if (e != hipSuccess) return e;
     return with_length(g.N_in, [&]<int L>() {
         mark();
-        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        else hipLaunchKernelGGL((k_row_inv<L, false, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true, false, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_inv<L, false, false, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
+}
+
+hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
+{
+    return a.g.circ ? forward_chunk<true>(a, st, tr) : forward_chunk<false>(a, st, tr);
 }
 
 hipError_t launch_zero(float* p, long long n, hipStream_t st)

@@ -90,8 +90,9 @@ struct Geom {
     long long wsp;         // workspace complex per pair: n_out * N_mid * S (0 for d = 1)
     long long kmain;       // main block complex per channel: N_out * N_mid * S
     long long ksz;         // kmain + N_out * N_mid
-    int ke_out, ke_mid, ke_in;  // kernel extents 2n-1 (1 for absent axes)
+    int ke_out, ke_mid, ke_in;  // kernel extents 2n-1 (1 for absent axes); n when circular
     int lt, lt_log;        // slot tile of the tile-major planes (a power of two <= S)
+    int circ;              // circular mode: periodic grid, N = n, no padding or crop
 };
 
 // Slot tile of the kernel spectrum and the workspace: the out-axis kernel's
@@ -118,27 +119,35 @@ __host__ __device__ __forceinline__ long long tm_index(const Geom& g, long long 
 
 inline bool is_pow2(long long v) { return v > 0 && (v & (v - 1)) == 0; }
 
-// Returns false for an unsupported shape: d in {1,2,3}, every n a power of two in [2, 1024].
-inline bool make_geom(int d, const int64_t* dims, Geom* g)
+// Returns false for an unsupported shape: d in {1,2,3}, every n a power of two
+// in [2, 1024] ([4, 1024] in circular mode, whose transforms have length n).
+//
+// Circular mode (gist.science summary, "Methodology", "Boundary handling":
+// circular convolutions for periodic systems): every axis keeps N = n, the
+// kernel lives on the n offsets modulo n ([C][n_0]..[n_{d-1}], index = offset
+// mod n), no transform is pruned and every output is kept.
+inline bool make_geom(int d, const int64_t* dims, Geom* g, bool circ = false)
 {
     if (d < 1 || d > 3 || !dims) return false;
     for (int a = 0; a < d; ++a)
-        if (dims[a] < 2 || dims[a] > 1024 || !is_pow2(dims[a])) return false;
+        if (dims[a] < (circ ? 4 : 2) || dims[a] > 1024 || !is_pow2(dims[a])) return false;
     g->d = d;
+    g->circ = circ ? 1 : 0;
     if (d == 3) { g->n_out = (int)dims[0]; g->n_mid = (int)dims[1]; g->n_in = (int)dims[2]; }
     else if (d == 2) { g->n_out = (int)dims[0]; g->n_mid = 1; g->n_in = (int)dims[1]; }
     else { g->n_out = 1; g->n_mid = 1; g->n_in = (int)dims[0]; }
-    g->N_out = d >= 2 ? 2 * g->n_out : 1;
-    g->N_mid = d >= 3 ? 2 * g->n_mid : 1;
-    g->N_in = 2 * g->n_in;
-    g->S = g->n_in;
+    const int pad = circ ? 1 : 2;
+    g->N_out = d >= 2 ? pad * g->n_out : 1;
+    g->N_mid = d >= 3 ? pad * g->n_mid : 1;
+    g->N_in = pad * g->n_in;
+    g->S = g->N_in / 2;
     g->vox = (long long)g->n_out * g->n_mid * g->n_in;
     g->wsp = d >= 2 ? (long long)g->n_out * g->N_mid * g->S : 0;
     g->kmain = (long long)g->N_out * g->N_mid * g->S;
     g->ksz = g->kmain + (long long)g->N_out * g->N_mid;
-    g->ke_out = 2 * g->n_out - 1;
-    g->ke_mid = 2 * g->n_mid - 1;
-    g->ke_in = 2 * g->n_in - 1;
+    g->ke_out = circ ? g->n_out : 2 * g->n_out - 1;
+    g->ke_mid = circ ? g->n_mid : 2 * g->n_mid - 1;
+    g->ke_in = circ ? g->n_in : 2 * g->n_in - 1;
     g->lt = slot_tile(d, g->N_out, g->S);
     g->lt_log = 0;
     while ((1 << g->lt_log) < g->lt) ++g->lt_log;

@@ -203,6 +203,37 @@ int hyenand_fftconv_bwd_traced(const void* x, const float* phi_alpha, const floa
                                int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
                                void* stream, void* const* events, int n_events, int* n_launches);
 
+/*
+ * Circular mode.  The gist.science summary of the paper ("Methodology",
+ * "Boundary handling") gives the method circular convolutions for periodic
+ * physical systems next to the zero-padded non-circular ones.  On a periodic
+ * grid the offset i - j is taken modulo n:
+ *
+ *     y[b,c,i] = sum_{j in G} phi_c(x[b,c,j]) x[b,c,j] K_c[(i - j) mod n],
+ *
+ * with the kernel stored by offset modulo n: K  [C][dims[0]]..[dims[d-1]] fp32,
+ * index m_a = delta_a mod n_a (offset 0 at index 0).  The transforms have
+ * length N_a = n_a (no padding, no crop).  Supported: d in {1, 2, 3}, every
+ * dims[a] a power of two in [4, 1024].  The entry points mirror the
+ * non-circular ones (same conventions, errors and K_hat layout, with N_a = n_a
+ * and S = n_in / 2); a circular K_hat must only be used with
+ * hyenand_fftconv_fwd_circ.  The minimum workspace is one channel,
+ * B * n_0 * (n_1 for 3-D) * S * 8 bytes (0 for d = 1).
+ */
+size_t hyenand_kernel_spectrum_circ_bytes(int C, int d, const int64_t* dims);
+int hyenand_kernel_spectrum_circ_tile(int d, const int64_t* dims);
+int hyenand_kernel_spectrum_circ(const float* K, void* K_hat, int C, int d, const int64_t* dims, void* stream);
+size_t hyenand_fftconv_circ_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype);
+size_t hyenand_fftconv_circ_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype);
+int hyenand_fftconv_fwd_circ(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat, void* y,
+                             int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+/* hyenand_fftconv_fwd_circ with the launch trace of hyenand_fftconv_fwd_traced. */
+int hyenand_fftconv_fwd_circ_traced(const void* x, const float* phi_alpha, const float* phi_beta,
+                                    const void* K_hat, void* y, int B, int C, int d, const int64_t* dims, int dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                                    int n_events, int* n_launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -201,3 +201,19 @@ def sample_kernel_points(dims, chans, per_chan: int, seed: int) -> np.ndarray:
         for _ in range(per_chan):
             rows.append([c] + [int(rng.integers(0, 2 * n - 1)) for n in dims])
     return np.asarray(rows, dtype=np.int64)
+
+
+def circular_kernel(dims, p: Params, device="cpu"):
+    """Circular-mode kernel [C, *dims] fp32: the same generator evaluated on the
+    periodic grid's minimal-image offsets (index m holds offset m for
+    m <= n/2 and m - n above), i.e. a gather from the non-circular kernel of
+    offsets -(n-1)..(n-1)."""
+    import torch
+
+    full = kernel_channels(dims, p, device=device)
+    idx = [torch.tensor([(m if m <= n // 2 else m - n) + n - 1 for m in range(n)], device=full.device)
+           for n in dims]
+    out = full
+    for a, ix in enumerate(idx):
+        out = out.index_select(a + 1, ix)
+    return out.contiguous()

@@ -171,3 +171,31 @@ def test_bwd_rejects_arguments(H):
     assert call(wb=need - 1) == 3
     assert call(d=2, dims=_dims(8, 6)) == 2 and call(d=0) == 2 and call(dims=None) == 1
     assert call(x=None, dy=None, dx=None, C=0) == 0
+
+
+def test_circular_sizes_and_rejects(H):
+    lib = H.get_lib()
+    # 2-D 256x256 circular: N = n, S = 128; main N0 * S = 256 * 128, dblk N0 = 256.
+    assert lib.hyenand_kernel_spectrum_circ_bytes(4, 2, _dims(256, 256)) == 4 * (256 * 128 + 256) * 8
+    assert lib.hyenand_kernel_spectrum_circ_bytes(2, 3, _dims(8, 8, 8)) == 2 * (8 * 8 * 4 + 8 * 8) * 8
+    assert lib.hyenand_kernel_spectrum_circ_bytes(3, 1, _dims(64)) == 3 * (32 + 1) * 8
+    # workspace per pair n0 * N_mid * S with N_mid = n_mid
+    assert lib.hyenand_fftconv_circ_workspace_min_bytes(2, 3, 2, _dims(64, 32), 0) == 2 * 64 * 16 * 8
+    assert lib.hyenand_fftconv_circ_workspace_min_bytes(1, 1, 3, _dims(8, 16, 32), 0) == 8 * 16 * 16 * 8
+    # n = 2 has no circular transform here (length >= 4); non-powers of two are unsupported
+    for d, dims in [(1, _dims(2)), (2, _dims(4, 2)), (2, _dims(12, 8)), (1, _dims(2048))]:
+        assert lib.hyenand_kernel_spectrum_circ_bytes(1, d, dims) == 0
+        assert lib.hyenand_kernel_spectrum_circ_tile(d, dims) == 0
+    for d in (1, 2, 3):
+        for e in range(2, 11):
+            t = lib.hyenand_kernel_spectrum_circ_tile(d, _dims(*([2 ** e] * d)))
+            S = 2 ** (e - 1)
+            assert t >= 1 and S % t == 0
+    dd = _dims(8, 8)
+    call = lambda x=FAKE, k=FAKE, y=FAKE, B=1, C=1, d=2, dims=dd, dt=0, w=FAKE, wb=1 << 20: \
+        lib.hyenand_fftconv_fwd_circ(x, FAKE, FAKE, k, y, B, C, d, dims, dt, w, wb, None)
+    assert call(x=None) == 1 and call(y=None) == 1 and call(k=MISALIGNED) == 1 and call(dt=5) == 1
+    assert call(dims=_dims(2, 8)) == 2 and call(w=None) == 3 and call(wb=8 * 4 * 8 - 1) == 3
+    assert call(x=None, y=None, B=0) == 0
+    assert lib.hyenand_kernel_spectrum_circ(FAKE, FAKE, 2, 2, _dims(8, 2), None) == 2
+    assert lib.hyenand_kernel_spectrum_circ(None, FAKE, 2, 2, _dims(8, 8), None) == 1
