@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gvoxel·channels/s of gated N-D FFT conv fwd; % of HBM roofline (1 GPU)"
 METRIC_CIRC = "Gvoxel·channels/s of gated N-D FFT conv fwd, circular mode; % of HBM roofline (1 GPU)"
+METRIC_PS = "Gvoxel·channels/s of gated N-D FFT conv fwd, one kernel per (b, c); % of HBM roofline (1 GPU)"
 METRIC_BWD = "Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK); % of HBM roofline (1 GPU)"
 UNIT = "Gvoxel·channels/s"
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
@@ -212,6 +213,9 @@ def main():
                     help="time the forward (default) or the backward with the kernel gradient")
     ap.add_argument("--boundary", choices=("padded", "circular"), default="padded",
                     help="zero-padded non-circular convolution (default) or the circular mode (forward only)")
+    ap.add_argument("--kernel", choices=("shared", "per-sample"), default="shared",
+                    help="one kernel per channel (default) or one per (b, c): input-dependent kernels "
+                         "(zero-padded forward only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ws-mb", type=float, default=None,
                     help="workspace size in MiB (default: the library's recommendation)")
@@ -236,13 +240,19 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "copies": 5}))
         return 0
 
+    import numpy as np
+
     import dimensional_fft_long_amd as H
     import synth
 
     wl = {w.name: w for w in synth.WORKLOADS}[args.workload]
     circ = args.boundary == "circular"
-    if circ and args.which == "bwd":
-        print("bench.py: the backward is built for the zero-padded mode only", file=sys.stderr)
+    ps = args.kernel == "per-sample"
+    if (circ or ps) and args.which == "bwd":
+        print("bench.py: the backward is built for the zero-padded shared-kernel mode only", file=sys.stderr)
+        return 2
+    if circ and ps:
+        print("bench.py: per-sample kernels are built for the zero-padded mode only", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -252,12 +262,20 @@ def main():
     p = synth.draw_params(wl.dims, wl.C, wl.seed)
     x = synth.draw_x(p.rng, wl.B, wl.C, wl.dims, wl.dtype).to(dev)
     K = synth.circular_kernel(wl.dims, p, device=dev) if circ else synth.kernel_channels(wl.dims, p, device=dev)
+    if ps:
+        # One kernel per (b, c): the channel's kernel scaled and shifted by a
+        # seeded per-sample factor (a stand-in for the FiLM modulation).
+        rng_ps = np.random.Generator(np.random.PCG64([wl.seed, 3]))
+        gsc = torch.from_numpy(rng_ps.uniform(0.5, 1.5, (wl.B, wl.C)).astype(np.float32)).to(dev)
+        gsh = torch.from_numpy(rng_ps.uniform(-0.1, 0.1, (wl.B, wl.C)).astype(np.float32)).to(dev)
+        shape = (wl.B, wl.C) + (1,) * len(wl.dims)
+        K = (K.unsqueeze(0) * gsc.reshape(shape) + gsh.reshape(shape)).contiguous()
     al = torch.from_numpy(p.alpha).to(dev)
     be = torch.from_numpy(p.beta).to(dev)
     torch.cuda.synchronize()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record()
-    kh = H.kernel_spectrum_circ(K) if circ else H.kernel_spectrum(K)
+    kh = H.kernel_spectrum_circ(K) if circ else (H.kernel_spectrum_per_sample(K) if ps else H.kernel_spectrum(K))
     s1.record()
     torch.cuda.synchronize()
     spectrum_ms = s0.elapsed_time(s1)
@@ -287,6 +305,8 @@ def main():
             H.fftconv_bwd(x, al, be, kh, dy, *outs, workspace=ws)
         elif circ:
             H.fftconv_fwd_circ(x, al, be, kh, y=y, workspace=ws)
+        elif ps:
+            H.fftconv_fwd_per_sample(x, al, be, kh, y=y, workspace=ws)
         else:
             H.fftconv_fwd(x, al, be, kh, y=y, workspace=ws)
 
@@ -295,6 +315,8 @@ def main():
             return H.fftconv_bwd_traced(x, al, be, kh, dy, outs, ws, events)
         if circ:
             return H.fftconv_fwd_circ_traced(x, al, be, kh, y, ws, events)
+        if ps:
+            return H.fftconv_fwd_per_sample_traced(x, al, be, kh, y, ws, events)
         return H.fftconv_fwd_traced(x, al, be, kh, y, ws, events)
 
     # Launch count per step, then one event slot before each launch and one at the end.
@@ -361,7 +383,7 @@ def main():
         else:
             nch = wl.C
         plan = {"chunk_channels": nch}
-        bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8
+        bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8 * (wl.B if ps else 1)
         names = H.PASS_NAMES[wl.d]
     per_pass = {nm: [] for nm in names}
     step_ms = []
@@ -373,7 +395,7 @@ def main():
     dominant = max(per_pass, key=lambda nm: sum(per_pass[nm]))
     dom_s = sum(per_pass[dominant]) / len(per_pass[dominant]) / 1e3
     nch = plan["chunk_channels"]
-    by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch, es, circ)
+    by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch * (wl.B if ps else 1), es, circ)
     kernel_label = KERNEL_LABEL[dominant]
     hbm = {"bound": "hbm", "achieved": by / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     alu = {"bound": "alu", "achieved": fl / dom_s / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s"}
@@ -381,13 +403,13 @@ def main():
         r["frac"] = r["achieved"] / r["peak"]
     roof = hbm if hbm["frac"] >= alu["frac"] else alu
     roof.update({"kernel": kernel_label, "avg_us": dom_s * 1e6,
-                 "traffic": None if circ else _traffic_from_profile(kernel_label, wl.name, nch)})
+                 "traffic": None if (circ or ps) else _traffic_from_profile(kernel_label, wl.name, nch)})
     roof["other_bound"] = {k: v for k, v in (alu if roof is hbm else hbm).items()}
 
     voxch = wl.B * wl.C * wl.voxels
     value = voxch / (ms_per_step / 1e3) / 1e9
     out = {
-        "metric": METRIC_BWD if bwd else (METRIC_CIRC if circ else METRIC),
+        "metric": METRIC_BWD if bwd else (METRIC_CIRC if circ else (METRIC_PS if ps else METRIC)),
         "value": value,
         "unit": UNIT,
         "n_gpus": 1,
@@ -399,7 +421,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "pass": args.which, "boundary": args.boundary, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
+        "config": {"workload": wl.name, "pass": args.which, "boundary": args.boundary, "kernel": args.kernel, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
                    "C": wl.C, "io_dtype": "bf16" if wl.dtype == "bf16" else "fp32", "launches_per_step": n_launch, "workspace_mib": ws_bytes / 2**20,
                    "chunk_channels": plan["chunk_channels"]},
         "hbm_roofline_frac_of_metric": bytes_min / (ms_per_step / 1e3) / HBM_PEAK,

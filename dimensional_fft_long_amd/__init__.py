@@ -20,6 +20,8 @@ zero outside the grid.  Entry points mirror ``include/hyenand.h``:
   backward, recomputing the forward transforms (explainer, "Implementation and
   operation patterns", "Concrete implementation pattern (PyTorch)")
 * ``HyenaConvolutionFunction`` -- the autograd wrapper of that pattern
+* ``fftconv_fwd_per_sample(x, alpha, beta, K_hat)`` -- input-dependent kernels:
+  K_hat = kernel_spectrum(K) of kernels [B, C, *(2n-1)], one per (b, c)
 * ``kernel_spectrum_circ(K)`` / ``fftconv_fwd_circ(...)`` -- the circular mode
   (gist.science summary, "Boundary handling": periodic grids, no padding; K is
   [C, *dims] indexed by offset mod n)
@@ -44,7 +46,8 @@ EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_
            "hyenand_fftconv_bwd_workspace_bytes", "hyenand_fftconv_bwd_workspace_min_bytes",
            "hyenand_fftconv_bwd_traced", "hyenand_kernel_spectrum_circ_bytes", "hyenand_kernel_spectrum_circ_tile",
            "hyenand_kernel_spectrum_circ", "hyenand_fftconv_circ_workspace_bytes",
-           "hyenand_fftconv_circ_workspace_min_bytes", "hyenand_fftconv_fwd_circ", "hyenand_fftconv_fwd_circ_traced")
+           "hyenand_fftconv_circ_workspace_min_bytes", "hyenand_fftconv_fwd_circ", "hyenand_fftconv_fwd_circ_traced",
+           "hyenand_fftconv_fwd_per_sample", "hyenand_fftconv_fwd_per_sample_traced")
 
 _lib = None
 
@@ -101,6 +104,11 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_fwd_circ.restype = I
     lib.hyenand_fftconv_fwd_circ_traced.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I, ctypes.POINTER(I)]
     lib.hyenand_fftconv_fwd_circ_traced.restype = I
+    lib.hyenand_fftconv_fwd_per_sample.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_fftconv_fwd_per_sample.restype = I
+    lib.hyenand_fftconv_fwd_per_sample_traced.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I,
+                                                          ctypes.POINTER(I)]
+    lib.hyenand_fftconv_fwd_per_sample_traced.restype = I
     _lib = lib
     return lib
 
@@ -438,4 +446,57 @@ def fftconv_fwd_circ_traced(x, alpha, beta, K_hat, y, workspace, events, stream=
     rc = get_lib().hyenand_fftconv_fwd_circ_traced(*args, _stream(stream), arr, len(events), ctypes.byref(n))
     if rc != OK:
         raise HyenandError(rc, "fftconv_fwd_circ_traced")
+    return int(n.value)
+
+
+# ------------------------------------------------------- per-sample kernels
+
+def kernel_spectrum_per_sample(K: torch.Tensor, stream=None) -> torch.Tensor:
+    """Input-dependent kernels K [B, C, *(2n-1)] (fp32, device) -> K_hat [B * C, ksz]."""
+    B, C = int(K.shape[0]), int(K.shape[1])
+    dims = tuple((v + 1) // 2 for v in K.shape[2:])
+    return kernel_spectrum(K.reshape((B * C,) + tuple(K.shape[2:])), dims, stream=stream)
+
+
+def _ps_args(x, alpha, beta, K_hat, y, workspace):
+    if not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous device tensor")
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    for t, nm in ((alpha, "alpha"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
+    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum_per_sample")
+    if K_hat.numel() * 8 < spectrum_bytes(B * C, dims):
+        raise ValueError("K_hat must hold B * C spectra of this shape")
+    y = torch.empty_like(x) if y is None else y
+    if workspace is None:
+        workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    return [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
+            B, C, len(dims), _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()), ws_bytes], y
+
+
+def fftconv_fwd_per_sample(x, alpha, beta, K_hat, y=None, workspace=None, stream=None) -> torch.Tensor:
+    """Gated N-D convolution with one kernel per (b, c) (K_hat from kernel_spectrum_per_sample)."""
+    args, y = _ps_args(x, alpha, beta, K_hat, y, workspace)
+    rc = get_lib().hyenand_fftconv_fwd_per_sample(*args, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd_per_sample")
+    return y
+
+
+def fftconv_fwd_per_sample_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None) -> int:
+    args, y = _ps_args(x, alpha, beta, K_hat, y, workspace)
+    st = torch.cuda.current_stream() if stream is None else stream
+    for e in events:
+        if e.cuda_event == 0:
+            e.record(st)
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    n = ctypes.c_int(0)
+    rc = get_lib().hyenand_fftconv_fwd_per_sample_traced(*args, _stream(stream), arr, len(events), ctypes.byref(n))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd_per_sample_traced")
     return int(n.value)

@@ -132,7 +132,7 @@ size_t hyenand_fftconv_circ_workspace_min_bytes(int B, int C, int d, const int64
 
 static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y, int B,
                             int C, int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
-                            void* stream, LaunchTrace* trace, bool circ)
+                            void* stream, LaunchTrace* trace, bool circ, bool per_sample = false)
 {
     if (B < 0 || C < 0) return HYENAND_ERR_INVALID_ARG;
     if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
@@ -157,6 +157,7 @@ static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta
     a.alpha = alpha;
     a.beta = beta;
     a.khat = static_cast<const float2*>(K_hat);
+    a.khat_bstride = per_sample ? (long long)C * g.ksz : 0;
     a.ws = static_cast<float2*>(workspace);
     a.g = g;
     a.B = B;
@@ -328,6 +329,28 @@ int hyenand_fftconv_bwd_traced(const void* x, const float* phi_alpha, const floa
     LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
     const int rc = fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
                                     workspace, workspace_bytes, stream, &tr);
+    if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
+    return rc;
+}
+
+// ------------------------------------------------------- per-sample kernels
+int hyenand_fftconv_fwd_per_sample(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y,
+                                   int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream)
+{
+    return fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes, stream,
+                            nullptr, false, true);
+}
+
+int hyenand_fftconv_fwd_per_sample_traced(const void* x, const float* alpha, const float* beta, const void* K_hat,
+                                          void* y, int B, int C, int d, const int64_t* dims, int dtype,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* const* events, int n_events, int* n_launches)
+{
+    if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
+    LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
+    const int rc = fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, workspace, workspace_bytes,
+                                    stream, &tr, false, true);
     if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
     return rc;
 }

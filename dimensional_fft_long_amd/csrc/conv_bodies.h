@@ -470,7 +470,7 @@ __host__ __device__ __forceinline__ OutView out_view(const ConvArgs& a, int item
     v.o = out_tile<NR, TW>(g, a.B, a.nch, item);
     v.k0 = v.o.t * TW;
     v.u0 = v.k0 & (g.lt - 1);
-    v.kc = a.khat + (long long)(a.c0 + v.o.c_local) * g.ksz;
+    v.kc = a.khat + (long long)(a.c0 + v.o.c_local) * g.ksz + (long long)v.o.b * a.khat_bstride;
     v.kt = v.kc + (long long)(v.k0 >> g.lt_log) * ((long long)g.N_out * g.N_mid * g.lt);
     v.base = a.ws + ((long long)v.o.c_local * a.B + v.o.b) * g.wsp + (long long)(v.k0 >> g.lt_log) * ws_tile_stride(g);
     return v;
@@ -769,8 +769,8 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
             const int cb = m.valid1 ? a.c0 + qb / a.B : ca, bb = m.valid1 ? qb % a.B : ba;
             m.o0 = ((long long)ba * a.C + ca) * g.vox;
             m.o1 = ((long long)bb * a.C + cb) * g.vox;
-            m.w0 = (long long)ca * g.ksz;
-            m.w1 = (long long)cb * g.ksz;
+            m.w0 = (long long)ca * g.ksz + (long long)ba * a.khat_bstride;
+            m.w1 = (long long)cb * g.ksz + (long long)bb * a.khat_bstride;
             m.al0 = a.alpha[ca]; m.be0 = a.beta[ca];
             m.al1 = a.alpha[cb]; m.be1 = a.beta[cb];
         }

@@ -161,6 +161,8 @@ struct ConvArgs {
     const float* alpha;     // [C]
     const float* beta;      // [C]
     const float2* khat;     // [C][ksz] (kernel spectrum) -- written by the spectrum kernels
+    long long khat_bstride; // complex values between batch entries of a per-sample spectrum
+                            // ([B][C][ksz]: C * ksz), 0 when one spectrum serves the batch
     float2* ws;             // workspace, [pairs in chunk][wsp]
     const float* K;         // spectrum input: [C][ke_out][ke_mid][ke_in] fp32
     Geom g;

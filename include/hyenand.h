@@ -234,6 +234,29 @@ int hyenand_fftconv_fwd_circ_traced(const void* x, const float* phi_alpha, const
                                     void* workspace, size_t workspace_bytes, void* stream, void* const* events,
                                     int n_events, int* n_launches);
 
+/*
+ * Input-dependent kernels.  The gist.science summary ("Methodology", "Input
+ * dependent kernels via registers and FiLM", "Kernel synthesis") conditions
+ * the kernel on the whole input sample, K(x) = w(c) * f(c; z(x)), so every
+ * batch entry has its own kernel while the FFT path stays the same:
+ *
+ *     y[b,c,i] = sum_{j in G} phi_c(x[b,c,j]) x[b,c,j] K_{b,c}[i - j].
+ *
+ * K_hat here holds B * C spectra in the order [B][C]: it is the output of
+ * hyenand_kernel_spectrum called on the kernels [B * C][2n-1 ...] (batch entry
+ * major), hyenand_kernel_spectrum_bytes(B * C, d, dims) bytes.  Everything
+ * else (arguments, workspace, errors) is as for hyenand_fftconv_fwd; the
+ * zero-padded boundary only.
+ */
+int hyenand_fftconv_fwd_per_sample(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                                   void* y, int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+/* hyenand_fftconv_fwd_per_sample with the launch trace of hyenand_fftconv_fwd_traced. */
+int hyenand_fftconv_fwd_per_sample_traced(const void* x, const float* phi_alpha, const float* phi_beta,
+                                          const void* K_hat, void* y, int B, int C, int d, const int64_t* dims,
+                                          int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                                          void* const* events, int n_events, int* n_launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,10 @@ Routes (all fp64, in ``oracle.c``):
   * ``direct_circ`` / ``fftconv_circ`` -- the circular mode (summary, "Boundary
     handling": periodic grids, no padding): y[i] = sum_j u[j] K[(i-j) mod n]
     with K stored [C, *dims], index m = offset mod n.
+  * ``direct_per_sample`` / ``fftconv_per_sample`` -- input-dependent kernels
+    (summary, "Input dependent kernels via registers and FiLM": the kernel is
+    conditioned on the whole sample): y[b,c,i] = sum_j u[b,c,j] K[b,c][i-j],
+    K [B, C, *(2n-1)]; O1 / O2 applied per batch entry with that entry's kernels.
   * ``bwd_direct`` / ``bwd_points`` / ``bwd_fft`` -- the backward (vector-Jacobian
     product, explainer section "Implementation and operation patterns", item
     "Concrete implementation pattern (PyTorch)": gradients of the input and of
@@ -170,6 +174,23 @@ def kernel_spectrum(K, dims) -> np.ndarray:
     im = np.empty(shape, dtype=np.float64)
     _check(_load().oracle_kernel_spectrum(_ptr(K), C, d, _ptr(dd), _ptr(re), _ptr(im)), "kernel_spectrum")
     return re + 1j * im
+
+
+def direct_per_sample(x, alpha, beta, K) -> np.ndarray:
+    """O1 with one kernel per (b, c): K [B, C, *(2n-1)] -> fp64 [B, C, *dims]."""
+    x, K = _f32(x), _f32(K)
+    if K.shape[:2] != x.shape[:2]:
+        raise ValueError("per-sample kernels are [B, C, *(2n-1)]")
+    return np.concatenate([direct(x[b:b + 1], alpha, beta, K[b]) for b in range(x.shape[0])], axis=0)
+
+
+def fftconv_per_sample(x, alpha, beta, K, batch=None) -> np.ndarray:
+    """O2 with one kernel per (b, c), for the listed batch entries (all when None): fp64 [len, C, *dims]."""
+    x, K = _f32(x), _f32(K)
+    if K.shape[:2] != x.shape[:2]:
+        raise ValueError("per-sample kernels are [B, C, *(2n-1)]")
+    bs = range(x.shape[0]) if batch is None else batch
+    return np.concatenate([fftconv(x[b:b + 1], alpha, beta, K[b]) for b in bs], axis=0)
 
 
 def direct_circ(x, alpha, beta, K) -> np.ndarray:

@@ -308,3 +308,24 @@ def test_pins_reject_mutants(mutant):
         if np.max(np.abs(y - _shifted(u, shift))) > 1e-9:
             fails += 1
     assert fails > 0, "the shifted-delta pin accepted a planted mistake"
+
+
+# ------------------------------------------------ input-dependent kernels
+
+def test_per_sample_kernels_match_brute_force():
+    """One kernel per (b, c) (the summary's kernels conditioned on the input
+    sample): the per-sample routes against the pure-Python brute force run
+    with each batch entry's own kernels, and identical kernels across the
+    batch reduce to the shared-kernel oracle."""
+    dims = (3, 4)
+    x, a, b, _ = _rand_case(dims, C=2, B=3, seed=21)
+    rng = np.random.default_rng(22)
+    K = rng.standard_normal((3, 2) + tuple(2 * n - 1 for n in dims)).astype(np.float32)
+    want = np.concatenate([_brute(x[i:i + 1], a, b, K[i]) for i in range(3)], axis=0)
+    assert _rel(oracle.direct_per_sample(x, a, b, K), want) < 1e-12
+    dims2 = (4, 8)
+    x2, a2, b2, K2 = _rand_case(dims2, C=2, B=2, seed=23)
+    Kb = np.stack([K2, K2 * 0.5 + 1.0])
+    got = oracle.fftconv_per_sample(x2, a2, b2, Kb)
+    assert _rel(got[0], oracle.direct(x2[:1], a2, b2, K2)[0]) < 1e-12
+    assert _rel(got[1], oracle.direct(x2[1:], a2, b2, Kb[1])[0]) < 1e-12
