@@ -274,8 +274,14 @@ def main():
     be = torch.from_numpy(p.beta).to(dev)
     torch.cuda.synchronize()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def spectrum():
+        return H.kernel_spectrum_circ(K) if circ else (H.kernel_spectrum_per_sample(K) if ps else H.kernel_spectrum(K))
+
+    kh = spectrum()  # the first call also loads the spectrum kernels' code
+    torch.cuda.synchronize()
     s0.record()
-    kh = H.kernel_spectrum_circ(K) if circ else (H.kernel_spectrum_per_sample(K) if ps else H.kernel_spectrum(K))
+    kh = spectrum()
     s1.record()
     torch.cuda.synchronize()
     spectrum_ms = s0.elapsed_time(s1)
