@@ -98,14 +98,17 @@ struct Geom {
 // Slot tile of the kernel spectrum and the workspace: the out-axis kernel's
 // tile width (capped at S), so that each out-axis workgroup's block of a 2-D
 // plane is contiguous.  In 3-D the workgroup's two mirrored k_mid rows stay
-// apart whatever the tile; there tiles of 16 slots (128-byte runs) win on
-// MI355X (128^3: 1.97 -> 1.91 ms) but 8-slot tiles lose to plain rows (512^3:
-// 24.7 -> 26.0 ms), so narrower out-axis tiles keep one tile of S slots.
+// apart whatever the tile, and consecutive out-axis positions of a tile are
+// N_mid * T slots apart: there tiles of 16 slots (128-byte runs) serve the
+// 16-line out-axis tiles (128^3: 1.97 -> 1.91 ms against plain rows; 32 or 64
+// slots give no gain), and the 8-line tiles of 1024-point lines take 64-slot
+// tiles (512^3 per call: plain rows 25.5, 16 slots 23.8, 32 slots 22.0,
+// 64 slots 21.3, 128 slots 21.7, 256 slots 23.9 ms).
 constexpr int slot_tile(int d, int N_out, int S)
 {
     int tw = S;
     if (d == 2) tw = out_tw(N_out, 1);
-    if (d == 3 && out_tw(N_out, 2) >= 16) tw = out_tw(N_out, 2);
+    if (d == 3) tw = out_tw(N_out, 2) >= 16 ? out_tw(N_out, 2) : 64;
     return tw < S ? tw : S;
 }
 

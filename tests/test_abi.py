@@ -78,7 +78,7 @@ def test_spectrum_slot_tile(H):
     assert lib.hyenand_kernel_spectrum_tile(2, _dims(1024, 1024)) == 8     # 2048-point: 16384 / 2048
     assert lib.hyenand_kernel_spectrum_tile(2, _dims(512, 4)) == 4         # capped at S = 4
     assert lib.hyenand_kernel_spectrum_tile(3, _dims(128, 128, 128)) == 16  # 256-point, two mirrored rows
-    assert lib.hyenand_kernel_spectrum_tile(3, _dims(512, 512, 512)) == 512  # 8-slot out tiles: plain rows
+    assert lib.hyenand_kernel_spectrum_tile(3, _dims(512, 512, 512)) == 64   # 8-line out tiles: 64-slot tiles
     assert lib.hyenand_kernel_spectrum_tile(1, _dims(64)) == 64
     for d in (1, 2, 3):
         for e in range(1, 11):
