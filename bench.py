@@ -106,6 +106,22 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
     elif name == "conv1d_bwd":
         by = 3 * P * g["vox"] * es + nch * g["ksz"] * 8 + P * 8
         fl = 2 * _fft_flops(g["Ni"], P / 2, 1) + P * g["S"] * (6 + 4) + P * g["vox"] * 14
+    # ---- long 1-D (four-step: N = 2n = N1 x N2, complex arithmetic)
+    elif name == "lng_col_fwd":
+        N = 2 * g["ni"]
+        N2 = min(N // 4, 2048)
+        by = P * g["vox"] * es + P * N * 8
+        fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6 + P * g["vox"] * 5
+    elif name == "lng_row":
+        N = 2 * g["ni"]
+        N2 = min(N // 4, 2048)
+        by = 2 * P * N * 8 + nch * N * 8
+        fl = 2 * P * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 6
+    elif name == "lng_col_inv":
+        N = 2 * g["ni"]
+        N2 = min(N // 4, 2048)
+        by = P * N * 8 + P * g["vox"] * es
+        fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6
     elif name == "corr1d":
         by = 2 * P * g["vox"] * es + P * g["S"] * 8
         fl = _fft_flops(g["Ni"], P, 1) + P * g["S"] * 10 + P * g["vox"] * 5
@@ -118,7 +134,8 @@ KERNEL_LABEL = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_co
                 "col_mid_inv": "k_col_mid", "conv1d": "k_conv1d", "row_fwd_dy": "k_row_fwd", "row_fwd_u": "k_row_fwd",
                 "col_mid_fwd_dy": "k_col_mid", "col_mid_fwd_u": "k_col_mid", "col_out_bwd": "k_col_out_bwd",
                 "row_inv_bwd": "k_row_inv", "gate_reduce": "k_gate_reduce", "mid_inv_dk": "k_plane_mid_inv",
-                "dk_row": "k_dk_row", "conv1d_bwd": "k_conv1d", "corr1d": "k_corr1d"}
+                "dk_row": "k_dk_row", "conv1d_bwd": "k_conv1d", "corr1d": "k_corr1d", "lng_col_fwd": "k_lng_col_fwd",
+                "lng_row": "k_lng_row", "lng_col_inv": "k_lng_col_inv"}
 
 
 def _src_hash():
@@ -389,8 +406,10 @@ def main():
         else:
             nch = wl.C
         plan = {"chunk_channels": nch}
-        bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8 * (wl.B if ps else 1)
-        names = H.PASS_NAMES[wl.d]
+        long1d = wl.d == 1 and wl.dims[0] > 1024
+        ksz = 2 * wl.dims[0] if long1d else g["ksz"]
+        bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * ksz * 8 * (wl.B if ps else 1)
+        names = ("lng_col_fwd", "lng_row", "lng_col_inv") if long1d else H.PASS_NAMES[wl.d]
     per_pass = {nm: [] for nm in names}
     step_ms = []
     for k in range(args.steps):

@@ -23,14 +23,14 @@ struct CallPlan {
 CallPlan plan_call(const Geom& g, int B, int C, size_t ws_bytes)
 {
     CallPlan cp{C, 1, 1};
-    if (g.d == 1) return cp;
+    if (g.d == 1 && !g.lng) return cp;
     int per = chunk_channels(g, B, C, ws_bytes);
     if (per > C) per = C;
     if (per < 1) per = 1;
     const int chunks = (C + per - 1) / per;
     cp.per = (C + chunks - 1) / chunks;
     cp.chunks = (C + cp.per - 1) / cp.per;
-    cp.launches = cp.chunks * (g.d == 3 ? 5 : 3);
+    cp.launches = cp.chunks * (g.d == 3 ? 5 : 3);  // long 1-D: column, row, column
     return cp;
 }
 
@@ -236,14 +236,16 @@ int hyenand_fftconv_fwd_circ_traced(const void* x, const float* alpha, const flo
 size_t hyenand_fftconv_bwd_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
 {
     Geom g;
-    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g) || g.lng)
+        return 0;
     return recommended_bwd_workspace(g, B, C, with_dK != 0);
 }
 
 size_t hyenand_fftconv_bwd_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
 {
     Geom g;
-    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g)) return 0;
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g) || g.lng)
+        return 0;
     return bwd_channel_bytes(g, B, with_dK != 0);
 }
 
@@ -257,7 +259,7 @@ static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta
     if (d < 1 || d > 3) return HYENAND_ERR_UNSUPPORTED;
     if (!dims) return HYENAND_ERR_INVALID_ARG;
     Geom g;
-    if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
+    if (!make_geom(d, dims, &g) || g.lng) return HYENAND_ERR_UNSUPPORTED;
     if (C == 0) return HYENAND_OK;
     if (!dalpha || !dbeta || !aligned(dalpha, 4) || !aligned(dbeta, 4) || (dK && !aligned(dK, 4)))
         return HYENAND_ERR_INVALID_ARG;

@@ -1240,4 +1240,145 @@ __host__ __device__ __forceinline__ void dk_row_body(const Ctx& ctx, int bid, co
     }
 }
 
+// ============================================================= long 1-D
+// Signals longer than one workgroup's transform (n > 1024): the padded length
+// N = 2n is factored as N1 x N2 (sample m = N2 n1 + n2), and
+//   X[k1 + N1 k2] = sum_n2 W_N2^(n2 k2) W_N^(n2 k1) sum_n1 x[N2 n1 + n2] W_N1^(n1 k1)
+// (the four-step decomposition of a length-N DFT): column transforms of N1
+// points, the twiddle W_N^(n2 k1), row transforms of N2 points; the inverse
+// runs the same steps backwards with conjugate twiddles.  Zero padding makes
+// the rows n1 >= N1/2 zero on input and unused on output, so the column
+// transforms prune their first / last pass.  Arithmetic is complex throughout
+// (the real input occupies the real parts).  The spectrum of frequency
+// k1 + N1 k2 is stored at row k1, column k2, scaled by 1/N: the workspace and
+// the spectrum share the N1 x N2 layout, so the product is elementwise.
+
+// Step 1 (and the spectrum's first step with SPEC): TW adjacent columns per
+// workgroup, N1-point forward transforms, twiddled, into rows k1.
+// Forward: gated x, rows n1 < N1/2 read (pruned), workspace of pair q.
+// SPEC: the kernel wrap-placed at offset delta -> delta mod N (index n empty),
+// all rows read, into the spectrum of channel q.
+template <int L, bool SPEC, bool BF16, class Ctx>
+__host__ __device__ __forceinline__ void lng_col_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = col_tw(L), NT = col_nt(L);
+    const Geom& g = a.g;
+    const int N2 = g.N2;
+    const int tpp = N2 / TW;
+    const int q = bid / tpp, n20 = (bid % tpp) * TW;
+    const unsigned nmask = (1u << g.logN) - 1u;
+    float2* dst = SPEC ? const_cast<float2*>(a.khat) + (long long)q * g.ksz : a.ws + (long long)q * g.wsp;
+    long long xo = 0;
+    float al = 0.f, be = 0.f;
+    if constexpr (!SPEC) {
+        const int c = a.c0 + q / a.B, b = q % a.B;
+        xo = ((long long)b * a.C + c) * g.vox;
+        al = a.alpha[c];
+        be = a.beta[c];
+    }
+    auto ld = [&](int pos, int l) -> float2 {
+        const long long m = (long long)N2 * pos + n20 + l;
+        if constexpr (SPEC) {
+            const int dl = unwrap((int)m, g.n_in, g.N_in);
+            return make_float2(dl == kEmpty ? 0.f : a.K[(long long)q * g.ke_in + dl + g.n_in - 1], 0.f);
+        } else {
+            return make_float2(ctx.gate(load_x<BF16>(a, xo + m), al, be), 0.f);
+        }
+    };
+    auto st = [&](int pos, int l, const float2& v) {
+        const unsigned e = ((unsigned)(n20 + l) * (unsigned)pos) & nmask;
+        dst[(long long)pos * N2 + n20 + l] = cmul(v, ctx.twiddle(e, g.logN));
+    };
+    auto after_load = [&]() { ctx.stage(); };
+    fwd_fn_to_fn<L, TW, NT, !SPEC>(ctx, T, ld, st, after_load);
+}
+
+// Step 2: NP rows k1 per workgroup, N2 points each.  Forward: forward
+// transform, product with the spectrum row, inverse transform, in place.
+// SPEC: forward transform scaled by 1/N, in place in the spectrum.
+template <int L, bool SPEC, class Ctx>
+__host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
+    constexpr int ITER = NP * L / NT;
+    static_assert(NP * L % NT == 0, "whole element loops");
+    const Geom& g = a.g;
+    const int N1 = g.N1;
+    const int H = (SPEC ? a.C : a.nch * a.B) * N1;
+    const int tid = ctx.tid();
+    ctx.stage();
+    auto row_base = [&](int lp) -> float2* {
+        const int h = bid * NP + lp, q = h / N1, k1 = h % N1;
+        return (SPEC ? const_cast<float2*>(a.khat) + (long long)q * g.ksz : a.ws + (long long)q * g.wsp) +
+               (long long)k1 * L;
+    };
+    float2 v[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+        v[i] = bid * NP + lp < H ? row_base(lp)[pos] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+        T[pos * LP + lp] = v[i];
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, false, false, false>(ctx, T);
+    if constexpr (SPEC) {
+        const float sc = 1.0f / (float)(1ll << g.logN);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+            if (bid * NP + lp < H) row_base(lp)[pos] = cscale(T[pos * LP + lp], sc);
+        }
+    } else {
+        // The spectrum row of this (b, c) pair: channel c, batch entry b (per-sample spectra: b * bstride).
+        float2 kv[ITER];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / L, pos = idx % L, h = bid * NP + lp;
+            const int q = h / N1, k1 = h % N1;
+            const int c = a.c0 + q / a.B, b = q % a.B;
+            kv[i] = h < H ? a.khat[(long long)c * g.ksz + (long long)b * a.khat_bstride + (long long)k1 * L + pos]
+                          : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+            T[pos * LP + lp] = cmul(T[pos * LP + lp], kv[i]);
+        }
+        ctx.sync();
+        tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+            if (bid * NP + lp < H) row_base(lp)[pos] = T[pos * LP + lp];
+        }
+    }
+}
+
+// Step 3: TW adjacent columns per workgroup: conjugate twiddle, inverse
+// N1-point transforms keeping rows n1 < N1/2 (the crop), real part to y.
+template <int L, bool BF16, class Ctx>
+__host__ __device__ __forceinline__ void lng_col_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = col_tw(L), NT = col_nt(L);
+    const Geom& g = a.g;
+    const int N2 = g.N2;
+    const int tpp = N2 / TW;
+    const int q = bid / tpp, n20 = (bid % tpp) * TW;
+    const unsigned nmask = (1u << g.logN) - 1u;
+    const float2* src = a.ws + (long long)q * g.wsp;
+    const int c = a.c0 + q / a.B, b = q % a.B;
+    const long long yo = ((long long)b * a.C + c) * g.vox;
+    auto ld = [&](int pos, int l) -> float2 {
+        const unsigned e = ((unsigned)(n20 + l) * (unsigned)pos) & nmask;
+        return cmulc(src[(long long)pos * N2 + n20 + l], ctx.twiddle(e, g.logN));
+    };
+    auto st = [&](int pos, int l, const float2& v) { store_y<BF16>(a, yo + (long long)N2 * pos + n20 + l, v.x); };
+    auto after_load = [&]() { ctx.stage(); };
+    inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
+}
+
 }  // namespace hyenand

@@ -36,6 +36,14 @@ struct DevCtx {
     {
         return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * 1.44269504088896341f));
     }
+    // exp(-2 pi i e / N), N = 2^logN, e < N: the exact fraction e / N through
+    // sincospi (accurate to a few ulp over the whole circle).
+    __device__ float2 twiddle(unsigned e, int logN) const
+    {
+        float sn, cs;
+        sincospif(2.0f * __builtin_ldexpf((float)e, -logN), &sn, &cs);
+        return make_float2(cs, -sn);
+    }
     // Two halves so that callers can issue other loads in between: every
     // load of the copy is issued before the first store.
     static constexpr int kTwSize = tw_table_size<L, PLANS>();
@@ -135,6 +143,30 @@ __global__ __launch_bounds__(row_nt(L)) void k_dk_row(ConvArgs a)
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
     dk_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+}
+
+template <int L, bool SPEC, bool BF16>
+__global__ __launch_bounds__(col_nt(L)) void k_lng_col_fwd(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * col_tw(L)];
+    lng_col_fwd_body<L, SPEC, BF16>(make_ctx<L, col_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
+}
+
+template <int L, bool SPEC>
+__global__ __launch_bounds__(row_nt(L)) void k_lng_row(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * row_lp(L)];
+    lng_row_body<L, SPEC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
+}
+
+template <int L, bool BF16>
+__global__ __launch_bounds__(col_nt(L)) void k_lng_col_inv(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanR>()];
+    __shared__ float2 T[L * col_tw(L)];
+    lng_col_inv_body<L, BF16>(make_ctx<L, col_nt(L), kPlanR>(TWL), (int)blockIdx.x, a, T);
 }
 
 constexpr int kReduceNT = 1024;
@@ -303,8 +335,52 @@ static hipError_t forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
     });
 }
 
+// Row lengths of the long 1-D path: N2 in {1024, 2048}.
+template <class F>
+static hipError_t with_row_length(int L, F&& f)
+{
+    switch (L) {
+    case 1024: return f.template operator()<1024>();
+    case 2048: return f.template operator()<2048>();
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Long 1-D forward (and, with SPEC, the spectrum): column pass, row pass, column pass.
+static hipError_t long1d_chunk(const ConvArgs& a, bool spec, hipStream_t st, LaunchTrace* tr)
+{
+    auto mark = [&]() { if (tr) tr->mark(st); };
+    const Geom& g = a.g;
+    const long long sigs = spec ? a.C : (long long)a.nch * a.B;
+    hipError_t e = with_length(g.N1, [&]<int L>() {
+        const unsigned grid = (unsigned)(sigs * (g.N2 / col_tw(L)));
+        mark();
+        if (spec) hipLaunchKernelGGL((k_lng_col_fwd<L, true, false>), dim3(grid), dim3(col_nt(L)), 0, st, a);
+        else if (a.bf16) hipLaunchKernelGGL((k_lng_col_fwd<L, false, true>), dim3(grid), dim3(col_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_lng_col_fwd<L, false, false>), dim3(grid), dim3(col_nt(L)), 0, st, a);
+        return last_error();
+    });
+    if (e != hipSuccess) return e;
+    e = with_row_length(g.N2, [&]<int L>() {
+        const unsigned grid = ceil_div(sigs * g.N1, row_np(L));
+        mark();
+        if (spec) hipLaunchKernelGGL((k_lng_row<L, true>), dim3(grid), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_lng_row<L, false>), dim3(grid), dim3(row_nt(L)), 0, st, a);
+        return last_error();
+    });
+    if (e != hipSuccess || spec) return e;
+    return with_length(g.N1, [&]<int L>() {
+        const unsigned grid = (unsigned)(sigs * (g.N2 / col_tw(L)));
+        mark();
+        if (a.bf16) hipLaunchKernelGGL((k_lng_col_inv<L, true>), dim3(grid), dim3(col_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_lng_col_inv<L, false>), dim3(grid), dim3(col_nt(L)), 0, st, a);
+        return last_error();
+    });
+}
+
 hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
 {
+    if (a.g.lng) return long1d_chunk(a, false, st, tr);
     return a.g.circ ? forward_chunk<true>(a, st, tr) : forward_chunk<false>(a, st, tr);
 }
 
@@ -415,6 +491,7 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
 hipError_t launch_spectrum(const ConvArgs& a, hipStream_t st)
 {
     const Geom& g = a.g;
+    if (g.lng) return long1d_chunk(a, true, st, nullptr);
     hipError_t e;
     const long long H = g.d == 1 ? ((long long)a.C + 1) / 2 : (long long)a.C * (g.N_out * g.N_mid / 2);
     e = with_length(g.N_in, [&]<int L>() {

@@ -93,6 +93,12 @@ struct Geom {
     int ke_out, ke_mid, ke_in;  // kernel extents 2n-1 (1 for absent axes); n when circular
     int lt, lt_log;        // slot tile of the tile-major planes (a power of two <= S)
     int circ;              // circular mode: periodic grid, N = n, no padding or crop
+    // Long 1-D signals (n > 1024): the padded length N = 2n is transformed as an
+    // N1 x N2 array (sample m = N2 * n1 + n2) -- column transforms of N1
+    // points, a twiddle, row transforms of N2 points -- and the spectrum value
+    // of frequency k1 + N1 k2 sits at row k1, column k2.
+    int lng;               // 1 for the long 1-D path
+    int N1, N2, logN;      // column / row transform lengths, log2 N
 };
 
 // Slot tile of the kernel spectrum and the workspace: the out-axis kernel's
@@ -123,7 +129,8 @@ __host__ __device__ __forceinline__ long long tm_index(const Geom& g, long long 
 inline bool is_pow2(long long v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Returns false for an unsupported shape: d in {1,2,3}, every n a power of two
-// in [2, 1024] ([4, 1024] in circular mode, whose transforms have length n).
+// in [2, 1024] ([4, 1024] in circular mode, whose transforms have length n);
+// d = 1 (zero-padded) also takes n up to 2^21 through the long 1-D path.
 //
 // Circular mode (gist.science summary, "Methodology", "Boundary handling":
 // circular convolutions for periodic systems): every axis keeps N = n, the
@@ -132,6 +139,33 @@ inline bool is_pow2(long long v) { return v > 0 && (v & (v - 1)) == 0; }
 inline bool make_geom(int d, const int64_t* dims, Geom* g, bool circ = false)
 {
     if (d < 1 || d > 3 || !dims) return false;
+    *g = Geom{};
+    if (d == 1 && !circ && dims[0] > 1024) {
+        // Long 1-D: n a power of two up to 2^21 (N1, N2 <= 2048).
+        const long long n = dims[0];
+        if (!is_pow2(n) || n > (1ll << 21)) return false;
+        const long long N = 2 * n;
+        g->d = 1;
+        g->lng = 1;
+        g->N2 = (int)(N / 4 < 2048 ? N / 4 : 2048);
+        g->N1 = (int)(N / g->N2);
+        g->logN = 0;
+        while ((1ll << g->logN) < N) ++g->logN;
+        g->n_out = g->n_mid = 1;
+        g->n_in = (int)n;
+        g->N_out = g->N_mid = 1;
+        g->N_in = (int)N;
+        g->S = (int)n;
+        g->vox = n;
+        g->wsp = N;
+        g->kmain = N;
+        g->ksz = N;
+        g->ke_out = g->ke_mid = 1;
+        g->ke_in = (int)(2 * n - 1);
+        g->lt = 1;
+        g->lt_log = 0;
+        return true;
+    }
     for (int a = 0; a < d; ++a)
         if (dims[a] < (circ ? 4 : 2) || dims[a] > 1024 || !is_pow2(dims[a])) return false;
     g->d = d;

@@ -67,6 +67,8 @@ WORKLOADS = [
     Workload("2d_1024x1024_b2_c128_bf16", (1024, 1024), 2, 128, "bf16", 1002),
     Workload("3d_128x128x128_b1_c32_f32", (128, 128, 128), 1, 32, "f32", 1003),
     Workload("3d_512x512x512_b1_c4_bf16", (512, 512, 512), 1, 4, "bf16", 1004),
+    # long 1-D sequence (the summary's genomics context, "Results": throughput up to 10M tokens)
+    Workload("1d_2097152_b1_c8_bf16", (2097152,), 1, 8, "bf16", 1005),
 ]
 
 
@@ -128,6 +130,17 @@ def kernel_channels(dims, p: Params, channels=None, device="cpu", out=None):
     lam = torch.tensor(p.lam[chans], dtype=f64, device=dev)
     offs = [torch.arange(-(n - 1), n, dtype=f64, device=dev) for n in dims]
     chat = [o / (n - 1) if n > 1 else torch.zeros_like(o) for o, n in zip(offs, dims)]
+    if d == 1:
+        # One axis: evaluate the offsets in blocks (a slab per offset would be
+        # millions of tiny steps for long signals).
+        step = 1 << 18
+        for s0 in range(0, ext[0], step):
+            o, ch = offs[0][s0:s0 + step], chat[0][s0:s0 + step]
+            h = torch.sin(OMEGA0 * (b1.reshape(HIDDEN, 1) + W1[:, 0].reshape(HIDDEN, 1) * ch.reshape(1, -1)))
+            mlp = torch.tensordot(W2, h, dims=([1], [0]))             # [C', block]
+            win = torch.exp(-lam.reshape(-1, 1) * torch.sqrt(o ** 2).reshape(1, -1))
+            out[:, s0:s0 + step] = (mlp * win).to(torch.float32)
+        return out
     # Contribution of the trailing axes to the sine argument and to ||delta||^2.
     rest_arg = torch.zeros([HIDDEN] + ext[1:], dtype=f64, device=dev)
     rest_r2 = torch.zeros(ext[1:], dtype=f64, device=dev)

@@ -65,7 +65,7 @@ def test_sizes(H):
     assert rec == lib.hyenand_fftconv_workspace_bytes(8, 64, 2, _dims(256, 256), 0)
     assert lib.hyenand_fftconv_workspace_bytes(4, 4, 1, _dims(1024), 0) == 0  # 1-D needs none
     # Unsupported shapes size to 0.
-    for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(2048)), (4, _dims(2, 2, 2, 2))]:
+    for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(1 << 22)), (1, _dims(3 << 11)), (4, _dims(2, 2, 2, 2))]:
         assert lib.hyenand_kernel_spectrum_bytes(2, d, dims) == 0
         assert lib.hyenand_kernel_spectrum_tile(d, dims) == 0
 
@@ -199,3 +199,22 @@ def test_circular_sizes_and_rejects(H):
     assert call(x=None, y=None, B=0) == 0
     assert lib.hyenand_kernel_spectrum_circ(FAKE, FAKE, 2, 2, _dims(8, 2), None) == 2
     assert lib.hyenand_kernel_spectrum_circ(None, FAKE, 2, 2, _dims(8, 8), None) == 1
+
+
+def test_long_1d_sizes(H):
+    """1-D signals longer than 1024 take the long path: the full N = 2n complex
+    spectrum per channel (no Nyquist packing), N complex of workspace per pair,
+    three launches per channel chunk; no backward and no circular mode."""
+    lib = H.get_lib()
+    for n in (2048, 1 << 16, 1 << 21):
+        assert lib.hyenand_kernel_spectrum_bytes(3, 1, _dims(n)) == 3 * 2 * n * 8
+        assert lib.hyenand_fftconv_workspace_min_bytes(2, 3, 1, _dims(n), 0) == 2 * 2 * n * 8
+        assert lib.hyenand_fftconv_bwd_workspace_min_bytes(2, 3, 1, _dims(n), 0, 1) == 0
+        assert lib.hyenand_kernel_spectrum_circ_bytes(3, 1, _dims(n)) == 0
+    import torch
+
+    assert H.launch_plan(1, 4, (1 << 20,), torch.float32, 1 << 30)["launches"] == 3
+    assert H.launch_plan(2, 4, (1 << 20,), torch.float32, 2 * 2 * (1 << 20) * 8)["launches"] == 4 * 3
+    bw = lib.hyenand_fftconv_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, _dims(4096), 0, FAKE,
+                                 1 << 30, None)
+    assert bw == 2

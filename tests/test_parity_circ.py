@@ -53,7 +53,10 @@ def _gpu(H, x, al, be, K, workspace=None):
 SMALL = [((4,), 1, 1, "f32"), ((64,), 3, 3, "f32"), ((1024,), 2, 3, "f32"), ((256,), 1, 5, "bf16"),
          ((4, 4), 1, 1, "f32"), ((8, 4), 2, 3, "f32"), ((4, 16), 1, 2, "f32"), ((32, 32), 1, 4, "f32"),
          ((16, 64), 2, 2, "f32"), ((64, 16), 1, 3, "bf16"), ((4, 512), 1, 2, "f32"), ((512, 4), 1, 2, "f32"),
-         ((4, 4, 4), 1, 1, "f32"), ((4, 8, 16), 2, 3, "f32"), ((16, 4, 8), 1, 2, "f32"), ((8, 16, 8), 2, 3, "bf16")]
+         ((4, 4, 4), 1, 1, "f32"), ((4, 8, 16), 2, 3, "f32"), ((16, 4, 8), 1, 2, "f32"), ((8, 16, 8), 2, 3, "bf16"),
+         # maximum extents
+         ((1024, 4), 1, 2, "f32"), ((4, 1024), 2, 1, "bf16"), ((1024, 4, 4), 1, 1, "f32"), ((4, 1024, 4), 1, 1, "f32"),
+         ((4, 4, 1024), 1, 2, "f32")]
 
 
 @pytest.mark.parametrize("dims,B,C,dtype", SMALL, ids=lambda v: str(v))

@@ -1,0 +1,97 @@
+"""GPU parity of long 1-D convolutions (n > 1024: the four-step path) against
+the fp64 oracle.
+
+The gist.science summary ("Results", genomics) reports throughput up to 10M
+tokens for 1-D signals; here the zero-padded length N = 2n is factored as
+N1 x N2 (column transforms, twiddle, row transforms with the spectrum product)
+for n up to 2^21.  Bar as for the other forwards: max|y_gpu - y_ref| / max|y_ref|
+<= 1e-4 (fp32 I/O), <= 2e-2 (bf16 I/O).  Whole signals against the oracle's
+FFT route (O2) and sampled outputs against the direct sum (O1).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def H():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dimensional_fft_long_amd as H
+
+    H.get_lib()
+    return H
+
+
+def _rel(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+def _run(H, dims, B, C, dtype, seed, per_sample=False, workspace=None):
+    dev = torch.device("cuda:0")
+    p = synth.draw_params(dims, C, seed)
+    x = synth.draw_x(p.rng, B, C, dims, dtype)
+    K = synth.kernel_channels(dims, p, device=dev)
+    al, be = torch.from_numpy(p.alpha).to(dev), torch.from_numpy(p.beta).to(dev)
+    if per_sample:
+        scale = torch.linspace(0.5, 1.5, B, device=dev).reshape(B, 1, 1)
+        Kb = (K.unsqueeze(0) * scale).contiguous()
+        y = H.fftconv_fwd_per_sample(x.to(dev), al, be, H.kernel_spectrum_per_sample(Kb), workspace=workspace)
+        K = Kb
+    else:
+        y = H.fftconv_fwd(x.to(dev), al, be, H.kernel_spectrum(K), workspace=workspace)
+    torch.cuda.synchronize()
+    return x.float().numpy(), p, K.cpu().numpy(), y.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("n,B,C,dtype", [(2048, 2, 3, "f32"), (4096, 1, 2, "bf16"), (8192, 3, 2, "f32"),
+                                         (1 << 16, 2, 2, "f32"), (1 << 18, 1, 2, "bf16"), (1 << 20, 1, 2, "f32")],
+                         ids=lambda v: str(v))
+def test_matches_fft_oracle(H, n, B, C, dtype):
+    x, p, K, y = _run(H, (n,), B, C, dtype, seed=200 + n % 97 + B)
+    ref = oracle.fftconv(x, p.alpha, p.beta, K)
+    assert np.all(np.isfinite(y))
+    assert _rel(y, ref) <= TOL[dtype]
+
+
+def test_sampled_outputs_match_direct_sum(H):
+    n = 1 << 14
+    x, p, K, y = _run(H, (n,), 2, 2, "f32", seed=7)
+    pts = synth.sample_points((n,), 2, 2, [(0, 0), (1, 1)], 24, seed=7)
+    ref = oracle.direct_points(x, p.alpha, p.beta, K, pts)
+    got = np.array([y[tuple(r)] for r in pts])
+    assert _rel(got, ref) <= 1e-4
+
+
+def test_per_sample_kernels(H):
+    n = 1 << 13
+    x, p, Kb, y = _run(H, (n,), 3, 2, "f32", seed=8, per_sample=True)
+    ref = oracle.direct_per_sample(x, p.alpha, p.beta, Kb)
+    assert _rel(y, ref) <= 1e-4
+
+
+def test_every_chunking_gives_the_same_output(H):
+    n, B, C = 1 << 12, 2, 5
+    minb = H.workspace_bytes(B, C, (n,), torch.float32, minimum=True)
+    outs = [_run(H, (n,), B, C, "f32", seed=9, workspace=torch.empty(k * minb, dtype=torch.uint8, device="cuda"))[3]
+            for k in (1, 2, C)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.timeout(300)
+def test_workload_full_size(H):
+    """The 2M-token workload at full size (8 channels, bf16): two whole
+    channels against the FFT oracle."""
+    wl = synth.WORKLOADS[5]
+    x, p, K, y = _run(H, wl.dims, wl.B, wl.C, wl.dtype, seed=wl.seed)
+    for c in (0, wl.C - 1):
+        ref = oracle.fftconv(x[:, c:c + 1], p.alpha[c:c + 1], p.beta[c:c + 1], K[c:c + 1])
+        assert _rel(y[:, c], ref[:, 0]) <= TOL[wl.dtype], c
