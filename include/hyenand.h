@@ -28,7 +28,9 @@
  *       K_hat  library-defined complex64 layout, size from
  *              hyenand_kernel_spectrum_bytes (see below)
  *   - Supported shapes: d in {1, 2, 3}; every dims[a] a power of two in
- *     [2, 1024].  Other shapes return HYENAND_ERR_UNSUPPORTED.
+ *     [2, 1024]; for d = 1 also n a power of two up to 2^21 (long signals, the
+ *     summary's 1-D genomics context: see "Long 1-D signals" below).  Other
+ *     shapes return HYENAND_ERR_UNSUPPORTED.
  *   - Pointers must be aligned to their element size (x, y: 4 bytes for fp32,
  *     2 for bf16; alpha, beta, K: 4; K_hat, workspace: 8).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
@@ -81,6 +83,14 @@ int hyenand_version(void);
  * delta -> index delta mod N_a, and g = 1 / (2 * prod_a N_a).  (For d = 1 the
  * main block is simply [k_in].)  The slot tiles make each out-axis workgroup's
  * block of the spectrum contiguous.
+ *
+ * Long 1-D signals (d = 1, n > 1024): the padded length N = 2n is transformed
+ * as an N1 x N2 array, N2 = min(N/4, 2048), N1 = N / N2 (sample m = N2 n1 + n2;
+ * column transforms of N1 points, twiddle W_N^(n2 k1), row transforms of N2
+ * points).  K_hat holds N complex values per channel, the value of frequency
+ * k = k1 + N1 k2 at [k1][k2], equal to Khat(k) / N (no Nyquist packing).  The
+ * workspace minimum is B * N * 8 bytes (one channel); the backward and the
+ * circular mode do not take long signals (UNSUPPORTED).
  */
 size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims);
 
