@@ -109,17 +109,17 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
     # ---- long 1-D (four-step: N = 2n = N1 x N2, complex arithmetic)
     elif name == "lng_col_fwd":
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048)
+        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
         by = P * g["vox"] * es + P * N * 8
         fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6 + P * g["vox"] * 5
     elif name == "lng_row":
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048)
+        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
         by = 2 * P * N * 8 + nch * N * 8
         fl = 2 * P * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 6
     elif name == "lng_col_inv":
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048)
+        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
         by = P * N * 8 + P * g["vox"] * es
         fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6
     elif name == "corr1d":

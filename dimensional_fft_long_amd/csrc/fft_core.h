@@ -49,20 +49,21 @@ __host__ __device__ __forceinline__ float2 mul_mi(float2 a)
 }
 
 // ----------------------------------------------------------- twiddle table
-// W_2048^t = exp(-2 pi i t / 2048), t in [0, 2048), evaluated at compile time
+// W_4096^t = exp(-2 pi i t / 4096), t in [0, 4096), evaluated at compile time
 // in double precision (Taylor series of sin on the first quadrant, extended by
 // the quadrant symmetries) and rounded once to float.  Any power-of-two length
-// L <= 2048 uses W_L^s = W_2048^(s * 2048 / L).
-constexpr int TW_N = 2048;
+// L <= 4096 uses W_L^s = W_4096^(s * 4096 / L).  (4096-point transforms serve
+// the long 1-D path only.)
+constexpr int TW_N = 4096;
 
 struct TwTable {
     float2 w[TW_N];
 };
 
-// sin(pi * m / 1024) for m in [0, 512], by its Taylor series (|x| <= pi/2).
+// sin(pi * m / (TW_N / 2)) for m in [0, TW_N / 4], by its Taylor series (|x| <= pi/2).
 constexpr double quarter_sin(int m)
 {
-    const double x = 3.14159265358979323846264338327950288 * (double)m / 1024.0;
+    const double x = 3.14159265358979323846264338327950288 * (double)m / (double)(TW_N / 2);
     const double x2 = x * x;
     double term = x, sum = x;
     for (int k = 1; k < 16; ++k) {
@@ -75,9 +76,10 @@ constexpr double quarter_sin(int m)
 constexpr TwTable make_twiddles()
 {
     TwTable t{};
+    constexpr int Q = TW_N / 4;
     for (int i = 0; i < TW_N; ++i) {
-        const int q = i / 512, r = i % 512;
-        const double s = quarter_sin(r), c = quarter_sin(512 - r);
+        const int q = i / Q, r = i % Q;
+        const double s = quarter_sin(r), c = quarter_sin(Q - r);
         double cs = 0.0, sn = 0.0;
         if (q == 0) { cs = c; sn = s; }
         else if (q == 1) { cs = -s; sn = c; }
@@ -437,7 +439,7 @@ struct LdsPasses {
 template <int L, int NL, int LP, int NT, bool INV, bool PIN, bool POUT, class Ctx>
 __host__ __device__ __forceinline__ void tile_fft(const Ctx& ctx, float2* T)
 {
-    static_assert(L >= 2 && L <= TW_N && (L & (L - 1)) == 0, "power-of-two length up to 2048");
+    static_assert(L >= 2 && L <= TW_N && (L & (L - 1)) == 0, "power-of-two length up to 4096");
     constexpr int NP = plan_passes(L);
     constexpr int R0 = pass_radix<L, false>(0);
     PassRegs<L, R0, NL, NT> s;

@@ -335,15 +335,24 @@ static hipError_t forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
     });
 }
 
-// Row lengths of the long 1-D path: N2 in {1024, 2048}.
+// Transform lengths of the long 1-D path: rows N2 in {1024, 2048, 4096},
+// columns N1 in {4, ..., 4096}.
 template <class F>
 static hipError_t with_row_length(int L, F&& f)
 {
     switch (L) {
     case 1024: return f.template operator()<1024>();
     case 2048: return f.template operator()<2048>();
+    case 4096: return f.template operator()<4096>();
     default: return hipErrorInvalidValue;
     }
+}
+
+template <class F>
+static hipError_t with_col_length(int L, F&& f)
+{
+    if (L == 4096) return f.template operator()<4096>();
+    return with_length(L, f);
 }
 
 // Long 1-D forward (and, with SPEC, the spectrum): column pass, row pass, column pass.
@@ -352,7 +361,7 @@ static hipError_t long1d_chunk(const ConvArgs& a, bool spec, hipStream_t st, Lau
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
     const long long sigs = spec ? a.C : (long long)a.nch * a.B;
-    hipError_t e = with_length(g.N1, [&]<int L>() {
+    hipError_t e = with_col_length(g.N1, [&]<int L>() {
         const unsigned grid = (unsigned)(sigs * (g.N2 / col_tw(L)));
         mark();
         if (spec) hipLaunchKernelGGL((k_lng_col_fwd<L, true, false>), dim3(grid), dim3(col_nt(L)), 0, st, a);
@@ -369,7 +378,7 @@ static hipError_t long1d_chunk(const ConvArgs& a, bool spec, hipStream_t st, Lau
         return last_error();
     });
     if (e != hipSuccess || spec) return e;
-    return with_length(g.N1, [&]<int L>() {
+    return with_col_length(g.N1, [&]<int L>() {
         const unsigned grid = (unsigned)(sigs * (g.N2 / col_tw(L)));
         mark();
         if (a.bf16) hipLaunchKernelGGL((k_lng_col_inv<L, true>), dim3(grid), dim3(col_nt(L)), 0, st, a);

@@ -130,7 +130,7 @@ inline bool is_pow2(long long v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Returns false for an unsupported shape: d in {1,2,3}, every n a power of two
 // in [2, 1024] ([4, 1024] in circular mode, whose transforms have length n);
-// d = 1 (zero-padded) also takes n up to 2^21 through the long 1-D path.
+// d = 1 (zero-padded) also takes n up to 2^23 through the long 1-D path.
 //
 // Circular mode (gist.science summary, "Methodology", "Boundary handling":
 // circular convolutions for periodic systems): every axis keeps N = n, the
@@ -141,13 +141,14 @@ inline bool make_geom(int d, const int64_t* dims, Geom* g, bool circ = false)
     if (d < 1 || d > 3 || !dims) return false;
     *g = Geom{};
     if (d == 1 && !circ && dims[0] > 1024) {
-        // Long 1-D: n a power of two up to 2^21 (N1, N2 <= 2048).
+        // Long 1-D: n a power of two up to 2^23.  Rows of N2 = min(N/4, 2048)
+        // points up to N = 2^22, then rows and columns of up to 4096 points.
         const long long n = dims[0];
-        if (!is_pow2(n) || n > (1ll << 21)) return false;
+        if (!is_pow2(n) || n > (1ll << 23)) return false;
         const long long N = 2 * n;
         g->d = 1;
         g->lng = 1;
-        g->N2 = (int)(N / 4 < 2048 ? N / 4 : 2048);
+        g->N2 = (int)(N <= (1ll << 22) ? (N / 4 < 2048 ? N / 4 : 2048) : 4096);
         g->N1 = (int)(N / g->N2);
         g->logN = 0;
         while ((1ll << g->logN) < N) ++g->logN;

@@ -69,6 +69,7 @@ WORKLOADS = [
     Workload("3d_512x512x512_b1_c4_bf16", (512, 512, 512), 1, 4, "bf16", 1004),
     # long 1-D sequence (the summary's genomics context, "Results": throughput up to 10M tokens)
     Workload("1d_2097152_b1_c8_bf16", (2097152,), 1, 8, "bf16", 1005),
+    Workload("1d_8388608_b1_c4_bf16", (8388608,), 1, 4, "bf16", 1006),
 ]
 
 

@@ -65,7 +65,7 @@ def test_sizes(H):
     assert rec == lib.hyenand_fftconv_workspace_bytes(8, 64, 2, _dims(256, 256), 0)
     assert lib.hyenand_fftconv_workspace_bytes(4, 4, 1, _dims(1024), 0) == 0  # 1-D needs none
     # Unsupported shapes size to 0.
-    for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(1 << 22)), (1, _dims(3 << 11)), (4, _dims(2, 2, 2, 2))]:
+    for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(1 << 24)), (1, _dims(3 << 11)), (4, _dims(2, 2, 2, 2))]:
         assert lib.hyenand_kernel_spectrum_bytes(2, d, dims) == 0
         assert lib.hyenand_kernel_spectrum_tile(d, dims) == 0
 
@@ -206,7 +206,7 @@ def test_long_1d_sizes(H):
     spectrum per channel (no Nyquist packing), N complex of workspace per pair,
     three launches per channel chunk; no backward and no circular mode."""
     lib = H.get_lib()
-    for n in (2048, 1 << 16, 1 << 21):
+    for n in (2048, 1 << 16, 1 << 21, 1 << 23):
         assert lib.hyenand_kernel_spectrum_bytes(3, 1, _dims(n)) == 3 * 2 * n * 8
         assert lib.hyenand_fftconv_workspace_min_bytes(2, 3, 1, _dims(n), 0) == 2 * 2 * n * 8
         assert lib.hyenand_fftconv_bwd_workspace_min_bytes(2, 3, 1, _dims(n), 0, 1) == 0

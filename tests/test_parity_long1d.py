@@ -4,7 +4,7 @@ the fp64 oracle.
 The gist.science summary ("Results", genomics) reports throughput up to 10M
 tokens for 1-D signals; here the zero-padded length N = 2n is factored as
 N1 x N2 (column transforms, twiddle, row transforms with the spectrum product)
-for n up to 2^21.  Bar as for the other forwards: max|y_gpu - y_ref| / max|y_ref|
+for n up to 2^23 (rows of 4096 points beyond N = 2^22).  Bar as for the other forwards: max|y_gpu - y_ref| / max|y_ref|
 <= 1e-4 (fp32 I/O), <= 2e-2 (bf16 I/O).  Whole signals against the oracle's
 FFT route (O2) and sampled outputs against the direct sum (O1).
 """
@@ -52,7 +52,8 @@ def _run(H, dims, B, C, dtype, seed, per_sample=False, workspace=None):
 
 
 @pytest.mark.parametrize("n,B,C,dtype", [(2048, 2, 3, "f32"), (4096, 1, 2, "bf16"), (8192, 3, 2, "f32"),
-                                         (1 << 16, 2, 2, "f32"), (1 << 18, 1, 2, "bf16"), (1 << 20, 1, 2, "f32")],
+                                         (1 << 16, 2, 2, "f32"), (1 << 18, 1, 2, "bf16"), (1 << 20, 1, 2, "f32"),
+                                         (1 << 22, 1, 1, "f32"), (1 << 23, 1, 1, "bf16")],
                          ids=lambda v: str(v))
 def test_matches_fft_oracle(H, n, B, C, dtype):
     x, p, K, y = _run(H, (n,), B, C, dtype, seed=200 + n % 97 + B)
@@ -87,10 +88,11 @@ def test_every_chunking_gives_the_same_output(H):
 
 
 @pytest.mark.timeout(300)
-def test_workload_full_size(H):
-    """The 2M-token workload at full size (8 channels, bf16): two whole
-    channels against the FFT oracle."""
-    wl = synth.WORKLOADS[5]
+@pytest.mark.parametrize("idx", [5, 6])
+def test_workload_full_size(H, idx):
+    """The 2M-token (8 channels) and 8M-token (4 channels) bf16 workloads at full
+    size: the first and last channel against the FFT oracle."""
+    wl = synth.WORKLOADS[idx]
     x, p, K, y = _run(H, wl.dims, wl.B, wl.C, wl.dtype, seed=wl.seed)
     for c in (0, wl.C - 1):
         ref = oracle.fftconv(x[:, c:c + 1], p.alpha[c:c + 1], p.beta[c:c + 1], K[c:c + 1])
