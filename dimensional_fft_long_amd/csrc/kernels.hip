@@ -111,8 +111,14 @@ __global__ __launch_bounds__(row_nt(L)) void k_conv1d(ConvArgs a)
     conv1d_body<L, BF16, BWD, CIRC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
+// Waves per SIMD the compiler must leave room for: two workgroups per CU for
+// the 512-point 2-D tiles (at most 128 VGPRs; 256^2 backward 0.80 -> 0.71 ms
+// per call); one elsewhere.
+template <int L, int NR>
+constexpr int bwd_min_waves() { return (NR == 1 && L == 512) ? 2 * bwd_nt(L, NR) / 64 / 4 : 1; }
+
 template <int L, int NR, bool DK>
-__global__ __launch_bounds__(bwd_nt(L, NR)) void k_col_out_bwd(ConvArgs a)
+__global__ __launch_bounds__(bwd_nt(L, NR), (bwd_min_waves<L, NR>())) void k_col_out_bwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
     __shared__ float2 T[L * NR * bwd_tw(L, NR)];
