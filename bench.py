@@ -389,6 +389,22 @@ def main():
     torch.cuda.synchronize()
     marker_ms = sorted(mk[2 * k].elapsed_time(mk[2 * k + 1]) for k in range(args.steps))[args.steps // 2]
 
+    # Cold-cache steps (secondary figure): a 1 GiB buffer is rewritten before
+    # each call, evicting the 256 MB Infinity Cache and the L2s, so every input
+    # comes from HBM.  Percentiles over `steps` single calls.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for k in range(args.steps):
+        flush.fill_(float(k))
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(st)
+        call()
+        c1.record(st)
+        cold.append((c0, c1))
+    torch.cuda.synchronize()
+    cold_ms = sorted(c0.elapsed_time(c1) for c0, c1 in cold)
+    del flush
+
     g = _geom(wl.dims, circ)
     if bwd:
         per_ch = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True)
@@ -452,6 +468,9 @@ def main():
         "hbm_roofline_frac_of_metric": bytes_min / (ms_per_step / 1e3) / HBM_PEAK,
         "bytes_min": bytes_min,
         "traced_step_ms_median": sorted(step_ms)[len(step_ms) // 2],
+        "traced_step_ms_p10_p90": [sorted(step_ms)[len(step_ms) // 10], sorted(step_ms)[(9 * len(step_ms)) // 10]],
+        "cold_cache_ms_per_step": {"median": cold_ms[len(cold_ms) // 2], "p10": cold_ms[len(cold_ms) // 10],
+                                   "p90": cold_ms[(9 * len(cold_ms)) // 10]},
         "per_kernel_us": {nm: 1e3 * sum(v) / len(v) for nm, v in per_pass.items()},
         "event_marker_us": 1e3 * marker_ms,
         "settle_calls": settle_calls,

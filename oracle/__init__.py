@@ -27,6 +27,8 @@ Routes (all fp64, in ``oracle.c``):
     (summary, "Input dependent kernels via registers and FiLM": the kernel is
     conditioned on the whole sample): y[b,c,i] = sum_j u[b,c,j] K[b,c][i-j],
     K [B, C, *(2n-1)]; O1 / O2 applied per batch entry with that entry's kernels.
+  * ``bwd_direct_circ`` / ``bwd_fft_circ`` -- the backward of the circular mode
+    (offsets modulo n; dK on the n offsets).
   * ``bwd_direct`` / ``bwd_points`` / ``bwd_fft`` -- the backward (vector-Jacobian
     product, explainer section "Implementation and operation patterns", item
     "Concrete implementation pattern (PyTorch)": gradients of the input and of
@@ -81,13 +83,16 @@ def _load():
         lib.oracle_fftconv_pairs.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_direct_circ.argtypes = [P, P, P, P, P, I, I, I, P]
+        lib.oracle_bwd_direct_circ.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, P]
+        lib.oracle_bwd_fft_circ.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, P, P, P]
         lib.oracle_fftconv_circ_pairs.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
         lib.oracle_bwd_direct.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, P]
         lib.oracle_bwd_direct_points.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, I64, P, P]
         lib.oracle_bwd_fft.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, P, P, P]
         for f in ("oracle_gate", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
                   "oracle_fftconv_pairs", "oracle_num_threads", "oracle_bwd_direct", "oracle_bwd_direct_points",
-                  "oracle_bwd_fft", "oracle_direct_circ", "oracle_fftconv_circ_pairs"):
+                  "oracle_bwd_fft", "oracle_direct_circ", "oracle_fftconv_circ_pairs", "oracle_bwd_direct_circ",
+                  "oracle_bwd_fft_circ"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -276,6 +281,41 @@ def bwd_fft(x, alpha, beta, K, dy, chans=None):
     dK = np.empty((n,) + tuple(K.shape[1:]), dtype=np.float64)
     _check(_load().oracle_bwd_fft(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(dy), B, C, d, _ptr(dims),
                                   n, _ptr(ch), _ptr(dx), _ptr(da), _ptr(db), _ptr(dK)), "bwd_fft")
+    return np.ascontiguousarray(dx.swapaxes(0, 1)), da, db, dK
+
+
+def bwd_direct_circ(x, alpha, beta, K, dy):
+    """O1 backward of the circular mode: (dx, dalpha, dbeta, dK [C, *dims]), fp64."""
+    x, alpha, beta, K, dy = _f32(x), _f32(alpha), _f32(beta), _f32(K), _f32(dy)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    if dy.shape != x.shape or tuple(K.shape) != (C,) + tuple(x.shape[2:]):
+        raise ValueError("dy is shaped like x, the circular kernel [C, *dims]")
+    dx = np.empty(x.shape, dtype=np.float64)
+    da = np.empty(C, dtype=np.float64)
+    db = np.empty(C, dtype=np.float64)
+    dK = np.empty(K.shape, dtype=np.float64)
+    _check(_load().oracle_bwd_direct_circ(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(dy), B, C, d, _ptr(dims),
+                                          _ptr(dx), _ptr(da), _ptr(db), _ptr(dK)), "bwd_direct_circ")
+    return dx, da, db, dK
+
+
+def bwd_fft_circ(x, alpha, beta, K, dy, chans=None):
+    """O2 backward of the circular mode for the listed channels (all when None):
+    (dx [B, len, *dims], dalpha [len], dbeta [len], dK [len, *dims]), fp64."""
+    x, alpha, beta, K, dy = _f32(x), _f32(alpha), _f32(beta), _f32(K), _f32(dy)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    ch = np.arange(C, dtype=np.int64) if chans is None else np.ascontiguousarray(np.asarray(chans, dtype=np.int64))
+    n = ch.size
+    dx = np.empty((n, B) + tuple(x.shape[2:]), dtype=np.float64)
+    da = np.empty(n, dtype=np.float64)
+    db = np.empty(n, dtype=np.float64)
+    dK = np.empty((n,) + tuple(x.shape[2:]), dtype=np.float64)
+    _check(_load().oracle_bwd_fft_circ(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(K), _ptr(dy), B, C, d, _ptr(dims),
+                                       n, _ptr(ch), _ptr(dx), _ptr(da), _ptr(db), _ptr(dK)), "bwd_fft_circ")
     return np.ascontiguousarray(dx.swapaxes(0, 1)), da, db, dK
 
 

@@ -729,6 +729,128 @@ int oracle_bwd_fft(const float *x, const float *alpha, const float *beta, const 
     return rc;
 }
 
+/*
+ * Backward of the circular mode: the same chain rule with every offset taken
+ * modulo n (K stored by offset mod n, as for the circular forward):
+ *   du[j]    = sum_{i in G} dy[i] K[(i - j) mod n]
+ *   dK_c[m]  = sum_b sum_{j in G} dy[(j + m) mod n] u[j]
+ * dx, dalpha, dbeta from du as in the non-circular backward.  O1 writes the
+ * sums out; O2 takes them as products with conjugate spectra of size n.
+ */
+int oracle_bwd_direct_circ(const float *x, const float *alpha, const float *beta, const float *K, const float *dy,
+                           int B, int C, int d, const int64_t *dims,
+                           double *dx, double *dalpha, double *dbeta, double *dK)
+{
+    geom_t g;
+    if (!x || !alpha || !beta || !K || !dy || !dx || !dalpha || !dbeta || !dK || B < 0 || C < 0) return ORC_EINVAL;
+    if (geom_init(&g, d, dims)) return ORC_EINVAL;
+    const size_t n = (size_t)(g.L ? g.L : 1);
+    double *u = (double *)malloc(sizeof(double) * n), *du = (double *)malloc(sizeof(double) * n);
+    if (!u || !du) { free(u); free(du); return ORC_ENOMEM; }
+    for (int c = 0; c < C; ++c) {
+        const float *Kc = K + (int64_t)c * g.L;
+        double *dKc = dK + (int64_t)c * g.L;
+        for (int64_t m = 0; m < g.L; ++m) dKc[m] = 0.0;
+        dalpha[c] = 0.0;
+        dbeta[c] = 0.0;
+        for (int b = 0; b < B; ++b) {
+            const int64_t p = (int64_t)b * C + c;
+            const float *xs = x + p * g.L, *dys = dy + p * g.L;
+            for (int64_t j = 0; j < g.L; ++j) u[j] = gate((double)xs[j], alpha[c], beta[c]);
+#pragma omp parallel for schedule(static)
+            for (int64_t j = 0; j < g.L; ++j) {
+                const int64_t j2 = j % g.n[2], j1 = (j / g.n[2]) % g.n[1], j0 = j / (g.n[1] * g.n[2]);
+                double acc = 0.0;
+                for (int64_t i = 0; i < g.L; ++i) {
+                    const int64_t i2 = i % g.n[2], i1 = (i / g.n[2]) % g.n[1], i0 = i / (g.n[1] * g.n[2]);
+                    const int64_t m0 = ((i0 - j0) % g.n[0] + g.n[0]) % g.n[0];
+                    const int64_t m1 = ((i1 - j1) % g.n[1] + g.n[1]) % g.n[1];
+                    const int64_t m2 = ((i2 - j2) % g.n[2] + g.n[2]) % g.n[2];
+                    acc += (double)dys[i] * (double)Kc[(m0 * g.n[1] + m1) * g.n[2] + m2];
+                }
+                du[j] = acc;
+            }
+            gate_vjp(xs, du, g.L, alpha[c], beta[c], dx + p * g.L, &dalpha[c], &dbeta[c]);
+#pragma omp parallel for schedule(static)
+            for (int64_t m = 0; m < g.L; ++m) {
+                const int64_t m2 = m % g.n[2], m1 = (m / g.n[2]) % g.n[1], m0 = m / (g.n[1] * g.n[2]);
+                double acc = 0.0;
+                for (int64_t j = 0; j < g.L; ++j) {
+                    const int64_t j2 = j % g.n[2], j1 = (j / g.n[2]) % g.n[1], j0 = j / (g.n[1] * g.n[2]);
+                    const int64_t i0 = (j0 + m0) % g.n[0], i1 = (j1 + m1) % g.n[1], i2 = (j2 + m2) % g.n[2];
+                    acc += (double)dys[(i0 * g.n[1] + i1) * g.n[2] + i2] * u[j];
+                }
+                dKc[m] += acc;
+            }
+        }
+    }
+    free(u);
+    free(du);
+    return ORC_OK;
+}
+
+int oracle_bwd_fft_circ(const float *x, const float *alpha, const float *beta, const float *K, const float *dy,
+                        int B, int C, int d, const int64_t *dims, int64_t nch, const int64_t *chans,
+                        double *dx, double *dalpha, double *dbeta, double *dK)
+{
+    geom_t g;
+    if (!x || !alpha || !beta || !K || !dy || !chans || !dx || !dalpha || !dbeta || !dK || nch < 0) return ORC_EINVAL;
+    if (geom_init(&g, d, dims)) return ORC_EINVAL;
+    for (int a = 0; a < 3; ++a)
+        if (!is_pow2(g.n[a])) return ORC_EINVAL;
+    for (int64_t q = 0; q < nch; ++q)
+        if (chans[q] < 0 || chans[q] >= C) return ORC_EINVAL;
+    const size_t bytes = sizeof(double) * (size_t)g.L;
+    double *buf[10];
+    int fail = 0;
+    for (int k = 0; k < 10; ++k) {
+        buf[k] = (double *)malloc(bytes);
+        if (!buf[k]) fail = 1;
+    }
+    double *v = (double *)malloc(bytes);
+    if (fail || !v) {
+        for (int k = 0; k < 10; ++k) free(buf[k]);
+        free(v);
+        return ORC_ENOMEM;
+    }
+    double *kr = buf[0], *ki = buf[1], *pr = buf[2], *pi = buf[3], *yr = buf[4], *yi = buf[5];
+    double *ur = buf[6], *ui = buf[7], *tr = buf[8], *ti = buf[9];
+    const double scale = 1.0 / (double)g.L;
+    int rc = ORC_OK;
+    for (int64_t q = 0; q < nch && rc == ORC_OK; ++q) {
+        const int64_t c = chans[q];
+        for (int64_t m = 0; m < g.L; ++m) { kr[m] = (double)K[c * g.L + m]; ki[m] = 0.0; pr[m] = 0.0; pi[m] = 0.0; }
+        if ((rc = fft_nd(kr, ki, g.n, -1))) break;
+        dalpha[q] = 0.0;
+        dbeta[q] = 0.0;
+        for (int64_t b = 0; b < B && rc == ORC_OK; ++b) {
+            const int64_t p = b * C + c;
+            const float *xs = x + p * g.L, *dys = dy + p * g.L;
+            for (int64_t j = 0; j < g.L; ++j) {
+                yr[j] = (double)dys[j]; yi[j] = 0.0;
+                ur[j] = gate((double)xs[j], alpha[c], beta[c]); ui[j] = 0.0;
+            }
+            if ((rc = fft_nd(yr, yi, g.n, -1))) break;
+            if ((rc = fft_nd(ur, ui, g.n, -1))) break;
+            for (int64_t m = 0; m < g.L; ++m) {
+                pr[m] += yr[m] * ur[m] + yi[m] * ui[m];
+                pi[m] += yi[m] * ur[m] - yr[m] * ui[m];
+                tr[m] = yr[m] * kr[m] + yi[m] * ki[m];
+                ti[m] = yi[m] * kr[m] - yr[m] * ki[m];
+            }
+            if ((rc = fft_nd(tr, ti, g.n, +1))) break;
+            for (int64_t j = 0; j < g.L; ++j) v[j] = tr[j] * scale;
+            gate_vjp(xs, v, g.L, alpha[c], beta[c], dx + (q * B + b) * g.L, &dalpha[q], &dbeta[q]);
+        }
+        if (rc) break;
+        if ((rc = fft_nd(pr, pi, g.n, +1))) break;
+        for (int64_t m = 0; m < g.L; ++m) dK[q * g.L + m] = pr[m] * scale;
+    }
+    for (int k = 0; k < 10; ++k) free(buf[k]);
+    free(v);
+    return rc;
+}
+
 /* Threads OpenMP will use (reported by the CPU-baseline leg). */
 int oracle_num_threads(void)
 {

@@ -124,3 +124,81 @@ def test_pins_reject_mutants(mutant):
         if np.max(np.abs(mutant(x, a, b, K)[0, 0] - np.roll(u, shift, axis=(0, 1)))) > 1e-9:
             fails += 1
     assert fails > 0
+
+
+# ------------------------------------------------------------------ backward
+
+def _autograd_circ(x, a, b, K, dy):
+    """Gradients of sum(dy * y) by torch autograd, y the circular sum as a gather."""
+    import torch
+
+    B, C = x.shape[:2]
+    dims = x.shape[2:]
+    L = int(np.prod(dims))
+    grid = np.stack(np.meshgrid(*[np.arange(n) for n in dims], indexing="ij"), -1).reshape(-1, len(dims))
+    off = (grid[:, None, :] - grid[None, :, :]) % np.asarray(dims)
+    flat = np.zeros(off.shape[:2], dtype=np.int64)
+    for ax, n in enumerate(dims):
+        flat = flat * n + off[..., ax]
+    idx = torch.from_numpy(flat)
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    at = torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+    Kt = torch.tensor(K, dtype=torch.float64, requires_grad=True)
+    xs = xt.reshape(B, C, L)
+    u = xs * torch.sigmoid(at[None, :, None] * xs + bt[None, :, None])
+    T = Kt.reshape(C, -1)[:, idx]
+    y = torch.einsum("cij,bcj->bci", T, u)
+    loss = (y * torch.tensor(dy, dtype=torch.float64).reshape(B, C, L)).sum()
+    return [g.numpy() for g in torch.autograd.grad(loss, [xt, at, bt, Kt])]
+
+
+@pytest.mark.parametrize("dims", [(6,), (3, 4), (2, 3, 2)])
+def test_bwd_matches_autograd_of_definition(dims):
+    x, a, b, K = _case(dims, B=2, C=2, seed=30)
+    dy = np.random.default_rng(31).standard_normal(x.shape).astype(np.float32)
+    got = oracle.bwd_direct_circ(x, a, b, K, dy)
+    for g, w in zip(got, _autograd_circ(x, a, b, K, dy)):
+        assert _rel(g, w) < 1e-12
+
+
+@pytest.mark.parametrize("dims", [(16,), (8, 4), (4, 2, 8)])
+def test_bwd_fft_matches_direct(dims):
+    x, a, b, K = _case(dims, B=3, C=2, seed=32)
+    dy = np.random.default_rng(33).standard_normal(x.shape).astype(np.float32)
+    d1 = oracle.bwd_direct_circ(x, a, b, K, dy)
+    d2 = oracle.bwd_fft_circ(x, a, b, K, dy)
+    for g, w in zip(d2, d1):
+        assert _rel(g, w) < 1e-12
+
+
+def test_bwd_finite_differences():
+    # The explainer's central differences (eps = 1e-4) on x, and exact linearity in K.
+    dims = (4, 4)
+    x, a, b, K = _case(dims, B=2, C=2, seed=34)
+    rng = np.random.default_rng(35)
+    dy = rng.standard_normal(x.shape).astype(np.float32)
+    dx, _, _, dK = oracle.bwd_direct_circ(x, a, b, K, dy)
+    loss = lambda xx, KK: float(np.sum(oracle.direct_circ(xx, a, b, KK) * dy.astype(np.float64)))
+    v = rng.standard_normal(x.shape)
+    xp, xm = (x + 1e-4 * v).astype(np.float32), (x - 1e-4 * v).astype(np.float32)
+    an = float(np.sum(dx * (xp.astype(np.float64) - xm.astype(np.float64))))
+    assert abs(loss(xp, K) - loss(xm, K) - an) < 1e-6 * abs(an)
+    step = rng.standard_normal(K.shape).astype(np.float32)
+    an = float(np.sum(dK * ((K + step).astype(np.float64) - K.astype(np.float64))))
+    assert abs(loss(x, K + step) - loss(x, K) - an) < 1e-10 * max(abs(an), 1.0)
+
+
+def test_bwd_pins_reject_planted_mistakes():
+    dims = (4, 4)
+    x, a, b, K = _case(dims, B=1, C=1, seed=36)
+    dy = np.random.default_rng(37).standard_normal(x.shape).astype(np.float32)
+    want = _autograd_circ(x, a, b, K, dy)
+    dx, da, db, dK = oracle.bwd_direct_circ(x, a, b, K, dy)
+    ax = tuple(range(1, dK.ndim))
+    mutants = [
+        (dx, da, db, np.roll(np.flip(dK, ax), 1, ax)),              # dK with the offset sign flipped
+        oracle.bwd_direct_circ(x, a, b, np.ascontiguousarray(np.roll(np.flip(K, ax), 1, ax)), dy),  # du a convolution
+    ]
+    for m in mutants:
+        assert max(_rel(g, w) for g, w in zip(m, want)) > 1e-6
