@@ -28,6 +28,8 @@ METRIC = "Gvoxel·channels/s of gated N-D FFT conv fwd; % of HBM roofline (1 GPU
 METRIC_CIRC = "Gvoxel·channels/s of gated N-D FFT conv fwd, circular mode; % of HBM roofline (1 GPU)"
 METRIC_PS = "Gvoxel·channels/s of gated N-D FFT conv fwd, one kernel per (b, c); % of HBM roofline (1 GPU)"
 METRIC_BWD = "Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK); % of HBM roofline (1 GPU)"
+METRIC_BWD_CIRC = ("Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK), circular mode; "
+                   "% of HBM roofline (1 GPU)")
 UNIT = "Gvoxel·channels/s"
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
 # fp32 vector peak without packed-FP32 instructions (the build disables them):
@@ -46,7 +48,8 @@ def _geom(dims, circ=False):
     No, Nm, Ni = (f * no if d >= 2 else 1), (f * nm if d == 3 else 1), f * ni
     S = Ni // 2
     return dict(no=no, nm=nm, ni=ni, No=No, Nm=Nm, Ni=Ni, S=S, vox=no * nm * ni, wsp=no * Nm * S if d >= 2 else 0,
-                ksz=No * Nm * S + No * Nm, kmain=No * Nm * S, kl=(2 * no - 1) * (2 * nm - 1) * (2 * ni - 1),
+                ksz=No * Nm * S + No * Nm, kmain=No * Nm * S,
+                kl=no * nm * ni if circ else (2 * no - 1) * (2 * nm - 1) * (2 * ni - 1),
                 prune=0 if circ else 1)
 
 
@@ -83,17 +86,17 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
     # ---- backward passes (dK wanted)
     elif name in ("row_fwd_dy", "row_fwd_u"):
         by = P * g["vox"] * es + P * rows * g["S"] * 8
-        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 2 * 2 + (P * g["vox"] * 5 if name == "row_fwd_u" else 0)
+        fl = _fft_flops(g["Ni"], P * rows / 2, pr) + P * rows * g["S"] * 2 * 2 + (P * g["vox"] * 5 if name == "row_fwd_u" else 0)
     elif name in ("col_mid_fwd_dy", "col_mid_fwd_u"):
-        return pass_model("col_mid_fwd", dims, P, nch, es)
+        return pass_model("col_mid_fwd", dims, P, nch, es, circ)
     elif name == "col_out_bwd":
         # dy planes read and written, u planes read, K_hat read, kernel-gradient planes written
         by = 3 * P * g["wsp"] * 8 + nch * g["ksz"] * 8 + nch * g["kmain"] * 8
         lines = P * g["Nm"] * g["S"]
-        fl = 3 * _fft_flops(g["No"], lines, 1) + lines * g["No"] * (6 + 8) + _fft_flops(g["No"], nch * g["Nm"] * g["S"], 0)
+        fl = 3 * _fft_flops(g["No"], lines, pr) + lines * g["No"] * (6 + 8) + _fft_flops(g["No"], nch * g["Nm"] * g["S"], 0)
     elif name == "row_inv_bwd":
         by = P * rows * g["S"] * 8 + 2 * P * g["vox"] * es + P * max(rows // 2, 1) * 8
-        fl = _fft_flops(g["Ni"], P * rows / 2, 1) + P * rows * g["S"] * 4 + P * g["vox"] * 14
+        fl = _fft_flops(g["Ni"], P * rows / 2, pr) + P * rows * g["S"] * 4 + P * g["vox"] * 14
     elif name == "gate_reduce":
         by = P * max(rows // 2, 1) * 8
         fl = P * max(rows // 2, 1) * 2
@@ -105,7 +108,7 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
         fl = _fft_flops(g["Ni"], nch * g["No"] * g["Nm"] / 2, 0) + nch * g["No"] * g["Nm"] * g["S"] * 4
     elif name == "conv1d_bwd":
         by = 3 * P * g["vox"] * es + nch * g["ksz"] * 8 + P * 8
-        fl = 2 * _fft_flops(g["Ni"], P / 2, 1) + P * g["S"] * (6 + 4) + P * g["vox"] * 14
+        fl = 2 * _fft_flops(g["Ni"], P / 2, pr) + P * g["S"] * (6 + 4) + P * g["vox"] * 14
     # ---- long 1-D (four-step: N = 2n = N1 x N2, complex arithmetic)
     elif name == "lng_col_fwd":
         N = 2 * g["ni"]
@@ -124,7 +127,7 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
         fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6
     elif name == "corr1d":
         by = 2 * P * g["vox"] * es + P * g["S"] * 8
-        fl = _fft_flops(g["Ni"], P, 1) + P * g["S"] * 10 + P * g["vox"] * 5
+        fl = _fft_flops(g["Ni"], P, pr) + P * g["S"] * 10 + P * g["vox"] * 5
     else:
         raise KeyError(name)
     return by, fl
@@ -195,10 +198,10 @@ def cpu_baseline(wl, circ=False, max_seconds=20.0):
                       f"{t_total:.1f} s"}
 
 
-def cpu_baseline_bwd(wl, max_seconds=20.0):
-    """The fp64 oracle's backward (O2 FFT route, as written) on a bounded
-    sample of the same workload: whole channels (every batch entry) until
-    about `max_seconds` pass."""
+def cpu_baseline_bwd(wl, circ=False, max_seconds=20.0):
+    """The fp64 oracle's backward (O2 FFT route, as written; its circular
+    route in circular mode) on a bounded sample of the same workload: whole
+    channels (every batch entry) until about `max_seconds` pass."""
     import oracle
     import synth
 
@@ -209,15 +212,19 @@ def cpu_baseline_bwd(wl, max_seconds=20.0):
     t_total = 0.0
     while t_total < max_seconds and done < wl.C:
         c = done
-        K = synth.kernel_channels(wl.dims, p, channels=[c]).numpy()
+        if circ:
+            K = synth.circular_kernel(wl.dims, p).numpy()[c:c + 1]
+        else:
+            K = synth.kernel_channels(wl.dims, p, channels=[c]).numpy()
         t0 = time.perf_counter()
-        oracle.bwd_fft(x[:, c:c + 1], p.alpha[c:c + 1], p.beta[c:c + 1], K, dy[:, c:c + 1])
+        (oracle.bwd_fft_circ if circ else oracle.bwd_fft)(x[:, c:c + 1], p.alpha[c:c + 1], p.beta[c:c + 1], K,
+                                                          dy[:, c:c + 1])
         t_total += time.perf_counter() - t0
         done += 1
     vox = done * wl.B * wl.voxels
     return {"value": vox / t_total / 1e9, "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} of {wl.C} channels (all {wl.B} batch entries each) of {wl.name}, fp64 O2 backward "
-                      f"(radix-2 FFT) route, {t_total:.1f} s"}
+                      f"(radix-2 FFT) route{', circular' if circ else ''}, {t_total:.1f} s"}
 
 
 def main():
@@ -229,7 +236,7 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward with the kernel gradient")
     ap.add_argument("--boundary", choices=("padded", "circular"), default="padded",
-                    help="zero-padded non-circular convolution (default) or the circular mode (forward only)")
+                    help="zero-padded non-circular convolution (default) or the circular mode")
     ap.add_argument("--kernel", choices=("shared", "per-sample"), default="shared",
                     help="one kernel per channel (default) or one per (b, c): input-dependent kernels "
                          "(zero-padded forward only)")
@@ -265,8 +272,8 @@ def main():
     wl = {w.name: w for w in synth.WORKLOADS}[args.workload]
     circ = args.boundary == "circular"
     ps = args.kernel == "per-sample"
-    if (circ or ps) and args.which == "bwd":
-        print("bench.py: the backward is built for the zero-padded shared-kernel mode only", file=sys.stderr)
+    if ps and args.which == "bwd":
+        print("bench.py: the backward is built for shared kernels only", file=sys.stderr)
         return 2
     if circ and ps:
         print("bench.py: per-sample kernels are built for the zero-padded mode only", file=sys.stderr)
@@ -307,10 +314,11 @@ def main():
     if bwd:
         dy = synth.draw_dy(wl.dims, wl.B, wl.C, wl.dtype, wl.seed).to(dev)
         outs = (torch.empty_like(x), torch.empty(wl.C, device=dev), torch.empty(wl.C, device=dev),
-                torch.empty((wl.C,) + tuple(2 * n - 1 for n in wl.dims), device=dev))
-        ws_bytes = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
+                torch.empty((wl.C,) + (tuple(wl.dims) if circ else tuple(2 * n - 1 for n in wl.dims)), device=dev))
+        ws_bytes = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, circular=circ)
         if args.ws_mb is not None:
-            ws_bytes = max(H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
+            ws_bytes = max(H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True, circular=circ),
+                           int(args.ws_mb * 2**20))
     elif circ:
         y = torch.empty_like(x)
         ws_bytes = H.circ_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
@@ -325,7 +333,7 @@ def main():
 
     def call():
         if bwd:
-            H.fftconv_bwd(x, al, be, kh, dy, *outs, workspace=ws)
+            (H.fftconv_bwd_circ if circ else H.fftconv_bwd)(x, al, be, kh, dy, *outs, workspace=ws)
         elif circ:
             H.fftconv_fwd_circ(x, al, be, kh, y=y, workspace=ws)
         elif ps:
@@ -335,7 +343,7 @@ def main():
 
     def traced(events):
         if bwd:
-            return H.fftconv_bwd_traced(x, al, be, kh, dy, outs, ws, events)
+            return H.fftconv_bwd_traced(x, al, be, kh, dy, outs, ws, events, circular=circ)
         if circ:
             return H.fftconv_fwd_circ_traced(x, al, be, kh, y, ws, events)
         if ps:
@@ -407,7 +415,7 @@ def main():
 
     g = _geom(wl.dims, circ)
     if bwd:
-        per_ch = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True)
+        per_ch = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True, circular=circ)
         nch = min(wl.C, ws_bytes // per_ch)
         nch = -(-wl.C // -(-wl.C // nch))  # balanced chunks, as the library splits them
         plan = {"chunk_channels": nch}
@@ -450,7 +458,8 @@ def main():
     voxch = wl.B * wl.C * wl.voxels
     value = voxch / (ms_per_step / 1e3) / 1e9
     out = {
-        "metric": METRIC_BWD if bwd else (METRIC_CIRC if circ else (METRIC_PS if ps else METRIC)),
+        "metric": ((METRIC_BWD_CIRC if circ else METRIC_BWD) if bwd
+                   else (METRIC_CIRC if circ else (METRIC_PS if ps else METRIC))),
         "value": value,
         "unit": UNIT,
         "n_gpus": 1,
@@ -462,7 +471,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "pass": args.which, "boundary": args.boundary, "kernel": args.kernel, "grid": list(wl.dims), "padded": [2 * n for n in wl.dims], "B": wl.B,
+        "config": {"workload": wl.name, "pass": args.which, "boundary": args.boundary, "kernel": args.kernel, "grid": list(wl.dims), "padded": [n if circ else 2 * n for n in wl.dims], "B": wl.B,
                    "C": wl.C, "io_dtype": "bf16" if wl.dtype == "bf16" else "fp32", "launches_per_step": n_launch, "workspace_mib": ws_bytes / 2**20,
                    "chunk_channels": plan["chunk_channels"]},
         "hbm_roofline_frac_of_metric": bytes_min / (ms_per_step / 1e3) / HBM_PEAK,
@@ -478,7 +487,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_bwd(wl) if bwd else cpu_baseline(wl, circ)
+        out["cpu_baseline"] = cpu_baseline_bwd(wl, circ) if bwd else cpu_baseline(wl, circ)
     print(json.dumps(out), flush=True)
     return 0
 

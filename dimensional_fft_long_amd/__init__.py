@@ -22,9 +22,10 @@ zero outside the grid.  Entry points mirror ``include/hyenand.h``:
 * ``HyenaConvolutionFunction`` -- the autograd wrapper of that pattern
 * ``fftconv_fwd_per_sample(x, alpha, beta, K_hat)`` -- input-dependent kernels:
   K_hat = kernel_spectrum(K) of kernels [B, C, *(2n-1)], one per (b, c)
-* ``kernel_spectrum_circ(K)`` / ``fftconv_fwd_circ(...)`` -- the circular mode
-  (gist.science summary, "Boundary handling": periodic grids, no padding; K is
-  [C, *dims] indexed by offset mod n)
+* ``kernel_spectrum_circ(K)`` / ``fftconv_fwd_circ(...)`` /
+  ``fftconv_bwd_circ(...)`` -- the circular mode (gist.science summary,
+  "Boundary handling": periodic grids, no padding; K is [C, *dims] indexed by
+  offset mod n)
 """
 from __future__ import annotations
 
@@ -47,7 +48,9 @@ EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_
            "hyenand_fftconv_bwd_traced", "hyenand_kernel_spectrum_circ_bytes", "hyenand_kernel_spectrum_circ_tile",
            "hyenand_kernel_spectrum_circ", "hyenand_fftconv_circ_workspace_bytes",
            "hyenand_fftconv_circ_workspace_min_bytes", "hyenand_fftconv_fwd_circ", "hyenand_fftconv_fwd_circ_traced",
-           "hyenand_fftconv_fwd_per_sample", "hyenand_fftconv_fwd_per_sample_traced")
+           "hyenand_fftconv_fwd_per_sample", "hyenand_fftconv_fwd_per_sample_traced", "hyenand_fftconv_bwd_circ",
+           "hyenand_fftconv_bwd_circ_workspace_bytes", "hyenand_fftconv_bwd_circ_workspace_min_bytes",
+           "hyenand_fftconv_bwd_circ_traced")
 
 _lib = None
 
@@ -90,6 +93,15 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_bwd_workspace_bytes.restype = SZ
     lib.hyenand_fftconv_bwd_workspace_min_bytes.argtypes = [I, I, I, P, I, I]
     lib.hyenand_fftconv_bwd_workspace_min_bytes.restype = SZ
+    lib.hyenand_fftconv_bwd_circ.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_fftconv_bwd_circ.restype = I
+    lib.hyenand_fftconv_bwd_circ_traced.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I,
+                                                    ctypes.POINTER(I)]
+    lib.hyenand_fftconv_bwd_circ_traced.restype = I
+    lib.hyenand_fftconv_bwd_circ_workspace_bytes.argtypes = [I, I, I, P, I, I]
+    lib.hyenand_fftconv_bwd_circ_workspace_bytes.restype = SZ
+    lib.hyenand_fftconv_bwd_circ_workspace_min_bytes.argtypes = [I, I, I, P, I, I]
+    lib.hyenand_fftconv_bwd_circ_workspace_min_bytes.restype = SZ
     lib.hyenand_kernel_spectrum_circ_bytes.argtypes = [I, I, P]
     lib.hyenand_kernel_spectrum_circ_bytes.restype = SZ
     lib.hyenand_kernel_spectrum_circ_tile.argtypes = [I, P]
@@ -258,14 +270,18 @@ def fftconv_fwd_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None)
 
 
 def bwd_workspace_bytes(B: int, C: int, dims, dtype=torch.float32, with_dK: bool = True,
-                        minimum: bool = False) -> int:
+                        minimum: bool = False, circular: bool = False) -> int:
     lib = get_lib()
-    f = lib.hyenand_fftconv_bwd_workspace_min_bytes if minimum else lib.hyenand_fftconv_bwd_workspace_bytes
+    if circular:
+        f = (lib.hyenand_fftconv_bwd_circ_workspace_min_bytes if minimum
+             else lib.hyenand_fftconv_bwd_circ_workspace_bytes)
+    else:
+        f = lib.hyenand_fftconv_bwd_workspace_min_bytes if minimum else lib.hyenand_fftconv_bwd_workspace_bytes
     return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype), int(bool(with_dK))))
 
 
-def _bwd_workspace(B, C, dims, dtype, with_dK, device):
-    nbytes = bwd_workspace_bytes(B, C, dims, dtype, with_dK)
+def _bwd_workspace(B, C, dims, dtype, with_dK, device, circular=False):
+    nbytes = bwd_workspace_bytes(B, C, dims, dtype, with_dK, circular=circular)
     key = ("bwd", str(device), nbytes)
     buf = _ws_cache.get(key)
     if buf is None:
@@ -274,7 +290,7 @@ def _bwd_workspace(B, C, dims, dtype, with_dK, device):
     return buf, nbytes
 
 
-def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace):
+def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, circular=False):
     if not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous device tensor")
     if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_cuda or not dy.is_contiguous():
@@ -286,15 +302,16 @@ def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspa
             raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
     if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
-    if K_hat.numel() * 8 < spectrum_bytes(C, dims):
+    if K_hat.numel() * 8 < (spectrum_circ_bytes(C, dims) if circular else spectrum_bytes(C, dims)):
         raise ValueError("K_hat is smaller than the spectrum of this shape")
     dx = torch.empty_like(x) if dx is None else dx
     dalpha = torch.empty(C, dtype=torch.float32, device=x.device) if dalpha is None else dalpha
     dbeta = torch.empty(C, dtype=torch.float32, device=x.device) if dbeta is None else dbeta
     if with_dK and dK is None:
-        dK = torch.empty((C,) + tuple(2 * n - 1 for n in dims), dtype=torch.float32, device=x.device)
+        kdims = dims if circular else tuple(2 * n - 1 for n in dims)
+        dK = torch.empty((C,) + kdims, dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace, ws_bytes = _bwd_workspace(B, C, dims, x.dtype, dK is not None, x.device)
+        workspace, ws_bytes = _bwd_workspace(B, C, dims, x.dtype, dK is not None, x.device, circular)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(dy.data_ptr()),
@@ -327,18 +344,20 @@ BWD_PASS_NAMES = {
 }
 
 
-def fftconv_bwd_traced(x, alpha, beta, K_hat, dy, outs, workspace, events, stream=None) -> int:
-    """fftconv_bwd into ``outs`` = (dx, dalpha, dbeta, dK or None), recording
-    ``events`` before each kernel launch and after the last; returns the launch count."""
+def fftconv_bwd_traced(x, alpha, beta, K_hat, dy, outs, workspace, events, stream=None, circular=False) -> int:
+    """fftconv_bwd (fftconv_bwd_circ with ``circular``) into ``outs`` = (dx,
+    dalpha, dbeta, dK or None), recording ``events`` before each kernel launch
+    and after the last; returns the launch count."""
     dx, dalpha, dbeta, dK = outs
-    args, _ = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, dK is not None, workspace)
+    args, _ = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, dK is not None, workspace, circular)
     st = torch.cuda.current_stream() if stream is None else stream
     for e in events:
         if e.cuda_event == 0:
             e.record(st)
     arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     n = ctypes.c_int(0)
-    rc = get_lib().hyenand_fftconv_bwd_traced(*args, _stream(stream), arr, len(events), ctypes.byref(n))
+    f = get_lib().hyenand_fftconv_bwd_circ_traced if circular else get_lib().hyenand_fftconv_bwd_traced
+    rc = f(*args, _stream(stream), arr, len(events), ctypes.byref(n))
     if rc != OK:
         raise HyenandError(rc, "fftconv_bwd_traced")
     return int(n.value)
@@ -367,6 +386,18 @@ class HyenaConvolutionFunction(torch.autograd.Function):
 
 
 # ----------------------------------------------------------- circular mode
+
+def fftconv_bwd_circ(x, alpha, beta, K_hat, dy, dx=None, dalpha=None, dbeta=None, dK=None, with_dK: bool = True,
+                     workspace=None, stream=None):
+    """Backward of fftconv_fwd_circ for the output gradient dy; K_hat from
+    kernel_spectrum_circ.  Returns (dx, dalpha, dbeta, dK [C, *dims] or None),
+    dK indexed by offset mod n like the circular K."""
+    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, circular=True)
+    rc = get_lib().hyenand_fftconv_bwd_circ(*args, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_bwd_circ")
+    return outs
+
 
 def spectrum_circ_bytes(C: int, dims) -> int:
     return int(get_lib().hyenand_kernel_spectrum_circ_bytes(C, len(dims), _dims_arr(dims)))

@@ -233,33 +233,45 @@ int hyenand_fftconv_fwd_circ_traced(const void* x, const float* alpha, const flo
 }
 
 // ------------------------------------------------------------------ backward
-size_t hyenand_fftconv_bwd_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
+static size_t bwd_workspace(int B, int C, int d, const int64_t* dims, int dtype, int with_dK, bool circ, bool minimum)
 {
     Geom g;
-    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g) || g.lng)
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g, circ) || g.lng)
         return 0;
-    return recommended_bwd_workspace(g, B, C, with_dK != 0);
+    return minimum ? bwd_channel_bytes(g, B, with_dK != 0) : recommended_bwd_workspace(g, B, C, with_dK != 0);
+}
+
+size_t hyenand_fftconv_bwd_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
+{
+    return bwd_workspace(B, C, d, dims, dtype, with_dK, false, false);
 }
 
 size_t hyenand_fftconv_bwd_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
 {
-    Geom g;
-    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g) || g.lng)
-        return 0;
-    return bwd_channel_bytes(g, B, with_dK != 0);
+    return bwd_workspace(B, C, d, dims, dtype, with_dK, false, true);
+}
+
+size_t hyenand_fftconv_bwd_circ_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
+{
+    return bwd_workspace(B, C, d, dims, dtype, with_dK, true, false);
+}
+
+size_t hyenand_fftconv_bwd_circ_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK)
+{
+    return bwd_workspace(B, C, d, dims, dtype, with_dK, true, true);
 }
 
 static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta, const void* K_hat, const void* dy,
                             void* dx, float* dalpha, float* dbeta, float* dK, int B, int C, int d,
                             const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                            LaunchTrace* trace)
+                            LaunchTrace* trace, bool circ)
 {
     if (B < 0 || C < 0) return HYENAND_ERR_INVALID_ARG;
     if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
     if (d < 1 || d > 3) return HYENAND_ERR_UNSUPPORTED;
     if (!dims) return HYENAND_ERR_INVALID_ARG;
     Geom g;
-    if (!make_geom(d, dims, &g) || g.lng) return HYENAND_ERR_UNSUPPORTED;
+    if (!make_geom(d, dims, &g, circ) || g.lng) return HYENAND_ERR_UNSUPPORTED;
     if (C == 0) return HYENAND_OK;
     if (!dalpha || !dbeta || !aligned(dalpha, 4) || !aligned(dbeta, 4) || (dK && !aligned(dK, 4)))
         return HYENAND_ERR_INVALID_ARG;
@@ -319,7 +331,15 @@ int hyenand_fftconv_bwd(const void* x, const float* phi_alpha, const float* phi_
                         const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
     return fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
-                            workspace, workspace_bytes, stream, nullptr);
+                            workspace, workspace_bytes, stream, nullptr, false);
+}
+
+int hyenand_fftconv_bwd_circ(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                             const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C, int d,
+                             const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
+                            workspace, workspace_bytes, stream, nullptr, true);
 }
 
 int hyenand_fftconv_bwd_traced(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
@@ -330,7 +350,21 @@ int hyenand_fftconv_bwd_traced(const void* x, const float* phi_alpha, const floa
     if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
     LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
     const int rc = fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
-                                    workspace, workspace_bytes, stream, &tr);
+                                    workspace, workspace_bytes, stream, &tr, false);
+    if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
+    return rc;
+}
+
+int hyenand_fftconv_bwd_circ_traced(const void* x, const float* phi_alpha, const float* phi_beta,
+                                    const void* K_hat, const void* dy, void* dx, float* dalpha, float* dbeta,
+                                    float* dK, int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                                    int* n_launches)
+{
+    if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
+    LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
+    const int rc = fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
+                                    workspace, workspace_bytes, stream, &tr, true);
     if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
     return rc;
 }

@@ -195,11 +195,12 @@ __host__ __device__ __forceinline__ float gate_vjp(const Ctx& ctx, float du, flo
 // line), written to part: one float2 per line pair for d >= 2 (both rows
 // belong to one (b, c) pair), one per signal for d = 1 (part[2h], part[2h+1]).
 // xa, xb: the x values of the thread's elements, loaded before the transform.
-template <int L, bool BF16, int ITER, class Ctx>
+// n: samples per line (L / 2 zero-padded, L circular).
+template <int L, int n, bool BF16, int ITER, class Ctx>
 __host__ __device__ __forceinline__ void bwd_epilogue(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       const RowMeta* M, const float* xa, const float* xb)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2;
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
     const int tid = ctx.tid();
     float2 ea[ITER], eb[ITER];
 #pragma unroll
@@ -215,33 +216,40 @@ __host__ __device__ __forceinline__ void bwd_epilogue(const Ctx& ctx, int bid, c
         }
     }
     ctx.sync();  // every read of du in T is done
-    float2* Ea = T;
-    float2* Eb = T + NP * n;
+    // The two rows' terms sit side by side in T when they fit (n = L/2);
+    // circular lines (n = L) take them one row after the other.
+    constexpr int NH = 2 * NP * n <= L * LP ? 2 : 1;
+    for (int r0 = 0; r0 < 2; r0 += NH) {
 #pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT;
-        Ea[idx] = ea[i];
-        Eb[idx] = eb[i];
-    }
-    ctx.sync();
-    for (int h = n / 2; h >= 1; h /= 2) {
-        for (int e = tid; e < 2 * NP * h; e += NT) {
-            const int half = e / (NP * h), r = e % (NP * h), lp = r / h, m = r % h;
-            float2* E = half ? Eb : Ea;
-            E[lp * n + m] = cadd(E[lp * n + m], E[lp * n + m + h]);
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT;
+            T[idx] = r0 ? eb[i] : ea[i];
+            if (NH == 2) T[NP * n + idx] = eb[i];
         }
         ctx.sync();
-    }
-    for (int lp = tid; lp < NP; lp += NT) {
-        const RowMeta& md = M[lp];
-        if (!md.valid) continue;
-        const long long h = (long long)bid * NP + lp;
-        if (a.g.d == 1) {
-            a.part[2 * h] = Ea[lp * n];
-            if (md.valid1) a.part[2 * h + 1] = Eb[lp * n];
-        } else {
-            a.part[h] = cadd(Ea[lp * n], Eb[lp * n]);
+        for (int h = n / 2; h >= 1; h /= 2) {
+            for (int e = tid; e < NH * NP * h; e += NT) {
+                const int half = e / (NP * h), r = e % (NP * h), lp = r / h, m = r % h;
+                float2* E = T + half * NP * n;
+                E[lp * n + m] = cadd(E[lp * n + m], E[lp * n + m + h]);
+            }
+            ctx.sync();
         }
+        for (int lp = tid; lp < NP; lp += NT) {
+            const RowMeta& md = M[lp];
+            if (!md.valid) continue;
+            const long long h = (long long)bid * NP + lp;
+            const float2 s0 = T[lp * n];
+            if (a.g.d == 1) {
+                if (r0 == 0) a.part[2 * h] = s0;
+                if (md.valid1 && (NH == 2 || r0 == 1)) a.part[2 * h + 1] = NH == 2 ? T[NP * n + lp * n] : s0;
+            } else if (NH == 2) {
+                a.part[h] = cadd(s0, T[NP * n + lp * n]);
+            } else {
+                a.part[h] = r0 == 0 ? s0 : cadd(a.part[h], s0);  // this thread wrote part[h] in the first pass
+            }
+        }
+        if (NH == 1 && r0 == 0) ctx.sync();  // the second row's terms overwrite T
     }
 }
 
@@ -257,7 +265,6 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
     constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
     constexpr int ITER = NP * S / NT, ITO = NP * n / NT;
     static_assert(NP * S % NT == 0 && NP * n % NT == 0, "whole element loops");
-    static_assert(!(BWD && CIRC), "the backward is built for the zero-padded mode");
     const int tid = ctx.tid();
     ctx.stage();
     row_meta<NP, NT>(ctx, bid, a, M);
@@ -293,10 +300,10 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
             T[(L - k) * LP + lp] = make_float2(ya[i].x + yb[i].y, yb[i].x - ya[i].y);
         }
     }
-    float xa[BWD ? ITER : 1], xb[BWD ? ITER : 1];
+    float xa[BWD ? ITO : 1], xb[BWD ? ITO : 1];
     if constexpr (BWD) {
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) {
+        for (int i = 0; i < ITO; ++i) {
             const int idx = tid + i * NT, lp = idx / n, m = idx % n;
             xa[i] = load_x<BF16>(a, M[lp].o0 + m);
             xb[i] = load_x<BF16>(a, M[lp].o1 + m);
@@ -305,7 +312,7 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
     ctx.sync();
     tile_fft<L, NP, LP, NT, true, false, !CIRC>(ctx, T);
     if constexpr (BWD) {
-        bwd_epilogue<L, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
+        bwd_epilogue<L, n, BF16, ITO>(ctx, bid, a, T, M, xa, xb);
     } else {
 #pragma unroll
         for (int i = 0; i < ITO; ++i) {
@@ -624,7 +631,8 @@ __host__ __device__ __forceinline__ void out_slot0_corr(const Ctx& ctx, const Ou
 //   P   += DY_b conj(U_b)   (registers; k_in = 0 lines through out_slot0_corr)
 // followed by the full inverse of P (all N_out positions: the kernel gradient
 // lives on every offset) into the kernel-gradient planes dkw.
-template <int L, int NR, bool DK, class Ctx>
+// CIRC (circular mode): all L positions read and written.
+template <int L, int NR, bool DK, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void col_out_bwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
     constexpr int TW = bwd_tw(L, NR);
@@ -650,7 +658,7 @@ __host__ __device__ __forceinline__ void col_out_bwd_body(const Ctx& ctx, int bi
     using P0 = PassRegs<L, R0, NL, NT>;
     using PL = PassRegs<L, RL, NL, NT>;
     auto load_cols = [&](const float2* base, P0& s) {
-        pass_load_fn<L, R0, NL, NT, true>(ctx, [&](int j, int q, int l) -> float2 {
+        pass_load_fn<L, R0, NL, NT, !CIRC>(ctx, [&](int j, int q, int l) -> float2 {
             const bool ok = lvalid(l);
             const float2 x = *at(base, q * PS, ok ? lane_bytes(j, l) : 0u);
             return ok ? x : make_float2(0.f, 0.f);
@@ -680,13 +688,13 @@ __host__ __device__ __forceinline__ void col_out_bwd_body(const Ctx& ctx, int bi
         float2* bdy = a.ws + poff;
         P0 s;
         load_cols(bdy, s);
-        PL t = fwd_from_regs<L, NL, NT, true>(ctx, T, s);
+        PL t = fwd_from_regs<L, NL, NT, !CIRC>(ctx, T, s);
         ctx.sync();  // every LDS read of the transform is done: T is free
         PL tu;
         if constexpr (DK) {
             P0 s2;
             load_cols(a.ws_u + poff, s2);
-            tu = fwd_from_regs<L, NL, NT, true>(ctx, T, s2);
+            tu = fwd_from_regs<L, NL, NT, !CIRC>(ctx, T, s2);
             ctx.sync();
         }
         if (o.t == 0) {
@@ -726,7 +734,7 @@ __host__ __device__ __forceinline__ void col_out_bwd_body(const Ctx& ctx, int bi
                 t.v[i][r] = kok[i] ? m : t.v[i][r];
             }
         }
-        inv_to_fn<L, NL, NT, true>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+        inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
             if (lvalid(l)) *at(bdy, q * PS, lane_bytes(j, l)) = x;
         });
         ctx.sync();  // the inverse's last LDS reads are done: T is free
@@ -752,7 +760,6 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
                                                      RowMeta* M)
 {
     constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
-    static_assert(!(BWD && CIRC), "the backward is built for the zero-padded mode");
     const Geom& g = a.g;
     const int P = a.nch * a.B;
     const int H = (P + 1) / 2;
@@ -832,7 +839,7 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
     ctx.sync();
     tile_fft<L, NP, LP, NT, true, false, !CIRC>(ctx, T);
     if constexpr (BWD) {
-        bwd_epilogue<L, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
+        bwd_epilogue<L, n, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
     } else {
         for (int idx = tid; idx < NP * n; idx += NT) {
             const int lp = idx / n, m = idx % n;
@@ -1101,11 +1108,11 @@ __host__ __device__ __forceinline__ void gate_reduce_body(const Ctx& ctx, int bi
 // input and output gradient of one signal) -> FFT -> separated 2U, 2DY ->
 // P_q = 2DY conj(2U) on the S slots (slot 0 packs the real bins 0 and S) into
 // dkw[q][S].
-template <int L, bool BF16, class Ctx>
+template <int L, bool BF16, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void corr1d_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                      RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
     const Geom& g = a.g;
     const int P = a.nch * a.B;
     const int tid = ctx.tid();
@@ -1133,7 +1140,7 @@ __host__ __device__ __forceinline__ void corr1d_body(const Ctx& ctx, int bid, co
         T[m * LP + lp] = z;
     }
     ctx.sync();
-    tile_fft<L, NP, LP, NT, false, true, false>(ctx, T);
+    tile_fft<L, NP, LP, NT, false, !CIRC, false>(ctx, T);
     for (int idx = tid; idx < NP * S; idx += NT) {
         const int lp = idx / S, k = idx % S;
         const RowMeta& md = M[lp];
@@ -1155,7 +1162,8 @@ __host__ __device__ __forceinline__ void corr1d_body(const Ctx& ctx, int bid, co
 // Kernel gradient, last step: inverse real FFT of the innermost axis over the
 // full length (every offset is kept), scaled by 1 / (4 prod N) (the planes
 // hold 4 DY conj(U) summed over the batch) and written to dK at the offsets
-// delta = unwrap(index); the wrap slot n of every axis carries nothing.
+// delta = unwrap(index); the wrap slot n of every axis carries nothing.  In
+// circular mode the index is the offset mod n, which is K's own index.
 // d >= 2: rows r, r+1 of a channel's dkw plane (N_out * N_mid rows, after the
 // outer inverse transforms); d = 1: the line pairs channels 2h, 2h+1 of the
 // chunk, each summing its B per-pair spectra.
@@ -1221,21 +1229,26 @@ __host__ __device__ __forceinline__ void dk_row_body(const Ctx& ctx, int bid, co
     for (int idx = tid; idx < NP * L; idx += NT) {
         const int lp = idx / L, t = idx % L;
         const RowMeta& md = M[lp];
-        const int d2 = unwrap(t, g.n_in, g.N_in);
-        if (!md.valid || d2 == kEmpty) continue;
+        // index into K's extent of padded-grid position m on an axis (kEmpty: the wrap slot)
+        auto kidx = [&](int m, int n, int N) {
+            if (g.circ) return m;
+            const int dl = unwrap(m, n, N);
+            return dl == kEmpty ? kEmpty : dl + n - 1;
+        };
+        const int e2 = kidx(t, g.n_in, g.N_in);
+        if (!md.valid || e2 == kEmpty) continue;
         const float2 z = T[t * LP + lp];
         for (int s2 = 0; s2 < 2; ++s2) {
             if (s2 == 1 && !md.valid1) break;
             const long long c = s2 ? md.w1 : md.w0;
-            int d0 = 0, d1 = 0;
+            int e0 = 0, e1 = 0;
             if (!one_d) {
                 const int row = (int)(s2 ? md.o1 : md.o0);
-                d0 = unwrap(row / g.N_mid, g.n_out, g.N_out);
-                d1 = unwrap(row % g.N_mid, g.n_mid, g.N_mid);
-                if (d0 == kEmpty || d1 == kEmpty) continue;
+                e0 = kidx(row / g.N_mid, g.n_out, g.N_out);
+                e1 = kidx(row % g.N_mid, g.n_mid, g.N_mid);
+                if (e0 == kEmpty || e1 == kEmpty) continue;
             }
-            a.dK[(a.c0 + c) * kl + ((long long)(d0 + g.n_out - 1) * g.ke_mid + (d1 + g.n_mid - 1)) * g.ke_in +
-                 (d2 + g.n_in - 1)] = (s2 ? z.y : z.x) * sc;
+            a.dK[(a.c0 + c) * kl + ((long long)e0 * g.ke_mid + e1) * g.ke_in + e2] = (s2 ? z.y : z.x) * sc;
         }
     }
 }

@@ -117,12 +117,12 @@ __global__ __launch_bounds__(row_nt(L)) void k_conv1d(ConvArgs a)
 template <int L, int NR>
 constexpr int bwd_min_waves() { return (NR == 1 && L == 512) ? 2 * bwd_nt(L, NR) / 64 / 4 : 1; }
 
-template <int L, int NR, bool DK>
+template <int L, int NR, bool DK, bool CIRC>
 __global__ __launch_bounds__(bwd_nt(L, NR), (bwd_min_waves<L, NR>())) void k_col_out_bwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
     __shared__ float2 T[L * NR * bwd_tw(L, NR)];
-    col_out_bwd_body<L, NR, DK>(make_ctx<L, bwd_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
+    col_out_bwd_body<L, NR, DK, CIRC>(make_ctx<L, bwd_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L>
@@ -133,13 +133,13 @@ __global__ __launch_bounds__(col_nt(L)) void k_plane_mid_inv(ConvArgs a)
     plane_mid_body<L, true>(make_ctx<L, col_nt(L), kPlanF>(TWL), (int)blockIdx.x, a.g, a.dkw, a.g.kmain, T);
 }
 
-template <int L, bool BF16>
+template <int L, bool BF16, bool CIRC>
 __global__ __launch_bounds__(row_nt(L)) void k_corr1d(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
     __shared__ RowMeta M[row_np(L)];
-    corr1d_body<L, BF16>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
+    corr1d_body<L, BF16, CIRC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
 template <int L>
@@ -406,7 +406,8 @@ hipError_t launch_zero(float* p, long long n, hipStream_t st)
     return last_error();
 }
 
-hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
+template <bool CIRC>
+static hipError_t backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
@@ -427,8 +428,8 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
         e = with_length(g.N_in, [&]<int L>() {
             const long long H = ((long long)a.nch * a.B + 1) / 2;
             mark();
-            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-            else hipLaunchKernelGGL((k_conv1d<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            if (a.bf16) hipLaunchKernelGGL((k_conv1d<L, true, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_conv1d<L, false, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
@@ -436,8 +437,8 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
         e = with_length(g.N_in, [&]<int L>() {
             mark();
             const unsigned grid = ceil_div((long long)a.nch * a.B, row_np(L));
-            if (a.bf16) hipLaunchKernelGGL((k_corr1d<L, true>), dim3(grid), dim3(row_nt(L)), 0, st, a);
-            else hipLaunchKernelGGL((k_corr1d<L, false>), dim3(grid), dim3(row_nt(L)), 0, st, a);
+            if (a.bf16) hipLaunchKernelGGL((k_corr1d<L, true, CIRC>), dim3(grid), dim3(row_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_corr1d<L, false, CIRC>), dim3(grid), dim3(row_nt(L)), 0, st, a);
             return last_error();
         });
         if (e != hipSuccess) return e;
@@ -450,12 +451,12 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
     const long long H = (long long)a.nch * a.B * (g.n_out * g.n_mid / 2);
     e = with_length(g.N_in, [&]<int L>() {
         mark();
-        if (ady.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, ady);
-        else hipLaunchKernelGGL((k_row_fwd<L, false, false>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, ady);
+        if (ady.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, false, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, ady);
+        else hipLaunchKernelGGL((k_row_fwd<L, false, false, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, ady);
         if (last_error() != hipSuccess || !dk) return last_error();
         mark();
-        if (au.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, au);
-        else hipLaunchKernelGGL((k_row_fwd<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, au);
+        if (au.bf16) hipLaunchKernelGGL((k_row_fwd<L, true, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, au);
+        else hipLaunchKernelGGL((k_row_fwd<L, false, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, au);
         return last_error();
     });
     if (e != hipSuccess) return e;
@@ -463,7 +464,7 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
         return with_length(g.N_mid, [&]<int L>() {
             const long long grid = (long long)arg.nch * arg.B * ceil_div((long long)g.n_out * g.S, col_tw(L));
             mark();
-            hipLaunchKernelGGL((k_col_mid<L, INV>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, arg);
+            hipLaunchKernelGGL((k_col_mid<L, INV, CIRC>), dim3((unsigned)grid), dim3(col_nt(L)), 0, st, arg);
             return last_error();
         });
     };
@@ -475,8 +476,8 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
         return with_length(g.N_out, [&]<int L>() {
             const long long grid = (long long)a.nch * (NR == 1 ? 1 : g.N_mid / 2) * ceil_div(g.S, bwd_tw(L, NR));
             mark();
-            if (dk) hipLaunchKernelGGL((k_col_out_bwd<L, NR, true>), dim3((unsigned)grid), dim3(bwd_nt(L, NR)), 0, st, a);
-            else hipLaunchKernelGGL((k_col_out_bwd<L, NR, false>), dim3((unsigned)grid), dim3(bwd_nt(L, NR)), 0, st, a);
+            if (dk) hipLaunchKernelGGL((k_col_out_bwd<L, NR, true, CIRC>), dim3((unsigned)grid), dim3(bwd_nt(L, NR)), 0, st, a);
+            else hipLaunchKernelGGL((k_col_out_bwd<L, NR, false, CIRC>), dim3((unsigned)grid), dim3(bwd_nt(L, NR)), 0, st, a);
             return last_error();
         });
     };
@@ -485,8 +486,8 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
     if (g.d == 3 && (e = col_mid.template operator()<true>(a)) != hipSuccess) return e;
     e = with_length(g.N_in, [&]<int L>() {
         mark();
-        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        else hipLaunchKernelGGL((k_row_inv<L, false, true>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        if (a.bf16) hipLaunchKernelGGL((k_row_inv<L, true, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else hipLaunchKernelGGL((k_row_inv<L, false, true, CIRC>), dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
         return last_error();
     });
     if (e != hipSuccess) return e;
@@ -501,6 +502,11 @@ hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
         if (e != hipSuccess) return e;
     }
     return dk_rows((long long)a.nch * (g.N_out * g.N_mid / 2));
+}
+
+hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
+{
+    return a.g.circ ? backward_chunk<true>(a, dk, st, tr) : backward_chunk<false>(a, dk, st, tr);
 }
 
 hipError_t launch_spectrum(const ConvArgs& a, hipStream_t st)

@@ -228,7 +228,7 @@ int hyenand_fftconv_bwd_traced(const void* x, const float* phi_alpha, const floa
  * dims[a] a power of two in [4, 1024].  The entry points mirror the
  * non-circular ones (same conventions, errors and K_hat layout, with N_a = n_a
  * and S = n_in / 2); a circular K_hat must only be used with
- * hyenand_fftconv_fwd_circ.  The minimum workspace is one channel,
+ * hyenand_fftconv_fwd_circ and hyenand_fftconv_bwd_circ.  The minimum workspace is one channel,
  * B * n_0 * (n_1 for 3-D) * S * 8 bytes (0 for d = 1).
  */
 size_t hyenand_kernel_spectrum_circ_bytes(int C, int d, const int64_t* dims);
@@ -239,6 +239,25 @@ size_t hyenand_fftconv_circ_workspace_min_bytes(int B, int C, int d, const int64
 int hyenand_fftconv_fwd_circ(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat, void* y,
                              int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
                              size_t workspace_bytes, void* stream);
+/*
+ * Backward of the circular mode: hyenand_fftconv_bwd with offsets modulo n,
+ *   du[j] = sum_i dy[i] K[(i - j) mod n],  dK_c[m] = sum_b sum_j dy[(j + m) mod n] u[j],
+ * dK laid out like the circular K ([C][dims], index = offset mod n); K_hat from
+ * hyenand_kernel_spectrum_circ.  Arguments, workspace rules and errors as for
+ * hyenand_fftconv_bwd, with the workspace sized by the _circ_ queries below.
+ */
+int hyenand_fftconv_bwd_circ(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                             const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C, int d,
+                             const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+size_t hyenand_fftconv_bwd_circ_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype, int with_dK);
+size_t hyenand_fftconv_bwd_circ_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype,
+                                                    int with_dK);
+/* hyenand_fftconv_bwd_circ with the launch trace of hyenand_fftconv_fwd_traced. */
+int hyenand_fftconv_bwd_circ_traced(const void* x, const float* phi_alpha, const float* phi_beta,
+                                    const void* K_hat, const void* dy, void* dx, float* dalpha, float* dbeta,
+                                    float* dK, int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                                    int* n_launches);
 /* hyenand_fftconv_fwd_circ with the launch trace of hyenand_fftconv_fwd_traced. */
 int hyenand_fftconv_fwd_circ_traced(const void* x, const float* phi_alpha, const float* phi_beta,
                                     const void* K_hat, void* y, int B, int C, int d, const int64_t* dims, int dtype,

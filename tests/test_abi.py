@@ -201,6 +201,29 @@ def test_circular_sizes_and_rejects(H):
     assert lib.hyenand_kernel_spectrum_circ(None, FAKE, 2, 2, _dims(8, 8), None) == 1
 
 
+def test_circular_bwd_sizes_and_rejects(H):
+    lib = H.get_lib()
+    # 2-D 64x32 circular, B=2: per channel two planes of B * n0 * S complex
+    # (S = 16), the kernel-gradient spectrum N0 * S and B * n0 / 2 float2.
+    assert lib.hyenand_fftconv_bwd_circ_workspace_min_bytes(2, 3, 2, _dims(64, 32), 0, 1) == \
+        (2 * 2 * 64 * 16 + 64 * 16 + 2 * 32) * 8
+    assert lib.hyenand_fftconv_bwd_circ_workspace_min_bytes(2, 3, 2, _dims(64, 32), 0, 0) == (2 * 64 * 16 + 2 * 32) * 8
+    # 1-D 64 circular, B=4: B * S complex (S = 32) and one float2 per signal
+    assert lib.hyenand_fftconv_bwd_circ_workspace_min_bytes(4, 2, 1, _dims(64), 0, 1) == (4 * 32 + 4) * 8
+    rec = lib.hyenand_fftconv_bwd_circ_workspace_bytes(2, 3, 2, _dims(64, 32), 1, 1)
+    assert rec == 3 * (2 * 2 * 64 * 16 + 64 * 16 + 2 * 32) * 8
+    for d, dims in [(1, _dims(2)), (2, _dims(4, 2)), (2, _dims(12, 8)), (1, _dims(2048))]:
+        assert lib.hyenand_fftconv_bwd_circ_workspace_bytes(1, 1, d, dims, 0, 1) == 0
+    dd = _dims(8, 8)
+    call = lambda x=FAKE, dy=FAKE, dx=FAKE, da=FAKE, B=1, C=1, d=2, dims=dd, dt=0, w=FAKE, wb=1 << 20: \
+        lib.hyenand_fftconv_bwd_circ(x, FAKE, FAKE, FAKE, dy, dx, da, FAKE, FAKE, B, C, d, dims, dt, w, wb, None)
+    assert call(x=None) == 1 and call(dy=None) == 1 and call(dx=MISALIGNED) == 1 and call(da=None) == 1
+    assert call(dims=_dims(2, 8)) == 2 and call(d=1, dims=_dims(4096)) == 2 and call(w=None) == 3
+    need = lib.hyenand_fftconv_bwd_circ_workspace_min_bytes(1, 1, 2, dd, 0, 1)
+    assert need > 0 and call(wb=need - 1) == 3
+    assert call(x=None, dy=None, dx=None, C=0) == 0
+
+
 def test_long_1d_sizes(H):
     """1-D signals longer than 1024 take the long path: the full N = 2n complex
     spectrum per channel (no Nyquist packing), N complex of workspace per pair,
