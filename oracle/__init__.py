@@ -27,6 +27,10 @@ Routes (all fp64, in ``oracle.c``):
     (summary, "Input dependent kernels via registers and FiLM": the kernel is
     conditioned on the whole sample): y[b,c,i] = sum_j u[b,c,j] K[b,c][i-j],
     K [B, C, *(2n-1)]; O1 / O2 applied per batch entry with that entry's kernels.
+  * ``bwd_direct_per_sample`` / ``bwd_fft_per_sample`` -- their backward: the
+    shared-kernel backward per batch entry with that entry's kernels, dK kept
+    per (b, c), dalpha and dbeta summed over the batch (the parameters are
+    shared by every sample).
   * ``bwd_direct_circ`` / ``bwd_fft_circ`` -- the backward of the circular mode
     (offsets modulo n; dK on the n offsets).
   * ``bwd_direct`` / ``bwd_points`` / ``bwd_fft`` -- the backward (vector-Jacobian
@@ -196,6 +200,31 @@ def fftconv_per_sample(x, alpha, beta, K, batch=None) -> np.ndarray:
         raise ValueError("per-sample kernels are [B, C, *(2n-1)]")
     bs = range(x.shape[0]) if batch is None else batch
     return np.concatenate([fftconv(x[b:b + 1], alpha, beta, K[b]) for b in bs], axis=0)
+
+
+def _bwd_per_sample(route, x, alpha, beta, K, dy, batch):
+    x, K, dy = _f32(x), _f32(K), _f32(dy)
+    if K.shape[:2] != x.shape[:2] or dy.shape != x.shape:
+        raise ValueError("per-sample kernels are [B, C, *(2n-1)], dy is shaped like x")
+    bs = range(x.shape[0]) if batch is None else batch
+    parts = [route(x[b:b + 1], alpha, beta, K[b], dy[b:b + 1]) for b in bs]
+    dx = np.concatenate([p[0] for p in parts], axis=0)
+    da = np.sum([p[1] for p in parts], axis=0)
+    db = np.sum([p[2] for p in parts], axis=0)
+    dK = np.stack([p[3] for p in parts])
+    return dx, da, db, dK
+
+
+def bwd_direct_per_sample(x, alpha, beta, K, dy, batch=None):
+    """O1 backward with one kernel per (b, c), for the listed batch entries (all
+    when None): (dx [len, C, *dims], dalpha [C], dbeta [C] summed over those
+    entries, dK [len, C, *(2n-1)]), fp64."""
+    return _bwd_per_sample(bwd_direct, x, alpha, beta, K, dy, batch)
+
+
+def bwd_fft_per_sample(x, alpha, beta, K, dy, batch=None):
+    """O2 backward with one kernel per (b, c); outputs as bwd_direct_per_sample."""
+    return _bwd_per_sample(bwd_fft, x, alpha, beta, K, dy, batch)
 
 
 def direct_circ(x, alpha, beta, K) -> np.ndarray:

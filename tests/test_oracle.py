@@ -329,3 +329,60 @@ def test_per_sample_kernels_match_brute_force():
     got = oracle.fftconv_per_sample(x2, a2, b2, Kb)
     assert _rel(got[0], oracle.direct(x2[:1], a2, b2, K2)[0]) < 1e-12
     assert _rel(got[1], oracle.direct(x2[1:], a2, b2, Kb[1])[0]) < 1e-12
+
+
+def _autograd_per_sample(x, a, b, K, dy):
+    """Gradients of sum(dy * y), y[b,c,i] = sum_j u[b,c,j] K[b,c][i-j] written
+    as a gather of each sample's Toeplitz matrix, by torch autograd (fp64)."""
+    import torch
+
+    B, C = x.shape[:2]
+    dims = x.shape[2:]
+    L = int(np.prod(dims))
+    grid = np.stack(np.meshgrid(*[np.arange(n) for n in dims], indexing="ij"), -1).reshape(-1, len(dims))
+    off = grid[:, None, :] - grid[None, :, :] + (np.asarray(dims) - 1)
+    flat = np.zeros(off.shape[:2], dtype=np.int64)
+    for ax, n in enumerate(dims):
+        flat = flat * (2 * n - 1) + off[..., ax]
+    idx = torch.from_numpy(flat)
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    at = torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+    Kt = torch.tensor(K, dtype=torch.float64, requires_grad=True)
+    xs = xt.reshape(B, C, L)
+    u = xs * torch.sigmoid(at[None, :, None] * xs + bt[None, :, None])
+    T = Kt.reshape(B, C, -1)[:, :, idx]
+    y = torch.einsum("bcij,bcj->bci", T, u)
+    loss = (y * torch.tensor(dy, dtype=torch.float64).reshape(B, C, L)).sum()
+    return [g.numpy() for g in torch.autograd.grad(loss, [xt, at, bt, Kt])]
+
+
+@pytest.mark.parametrize("dims", [(5,), (3, 4), (2, 3, 2)])
+def test_per_sample_bwd_matches_autograd_of_definition(dims):
+    """The per-sample backward (dK per (b, c), dalpha / dbeta summed over the
+    batch) against torch autograd of the definition with each sample's kernels;
+    the FFT route against the direct one; a planted mistake (dK summed over the
+    batch, the shared-kernel gradient) fails."""
+    B, C = 3, 2
+    x, a, b, _ = _rand_case(dims, C=C, B=B, seed=41)
+    rng = np.random.default_rng(42)
+    K = rng.standard_normal((B, C) + tuple(2 * n - 1 for n in dims)).astype(np.float32)
+    dy = rng.standard_normal(x.shape).astype(np.float32)
+    want = _autograd_per_sample(x, a, b, K, dy)
+    got = oracle.bwd_direct_per_sample(x, a, b, K, dy)
+    for g, w in zip(got, want):
+        assert g.shape == w.shape
+        assert _rel(g, w) < 1e-12
+    shared = np.broadcast_to(got[3].sum(axis=0), got[3].shape)
+    assert _rel(shared, want[3]) > 1e-3
+
+
+@pytest.mark.parametrize("dims", [(16,), (4, 8), (2, 4, 8)])
+def test_per_sample_bwd_fft_matches_direct(dims):
+    B, C = 3, 2
+    x, a, b, _ = _rand_case(dims, C=C, B=B, seed=43)
+    rng = np.random.default_rng(44)
+    K = rng.standard_normal((B, C) + tuple(2 * n - 1 for n in dims)).astype(np.float32)
+    dy = rng.standard_normal(x.shape).astype(np.float32)
+    for g, w in zip(oracle.bwd_fft_per_sample(x, a, b, K, dy), oracle.bwd_direct_per_sample(x, a, b, K, dy)):
+        assert _rel(g, w) < 1e-12
