@@ -28,6 +28,8 @@ METRIC = "Gvoxel·channels/s of gated N-D FFT conv fwd; % of HBM roofline (1 GPU
 METRIC_CIRC = "Gvoxel·channels/s of gated N-D FFT conv fwd, circular mode; % of HBM roofline (1 GPU)"
 METRIC_PS = "Gvoxel·channels/s of gated N-D FFT conv fwd, one kernel per (b, c); % of HBM roofline (1 GPU)"
 METRIC_BWD = "Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK); % of HBM roofline (1 GPU)"
+METRIC_BWD_PS = ("Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK), one kernel per (b, c); "
+                 "% of HBM roofline (1 GPU)")
 METRIC_BWD_CIRC = ("Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK), circular mode; "
                    "% of HBM roofline (1 GPU)")
 UNIT = "Gvoxel·channels/s"
@@ -239,7 +241,7 @@ def main():
                     help="zero-padded non-circular convolution (default) or the circular mode")
     ap.add_argument("--kernel", choices=("shared", "per-sample"), default="shared",
                     help="one kernel per channel (default) or one per (b, c): input-dependent kernels "
-                         "(zero-padded forward only)")
+                         "(zero-padded mode only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ws-mb", type=float, default=None,
                     help="workspace size in MiB (default: the library's recommendation)")
@@ -272,9 +274,6 @@ def main():
     wl = {w.name: w for w in synth.WORKLOADS}[args.workload]
     circ = args.boundary == "circular"
     ps = args.kernel == "per-sample"
-    if ps and args.which == "bwd":
-        print("bench.py: the backward is built for shared kernels only", file=sys.stderr)
-        return 2
     if circ and ps:
         print("bench.py: per-sample kernels are built for the zero-padded mode only", file=sys.stderr)
         return 2
@@ -313,11 +312,13 @@ def main():
     bwd = args.which == "bwd"
     if bwd:
         dy = synth.draw_dy(wl.dims, wl.B, wl.C, wl.dtype, wl.seed).to(dev)
+        kshape = ((wl.B,) if ps else ()) + (wl.C,) + (tuple(wl.dims) if circ else tuple(2 * n - 1 for n in wl.dims))
         outs = (torch.empty_like(x), torch.empty(wl.C, device=dev), torch.empty(wl.C, device=dev),
-                torch.empty((wl.C,) + (tuple(wl.dims) if circ else tuple(2 * n - 1 for n in wl.dims)), device=dev))
-        ws_bytes = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, circular=circ)
+                torch.empty(kshape, device=dev))
+        B_ws = 1 if ps else wl.B  # the per-sample backward runs the batch entries one at a time
+        ws_bytes = H.bwd_workspace_bytes(B_ws, wl.C, wl.dims, x.dtype, circular=circ)
         if args.ws_mb is not None:
-            ws_bytes = max(H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True, circular=circ),
+            ws_bytes = max(H.bwd_workspace_bytes(B_ws, wl.C, wl.dims, x.dtype, minimum=True, circular=circ),
                            int(args.ws_mb * 2**20))
     elif circ:
         y = torch.empty_like(x)
@@ -333,7 +334,8 @@ def main():
 
     def call():
         if bwd:
-            (H.fftconv_bwd_circ if circ else H.fftconv_bwd)(x, al, be, kh, dy, *outs, workspace=ws)
+            f = H.fftconv_bwd_circ if circ else (H.fftconv_bwd_per_sample if ps else H.fftconv_bwd)
+            f(x, al, be, kh, dy, *outs, workspace=ws)
         elif circ:
             H.fftconv_fwd_circ(x, al, be, kh, y=y, workspace=ws)
         elif ps:
@@ -343,7 +345,7 @@ def main():
 
     def traced(events):
         if bwd:
-            return H.fftconv_bwd_traced(x, al, be, kh, dy, outs, ws, events, circular=circ)
+            return H.fftconv_bwd_traced(x, al, be, kh, dy, outs, ws, events, circular=circ, per_sample=ps)
         if circ:
             return H.fftconv_fwd_circ_traced(x, al, be, kh, y, ws, events)
         if ps:
@@ -415,12 +417,13 @@ def main():
 
     g = _geom(wl.dims, circ)
     if bwd:
-        per_ch = H.bwd_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True, circular=circ)
+        per_ch = H.bwd_workspace_bytes(B_ws, wl.C, wl.dims, x.dtype, minimum=True, circular=circ)
         nch = min(wl.C, ws_bytes // per_ch)
         nch = -(-wl.C // -(-wl.C // nch))  # balanced chunks, as the library splits them
         plan = {"chunk_channels": nch}
         # x, dy and dx once, K_hat once, dK once (alpha, beta, dalpha, dbeta negligible)
-        bytes_min = 3 * wl.B * wl.C * wl.voxels * es + wl.C * g["ksz"] * 8 + wl.C * g["kl"] * 4
+        nk = wl.C * (wl.B if ps else 1)
+        bytes_min = 3 * wl.B * wl.C * wl.voxels * es + nk * g["ksz"] * 8 + nk * g["kl"] * 4
         names = H.BWD_PASS_NAMES[(wl.d, True)]
     else:
         per_ch = (H.circ_workspace_bytes if circ else H.workspace_bytes)(wl.B, wl.C, wl.dims, x.dtype, minimum=True)
@@ -444,7 +447,10 @@ def main():
     dominant = max(per_pass, key=lambda nm: sum(per_pass[nm]))
     dom_s = sum(per_pass[dominant]) / len(per_pass[dominant]) / 1e3
     nch = plan["chunk_channels"]
-    by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch * (wl.B if ps else 1), es, circ)
+    if bwd and ps:  # one batch entry per launch, its own spectra
+        by, fl = pass_model(dominant, wl.dims, nch, nch, es, circ)
+    else:
+        by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch * (wl.B if ps else 1), es, circ)
     kernel_label = KERNEL_LABEL[dominant]
     hbm = {"bound": "hbm", "achieved": by / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     alu = {"bound": "alu", "achieved": fl / dom_s / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s"}
@@ -458,7 +464,7 @@ def main():
     voxch = wl.B * wl.C * wl.voxels
     value = voxch / (ms_per_step / 1e3) / 1e9
     out = {
-        "metric": ((METRIC_BWD_CIRC if circ else METRIC_BWD) if bwd
+        "metric": ((METRIC_BWD_CIRC if circ else (METRIC_BWD_PS if ps else METRIC_BWD)) if bwd
                    else (METRIC_CIRC if circ else (METRIC_PS if ps else METRIC))),
         "value": value,
         "unit": UNIT,

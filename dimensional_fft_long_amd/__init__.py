@@ -21,7 +21,8 @@ zero outside the grid.  Entry points mirror ``include/hyenand.h``:
   operation patterns", "Concrete implementation pattern (PyTorch)")
 * ``HyenaConvolutionFunction`` -- the autograd wrapper of that pattern
 * ``fftconv_fwd_per_sample(x, alpha, beta, K_hat)`` -- input-dependent kernels:
-  K_hat = kernel_spectrum(K) of kernels [B, C, *(2n-1)], one per (b, c)
+  K_hat = kernel_spectrum(K) of kernels [B, C, *(2n-1)], one per (b, c);
+  ``fftconv_bwd_per_sample(...)`` its backward (dK per (b, c))
 * ``kernel_spectrum_circ(K)`` / ``fftconv_fwd_circ(...)`` /
   ``fftconv_bwd_circ(...)`` -- the circular mode (gist.science summary,
   "Boundary handling": periodic grids, no padding; K is [C, *dims] indexed by
@@ -50,7 +51,8 @@ EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_
            "hyenand_fftconv_circ_workspace_min_bytes", "hyenand_fftconv_fwd_circ", "hyenand_fftconv_fwd_circ_traced",
            "hyenand_fftconv_fwd_per_sample", "hyenand_fftconv_fwd_per_sample_traced", "hyenand_fftconv_bwd_circ",
            "hyenand_fftconv_bwd_circ_workspace_bytes", "hyenand_fftconv_bwd_circ_workspace_min_bytes",
-           "hyenand_fftconv_bwd_circ_traced")
+           "hyenand_fftconv_bwd_circ_traced", "hyenand_fftconv_bwd_per_sample",
+           "hyenand_fftconv_bwd_per_sample_traced")
 
 _lib = None
 
@@ -98,6 +100,11 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_bwd_circ_traced.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I,
                                                     ctypes.POINTER(I)]
     lib.hyenand_fftconv_bwd_circ_traced.restype = I
+    lib.hyenand_fftconv_bwd_per_sample.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_fftconv_bwd_per_sample.restype = I
+    lib.hyenand_fftconv_bwd_per_sample_traced.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, I, P, SZ, P, P,
+                                                          I, ctypes.POINTER(I)]
+    lib.hyenand_fftconv_bwd_per_sample_traced.restype = I
     lib.hyenand_fftconv_bwd_circ_workspace_bytes.argtypes = [I, I, I, P, I, I]
     lib.hyenand_fftconv_bwd_circ_workspace_bytes.restype = SZ
     lib.hyenand_fftconv_bwd_circ_workspace_min_bytes.argtypes = [I, I, I, P, I, I]
@@ -290,7 +297,8 @@ def _bwd_workspace(B, C, dims, dtype, with_dK, device, circular=False):
     return buf, nbytes
 
 
-def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, circular=False):
+def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, circular=False,
+              per_sample=False):
     if not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous device tensor")
     if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_cuda or not dy.is_contiguous():
@@ -302,16 +310,18 @@ def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspa
             raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
     if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
-    if K_hat.numel() * 8 < (spectrum_circ_bytes(C, dims) if circular else spectrum_bytes(C, dims)):
+    need = spectrum_circ_bytes(C, dims) if circular else spectrum_bytes(C, dims) * (B if per_sample else 1)
+    if K_hat.numel() * 8 < need:
         raise ValueError("K_hat is smaller than the spectrum of this shape")
     dx = torch.empty_like(x) if dx is None else dx
     dalpha = torch.empty(C, dtype=torch.float32, device=x.device) if dalpha is None else dalpha
     dbeta = torch.empty(C, dtype=torch.float32, device=x.device) if dbeta is None else dbeta
     if with_dK and dK is None:
         kdims = dims if circular else tuple(2 * n - 1 for n in dims)
-        dK = torch.empty((C,) + kdims, dtype=torch.float32, device=x.device)
+        dK = torch.empty(((B,) if per_sample else ()) + (C,) + kdims, dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace, ws_bytes = _bwd_workspace(B, C, dims, x.dtype, dK is not None, x.device, circular)
+        workspace, ws_bytes = _bwd_workspace(1 if per_sample else B, C, dims, x.dtype, dK is not None, x.device,
+                                             circular)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(dy.data_ptr()),
@@ -344,19 +354,24 @@ BWD_PASS_NAMES = {
 }
 
 
-def fftconv_bwd_traced(x, alpha, beta, K_hat, dy, outs, workspace, events, stream=None, circular=False) -> int:
-    """fftconv_bwd (fftconv_bwd_circ with ``circular``) into ``outs`` = (dx,
-    dalpha, dbeta, dK or None), recording ``events`` before each kernel launch
-    and after the last; returns the launch count."""
+def fftconv_bwd_traced(x, alpha, beta, K_hat, dy, outs, workspace, events, stream=None, circular=False,
+                       per_sample=False) -> int:
+    """fftconv_bwd (fftconv_bwd_circ with ``circular``, fftconv_bwd_per_sample
+    with ``per_sample``) into ``outs`` = (dx, dalpha, dbeta, dK or None),
+    recording ``events`` before each kernel launch and after the last; returns
+    the launch count."""
     dx, dalpha, dbeta, dK = outs
-    args, _ = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, dK is not None, workspace, circular)
+    args, _ = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, dK is not None, workspace, circular,
+                        per_sample)
     st = torch.cuda.current_stream() if stream is None else stream
     for e in events:
         if e.cuda_event == 0:
             e.record(st)
     arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     n = ctypes.c_int(0)
-    f = get_lib().hyenand_fftconv_bwd_circ_traced if circular else get_lib().hyenand_fftconv_bwd_traced
+    lib = get_lib()
+    f = (lib.hyenand_fftconv_bwd_circ_traced if circular else
+         (lib.hyenand_fftconv_bwd_per_sample_traced if per_sample else lib.hyenand_fftconv_bwd_traced))
     rc = f(*args, _stream(stream), arr, len(events), ctypes.byref(n))
     if rc != OK:
         raise HyenandError(rc, "fftconv_bwd_traced")
@@ -517,6 +532,19 @@ def fftconv_fwd_per_sample(x, alpha, beta, K_hat, y=None, workspace=None, stream
     if rc != OK:
         raise HyenandError(rc, "fftconv_fwd_per_sample")
     return y
+
+
+def fftconv_bwd_per_sample(x, alpha, beta, K_hat, dy, dx=None, dalpha=None, dbeta=None, dK=None,
+                           with_dK: bool = True, workspace=None, stream=None):
+    """Backward of fftconv_fwd_per_sample for the output gradient dy; K_hat from
+    kernel_spectrum_per_sample.  Returns (dx, dalpha [C], dbeta [C],
+    dK [B, C, *(2*dims-1)] or None): one kernel gradient per (b, c).  The
+    workspace is that of a batch of one (bwd_workspace_bytes(1, C, dims))."""
+    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, per_sample=True)
+    rc = get_lib().hyenand_fftconv_bwd_per_sample(*args, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_bwd_per_sample")
+    return outs
 
 
 def fftconv_fwd_per_sample_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None) -> int:

@@ -264,7 +264,7 @@ size_t hyenand_fftconv_bwd_circ_workspace_min_bytes(int B, int C, int d, const i
 static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta, const void* K_hat, const void* dy,
                             void* dx, float* dalpha, float* dbeta, float* dK, int B, int C, int d,
                             const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                            LaunchTrace* trace, bool circ)
+                            LaunchTrace* trace, bool circ, bool per_sample = false)
 {
     if (B < 0 || C < 0) return HYENAND_ERR_INVALID_ARG;
     if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
@@ -277,11 +277,11 @@ static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta
         return HYENAND_ERR_INVALID_ARG;
     const bool dk = dK != nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const long long kl = (long long)g.ke_out * g.ke_mid * g.ke_in;
     if (B == 0) {
-        // Sums over an empty batch.
-        const long long kl = (long long)g.ke_out * g.ke_mid * g.ke_in;
+        // Sums over an empty batch (the per-sample dK has no entries).
         if (launch_zero(dalpha, C, st) != hipSuccess || launch_zero(dbeta, C, st) != hipSuccess ||
-            (dk && launch_zero(dK, (long long)C * kl, st) != hipSuccess))
+            (dk && !per_sample && launch_zero(dK, (long long)C * kl, st) != hipSuccess))
             return HYENAND_ERR_HIP;
         if (trace) trace->mark(st);
         return HYENAND_OK;
@@ -293,7 +293,10 @@ static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta
         return HYENAND_ERR_INVALID_ARG;
     if (!workspace) return HYENAND_ERR_WORKSPACE;
     if (!aligned(workspace, 8)) return HYENAND_ERR_INVALID_ARG;
-    int per = bwd_chunk_channels(g, B, C, dk, workspace_bytes);
+    // Per-sample kernels: the batch entries run one after the other, each as a
+    // batch of one with its own spectra and dK, dalpha / dbeta accumulated.
+    const int Bk = per_sample ? 1 : B;
+    int per = bwd_chunk_channels(g, Bk, C, dk, workspace_bytes);
     if (per < 1) return HYENAND_ERR_WORKSPACE;
     const int chunks = (C + per - 1) / per;
     per = (C + chunks - 1) / chunks;  // balanced chunks
@@ -308,19 +311,31 @@ static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta
     a.dbeta = dbeta;
     a.dK = dK;
     a.g = g;
-    a.B = B;
+    a.B = Bk;
     a.C = C;
     a.bf16 = dtype == HYENAND_BF16;
     float2* w = static_cast<float2*>(workspace);
-    const long long plane = (long long)per * B * g.wsp;
+    const long long plane = (long long)per * Bk * g.wsp;
     a.ws = w;
     a.ws_u = dk ? w + plane : nullptr;
     a.dkw = dk ? w + plane * 2 : nullptr;
-    a.part = w + plane * (dk ? 2 : 1) + (dk ? (g.d == 1 ? (long long)per * B * g.S : (long long)per * g.kmain) : 0);
-    for (int c0 = 0; c0 < C; c0 += per) {
-        a.c0 = c0;
-        a.nch = (C - c0) < per ? (C - c0) : per;
-        if (launch_backward_chunk(a, dk, st, trace) != hipSuccess) return HYENAND_ERR_HIP;
+    a.part = w + plane * (dk ? 2 : 1) + (dk ? (g.d == 1 ? (long long)per * Bk * g.S : (long long)per * g.kmain) : 0);
+    const int nb = per_sample ? B : 1;
+    for (int b = 0; b < nb; ++b) {
+        if (per_sample) {
+            const long long eo = (long long)b * C * g.vox * (long long)es;  // byte offset of sample b
+            a.x = static_cast<const char*>(x) + eo;
+            a.dy = static_cast<const char*>(dy) + eo;
+            a.y = static_cast<char*>(dx) + eo;
+            a.khat = static_cast<const float2*>(K_hat) + (long long)b * C * g.ksz;
+            a.dK = dk ? dK + (long long)b * C * kl : nullptr;
+            a.accum = b > 0;
+        }
+        for (int c0 = 0; c0 < C; c0 += per) {
+            a.c0 = c0;
+            a.nch = (C - c0) < per ? (C - c0) : per;
+            if (launch_backward_chunk(a, dk, st, trace) != hipSuccess) return HYENAND_ERR_HIP;
+        }
     }
     if (trace) trace->mark(st);
     return HYENAND_OK;
@@ -370,6 +385,29 @@ int hyenand_fftconv_bwd_circ_traced(const void* x, const float* phi_alpha, const
 }
 
 // ------------------------------------------------------- per-sample kernels
+int hyenand_fftconv_bwd_per_sample(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                                   const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C,
+                                   int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream)
+{
+    return fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
+                            workspace, workspace_bytes, stream, nullptr, false, true);
+}
+
+int hyenand_fftconv_bwd_per_sample_traced(const void* x, const float* phi_alpha, const float* phi_beta,
+                                          const void* K_hat, const void* dy, void* dx, float* dalpha, float* dbeta,
+                                          float* dK, int B, int C, int d, const int64_t* dims, int dtype,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* const* events, int n_events, int* n_launches)
+{
+    if (n_events < 0 || (n_events > 0 && !events)) return HYENAND_ERR_INVALID_ARG;
+    LaunchTrace tr{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events, 0};
+    const int rc = fftconv_bwd_impl(x, phi_alpha, phi_beta, K_hat, dy, dx, dalpha, dbeta, dK, B, C, d, dims, dtype,
+                                    workspace, workspace_bytes, stream, &tr, false, true);
+    if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
+    return rc;
+}
+
 int hyenand_fftconv_fwd_per_sample(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y,
                                    int B, int C, int d, const int64_t* dims, int dtype, void* workspace,
                                    size_t workspace_bytes, void* stream)

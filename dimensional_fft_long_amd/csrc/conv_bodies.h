@@ -506,8 +506,8 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     const int tid = ctx.tid();
     // Position stride of the planes; element (pos = j + q, line l) is at q*PS
     // (wave-uniform, q a constant of the unrolled loops) plus the lane's byte
-    // offset 8*(j*PS + row*lt + u0 + l%TW), which stays below 4 GiB (j < L/R
-    // for R >= 2 and one channel's spectrum is at most 4 GiB).
+    // offset 8*(j*PS + row*lt + u0 + l%TW) inside one slot tile of a plane
+    // (N_out N_mid lt complex with N <= 2048, lt <= 64: at most 2 GiB).
     const long long PS = (long long)g.N_mid * g.lt;
     auto lane_bytes = [&](const OutView& v, int j, int l) -> unsigned {
         return 8u * ((unsigned)j * (unsigned)PS + (unsigned)v.o.rows[l / TW] * (unsigned)g.lt + (unsigned)(v.u0 + l % TW));
@@ -1055,7 +1055,9 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
 // dalpha, dbeta of the chunk's channel `bid`: the sum of its B * pair_lines
 // partial sums, in a fixed order (each thread sums a strided subset into
 // U independent fp64 accumulators, so that U loads are in flight at once;
-// then an LDS tree).  R: LDS scratch of 2 * NT doubles.
+// then an LDS tree).  R: LDS scratch of 2 * NT doubles.  accum: the sums are
+// added to the values already in dalpha, dbeta (the per-sample backward runs
+// one batch entry after the other).
 template <int NT, class Ctx>
 __host__ __device__ __forceinline__ void gate_reduce_body(const Ctx& ctx, int bid, const ConvArgs& a, double* R)
 {
@@ -1099,8 +1101,9 @@ __host__ __device__ __forceinline__ void gate_reduce_body(const Ctx& ctx, int bi
         ctx.sync();
     }
     if (tid == 0) {
-        a.dalpha[a.c0 + bid] = (float)R[0];
-        a.dbeta[a.c0 + bid] = (float)R[NT];
+        const int c = a.c0 + bid;
+        a.dalpha[c] = (float)(R[0] + (a.accum ? (double)a.dalpha[c] : 0.0));
+        a.dbeta[c] = (float)(R[NT] + (a.accum ? (double)a.dbeta[c] : 0.0));
     }
 }
 

@@ -208,6 +208,8 @@ struct ConvArgs {
     int c0;                 // first channel of this chunk
     int nch;                // channels in this chunk (pairs = nch * B, channel-major)
     int bf16;               // I/O dtype: 0 fp32, 1 bf16
+    int accum;              // backward: add dalpha / dbeta to what the output holds (later batch entries
+                            // of the per-sample backward)
     // Backward only (y then holds dx):
     const void* dy;         // [B][C][vox], dtype of x
     float2* ws_u;           // gated-input planes, like ws (when dK is wanted)

@@ -287,6 +287,31 @@ int hyenand_fftconv_fwd_per_sample_traced(const void* x, const float* phi_alpha,
                                           int dtype, void* workspace, size_t workspace_bytes, void* stream,
                                           void* const* events, int n_events, int* n_launches);
 
+/*
+ * Backward with input-dependent kernels: the gradients of
+ * y[b,c,i] = sum_j phi_c(x[b,c,j]) x[b,c,j] K_{b,c}[i - j] for the output
+ * gradient dy, by the chain rule as for hyenand_fftconv_bwd but with each
+ * batch entry's own kernel:
+ *   du[b,c,j] = sum_i dy[b,c,i] K_{b,c}[i - j],  dK_{b,c}[l] = sum_j dy[b,c,j+l] u[b,c,j],
+ * dalpha_c and dbeta_c summed over the batch.  K_hat: the [B][C] spectra of
+ * hyenand_fftconv_fwd_per_sample.  dK (nullable): fp32 [B][C][2n_0-1]..[2n_{d-1}-1],
+ * one kernel gradient per (b, c), every element written.  The batch entries
+ * run one after the other, each as a batch of one, so the workspace is sized
+ * by hyenand_fftconv_bwd_workspace_bytes(1, C, ...) (any size from the
+ * _min_bytes of B = 1 upward works).  Other arguments, errors and limits as for
+ * hyenand_fftconv_bwd (zero-padded boundary, n <= 1024).
+ */
+int hyenand_fftconv_bwd_per_sample(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                                   const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C,
+                                   int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+/* hyenand_fftconv_bwd_per_sample with the launch trace of hyenand_fftconv_fwd_traced. */
+int hyenand_fftconv_bwd_per_sample_traced(const void* x, const float* phi_alpha, const float* phi_beta,
+                                          const void* K_hat, const void* dy, void* dx, float* dalpha, float* dbeta,
+                                          float* dK, int B, int C, int d, const int64_t* dims, int dtype,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* const* events, int n_events, int* n_launches);
+
 #ifdef __cplusplus
 }
 #endif

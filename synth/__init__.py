@@ -70,6 +70,11 @@ WORKLOADS = [
     # long 1-D sequence (the summary's genomics context, "Results": throughput up to 10M tokens)
     Workload("1d_2097152_b1_c8_bf16", (2097152,), 1, 8, "bf16", 1005),
     Workload("1d_8388608_b1_c4_bf16", (8388608,), 1, 4, "bf16", 1006),
+    # the explainer's volumetric examples ("Quantified performance impact": a
+    # 512x512x64 tensor of 16M voxels in fp32; "Empirical validation": a
+    # 1024x1024x256 climate grid); the pages give no channel count
+    Workload("3d_512x512x64_b1_c16_f32", (512, 512, 64), 1, 16, "f32", 1007),
+    Workload("3d_1024x1024x256_b1_c2_f32", (1024, 1024, 256), 1, 2, "f32", 1008),
 ]
 
 

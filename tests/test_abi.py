@@ -224,6 +224,19 @@ def test_circular_bwd_sizes_and_rejects(H):
     assert call(x=None, dy=None, dx=None, C=0) == 0
 
 
+def test_per_sample_bwd_rejects(H):
+    lib = H.get_lib()
+    dd = _dims(8, 8)
+    call = lambda x=FAKE, dy=FAKE, dx=FAKE, db=FAKE, B=2, C=1, d=2, dims=dd, dt=0, w=FAKE, wb=1 << 20: \
+        lib.hyenand_fftconv_bwd_per_sample(x, FAKE, FAKE, FAKE, dy, dx, FAKE, db, FAKE, B, C, d, dims, dt, w, wb, None)
+    assert call(x=None) == 1 and call(dy=None) == 1 and call(dx=MISALIGNED) == 1 and call(db=None) == 1
+    assert call(dims=_dims(8, 6)) == 2 and call(d=1, dims=_dims(4096)) == 2 and call(w=None) == 3
+    # the workspace of a batch of one is enough, whatever B
+    need = lib.hyenand_fftconv_bwd_workspace_min_bytes(1, 1, 2, dd, 0, 1)
+    assert call(wb=need - 1) == 3
+    assert call(x=None, dy=None, dx=None, C=0) == 0
+
+
 def test_long_1d_sizes(H):
     """1-D signals longer than 1024 take the long path: the full N = 2n complex
     spectrum per channel (no Nyquist packing), N complex of workspace per pair,

@@ -215,6 +215,20 @@ def test_workload_3d_512_bf16(H):
     assert err <= TOL[wl.dtype]
 
 
+@pytest.mark.timeout(600)
+def test_workload_3d_512x512x64(H):
+    wl = synth.WORKLOADS[7]
+    err = _full_workload(H, wl, o2_pairs=[0], sample_pairs=[(0, 5), (0, 15)], per_pair=8)
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.timeout(600)
+def test_workload_3d_1024x1024x256(H):
+    wl = synth.WORKLOADS[8]
+    err = _full_workload(H, wl, o2_pairs=[], sample_pairs=[(0, 0), (0, 1)], per_pair=4)
+    assert err <= TOL[wl.dtype]
+
+
 # ------------------------------------------------------- channel chunking
 
 def test_launch_plan_and_balanced_chunks(H):

@@ -256,3 +256,17 @@ def test_workload_3d_512_bf16(H):
     wl = synth.WORKLOADS[4]
     _check(_full(H, wl, fft_chans=[], sample_pairs=[(0, 2)], per_pair=3, k_chans=[1], per_chan=2,
                  param_property=True), wl.dtype)
+
+
+@pytest.mark.timeout(600)
+def test_workload_3d_512x512x64(H):
+    wl = synth.WORKLOADS[7]
+    _check(_full(H, wl, fft_chans=[], sample_pairs=[(0, 3)], per_pair=6, k_chans=[9], per_chan=4,
+                 param_property=True), wl.dtype)
+
+
+@pytest.mark.timeout(600)
+def test_workload_3d_1024x1024x256(H):
+    wl = synth.WORKLOADS[8]
+    _check(_full(H, wl, fft_chans=[], sample_pairs=[(0, 1)], per_pair=3, k_chans=[0], per_chan=2,
+                 param_property=True), wl.dtype)
