@@ -127,6 +127,27 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
         N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
         by = P * N * 8 + P * g["vox"] * es
         fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6
+    elif name in ("lng_col_fwd_dy", "lng_col_fwd_u"):
+        by, fl = pass_model("lng_col_fwd", dims, P, nch, es, circ)
+        if name == "lng_col_fwd_dy":
+            fl -= P * g["vox"] * 5  # no gate
+    elif name == "lng_row_du":
+        return pass_model("lng_row", dims, P, nch, es, circ)
+    elif name == "lng_row_dk":
+        # dy and u rows read, the channel's kernel-gradient rows written
+        N = 2 * g["ni"]
+        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
+        by = 2 * P * N * 8 + nch * N * 8
+        fl = (2 * P + nch) * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 8
+    elif name == "lng_col_inv_bwd":
+        by, fl = pass_model("lng_col_inv", dims, P, nch, es, circ)
+        by += P * g["vox"] * es  # x read again for the gate derivative
+        fl += P * g["vox"] * 14
+    elif name == "lng_col_dk":
+        N = 2 * g["ni"]
+        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
+        by = nch * N * 8 + nch * (2 * g["ni"] - 1) * 4
+        fl = nch * N2 * 5.0 * (N // N2) * math.log2(N // N2) + nch * N * 6
     elif name == "corr1d":
         by = 2 * P * g["vox"] * es + P * g["S"] * 8
         fl = _fft_flops(g["Ni"], P, pr) + P * g["S"] * 10 + P * g["vox"] * 5
@@ -140,7 +161,9 @@ KERNEL_LABEL = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_co
                 "col_mid_fwd_dy": "k_col_mid", "col_mid_fwd_u": "k_col_mid", "col_out_bwd": "k_col_out_bwd",
                 "row_inv_bwd": "k_row_inv", "gate_reduce": "k_gate_reduce", "mid_inv_dk": "k_plane_mid_inv",
                 "dk_row": "k_dk_row", "conv1d_bwd": "k_conv1d", "corr1d": "k_corr1d", "lng_col_fwd": "k_lng_col_fwd",
-                "lng_row": "k_lng_row", "lng_col_inv": "k_lng_col_inv"}
+                "lng_row": "k_lng_row", "lng_col_inv": "k_lng_col_inv", "lng_col_fwd_dy": "k_lng_col_fwd",
+                "lng_col_fwd_u": "k_lng_col_fwd", "lng_row_dk": "k_lng_row_dk", "lng_row_du": "k_lng_row",
+                "lng_col_inv_bwd": "k_lng_col_inv", "lng_col_dk": "k_lng_col_dk"}
 
 
 def _src_hash():
@@ -424,7 +447,10 @@ def main():
         # x, dy and dx once, K_hat once, dK once (alpha, beta, dalpha, dbeta negligible)
         nk = wl.C * (wl.B if ps else 1)
         bytes_min = 3 * wl.B * wl.C * wl.voxels * es + nk * g["ksz"] * 8 + nk * g["kl"] * 4
-        names = H.BWD_PASS_NAMES[(wl.d, True)]
+        long1d = wl.d == 1 and wl.dims[0] > 1024
+        names = H.BWD_PASS_NAMES[("long" if long1d else wl.d, True)]
+        if long1d:
+            bytes_min = 3 * wl.B * wl.C * wl.voxels * es + wl.C * 2 * wl.dims[0] * 8 + wl.C * g["kl"] * 4
     else:
         per_ch = (H.circ_workspace_bytes if circ else H.workspace_bytes)(wl.B, wl.C, wl.dims, x.dtype, minimum=True)
         if per_ch > 0:

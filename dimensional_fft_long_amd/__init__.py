@@ -351,6 +351,10 @@ BWD_PASS_NAMES = {
     (3, False): ("row_fwd_dy", "col_mid_fwd_dy", "col_out_bwd", "col_mid_inv", "row_inv_bwd", "gate_reduce"),
     (3, True): ("row_fwd_dy", "row_fwd_u", "col_mid_fwd_dy", "col_mid_fwd_u", "col_out_bwd", "col_mid_inv",
                 "row_inv_bwd", "gate_reduce", "mid_inv_dk", "dk_row"),
+    # 1-D signals longer than 1024 (four-step transforms)
+    ("long", False): ("lng_col_fwd_dy", "lng_row_du", "lng_col_inv_bwd", "gate_reduce"),
+    ("long", True): ("lng_col_fwd_dy", "lng_col_fwd_u", "lng_row_dk", "lng_row_du", "lng_col_inv_bwd", "gate_reduce",
+                     "lng_col_dk"),
 }
 
 

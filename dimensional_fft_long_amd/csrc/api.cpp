@@ -236,7 +236,7 @@ int hyenand_fftconv_fwd_circ_traced(const void* x, const float* alpha, const flo
 static size_t bwd_workspace(int B, int C, int d, const int64_t* dims, int dtype, int with_dK, bool circ, bool minimum)
 {
     Geom g;
-    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g, circ) || g.lng)
+    if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g, circ))
         return 0;
     return minimum ? bwd_channel_bytes(g, B, with_dK != 0) : recommended_bwd_workspace(g, B, C, with_dK != 0);
 }
@@ -271,7 +271,7 @@ static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta
     if (d < 1 || d > 3) return HYENAND_ERR_UNSUPPORTED;
     if (!dims) return HYENAND_ERR_INVALID_ARG;
     Geom g;
-    if (!make_geom(d, dims, &g, circ) || g.lng) return HYENAND_ERR_UNSUPPORTED;
+    if (!make_geom(d, dims, &g, circ)) return HYENAND_ERR_UNSUPPORTED;
     if (C == 0) return HYENAND_OK;
     if (!dalpha || !dbeta || !aligned(dalpha, 4) || !aligned(dbeta, 4) || (dK && !aligned(dK, 4)))
         return HYENAND_ERR_INVALID_ARG;
@@ -319,7 +319,8 @@ static int fftconv_bwd_impl(const void* x, const float* alpha, const float* beta
     a.ws = w;
     a.ws_u = dk ? w + plane : nullptr;
     a.dkw = dk ? w + plane * 2 : nullptr;
-    a.part = w + plane * (dk ? 2 : 1) + (dk ? (g.d == 1 ? (long long)per * Bk * g.S : (long long)per * g.kmain) : 0);
+    a.part = w + plane * (dk ? 2 : 1) +
+             (dk ? ((g.d == 1 && !g.lng) ? (long long)per * Bk * g.S : (long long)per * g.kmain) : 0);
     const int nb = per_sample ? B : 1;
     for (int b = 0; b < nb; ++b) {
         if (per_sample) {

@@ -1285,7 +1285,9 @@ __host__ __device__ __forceinline__ int lng_col_item(int bid, int W)
 // Forward: gated x, rows n1 < N1/2 read (pruned), workspace of pair q.
 // SPEC: the kernel wrap-placed at offset delta -> delta mod N (index n empty),
 // all rows read, into the spectrum of channel q.
-template <int L, bool SPEC, bool BF16, class Ctx>
+// GATE = false (backward): the signal read through a.x is taken as it is (the
+// output gradient dy).
+template <int L, bool SPEC, bool BF16, bool GATE = true, class Ctx>
 __host__ __device__ __forceinline__ void lng_col_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
     constexpr int TW = col_tw(L), NT = col_nt(L);
@@ -1310,7 +1312,8 @@ __host__ __device__ __forceinline__ void lng_col_fwd_body(const Ctx& ctx, int bi
             const int dl = unwrap((int)m, g.n_in, g.N_in);
             return make_float2(dl == kEmpty ? 0.f : a.K[(long long)q * g.ke_in + dl + g.n_in - 1], 0.f);
         } else {
-            return make_float2(ctx.gate(load_x<BF16>(a, xo + m), al, be), 0.f);
+            const float v = load_x<BF16>(a, xo + m);
+            return make_float2(GATE ? ctx.gate(v, al, be) : v, 0.f);
         }
     };
     auto st = [&](int pos, int l, const float2& v) {
@@ -1324,7 +1327,9 @@ __host__ __device__ __forceinline__ void lng_col_fwd_body(const Ctx& ctx, int bi
 // Step 2: NP rows k1 per workgroup, N2 points each.  Forward: forward
 // transform, product with the spectrum row, inverse transform, in place.
 // SPEC: forward transform scaled by 1/N, in place in the spectrum.
-template <int L, bool SPEC, class Ctx>
+// CONJ (backward, du): the product takes the conjugate spectrum (a
+// correlation with K).
+template <int L, bool SPEC, bool CONJ = false, class Ctx>
 __host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
     constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
@@ -1374,7 +1379,7 @@ __host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, c
 #pragma unroll
         for (int i = 0; i < ITER; ++i) {
             const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-            T[pos * LP + lp] = cmul(T[pos * LP + lp], kv[i]);
+            T[pos * LP + lp] = cmul(T[pos * LP + lp], CONJ ? cconj(kv[i]) : kv[i]);
         }
         ctx.sync();
         tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
@@ -1386,9 +1391,78 @@ __host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, c
     }
 }
 
+// Backward, kernel gradient, step 2: NP rows (channel, k1) per workgroup; for
+// each batch entry the forward row transforms of the column-transformed dy
+// and u, P += DY conj(U) (registers, batch entries in order); then the inverse
+// row transform of P into the channel's kernel-gradient plane dkw.  Runs
+// before the du row pass, which overwrites the dy workspace.
+template <int L, class Ctx>
+__host__ __device__ __forceinline__ void lng_row_dk_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
+    constexpr int ITER = NP * L / NT;
+    static_assert(NP * L % NT == 0, "whole element loops");
+    const Geom& g = a.g;
+    const int N1 = g.N1;
+    const int H = a.nch * N1;
+    const int tid = ctx.tid();
+    ctx.stage();
+    auto row_off = [&](int lp, int b) -> long long {  // workspace offset of row k1 of pair (channel, b)
+        const int h = bid * NP + lp;
+        return ((long long)(h / N1) * a.B + b) * g.wsp + (long long)(h % N1) * L;
+    };
+    // forward row transform of the rows at workspace base `ws` of batch entry b, into registers
+    auto fwd_rows = [&](const float2* ws, int b, float2* out) {
+        float2 v[ITER];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+            v[i] = bid * NP + lp < H ? ws[row_off(lp, b) + pos] : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+            T[pos * LP + lp] = v[i];
+        }
+        ctx.sync();
+        tile_fft<L, NP, LP, NT, false, false, false>(ctx, T);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+            out[i] = T[pos * LP + lp];
+        }
+        ctx.sync();  // T is free for the next transform
+    };
+    float2 P[ITER], DY[ITER], U[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) P[i] = make_float2(0.f, 0.f);
+    for (int b = 0; b < a.B; ++b) {
+        fwd_rows(a.ws, b, DY);
+        fwd_rows(a.ws_u, b, U);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) P[i] = cadd(P[i], cmulc(DY[i], U[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+        T[pos * LP + lp] = P[i];
+    }
+    ctx.sync();
+    tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / L, pos = idx % L, h = bid * NP + lp;
+        if (h < H) a.dkw[(long long)(h / N1) * g.kmain + (long long)(h % N1) * L + pos] = T[pos * LP + lp];
+    }
+}
+
 // Step 3: TW adjacent columns per workgroup: conjugate twiddle, inverse
 // N1-point transforms keeping rows n1 < N1/2 (the crop), real part to y.
-template <int L, bool BF16, class Ctx>
+// BWD: the transforms carry du; each output becomes dx (stored through y) and
+// the workgroup's sums of the dalpha / dbeta terms (each thread's in the
+// order it visits its outputs, then an LDS tree) go to part[w], the
+// partials of pair q laid out [q][N2 / TW].
+template <int L, bool BF16, bool BWD = false, class Ctx>
 __host__ __device__ __forceinline__ void lng_col_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
     constexpr int TW = col_tw(L), NT = col_nt(L);
@@ -1405,9 +1479,61 @@ __host__ __device__ __forceinline__ void lng_col_inv_body(const Ctx& ctx, int bi
         const unsigned e = ((unsigned)(n20 + l) * (unsigned)pos) & nmask;
         return cmulc(src[(long long)pos * N2 + n20 + l], ctx.twiddle(e, g.logN));
     };
-    auto st = [&](int pos, int l, const float2& v) { store_y<BF16>(a, yo + (long long)N2 * pos + n20 + l, v.x); };
     auto after_load = [&]() { ctx.stage(); };
-    inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
+    if constexpr (!BWD) {
+        auto st = [&](int pos, int l, const float2& v) { store_y<BF16>(a, yo + (long long)N2 * pos + n20 + l, v.x); };
+        inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
+    } else {
+        static_assert((NT & (NT - 1)) == 0, "power-of-two workgroup for the tree");
+        const float al = a.alpha[c], be = a.beta[c];
+        float2 acc = make_float2(0.f, 0.f);
+        auto st = [&](int pos, int l, const float2& v) {
+            const long long m = yo + (long long)N2 * pos + n20 + l;
+            float2 terms;
+            store_y<BF16>(a, m, gate_vjp(ctx, v.x, load_x<BF16>(a, m), al, be, terms));
+            acc = cadd(acc, terms);
+        };
+        inv_fn_to_fn<L, TW, NT, true>(ctx, T, ld, st, after_load);
+        ctx.sync();  // the transform's last LDS reads are done: T is scratch
+        const int tid = ctx.tid();
+        T[tid] = acc;
+        ctx.sync();
+        for (int h = NT / 2; h >= 1; h /= 2) {
+            if (tid < h) T[tid] = cadd(T[tid], T[tid + h]);
+            ctx.sync();
+        }
+        if (tid == 0) a.part[w] = T[0];
+    }
+}
+
+// Backward, kernel gradient, last step: TW adjacent columns of a channel's
+// dkw plane per workgroup: conjugate twiddle, inverse N1-point transforms over
+// every row (the kernel gradient lives on all offsets), scaled by 1/N, written
+// to dK at the offset delta = unwrap(m) of position m = N2 n1 + n2 (index n
+// carries nothing).
+template <int L, class Ctx>
+__host__ __device__ __forceinline__ void lng_col_dk_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int TW = col_tw(L), NT = col_nt(L);
+    const Geom& g = a.g;
+    const int N2 = g.N2;
+    const int tpp = N2 / TW;
+    const int w = lng_col_item(bid, a.nch * tpp);
+    const int cl = w / tpp, n20 = (w % tpp) * TW;
+    const unsigned nmask = (1u << g.logN) - 1u;
+    const float2* src = a.dkw + (long long)cl * g.kmain;
+    float* dst = a.dK + (long long)(a.c0 + cl) * g.ke_in;
+    const float sc = 1.0f / (float)(1ll << g.logN);
+    auto ld = [&](int pos, int l) -> float2 {
+        const unsigned e = ((unsigned)(n20 + l) * (unsigned)pos) & nmask;
+        return cmulc(src[(long long)pos * N2 + n20 + l], ctx.twiddle(e, g.logN));
+    };
+    auto st = [&](int pos, int l, const float2& v) {
+        const int dl = unwrap(N2 * pos + n20 + l, g.n_in, g.N_in);
+        if (dl != kEmpty) dst[dl + g.n_in - 1] = v.x * sc;
+    };
+    auto after_load = [&]() { ctx.stage(); };
+    inv_fn_to_fn<L, TW, NT, false>(ctx, T, ld, st, after_load);
 }
 
 }  // namespace hyenand

@@ -151,28 +151,45 @@ __global__ __launch_bounds__(row_nt(L)) void k_dk_row(ConvArgs a)
     dk_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
 
-template <int L, bool SPEC, bool BF16>
+template <int L, bool SPEC, bool BF16, bool GATE = true>
 __global__ __launch_bounds__(col_nt(L)) void k_lng_col_fwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * col_tw(L)];
-    lng_col_fwd_body<L, SPEC, BF16>(make_ctx<L, col_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
+    lng_col_fwd_body<L, SPEC, BF16, GATE>(make_ctx<L, col_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
-template <int L, bool SPEC>
+template <int L, bool SPEC, bool CONJ = false>
 __global__ __launch_bounds__(row_nt(L)) void k_lng_row(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
-    lng_row_body<L, SPEC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
+    lng_row_body<L, SPEC, CONJ>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
-template <int L, bool BF16>
+template <int L>
+__global__ __launch_bounds__(row_nt(L)) void k_lng_row_dk(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, kPlanF>()];
+    __shared__ float2 T[L * row_lp(L)];
+    lng_row_dk_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
+}
+
+template <int L, bool BF16, bool BWD = false>
 __global__ __launch_bounds__(col_nt(L)) void k_lng_col_inv(ConvArgs a)
+{
+    static_assert(col_nt(L) <= L * col_tw(L), "the backward's tree fits in the tile");
+    __shared__ float2 TWL[twl_size<L, kPlanR>()];
+    __shared__ float2 T[L * col_tw(L)];
+    lng_col_inv_body<L, BF16, BWD>(make_ctx<L, col_nt(L), kPlanR>(TWL), (int)blockIdx.x, a, T);
+}
+
+template <int L>
+__global__ __launch_bounds__(col_nt(L)) void k_lng_col_dk(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanR>()];
     __shared__ float2 T[L * col_tw(L)];
-    lng_col_inv_body<L, BF16>(make_ctx<L, col_nt(L), kPlanR>(TWL), (int)blockIdx.x, a, T);
+    lng_col_dk_body<L>(make_ctx<L, col_nt(L), kPlanR>(TWL), (int)blockIdx.x, a, T);
 }
 
 constexpr int kReduceNT = 1024;
@@ -504,8 +521,72 @@ static hipError_t backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
     return dk_rows((long long)a.nch * (g.N_out * g.N_mid / 2));
 }
 
+// Long 1-D backward: column transforms of dy (and of the gated input for dK),
+// the kernel-gradient row pass (before the du row pass overwrites the dy
+// workspace), the du row pass, the inverse columns with the dx epilogue, the
+// dalpha / dbeta reduction and the kernel gradient's inverse columns.
+static hipError_t long1d_bwd_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
+{
+    auto mark = [&]() { if (tr) tr->mark(st); };
+    const Geom& g = a.g;
+    const long long sigs = (long long)a.nch * a.B;
+    ConvArgs ady = a;
+    ady.x = a.dy;
+    ConvArgs au = a;
+    au.ws = a.ws_u;
+    auto col_fwd = [&](const ConvArgs& arg, bool gate) {
+        return with_col_length(g.N1, [&]<int L>() {
+            const unsigned grid = (unsigned)(sigs * (g.N2 / col_tw(L)));
+            mark();
+            if (gate) {
+                if (a.bf16) hipLaunchKernelGGL((k_lng_col_fwd<L, false, true, true>), dim3(grid), dim3(col_nt(L)), 0, st, arg);
+                else hipLaunchKernelGGL((k_lng_col_fwd<L, false, false, true>), dim3(grid), dim3(col_nt(L)), 0, st, arg);
+            } else {
+                if (a.bf16) hipLaunchKernelGGL((k_lng_col_fwd<L, false, true, false>), dim3(grid), dim3(col_nt(L)), 0, st, arg);
+                else hipLaunchKernelGGL((k_lng_col_fwd<L, false, false, false>), dim3(grid), dim3(col_nt(L)), 0, st, arg);
+            }
+            return last_error();
+        });
+    };
+    hipError_t e = col_fwd(ady, false);
+    if (e == hipSuccess && dk) e = col_fwd(au, true);
+    if (e == hipSuccess && dk)
+        e = with_row_length(g.N2, [&]<int L>() {
+            mark();
+            hipLaunchKernelGGL((k_lng_row_dk<L>), dim3(ceil_div((long long)a.nch * g.N1, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            return last_error();
+        });
+    if (e == hipSuccess)
+        e = with_row_length(g.N2, [&]<int L>() {
+            mark();
+            hipLaunchKernelGGL((k_lng_row<L, false, true>), dim3(ceil_div(sigs * g.N1, row_np(L))), dim3(row_nt(L)), 0, st, a);
+            return last_error();
+        });
+    if (e == hipSuccess)
+        e = with_col_length(g.N1, [&]<int L>() {
+            const unsigned grid = (unsigned)(sigs * (g.N2 / col_tw(L)));
+            mark();
+            if (a.bf16) hipLaunchKernelGGL((k_lng_col_inv<L, true, true>), dim3(grid), dim3(col_nt(L)), 0, st, a);
+            else hipLaunchKernelGGL((k_lng_col_inv<L, false, true>), dim3(grid), dim3(col_nt(L)), 0, st, a);
+            return last_error();
+        });
+    if (e == hipSuccess) {
+        mark();
+        hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)a.nch), dim3(kReduceNT), 0, st, a);
+        e = last_error();
+    }
+    if (e == hipSuccess && dk)
+        e = with_col_length(g.N1, [&]<int L>() {
+            mark();
+            hipLaunchKernelGGL((k_lng_col_dk<L>), dim3((unsigned)((long long)a.nch * (g.N2 / col_tw(L)))), dim3(col_nt(L)), 0, st, a);
+            return last_error();
+        });
+    return e;
+}
+
 hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
 {
+    if (a.g.lng) return long1d_bwd_chunk(a, dk, st, tr);
     return a.g.circ ? backward_chunk<true>(a, dk, st, tr) : backward_chunk<false>(a, dk, st, tr);
 }
 

@@ -257,18 +257,23 @@ inline size_t recommended_workspace(const Geom& g, int B, int C)
     return n * per_ch;
 }
 
-// Line pairs of one (b, c) pair in the row kernels (d >= 2), or 1 for d = 1
-// (where the backward keeps one partial sum per pair).
-__host__ __device__ __forceinline__ int pair_lines(const Geom& g) { return g.d == 1 ? 1 : g.n_out * g.n_mid / 2; }
+// Backward partial sums of dalpha / dbeta per (b, c) pair: one per line pair
+// of the row kernels (d >= 2), one per pair (d = 1), one per inverse-column
+// workgroup (long 1-D).
+__host__ __device__ __forceinline__ int pair_lines(const Geom& g)
+{
+    if (g.lng) return g.N2 / col_tw(g.N1);  // long 1-D: one per inverse-column workgroup
+    return g.d == 1 ? 1 : g.n_out * g.n_mid / 2;
+}
 
 // Backward workspace per channel of a chunk (bytes): the planes of dy and, for
 // dK, of the gated input (B * wsp complex each), the kernel-gradient spectrum
-// (N_out N_mid S complex for d >= 2; B S for d = 1) and the partial sums of
+// (N_out N_mid S complex for d >= 2; B S for d = 1; N for long 1-D) and the partial sums of
 // dalpha and dbeta (B * pair_lines float2).
 inline size_t bwd_channel_bytes(const Geom& g, int B, bool dk)
 {
     size_t v = (size_t)B * (size_t)g.wsp * (dk ? 2u : 1u);
-    if (dk) v += g.d == 1 ? (size_t)B * (size_t)g.S : (size_t)g.kmain;
+    if (dk) v += (g.d == 1 && !g.lng) ? (size_t)B * (size_t)g.S : (size_t)g.kmain;
     v += (size_t)B * (size_t)pair_lines(g);
     return v * 8u;
 }

@@ -90,8 +90,9 @@ int hyenand_version(void);
  * column transforms of N1 points, twiddle W_N^(n2 k1), row transforms of N2
  * points).  K_hat holds N complex values per channel, the value of frequency
  * k = k1 + N1 k2 at [k1][k2], equal to Khat(k) / N (no Nyquist packing).  The
- * workspace minimum is B * N * 8 bytes (one channel); the backward and the
- * circular mode do not take long signals (UNSUPPORTED).
+ * workspace minimum is B * N * 8 bytes (one channel).  The backward takes
+ * long signals (the same decomposition, run backwards for du and the kernel
+ * gradient); the circular mode does not (UNSUPPORTED).
  */
 size_t hyenand_kernel_spectrum_bytes(int C, int d, const int64_t* dims);
 
@@ -299,7 +300,7 @@ int hyenand_fftconv_fwd_per_sample_traced(const void* x, const float* phi_alpha,
  * run one after the other, each as a batch of one, so the workspace is sized
  * by hyenand_fftconv_bwd_workspace_bytes(1, C, ...) (any size from the
  * _min_bytes of B = 1 upward works).  Other arguments, errors and limits as for
- * hyenand_fftconv_bwd (zero-padded boundary, n <= 1024).
+ * hyenand_fftconv_bwd (zero-padded boundary).
  */
 int hyenand_fftconv_bwd_per_sample(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
                                    const void* dy, void* dx, float* dalpha, float* dbeta, float* dK, int B, int C,
