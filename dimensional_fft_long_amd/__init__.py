@@ -387,21 +387,37 @@ class HyenaConvolutionFunction(torch.autograd.Function):
     pattern (PyTorch)": the forward keeps only the input and the kernel
     parameters (alpha, beta and the kernel spectrum computed from K), the
     backward recomputes the transforms and returns the gradients of x, alpha,
-    beta and K.  The FFT workspaces are preallocated per shape and reused."""
+    beta and K.  The FFT workspaces are preallocated per shape and reused.
+
+    K [C, *(2n-1)]: one kernel per channel; K [B, C, *(2n-1)]: one per (b, c)
+    (input-dependent kernels); ``circular=True``: the circular mode, K [C, *n]."""
 
     @staticmethod
-    def forward(ctx, x, alpha, beta, K):
+    def forward(ctx, x, alpha, beta, K, circular=False):
         dims = tuple(int(v) for v in x.shape[2:])
-        K_hat = kernel_spectrum(K.contiguous(), dims)
+        per_sample = K.dim() == x.dim()
+        if circular and per_sample:
+            raise ValueError("per-sample kernels are built for the zero-padded mode only")
+        if circular:
+            K_hat = kernel_spectrum_circ(K.contiguous())
+            y = fftconv_fwd_circ(x, alpha, beta, K_hat)
+        elif per_sample:
+            K_hat = kernel_spectrum_per_sample(K.contiguous())
+            y = fftconv_fwd_per_sample(x, alpha, beta, K_hat)
+        else:
+            K_hat = kernel_spectrum(K.contiguous(), dims)
+            y = fftconv_fwd(x, alpha, beta, K_hat)
         ctx.save_for_backward(x, alpha, beta, K_hat)
         ctx.needs_dK = ctx.needs_input_grad[3]
-        return fftconv_fwd(x, alpha, beta, K_hat)
+        ctx.mode = "circular" if circular else ("per_sample" if per_sample else "shared")
+        return y
 
     @staticmethod
     def backward(ctx, grad_out):
         x, alpha, beta, K_hat = ctx.saved_tensors
-        dx, da, db, dK = fftconv_bwd(x, alpha, beta, K_hat, grad_out.contiguous(), with_dK=ctx.needs_dK)
-        return dx, da, db, dK
+        f = {"circular": fftconv_bwd_circ, "per_sample": fftconv_bwd_per_sample, "shared": fftconv_bwd}[ctx.mode]
+        dx, da, db, dK = f(x, alpha, beta, K_hat, grad_out.contiguous(), with_dK=ctx.needs_dK)
+        return dx, da, db, dK, None
 
 
 # ----------------------------------------------------------- circular mode
