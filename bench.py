@@ -134,11 +134,15 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
     elif name == "lng_row_du":
         return pass_model("lng_row", dims, P, nch, es, circ)
     elif name == "lng_row_dk":
-        # dy and u rows read, the channel's kernel-gradient rows written
+        # dy and u rows read, the channel's kernel-gradient rows written; with
+        # 4096-point rows (N > 2^22) also the spectrum read and the du rows written
         N = 2 * g["ni"]
         N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
         by = 2 * P * N * 8 + nch * N * 8
         fl = (2 * P + nch) * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 8
+        if N2 == 4096:
+            by += P * N * 8 + nch * N * 8
+            fl += P * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 6
     elif name == "lng_col_inv_bwd":
         by, fl = pass_model("lng_col_inv", dims, P, nch, es, circ)
         by += P * g["vox"] * es  # x read again for the gate derivative
@@ -448,7 +452,7 @@ def main():
         nk = wl.C * (wl.B if ps else 1)
         bytes_min = 3 * wl.B * wl.C * wl.voxels * es + nk * g["ksz"] * 8 + nk * g["kl"] * 4
         long1d = wl.d == 1 and wl.dims[0] > 1024
-        names = H.BWD_PASS_NAMES[("long" if long1d else wl.d, True)]
+        names = H.BWD_PASS_NAMES[(("long4096" if 2 * wl.dims[0] > (1 << 22) else "long") if long1d else wl.d, True)]
         if long1d:
             bytes_min = 3 * wl.B * wl.C * wl.voxels * es + wl.C * 2 * wl.dims[0] * 8 + wl.C * g["kl"] * 4
     else:

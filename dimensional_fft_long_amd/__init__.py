@@ -355,6 +355,9 @@ BWD_PASS_NAMES = {
     ("long", False): ("lng_col_fwd_dy", "lng_row_du", "lng_col_inv_bwd", "gate_reduce"),
     ("long", True): ("lng_col_fwd_dy", "lng_col_fwd_u", "lng_row_dk", "lng_row_du", "lng_col_inv_bwd", "gate_reduce",
                      "lng_col_dk"),
+    # n > 2^21 (4096-point rows): the kernel-gradient row pass also writes du
+    ("long4096", True): ("lng_col_fwd_dy", "lng_col_fwd_u", "lng_row_dk", "lng_col_inv_bwd", "gate_reduce",
+                         "lng_col_dk"),
 }
 
 

@@ -1393,12 +1393,14 @@ __host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, c
 
 // Backward, kernel gradient, step 2: NP rows (channel, k1) per workgroup; for
 // each batch entry the forward row transforms of the column-transformed dy
-// and u, P += DY conj(U) (registers, batch entries in order); then the inverse
-// row transform of P into the channel's kernel-gradient plane dkw.  Runs
-// before the du row pass, which overwrites the dy workspace.
+// and u, P += DY conj(U) (registers, batch entries in order), and, where
+// lng_dk_fuses_du, the du row DY conj(Khat) inverse-transformed in place of
+// the dy row (the dy rows read once; elsewhere the du row pass follows); then
+// the inverse row transform of P into the channel's kernel-gradient plane dkw.
 template <int L, class Ctx>
 __host__ __device__ __forceinline__ void lng_row_dk_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
+    constexpr bool DU = lng_dk_fuses_du(L);
     constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
     constexpr int ITER = NP * L / NT;
     static_assert(NP * L % NT == 0, "whole element loops");
@@ -1433,14 +1435,35 @@ __host__ __device__ __forceinline__ void lng_row_dk_body(const Ctx& ctx, int bid
         }
         ctx.sync();  // T is free for the next transform
     };
-    float2 P[ITER], DY[ITER], U[ITER];
+    float2 P[ITER], DY[ITER], U[ITER], kv[DU ? ITER : 1];
 #pragma unroll
-    for (int i = 0; i < ITER; ++i) P[i] = make_float2(0.f, 0.f);
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / L, pos = idx % L, h = bid * NP + lp;
+        P[i] = make_float2(0.f, 0.f);
+        if constexpr (DU)
+            kv[i] = h < H ? a.khat[(long long)(a.c0 + h / N1) * g.ksz + (long long)(h % N1) * L + pos]
+                          : make_float2(0.f, 0.f);
+    }
     for (int b = 0; b < a.B; ++b) {
         fwd_rows(a.ws, b, DY);
         fwd_rows(a.ws_u, b, U);
 #pragma unroll
         for (int i = 0; i < ITER; ++i) P[i] = cadd(P[i], cmulc(DY[i], U[i]));
+        if constexpr (DU) {
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+                T[pos * LP + lp] = cmulc(DY[i], kv[i]);
+            }
+            ctx.sync();
+            tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+                if (bid * NP + lp < H) a.ws[row_off(lp, b) + pos] = T[pos * LP + lp];
+            }
+            ctx.sync();  // T is free for the next transform
+        }
     }
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {

@@ -522,9 +522,10 @@ static hipError_t backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
 }
 
 // Long 1-D backward: column transforms of dy (and of the gated input for dK),
-// the kernel-gradient row pass (before the du row pass overwrites the dy
-// workspace), the du row pass, the inverse columns with the dx epilogue, the
-// dalpha / dbeta reduction and the kernel gradient's inverse columns.
+// the kernel-gradient row pass (for dK; for 4096-point rows it also writes
+// the du rows), the du row pass (unless fused), the inverse columns with the dx
+// epilogue, the dalpha / dbeta reduction and the kernel gradient's inverse
+// columns.
 static hipError_t long1d_bwd_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
@@ -556,7 +557,7 @@ static hipError_t long1d_bwd_chunk(const ConvArgs& a, bool dk, hipStream_t st, L
             hipLaunchKernelGGL((k_lng_row_dk<L>), dim3(ceil_div((long long)a.nch * g.N1, row_np(L))), dim3(row_nt(L)), 0, st, a);
             return last_error();
         });
-    if (e == hipSuccess)
+    if (e == hipSuccess && !(dk && lng_dk_fuses_du(g.N2)))  // else the kernel-gradient row pass wrote du
         e = with_row_length(g.N2, [&]<int L>() {
             mark();
             hipLaunchKernelGGL((k_lng_row<L, false, true>), dim3(ceil_div(sigs * g.N1, row_np(L))), dim3(row_nt(L)), 0, st, a);

@@ -257,6 +257,14 @@ inline size_t recommended_workspace(const Geom& g, int B, int C)
     return n * per_ch;
 }
 
+// Long 1-D backward with dK: the kernel-gradient row kernel also writes the du
+// rows (the du row pass fused) for 4096-point rows, whose 96 KiB tile leaves
+// one workgroup per CU whatever the registers; shorter rows run three
+// workgroups per CU, which the fused kernel's extra registers would cost
+// (2M tokens, 2048-point rows: 1.28 ms separate against 1.44 fused; 8M tokens,
+// 4096-point rows: 3.05 against 2.81).
+constexpr bool lng_dk_fuses_du(int N2) { return N2 >= 4096; }
+
 // Backward partial sums of dalpha / dbeta per (b, c) pair: one per line pair
 // of the row kernels (d >= 2), one per pair (d = 1), one per inverse-column
 // workgroup (long 1-D).
