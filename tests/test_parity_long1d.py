@@ -136,7 +136,7 @@ def _check(got, ref, dtype):
 
 
 @pytest.mark.parametrize("n,B,C,dtype", [(2048, 2, 3, "f32"), (4096, 1, 2, "bf16"), (1 << 15, 3, 2, "f32"),
-                                         (1 << 18, 1, 2, "bf16"), (1 << 20, 2, 1, "f32"), (1 << 22, 1, 1, "f32"),
+                                         (1 << 18, 1, 2, "bf16"), (1 << 20, 2, 1, "f32"), (1 << 22, 2, 1, "f32"),
                                          (1 << 23, 1, 1, "bf16")],
                          ids=lambda v: str(v))
 def test_bwd_matches_fft_oracle(H, n, B, C, dtype):
