@@ -186,3 +186,23 @@ def test_bwd_workload_full_size(H, idx):
     c = wl.C - 1
     ref = oracle.bwd_fft(x[:, c:c + 1], p.alpha[c:c + 1], p.beta[c:c + 1], K[c:c + 1], dy[:, c:c + 1])
     _check([got[0][:, c:c + 1], got[1][c:c + 1], got[2][c:c + 1], got[3][c:c + 1]], ref, wl.dtype)
+
+
+def test_bwd_autograd_function(H):
+    """HyenaConvolutionFunction on a long 1-D signal: torch autograd through
+    the library's forward and backward against the oracle's gradients."""
+    n, B, C = 1 << 12, 2, 2
+    dev = torch.device("cuda:0")
+    p = synth.draw_params((n,), C, 23)
+    x0 = synth.draw_x(p.rng, B, C, (n,), "f32")
+    dy0 = synth.draw_dy((n,), B, C, "f32", 23)
+    K0 = synth.kernel_channels((n,), p)
+    x = x0.to(dev).requires_grad_()
+    al = torch.from_numpy(p.alpha).to(dev).requires_grad_()
+    be = torch.from_numpy(p.beta).to(dev).requires_grad_()
+    K = K0.to(dev).requires_grad_()
+    y = H.HyenaConvolutionFunction.apply(x, al, be, K)
+    (y * dy0.to(dev)).sum().backward()
+    ref = oracle.bwd_fft(x0.numpy(), p.alpha, p.beta, K0.numpy(), dy0.numpy())
+    for t, r in zip((x.grad, al.grad, be.grad, K.grad), ref):
+        assert _rel(t.cpu().numpy().astype(np.float64), r) <= 1e-4
