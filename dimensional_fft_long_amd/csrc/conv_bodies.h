@@ -24,7 +24,7 @@
 //   spec_*    the kernel spectrum (forward transforms only, full inputs).
 //
 // Every body is a function of (execution context, workgroup index, arguments,
-// LDS tile); the device kernels in hyenand_kernels.hip wrap them.
+// LDS tile); the device kernels in kernels_dev.h wrap them.
 #pragma once
 
 #include "fft_core.h"

@@ -19,7 +19,7 @@
 // the thread index (tid()), the workgroup barrier (sync()), the LDS twiddle
 // tables (twl, reversed-plan tables at kRevBase; stage() fills them and must
 // precede a barrier that precedes the first transform pass with twiddles) and
-// the gate (gate()); the device context is in kernels.hip.
+// the gate (gate()); the device context is in kernels_dev.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -90,6 +90,9 @@ constexpr TwTable make_twiddles()
     }
     return t;
 }
+
+// Evaluated once per translation unit (the per-plan tables below index it).
+inline constexpr TwTable kTwBase = make_twiddles();
 
 // ------------------------------------------------------------- radix DFTs
 // In-place DFT of R points held in registers, natural order in and out:
@@ -261,7 +264,7 @@ struct PlanTwiddles {
 template <int L, int PLANS>
 constexpr PlanTwiddles<L, PLANS> make_plan_twiddles()
 {
-    constexpr TwTable base = make_twiddles();
+    const TwTable& base = kTwBase;
     PlanTwiddles<L, PLANS> t{};
     int off = 0;
     for (int rev = 0; rev < 2; ++rev) {

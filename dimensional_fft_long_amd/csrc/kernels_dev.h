@@ -1,14 +1,21 @@
-// kernels.hip -- gfx950 kernels of the gated N-D FFT convolution and their
-// launchers.  The workgroup bodies are in conv_bodies.h; this file binds them
-// to the device (thread index, barrier, LDS tile, twiddle table) and picks the
-// template instance for each transform length.
+// kernels_dev.h -- gfx950 kernels of the gated N-D FFT convolution and the
+// chains that launch them.  The workgroup bodies are in conv_bodies.h; this
+// header binds them to the device (thread index, barrier, LDS tile, twiddle
+// table) and picks the template instance for each transform length.
+//
+// Every kernel translation unit (k_*.hip) includes this header and
+// instantiates only the kernels its chains launch.  Everything here sits in an
+// unnamed namespace, so a kernel instantiated by two units is two distinct
+// symbols, one in each unit's code object.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "conv_bodies.h"
 #include "launch.h"
 
 namespace hyenand {
-
+namespace {
 template <int L, int PLANS>
 constexpr int twl_size() { return tw_table_alloc<L, PLANS>(); }
 
@@ -247,36 +254,20 @@ __global__ __launch_bounds__(out_nt(L, NR)) void k_spec_out(ConvArgs a)
     spec_out_body<L, NR>(make_ctx<L, out_nt(L, NR), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
-static inline unsigned ceil_div(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
-
-// Workgroups of `kernel` (nt threads) resident at once on the current device
-// (CUs x workgroups per CU), queried once per kernel instance; every device
-// the library runs on is taken to be alike.  0 if the query fails.
-template <class K>
-static unsigned resident_wgs(K kernel, int nt)
-{
-    static const unsigned n = [&]() -> unsigned {
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess) return 0;
-        return (unsigned)(cus > 0 ? cus : 0) * (unsigned)(per_cu > 0 ? per_cu : 0);
-    }();
-    return n;
-}
+inline unsigned ceil_div(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 
 // Grid of an item-looping kernel: one workgroup per item up to the number
-// resident at once.
+// resident at once (resident_wgs, launch.h).
 template <class K>
-static unsigned loop_grid(K kernel, int nt, long long items)
+unsigned loop_grid(K kernel, int nt, long long items)
 {
-    const unsigned r = resident_wgs(kernel, nt);
+    const unsigned r = resident_wgs(reinterpret_cast<const void*>(kernel), nt);
     return r > 0 && items > (long long)r ? r : (unsigned)items;
 }
 
 // Calls F.template operator()<L>() for the runtime length L in {4, ..., 2048}.
 template <class F>
-static hipError_t with_length(int L, F&& f)
+hipError_t with_length(int L, F&& f)
 {
     switch (L) {
     case 4: return f.template operator()<4>();
@@ -293,10 +284,10 @@ static hipError_t with_length(int L, F&& f)
     }
 }
 
-static hipError_t last_error() { return hipGetLastError(); }
+hipError_t last_error() { return hipGetLastError(); }
 
 template <bool CIRC>
-static hipError_t forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
+hipError_t forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
@@ -361,7 +352,7 @@ static hipError_t forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* 
 // Transform lengths of the long 1-D path: rows N2 in {1024, 2048, 4096},
 // columns N1 in {4, ..., 4096}.
 template <class F>
-static hipError_t with_row_length(int L, F&& f)
+hipError_t with_row_length(int L, F&& f)
 {
     switch (L) {
     case 1024: return f.template operator()<1024>();
@@ -372,14 +363,14 @@ static hipError_t with_row_length(int L, F&& f)
 }
 
 template <class F>
-static hipError_t with_col_length(int L, F&& f)
+hipError_t with_col_length(int L, F&& f)
 {
     if (L == 4096) return f.template operator()<4096>();
     return with_length(L, f);
 }
 
 // Long 1-D forward (and, with SPEC, the spectrum): column pass, row pass, column pass.
-static hipError_t long1d_chunk(const ConvArgs& a, bool spec, hipStream_t st, LaunchTrace* tr)
+hipError_t long1d_chunk(const ConvArgs& a, bool spec, hipStream_t st, LaunchTrace* tr)
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
@@ -410,21 +401,8 @@ static hipError_t long1d_chunk(const ConvArgs& a, bool spec, hipStream_t st, Lau
     });
 }
 
-hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
-{
-    if (a.g.lng) return long1d_chunk(a, false, st, tr);
-    return a.g.circ ? forward_chunk<true>(a, st, tr) : forward_chunk<false>(a, st, tr);
-}
-
-hipError_t launch_zero(float* p, long long n, hipStream_t st)
-{
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_zero, dim3(ceil_div(n, 256)), dim3(256), 0, st, p, n);
-    return last_error();
-}
-
 template <bool CIRC>
-static hipError_t backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
+hipError_t backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
@@ -526,7 +504,7 @@ static hipError_t backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, Lau
 // the du rows), the du row pass (unless fused), the inverse columns with the dx
 // epilogue, the dalpha / dbeta reduction and the kernel gradient's inverse
 // columns.
-static hipError_t long1d_bwd_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
+hipError_t long1d_bwd_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
 {
     auto mark = [&]() { if (tr) tr->mark(st); };
     const Geom& g = a.g;
@@ -585,41 +563,5 @@ static hipError_t long1d_bwd_chunk(const ConvArgs& a, bool dk, hipStream_t st, L
     return e;
 }
 
-hipError_t launch_backward_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTrace* tr)
-{
-    if (a.g.lng) return long1d_bwd_chunk(a, dk, st, tr);
-    return a.g.circ ? backward_chunk<true>(a, dk, st, tr) : backward_chunk<false>(a, dk, st, tr);
-}
-
-hipError_t launch_spectrum(const ConvArgs& a, hipStream_t st)
-{
-    const Geom& g = a.g;
-    if (g.lng) return long1d_chunk(a, true, st, nullptr);
-    hipError_t e;
-    const long long H = g.d == 1 ? ((long long)a.C + 1) / 2 : (long long)a.C * (g.N_out * g.N_mid / 2);
-    e = with_length(g.N_in, [&]<int L>() {
-        hipLaunchKernelGGL(k_spec_row<L>, dim3(ceil_div(H, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        return last_error();
-    });
-    if (e != hipSuccess || g.d == 1) return e;
-    if (g.d == 3) {
-        e = with_length(g.N_mid, [&]<int L>() {
-            const long long grid = (long long)a.C * ceil_div((long long)g.N_out * g.S, col_tw(L));
-            hipLaunchKernelGGL(k_spec_mid<L>, dim3((unsigned)grid), dim3(col_nt(L)), 0, st, a);
-            return last_error();
-        });
-        if (e != hipSuccess) return e;
-        return with_length(g.N_out, [&]<int L>() {
-            const long long grid = (long long)a.C * (g.N_mid / 2) * ceil_div(g.S, mul3_tw(L));
-            hipLaunchKernelGGL((k_spec_out<L, 2>), dim3((unsigned)grid), dim3(out_nt(L, 2)), 0, st, a);
-            return last_error();
-        });
-    }
-    return with_length(g.N_out, [&]<int L>() {
-        const long long grid = (long long)a.C * ceil_div(g.S, col_tw(L));
-        hipLaunchKernelGGL((k_spec_out<L, 1>), dim3((unsigned)grid), dim3(out_nt(L, 1)), 0, st, a);
-        return last_error();
-    });
-}
-
+}  // namespace
 }  // namespace hyenand

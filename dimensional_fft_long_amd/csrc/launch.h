@@ -37,4 +37,18 @@ hipError_t launch_zero(float* p, long long n, hipStream_t stream);
 // Kernel spectrum of all channels into a.khat (in place, no workspace).
 hipError_t launch_spectrum(const ConvArgs& a, hipStream_t stream);
 
+// The chains of each kernel translation unit (k_*.hip), called by the
+// dispatchers above.
+hipError_t forward_chunk_padded(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace);
+hipError_t forward_chunk_circ(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace);
+hipError_t backward_chunk_padded(const ConvArgs& a, bool dk, hipStream_t stream, LaunchTrace* trace);
+hipError_t backward_chunk_circ(const ConvArgs& a, bool dk, hipStream_t stream, LaunchTrace* trace);
+hipError_t long1d_forward(const ConvArgs& a, bool spec, hipStream_t stream, LaunchTrace* trace);
+hipError_t long1d_backward(const ConvArgs& a, bool dk, hipStream_t stream, LaunchTrace* trace);
+
+// Workgroups of `kernel` (nt threads per workgroup) resident at once on the
+// current device: CUs x workgroups per CU, queried once per (kernel, nt,
+// device) and cached.  0 if the query fails.
+unsigned resident_wgs(const void* kernel, int nt);
+
 }  // namespace hyenand
