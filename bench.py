@@ -34,11 +34,16 @@ METRIC_BWD_CIRC = ("Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, db
                    "% of HBM roofline (1 GPU)")
 UNIT = "Gvoxel·channels/s"
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
-# fp32 vector peak without packed-FP32 instructions (the build disables them):
-# 256 CUs x 64 lanes x 2 flop (FMA) x 2.4 GHz.
-ALU_PEAK = 256 * 64 * 2 * 2.4e9
+# MI355X's published fp32 vector peak (157.3 TFLOP/s: 256 CUs x 2.4 GHz x 256
+# flop per CU per clock, counting FMA as two flops and packed-FP32 issue).  This
+# build compiles with packed FP32 disabled, so its own ceiling is half of that;
+# the roofline is still priced against the published figure.
+ALU_PEAK = 157.3e12
 SETTLE_S = 0.3               # untimed calls before the warmup steps (GPU clock ramp)
 DEFAULT_WORKLOAD = "2d_256x256_b8_c64_f32"
+# The second workload with a throughput target (the 128^3 volume), measured by
+# the default invocation as well.
+SECOND_WORKLOAD = "3d_128x128x128_b1_c32_f32"
 
 
 def _geom(dims, circ=False):
@@ -256,56 +261,36 @@ def cpu_baseline_bwd(wl, circ=False, max_seconds=20.0):
                       f"(radix-2 FFT) route{', circular' if circ else ''}, {t_total:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward (default) or the backward with the kernel gradient")
-    ap.add_argument("--boundary", choices=("padded", "circular"), default="padded",
-                    help="zero-padded non-circular convolution (default) or the circular mode")
-    ap.add_argument("--kernel", choices=("shared", "per-sample"), default="shared",
-                    help="one kernel per channel (default) or one per (b, c): input-dependent kernels "
-                         "(zero-padded mode only)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--ws-mb", type=float, default=None,
-                    help="workspace size in MiB (default: the library's recommendation)")
-    ap.add_argument("--copy-probe-mb", type=int, default=None,
-                    help="only run 5 device-to-device copies of this many MiB (a kernel of known HBM "
-                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
-              "channel with no communication, but no multi-GPU run is part of it.", file=sys.stderr)
-        return 2
+def _alg_bytes(name, wl, nch_pairs, nch, es, circ=False, ps=False):
+    """Algorithmic bytes of one launch of pass `name`: the method's own
+    traffic only (x read, K_hat read, y written, and in the backward dy read,
+    dx and dK written), never the workspace that the passes hand each other."""
+    g = _geom(wl.dims, circ)
+    P = nch_pairs
+    kbytes = nch * (2 * wl.dims[0] if (wl.d == 1 and wl.dims[0] > 1024) else g["ksz"]) * 8
+    xb = P * g["vox"] * es
+    table = {"row_fwd": xb, "row_inv": xb, "col_out": kbytes, "conv1d": 2 * xb + kbytes,
+             "col_mid_fwd": 0, "col_mid_inv": 0, "lng_col_fwd": xb, "lng_row": kbytes, "lng_col_inv": xb,
+             "plane_fwd": xb, "plane_inv": xb, "fused2d": 2 * xb + kbytes,
+             "row_fwd_dy": xb, "row_fwd_u": xb, "col_mid_fwd_dy": 0, "col_mid_fwd_u": 0,
+             "col_out_bwd": kbytes, "row_inv_bwd": 2 * xb, "gate_reduce": 0, "mid_inv_dk": 0,
+             "dk_row": nch * g["kl"] * 4, "conv1d_bwd": 3 * xb + kbytes, "corr1d": 2 * xb,
+             "lng_col_fwd_dy": xb, "lng_col_fwd_u": xb, "lng_row_dk": 0, "lng_row_du": kbytes,
+             "lng_col_inv_bwd": 2 * xb, "lng_col_dk": nch * g["kl"] * 4}
+    return table[name]
 
+
+def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=50, warmup=10, settle_s=SETTLE_S,
+                 ws_mb=None, with_cpu=True):
+    """Time one workload; returns the fields of its JSON line."""
+    import numpy as np
     import torch
 
-    if args.copy_probe_mb is not None:
-        n = args.copy_probe_mb << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "copies": 5}))
-        return 0
-
-    import numpy as np
-
-    import dimensional_fft_long_amd as H
     import synth
 
-    wl = {w.name: w for w in synth.WORKLOADS}[args.workload]
-    circ = args.boundary == "circular"
-    ps = args.kernel == "per-sample"
-    if circ and ps:
-        print("bench.py: per-sample kernels are built for the zero-padded mode only", file=sys.stderr)
-        return 2
+    circ = boundary == "circular"
+    ps = kernel == "per-sample"
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     es = 2 if wl.dtype == "bf16" else 4
 
     # Inputs of record: seeded parameters and x on the host, kernel evaluated on the device.
@@ -336,7 +321,7 @@ def main():
     torch.cuda.synchronize()
     spectrum_ms = s0.elapsed_time(s1)
     del K
-    bwd = args.which == "bwd"
+    bwd = which == "bwd"
     if bwd:
         dy = synth.draw_dy(wl.dims, wl.B, wl.C, wl.dtype, wl.seed).to(dev)
         kshape = ((wl.B,) if ps else ()) + (wl.C,) + (tuple(wl.dims) if circ else tuple(2 * n - 1 for n in wl.dims))
@@ -344,19 +329,19 @@ def main():
                 torch.empty(kshape, device=dev))
         B_ws = 1 if ps else wl.B  # the per-sample backward runs the batch entries one at a time
         ws_bytes = H.bwd_workspace_bytes(B_ws, wl.C, wl.dims, x.dtype, circular=circ)
-        if args.ws_mb is not None:
+        if ws_mb is not None:
             ws_bytes = max(H.bwd_workspace_bytes(B_ws, wl.C, wl.dims, x.dtype, minimum=True, circular=circ),
-                           int(args.ws_mb * 2**20))
+                           int(ws_mb * 2**20))
     elif circ:
         y = torch.empty_like(x)
         ws_bytes = H.circ_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
-        if args.ws_mb is not None:
-            ws_bytes = max(H.circ_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
+        if ws_mb is not None:
+            ws_bytes = max(H.circ_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(ws_mb * 2**20))
     else:
         y = torch.empty_like(x)
         ws_bytes = H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype)
-        if args.ws_mb is not None:
-            ws_bytes = max(H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(args.ws_mb * 2**20))
+        if ws_mb is not None:
+            ws_bytes = max(H.workspace_bytes(wl.B, wl.C, wl.dims, x.dtype, minimum=True), int(ws_mb * 2**20))
     ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
 
     def call():
@@ -385,15 +370,15 @@ def main():
     torch.cuda.synchronize()
     # Clock settle (untimed): the GPU needs tens of milliseconds of load to
     # reach its steady clock (256^2: the first ~20 ms of calls run ~10% slower),
-    # so calls repeat for at least SETTLE_S before the W warmup steps.
+    # so calls repeat for at least settle_s before the W warmup steps.
     t0 = time.perf_counter()
     settle_calls = 0
-    while time.perf_counter() - t0 < SETTLE_S:
+    while time.perf_counter() - t0 < settle_s:
         for _ in range(8):
             call()
         settle_calls += 8
         torch.cuda.synchronize()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         call()
     torch.cuda.synchronize()
 
@@ -401,37 +386,37 @@ def main():
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         call()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = total_ms / steps
 
     # Per-kernel durations: the same `steps` calls again through the traced
     # entry point, which records HIP events on the launch stream between kernels.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for k in range(args.steps):
+    for k in range(steps):
         traced(evs[k])
     torch.cuda.synchronize()
     # The interval between two events around a kernel also holds the
     # processing of one event marker; measured here as the interval between
     # two markers with nothing in between, then taken off each kernel's.
-    mk = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    mk = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     st = torch.cuda.current_stream()
-    for k in range(args.steps):
+    for k in range(steps):
         mk[2 * k].record(st)
         mk[2 * k + 1].record(st)
     torch.cuda.synchronize()
-    marker_ms = sorted(mk[2 * k].elapsed_time(mk[2 * k + 1]) for k in range(args.steps))[args.steps // 2]
+    marker_ms = sorted(mk[2 * k].elapsed_time(mk[2 * k + 1]) for k in range(steps))[steps // 2]
 
     # Cold-cache steps (secondary figure): a 1 GiB buffer is rewritten before
     # each call, evicting the 256 MB Infinity Cache and the L2s, so every input
     # comes from HBM.  Percentiles over `steps` single calls.
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cold = []
-    for k in range(args.steps):
+    for k in range(steps):
         flush.fill_(float(k))
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(st)
@@ -443,15 +428,14 @@ def main():
     del flush
 
     g = _geom(wl.dims, circ)
+    long1d = wl.d == 1 and wl.dims[0] > 1024
     if bwd:
         per_ch = H.bwd_workspace_bytes(B_ws, wl.C, wl.dims, x.dtype, minimum=True, circular=circ)
         nch = min(wl.C, ws_bytes // per_ch)
         nch = -(-wl.C // -(-wl.C // nch))  # balanced chunks, as the library splits them
-        plan = {"chunk_channels": nch}
         # x, dy and dx once, K_hat once, dK once (alpha, beta, dalpha, dbeta negligible)
         nk = wl.C * (wl.B if ps else 1)
         bytes_min = 3 * wl.B * wl.C * wl.voxels * es + nk * g["ksz"] * 8 + nk * g["kl"] * 4
-        long1d = wl.d == 1 and wl.dims[0] > 1024
         names = H.BWD_PASS_NAMES[(("long4096" if 2 * wl.dims[0] > (1 << 22) else "long") if long1d else wl.d, True)]
         if long1d:
             bytes_min = 3 * wl.B * wl.C * wl.voxels * es + wl.C * 2 * wl.dims[0] * 8 + wl.C * g["kl"] * 4
@@ -462,54 +446,44 @@ def main():
             nch = -(-wl.C // -(-wl.C // nch))  # balanced chunks, as the library splits them
         else:
             nch = wl.C
-        plan = {"chunk_channels": nch}
-        long1d = wl.d == 1 and wl.dims[0] > 1024
         ksz = 2 * wl.dims[0] if long1d else g["ksz"]
         bytes_min = 2 * wl.B * wl.C * wl.voxels * es + wl.C * ksz * 8 * (wl.B if ps else 1)
-        names = ("lng_col_fwd", "lng_row", "lng_col_inv") if long1d else H.PASS_NAMES[wl.d]
+        names = ("lng_col_fwd", "lng_row", "lng_col_inv") if long1d else H.pass_names(wl.dims, circ)
     per_pass = {nm: [] for nm in names}
     step_ms = []
-    for k in range(args.steps):
+    for k in range(steps):
         e = evs[k]
         step_ms.append(e[0].elapsed_time(e[-1]))
         for j in range(n_launch):
             per_pass[names[j % len(names)]].append(e[j].elapsed_time(e[j + 1]) - marker_ms)
     dominant = max(per_pass, key=lambda nm: sum(per_pass[nm]))
     dom_s = sum(per_pass[dominant]) / len(per_pass[dominant]) / 1e3
-    nch = plan["chunk_channels"]
     if bwd and ps:  # one batch entry per launch, its own spectra
-        by, fl = pass_model(dominant, wl.dims, nch, nch, es, circ)
+        P_l, nk_l = nch, nch
     else:
-        by, fl = pass_model(dominant, wl.dims, nch * wl.B, nch * (wl.B if ps else 1), es, circ)
+        P_l, nk_l = nch * wl.B, nch * (wl.B if ps else 1)
+    moved, fl = pass_model(dominant, wl.dims, P_l, nk_l, es, circ)
+    alg = _alg_bytes(dominant, wl, P_l, nk_l, es, circ, ps)
     kernel_label = KERNEL_LABEL[dominant]
-    hbm = {"bound": "hbm", "achieved": by / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    hbm = {"bound": "hbm", "achieved": alg / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     alu = {"bound": "alu", "achieved": fl / dom_s / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s"}
     for r in (hbm, alu):
         r["frac"] = r["achieved"] / r["peak"]
     roof = hbm if hbm["frac"] >= alu["frac"] else alu
-    roof.update({"kernel": kernel_label, "avg_us": dom_s * 1e6,
-                 "traffic": None if (circ or ps) else _traffic_from_profile(kernel_label, wl.name, nch)})
+    traffic = None if (circ or ps) else _traffic_from_profile(kernel_label, wl.name, nch)
+    roof.update({"traffic": traffic, "kernel": kernel_label, "avg_us": dom_s * 1e6,
+                 "traffic_over_algorithmic": (traffic / alg) if (traffic and alg) else None,
+                 "design_bytes_per_launch": moved})
     roof["other_bound"] = {k: v for k, v in (alu if roof is hbm else hbm).items()}
 
     voxch = wl.B * wl.C * wl.voxels
-    value = voxch / (ms_per_step / 1e3) / 1e9
     out = {
-        "metric": ((METRIC_BWD_CIRC if circ else (METRIC_BWD_PS if ps else METRIC_BWD)) if bwd
-                   else (METRIC_CIRC if circ else (METRIC_PS if ps else METRIC))),
-        "value": value,
-        "unit": UNIT,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "value": voxch / (ms_per_step / 1e3) / 1e9,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "pass": args.which, "boundary": args.boundary, "kernel": args.kernel, "grid": list(wl.dims), "padded": [n if circ else 2 * n for n in wl.dims], "B": wl.B,
-                   "C": wl.C, "io_dtype": "bf16" if wl.dtype == "bf16" else "fp32", "launches_per_step": n_launch, "workspace_mib": ws_bytes / 2**20,
-                   "chunk_channels": plan["chunk_channels"]},
+        "config": {"workload": wl.name, "pass": which, "boundary": boundary, "kernel": kernel,
+                   "grid": list(wl.dims), "padded": [n if circ else 2 * n for n in wl.dims], "B": wl.B,
+                   "C": wl.C, "io_dtype": "bf16" if wl.dtype == "bf16" else "fp32",
+                   "launches_per_step": n_launch, "workspace_mib": ws_bytes / 2**20, "chunk_channels": nch},
         "hbm_roofline_frac_of_metric": bytes_min / (ms_per_step / 1e3) / HBM_PEAK,
         "bytes_min": bytes_min,
         "traced_step_ms_median": sorted(step_ms)[len(step_ms) // 2],
@@ -522,8 +496,115 @@ def main():
         "spectrum_ms": spectrum_ms,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if with_cpu:
         out["cpu_baseline"] = cpu_baseline_bwd(wl, circ) if bwd else cpu_baseline(wl, circ)
+    return out
+
+
+def copy_bandwidth(mib=1024, reps=10):
+    """Device-to-device copy bandwidth (read + write bytes per second) on this
+    GPU, as context for the HBM figures (the roofline peak stays 8 TB/s)."""
+    import torch
+
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    return 2 * (mib << 20) * reps / (a.elapsed_time(b) / 1e3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward with the kernel gradient")
+    ap.add_argument("--boundary", choices=("padded", "circular"), default="padded",
+                    help="zero-padded non-circular convolution (default) or the circular mode")
+    ap.add_argument("--kernel", choices=("shared", "per-sample"), default="shared",
+                    help="one kernel per channel (default) or one per (b, c): input-dependent kernels "
+                         "(zero-padded mode only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated further workloads measured the same way and reported under "
+                         f"'also' (default for the default invocation: {SECOND_WORKLOAD}; 'none' for none)")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed calls before the warmup (0 for profiler runs)")
+    ap.add_argument("--ws-mb", type=float, default=None,
+                    help="workspace size in MiB (default: the library's recommendation)")
+    ap.add_argument("--copy-probe-mb", type=int, default=None,
+                    help="only run 5 device-to-device copies of this many MiB (a kernel of known HBM "
+                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "channel with no communication, but no multi-GPU run is part of it.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_probe_mb is not None:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "copies": 5}))
+        return 0
+
+    import dimensional_fft_long_amd as H
+    import synth
+
+    if args.boundary == "circular" and args.kernel == "per-sample":
+        print("bench.py: per-sample kernels are built for the zero-padded mode only", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(torch.device("cuda:0"))
+    by_name = {w.name: w for w in synth.WORKLOADS}
+    wl = by_name[args.workload]
+    main_run = run_workload(H, wl, args.which, args.boundary, args.kernel, args.steps, args.warmup, args.settle_s,
+                            args.ws_mb, with_cpu=not args.no_cpu_baseline)
+    circ, ps, bwd = args.boundary == "circular", args.kernel == "per-sample", args.which == "bwd"
+    out = {
+        "metric": ((METRIC_BWD_CIRC if circ else (METRIC_BWD_PS if ps else METRIC_BWD)) if bwd
+                   else (METRIC_CIRC if circ else (METRIC_PS if ps else METRIC))),
+        "value": main_run.pop("value"),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_run.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        # the arithmetic type of every transform, product and gate (bf16
+        # workloads read and write bf16: config.io_dtype)
+        "dtype": "f32",
+        "data": "synthetic",
+    }
+    out.update(main_run)
+    also = args.also
+    if also is None:
+        default_call = (args.workload == DEFAULT_WORKLOAD and not circ and not ps and not bwd)
+        also = SECOND_WORKLOAD if default_call else "none"
+    extra = {}
+    for name in [a for a in also.split(",") if a and a != "none"]:
+        r = run_workload(H, by_name[name], args.which, args.boundary, args.kernel, args.steps, args.warmup,
+                         args.settle_s, None, with_cpu=False)
+        extra[name] = {k: r[k] for k in ("value", "ms_per_step", "hbm_roofline_frac_of_metric", "bytes_min",
+                                         "cold_cache_ms_per_step", "per_kernel_us", "roofline", "config")}
+    if extra:
+        out["also"] = extra
+    out["copy_bandwidth_GBps"] = copy_bandwidth()
     print(json.dumps(out), flush=True)
     return 0
 

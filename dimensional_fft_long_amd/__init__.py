@@ -19,7 +19,8 @@ zero outside the grid.  Entry points mirror ``include/hyenand.h``:
 * ``fftconv_bwd(x, alpha, beta, K_hat, dy)`` -> (dx, dalpha, dbeta, dK): the
   backward, recomputing the forward transforms (explainer, "Implementation and
   operation patterns", "Concrete implementation pattern (PyTorch)")
-* ``HyenaConvolutionFunction`` -- the autograd wrapper of that pattern
+* ``gated_fftconv`` / ``GatedFFTConvFunction`` -- the differentiable operation
+  (torch autograd over the forward and the backward)
 * ``fftconv_fwd_per_sample(x, alpha, beta, K_hat)`` -- input-dependent kernels:
   K_hat = kernel_spectrum(K) of kernels [B, C, *(2n-1)], one per (b, c);
   ``fftconv_bwd_per_sample(...)`` its backward (dK per (b, c))
@@ -175,6 +176,15 @@ def workspace_bytes(B: int, C: int, dims, dtype=torch.float32, minimum: bool = F
     return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype)))
 
 
+def _check_spectrum_out(out, nbytes, device):
+    if not isinstance(out, torch.Tensor) or out.dtype != torch.complex64:
+        raise TypeError("out must be a complex64 tensor")
+    if out.device != torch.device(device) or not out.is_contiguous():
+        raise TypeError(f"out must be a contiguous tensor on {device}")
+    if out.numel() * 8 < nbytes:
+        raise ValueError(f"out holds {out.numel() * 8} bytes, the spectrum needs {nbytes}")
+
+
 def kernel_spectrum(K: torch.Tensor, dims=None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """K: fp32 device tensor [C, 2n_0-1, ..., 2n_{d-1}-1] -> K_hat (complex64 flat [C, ksz])."""
     if dims is None:
@@ -191,6 +201,8 @@ def kernel_spectrum(K: torch.Tensor, dims=None, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty(nbytes // 8, dtype=torch.complex64, device=K.device).view(C, -1) if C else \
             torch.empty(0, dtype=torch.complex64, device=K.device)
+    else:
+        _check_spectrum_out(out, nbytes, K.device)
     rc = get_lib().hyenand_kernel_spectrum(_P(K.data_ptr()), _P(out.data_ptr()), C, len(dims), _dims_arr(dims),
                                      _stream(stream))
     if rc != OK:
@@ -201,15 +213,42 @@ def kernel_spectrum(K: torch.Tensor, dims=None, out: torch.Tensor | None = None,
 _ws_cache: dict = {}
 
 
-def _workspace(B, C, dims, dtype, device):
-    """The workspace is sized once per shape and reused (allocated on first use)."""
-    nbytes = workspace_bytes(B, C, dims, dtype)
-    key = (str(device), nbytes)
+def _cached_ws(kind: str, nbytes: int, device, stream):
+    """A workspace of ``nbytes`` sized once per shape and reused (explainer,
+    "Implementation and operation patterns", "Memory allocation and buffer
+    management": the size follows from the input shape).  One buffer per
+    (kind, device, size, stream): calls in flight on different streams never
+    share a workspace, and calls on one stream are ordered by the stream."""
+    st = torch.cuda.current_stream(device) if stream is None else stream
+    key = (kind, str(device), int(nbytes), int(st.cuda_stream))
     buf = _ws_cache.get(key)
     if buf is None:
-        buf = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(int(nbytes), 8), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
-    return buf, nbytes
+    return buf, int(nbytes)
+
+
+def _workspace(B, C, dims, dtype, device, stream=None):
+    return _cached_ws("fwd", workspace_bytes(B, C, dims, dtype), device, stream)
+
+
+def _check_out(t, name, shape, dtype, device, like=None):
+    """A caller-provided output: contiguous, on ``device``, of exactly ``shape``
+    and ``dtype``, and not overlapping ``like`` (the input it must not alias)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != torch.device(device) or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous tensor on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if like is not None and t.numel() > 0:
+        a0, a1 = t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()
+        b0, b1 = like.data_ptr(), like.data_ptr() + like.numel() * like.element_size()
+        if a0 < b1 and b0 < a1:
+            raise ValueError(f"{name} must not overlap the input")
+    return t
 
 
 def fftconv_fwd(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, K_hat: torch.Tensor,
@@ -227,10 +266,9 @@ def fftconv_fwd(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, K_hat:
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
     if K_hat.numel() * 8 < spectrum_bytes(C, dims):
         raise ValueError("K_hat is smaller than the spectrum of this shape")
-    if y is None:
-        y = torch.empty_like(x)
+    y = torch.empty_like(x) if y is None else _check_out(y, "y", x.shape, x.dtype, x.device, like=x)
     if workspace is None:
-        workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device)
+        workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device, stream)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     rc = get_lib().hyenand_fftconv_fwd(_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()),
@@ -253,6 +291,11 @@ def launch_plan(B: int, C: int, dims, dtype, workspace_bytes: int) -> dict:
 
 PASS_NAMES = {1: ("conv1d",), 2: ("row_fwd", "col_out", "row_inv"),
               3: ("row_fwd", "col_mid_fwd", "col_out", "col_mid_inv", "row_inv")}
+
+
+def pass_names(dims, circular: bool = False):
+    """Names of the kernels one channel chunk of a forward call launches, in order."""
+    return PASS_NAMES[len(dims)]
 
 
 def fftconv_fwd_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None) -> int:
@@ -287,18 +330,12 @@ def bwd_workspace_bytes(B: int, C: int, dims, dtype=torch.float32, with_dK: bool
     return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype), int(bool(with_dK))))
 
 
-def _bwd_workspace(B, C, dims, dtype, with_dK, device, circular=False):
-    nbytes = bwd_workspace_bytes(B, C, dims, dtype, with_dK, circular=circular)
-    key = ("bwd", str(device), nbytes)
-    buf = _ws_cache.get(key)
-    if buf is None:
-        buf = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
-    return buf, nbytes
+def _bwd_workspace(B, C, dims, dtype, with_dK, device, circular=False, stream=None):
+    return _cached_ws("bwd", bwd_workspace_bytes(B, C, dims, dtype, with_dK, circular=circular), device, stream)
 
 
 def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, circular=False,
-              per_sample=False):
+              per_sample=False, stream=None):
     if not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous device tensor")
     if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_cuda or not dy.is_contiguous():
@@ -313,15 +350,23 @@ def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspa
     need = spectrum_circ_bytes(C, dims) if circular else spectrum_bytes(C, dims) * (B if per_sample else 1)
     if K_hat.numel() * 8 < need:
         raise ValueError("K_hat is smaller than the spectrum of this shape")
-    dx = torch.empty_like(x) if dx is None else dx
-    dalpha = torch.empty(C, dtype=torch.float32, device=x.device) if dalpha is None else dalpha
-    dbeta = torch.empty(C, dtype=torch.float32, device=x.device) if dbeta is None else dbeta
+    dev = x.device
+    dx = torch.empty_like(x) if dx is None else _check_out(dx, "dx", x.shape, x.dtype, dev, like=x)
+    if dx is not None:
+        _check_out(dx, "dx", x.shape, x.dtype, dev, like=dy)
+    dalpha = torch.empty(C, dtype=torch.float32, device=dev) if dalpha is None else \
+        _check_out(dalpha, "dalpha", (C,), torch.float32, dev)
+    dbeta = torch.empty(C, dtype=torch.float32, device=dev) if dbeta is None else \
+        _check_out(dbeta, "dbeta", (C,), torch.float32, dev)
+    kdims = dims if circular else tuple(2 * n - 1 for n in dims)
+    kshape = ((B,) if per_sample else ()) + (C,) + kdims
     if with_dK and dK is None:
-        kdims = dims if circular else tuple(2 * n - 1 for n in dims)
-        dK = torch.empty(((B,) if per_sample else ()) + (C,) + kdims, dtype=torch.float32, device=x.device)
+        dK = torch.empty(kshape, dtype=torch.float32, device=dev)
+    elif dK is not None:
+        _check_out(dK, "dK", kshape, torch.float32, dev)
     if workspace is None:
-        workspace, ws_bytes = _bwd_workspace(1 if per_sample else B, C, dims, x.dtype, dK is not None, x.device,
-                                             circular)
+        workspace, ws_bytes = _bwd_workspace(1 if per_sample else B, C, dims, x.dtype, dK is not None, dev,
+                                             circular, stream)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(dy.data_ptr()),
@@ -336,7 +381,7 @@ def fftconv_bwd(x, alpha, beta, K_hat, dy, dx=None, dalpha=None, dbeta=None, dK=
     """Backward of fftconv_fwd for the output gradient dy.
 
     Returns (dx [B, C, *dims] in x's dtype, dalpha [C], dbeta [C], dK [C, *(2*dims-1)] or None)."""
-    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace)
+    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, stream=stream)
     rc = get_lib().hyenand_fftconv_bwd(*args, _stream(stream))
     if rc != OK:
         raise HyenandError(rc, "fftconv_bwd")
@@ -369,7 +414,7 @@ def fftconv_bwd_traced(x, alpha, beta, K_hat, dy, outs, workspace, events, strea
     the launch count."""
     dx, dalpha, dbeta, dK = outs
     args, _ = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, dK is not None, workspace, circular,
-                        per_sample)
+                        per_sample, stream)
     st = torch.cuda.current_stream() if stream is None else stream
     for e in events:
         if e.cuda_event == 0:
@@ -385,42 +430,45 @@ def fftconv_bwd_traced(x, alpha, beta, K_hat, dy, outs, workspace, events, strea
     return int(n.value)
 
 
-class HyenaConvolutionFunction(torch.autograd.Function):
-    """Autograd wrapper in the shape of the explainer's "Concrete implementation
-    pattern (PyTorch)": the forward keeps only the input and the kernel
-    parameters (alpha, beta and the kernel spectrum computed from K), the
-    backward recomputes the transforms and returns the gradients of x, alpha,
-    beta and K.  The FFT workspaces are preallocated per shape and reused.
+class GatedFFTConvFunction(torch.autograd.Function):
+    """The library's forward and backward as one differentiable operation.
 
-    K [C, *(2n-1)]: one kernel per channel; K [B, C, *(2n-1)]: one per (b, c)
-    (input-dependent kernels); ``circular=True``: the circular mode, K [C, *n]."""
+    Inputs: x [B, C, *dims] (fp32 or bf16), alpha and beta [C], and the
+    spatial kernel K: [C, *(2n-1)] shared by the batch, [B, C, *(2n-1)] one per
+    (b, c) (input-dependent kernels), or [C, *dims] with ``circular=True``.
+    Only x, alpha, beta and the kernel spectrum are kept for the backward, which
+    recomputes every transform from them: the recompute-instead-of-store
+    trade-off the explainer recommends for the FFT intermediates ("Gradient
+    flow and numerical stability", gradient checkpointing).  Gradients flow to
+    x, alpha, beta and K; the FFT workspaces are sized once per shape and
+    reused."""
 
     @staticmethod
     def forward(ctx, x, alpha, beta, K, circular=False):
         dims = tuple(int(v) for v in x.shape[2:])
-        per_sample = K.dim() == x.dim()
-        if circular and per_sample:
+        mode = "circular" if circular else ("per_sample" if K.dim() == x.dim() else "shared")
+        if mode == "circular" and K.dim() == x.dim():
             raise ValueError("per-sample kernels are built for the zero-padded mode only")
-        if circular:
-            K_hat = kernel_spectrum_circ(K.contiguous())
-            y = fftconv_fwd_circ(x, alpha, beta, K_hat)
-        elif per_sample:
-            K_hat = kernel_spectrum_per_sample(K.contiguous())
-            y = fftconv_fwd_per_sample(x, alpha, beta, K_hat)
-        else:
-            K_hat = kernel_spectrum(K.contiguous(), dims)
-            y = fftconv_fwd(x, alpha, beta, K_hat)
+        spec, fwd = {"circular": (kernel_spectrum_circ, fftconv_fwd_circ),
+                     "per_sample": (kernel_spectrum_per_sample, fftconv_fwd_per_sample),
+                     "shared": (lambda k: kernel_spectrum(k, dims), fftconv_fwd)}[mode]
+        K_hat = spec(K.contiguous())
+        ctx.mode = mode
+        ctx.want_dK = bool(ctx.needs_input_grad[3])
         ctx.save_for_backward(x, alpha, beta, K_hat)
-        ctx.needs_dK = ctx.needs_input_grad[3]
-        ctx.mode = "circular" if circular else ("per_sample" if per_sample else "shared")
-        return y
+        return fwd(x, alpha, beta, K_hat)
 
     @staticmethod
-    def backward(ctx, grad_out):
+    def backward(ctx, dy):
         x, alpha, beta, K_hat = ctx.saved_tensors
-        f = {"circular": fftconv_bwd_circ, "per_sample": fftconv_bwd_per_sample, "shared": fftconv_bwd}[ctx.mode]
-        dx, da, db, dK = f(x, alpha, beta, K_hat, grad_out.contiguous(), with_dK=ctx.needs_dK)
-        return dx, da, db, dK, None
+        bwd = {"circular": fftconv_bwd_circ, "per_sample": fftconv_bwd_per_sample, "shared": fftconv_bwd}[ctx.mode]
+        dx, dalpha, dbeta, dK = bwd(x, alpha, beta, K_hat, dy.contiguous(), with_dK=ctx.want_dK)
+        return dx, dalpha, dbeta, dK, None  # no gradient for the boundary flag
+
+
+def gated_fftconv(x, alpha, beta, K, circular: bool = False) -> torch.Tensor:
+    """Differentiable gated N-D convolution (GatedFFTConvFunction)."""
+    return GatedFFTConvFunction.apply(x, alpha, beta, K, circular)
 
 
 # ----------------------------------------------------------- circular mode
@@ -430,7 +478,8 @@ def fftconv_bwd_circ(x, alpha, beta, K_hat, dy, dx=None, dalpha=None, dbeta=None
     """Backward of fftconv_fwd_circ for the output gradient dy; K_hat from
     kernel_spectrum_circ.  Returns (dx, dalpha, dbeta, dK [C, *dims] or None),
     dK indexed by offset mod n like the circular K."""
-    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, circular=True)
+    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, circular=True,
+                           stream=stream)
     rc = get_lib().hyenand_fftconv_bwd_circ(*args, _stream(stream))
     if rc != OK:
         raise HyenandError(rc, "fftconv_bwd_circ")
@@ -459,6 +508,8 @@ def kernel_spectrum_circ(K: torch.Tensor, out: torch.Tensor | None = None, strea
     if out is None:
         out = torch.empty(nbytes // 8, dtype=torch.complex64, device=K.device).view(C, -1) if C else \
             torch.empty(0, dtype=torch.complex64, device=K.device)
+    else:
+        _check_spectrum_out(out, nbytes, K.device)
     rc = get_lib().hyenand_kernel_spectrum_circ(_P(K.data_ptr()), _P(out.data_ptr()), C, len(dims), _dims_arr(dims),
                                                 _stream(stream))
     if rc != OK:
@@ -466,7 +517,7 @@ def kernel_spectrum_circ(K: torch.Tensor, out: torch.Tensor | None = None, strea
     return out
 
 
-def _circ_args(x, alpha, beta, K_hat, y, workspace):
+def _circ_args(x, alpha, beta, K_hat, y, workspace, stream=None):
     if not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous device tensor")
     B, C = int(x.shape[0]), int(x.shape[1])
@@ -478,15 +529,9 @@ def _circ_args(x, alpha, beta, K_hat, y, workspace):
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum_circ")
     if K_hat.numel() * 8 < spectrum_circ_bytes(C, dims):
         raise ValueError("K_hat is smaller than the circular spectrum of this shape")
-    y = torch.empty_like(x) if y is None else y
+    y = torch.empty_like(x) if y is None else _check_out(y, "y", x.shape, x.dtype, x.device, like=x)
     if workspace is None:
-        nbytes = circ_workspace_bytes(B, C, dims, x.dtype)
-        key = ("circ", str(x.device), nbytes)
-        workspace = _ws_cache.get(key)
-        if workspace is None:
-            workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
-            _ws_cache[key] = workspace
-        ws_bytes = nbytes
+        workspace, ws_bytes = _cached_ws("circ", circ_workspace_bytes(B, C, dims, x.dtype), x.device, stream)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
@@ -496,7 +541,7 @@ def _circ_args(x, alpha, beta, K_hat, y, workspace):
 
 def fftconv_fwd_circ(x, alpha, beta, K_hat, y=None, workspace=None, stream=None) -> torch.Tensor:
     """Circular-mode gated N-D convolution (periodic grid, no padding); K_hat from kernel_spectrum_circ."""
-    args, y = _circ_args(x, alpha, beta, K_hat, y, workspace)
+    args, y = _circ_args(x, alpha, beta, K_hat, y, workspace, stream)
     rc = get_lib().hyenand_fftconv_fwd_circ(*args, _stream(stream))
     if rc != OK:
         raise HyenandError(rc, "fftconv_fwd_circ")
@@ -505,7 +550,7 @@ def fftconv_fwd_circ(x, alpha, beta, K_hat, y=None, workspace=None, stream=None)
 
 def fftconv_fwd_circ_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None) -> int:
     """fftconv_fwd_circ recording ``events`` before each kernel launch and after the last."""
-    args, y = _circ_args(x, alpha, beta, K_hat, y, workspace)
+    args, y = _circ_args(x, alpha, beta, K_hat, y, workspace, stream)
     st = torch.cuda.current_stream() if stream is None else stream
     for e in events:
         if e.cuda_event == 0:
@@ -527,7 +572,7 @@ def kernel_spectrum_per_sample(K: torch.Tensor, stream=None) -> torch.Tensor:
     return kernel_spectrum(K.reshape((B * C,) + tuple(K.shape[2:])), dims, stream=stream)
 
 
-def _ps_args(x, alpha, beta, K_hat, y, workspace):
+def _ps_args(x, alpha, beta, K_hat, y, workspace, stream=None):
     if not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous device tensor")
     B, C = int(x.shape[0]), int(x.shape[1])
@@ -539,9 +584,9 @@ def _ps_args(x, alpha, beta, K_hat, y, workspace):
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum_per_sample")
     if K_hat.numel() * 8 < spectrum_bytes(B * C, dims):
         raise ValueError("K_hat must hold B * C spectra of this shape")
-    y = torch.empty_like(x) if y is None else y
+    y = torch.empty_like(x) if y is None else _check_out(y, "y", x.shape, x.dtype, x.device, like=x)
     if workspace is None:
-        workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device)
+        workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device, stream)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     return [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
@@ -550,7 +595,7 @@ def _ps_args(x, alpha, beta, K_hat, y, workspace):
 
 def fftconv_fwd_per_sample(x, alpha, beta, K_hat, y=None, workspace=None, stream=None) -> torch.Tensor:
     """Gated N-D convolution with one kernel per (b, c) (K_hat from kernel_spectrum_per_sample)."""
-    args, y = _ps_args(x, alpha, beta, K_hat, y, workspace)
+    args, y = _ps_args(x, alpha, beta, K_hat, y, workspace, stream)
     rc = get_lib().hyenand_fftconv_fwd_per_sample(*args, _stream(stream))
     if rc != OK:
         raise HyenandError(rc, "fftconv_fwd_per_sample")
@@ -563,7 +608,8 @@ def fftconv_bwd_per_sample(x, alpha, beta, K_hat, dy, dx=None, dalpha=None, dbet
     kernel_spectrum_per_sample.  Returns (dx, dalpha [C], dbeta [C],
     dK [B, C, *(2*dims-1)] or None): one kernel gradient per (b, c).  The
     workspace is that of a batch of one (bwd_workspace_bytes(1, C, dims))."""
-    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, per_sample=True)
+    args, outs = _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspace, per_sample=True,
+                           stream=stream)
     rc = get_lib().hyenand_fftconv_bwd_per_sample(*args, _stream(stream))
     if rc != OK:
         raise HyenandError(rc, "fftconv_bwd_per_sample")
@@ -571,7 +617,7 @@ def fftconv_bwd_per_sample(x, alpha, beta, K_hat, dy, dx=None, dalpha=None, dbet
 
 
 def fftconv_fwd_per_sample_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None) -> int:
-    args, y = _ps_args(x, alpha, beta, K_hat, y, workspace)
+    args, y = _ps_args(x, alpha, beta, K_hat, y, workspace, stream)
     st = torch.cuda.current_stream() if stream is None else stream
     for e in events:
         if e.cuda_event == 0:

@@ -81,6 +81,7 @@ def _load():
         I64 = ctypes.c_int64
         I = ctypes.c_int
         lib.oracle_gate.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
+        lib.oracle_gate_vjp.argtypes = [P, P, I64, ctypes.c_double, ctypes.c_double, P, P]
         lib.oracle_direct.argtypes = [P, P, P, P, P, I, I, I, P]
         lib.oracle_direct_points.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
         lib.oracle_kernel_spectrum.argtypes = [P, I, I, P, P, P]
@@ -93,7 +94,7 @@ def _load():
         lib.oracle_bwd_direct.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, P]
         lib.oracle_bwd_direct_points.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, I64, P, P]
         lib.oracle_bwd_fft.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, P, P, P]
-        for f in ("oracle_gate", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
+        for f in ("oracle_gate", "oracle_gate_vjp", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
                   "oracle_fftconv_pairs", "oracle_num_threads", "oracle_bwd_direct", "oracle_bwd_direct_points",
                   "oracle_bwd_fft", "oracle_direct_circ", "oracle_fftconv_circ_pairs", "oracle_bwd_direct_circ",
                   "oracle_bwd_fft_circ"):
@@ -128,6 +129,22 @@ def gate(x, alpha: float, beta: float) -> np.ndarray:
     u = np.empty(x.shape, dtype=np.float64)
     _check(_load().oracle_gate(_ptr(x), x.size, float(alpha), float(beta), _ptr(u)), "gate")
     return u
+
+
+def gate_vjp(x, du, alpha: float, beta: float):
+    """The gate's backward alone: for u = phi(x) x and an output gradient du
+    (same shape as x), returns (dx, sum du x^2 s(1-s), sum du x s(1-s)), s the
+    logistic of alpha*x + beta, in fp64 (the chain rule written out in the
+    backward section of oracle.c)."""
+    x = _f32(x)
+    du = np.ascontiguousarray(np.asarray(du, dtype=np.float64))
+    if du.shape != x.shape:
+        raise ValueError("du must have the shape of x")
+    dx = np.empty(x.shape, dtype=np.float64)
+    sums = np.zeros(2, dtype=np.float64)
+    _check(_load().oracle_gate_vjp(_ptr(x), _ptr(du), x.size, float(alpha), float(beta), _ptr(dx), _ptr(sums)),
+           "gate_vjp")
+    return dx, float(sums[0]), float(sums[1])
 
 
 def direct(x, alpha, beta, K) -> np.ndarray:

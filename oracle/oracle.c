@@ -500,6 +500,18 @@ static void gate_vjp(const float *xs, const double *du, int64_t L, double alpha,
     *db += sb;
 }
 
+/* The gate's vector-Jacobian product on its own, for an output gradient du of
+ * u = phi(x) x over `count` elements: dx, and the sums of the dalpha and dbeta
+ * terms (sums[0], sums[1]). */
+int oracle_gate_vjp(const float *x, const double *du, int64_t count, double alpha, double beta, double *dx,
+                    double *sums)
+{
+    if (!x || !du || !dx || !sums || count < 0) return ORC_EINVAL;
+    sums[0] = sums[1] = 0.0;
+    gate_vjp(x, du, count, alpha, beta, dx, &sums[0], &sums[1]);
+    return ORC_OK;
+}
+
 /* O1 of the backward: every sum above written out. */
 int oracle_bwd_direct(const float *x, const float *alpha, const float *beta, const float *K, const float *dy,
                       int B, int C, int d, const int64_t *dims,

@@ -181,17 +181,27 @@ def make(wl_or_dims, B=None, C=None, dtype="f32", seed=0, device="cpu", with_ker
             "B": B, "C": C, "dtype": dtype}
 
 
-def sample_points(dims, B: int, C: int, pairs, per_pair: int, seed: int) -> np.ndarray:
+def sample_points(dims, B: int, C: int, pairs, per_pair: int, seed: int, edges: bool = False) -> np.ndarray:
     """Output coordinates to check one by one: for each listed pair (b, c) the
-    2^d corners, the centre, and ``per_pair`` seeded random voxels.
-    Returns int64 [P, 2+d] rows (b, c, i_0..i_{d-1})."""
+    2^d corners, the centre, with ``edges`` the midpoint of every edge of the
+    grid box (and, in 3-D, the centre of every face), and ``per_pair`` seeded
+    random voxels.  Returns int64 [P, 2+d] rows (b, c, i_0..i_{d-1})."""
     rng = np.random.Generator(np.random.PCG64(seed))
     d = len(dims)
     rows = []
+    # Per axis: 0 = low end, 1 = high end, 2 = middle.  An edge midpoint has
+    # exactly one axis in the middle, a face centre exactly two (d = 3).
+    ends = [(0, n - 1, n // 2) for n in dims]
     for (b, c) in pairs:
         for corner in range(1 << d):
             rows.append([b, c] + [(dims[a] - 1) if (corner >> a) & 1 else 0 for a in range(d)])
         rows.append([b, c] + [n // 2 for n in dims])
+        if edges:
+            for code in range(3 ** d):
+                sel = [(code // 3 ** a) % 3 for a in range(d)]
+                mids = sum(1 for v in sel if v == 2)
+                if 1 <= mids <= max(1, d - 1):
+                    rows.append([b, c] + [ends[a][sel[a]] for a in range(d)])
         for _ in range(per_pair):
             rows.append([b, c] + [int(rng.integers(0, n)) for n in dims])
     return np.asarray(rows, dtype=np.int64)

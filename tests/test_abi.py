@@ -261,3 +261,47 @@ def test_long_1d_sizes(H):
     assert bw == 3  # accepted shape, workspace below one channel
     assert lib.hyenand_fftconv_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, _dims(1 << 24), 0,
                                    FAKE, 1 << 30, None) == 2
+
+
+def test_output_checks_reject_bad_outputs(H):
+    """Caller-provided outputs are checked before any call: dtype, device,
+    contiguity, exact shape, and no overlap with the input they must not alias
+    (host tensors here; the GPU entry points run the same checks)."""
+    import torch
+
+    x = torch.zeros(2, 3, 8, 8)
+    ok = torch.zeros(2, 3, 8, 8)
+    assert H._check_out(ok, "y", x.shape, x.dtype, x.device, like=x) is ok
+    with pytest.raises(TypeError):
+        H._check_out(torch.zeros(2, 3, 8, 8, dtype=torch.bfloat16), "y", x.shape, x.dtype, x.device)
+    with pytest.raises(ValueError):
+        H._check_out(torch.zeros(2, 3, 8, 4), "y", x.shape, x.dtype, x.device)  # undersized
+    with pytest.raises(ValueError):
+        H._check_out(torch.zeros(2, 3, 8, 16), "y", x.shape, x.dtype, x.device)
+    with pytest.raises(TypeError):
+        H._check_out(torch.zeros(2, 3, 8, 16)[..., ::2], "y", x.shape, x.dtype, x.device)  # not contiguous
+    with pytest.raises(ValueError):
+        H._check_out(x, "y", x.shape, x.dtype, x.device, like=x)                      # aliases x
+    with pytest.raises(ValueError):
+        H._check_out(x.view(-1)[5:5 + 16], "dalpha", (16,), x.dtype, x.device, like=x)  # overlaps x
+    with pytest.raises(TypeError):
+        H._check_out(torch.zeros(3, dtype=torch.float64), "dalpha", (3,), torch.float32, x.device)
+    with pytest.raises(ValueError):   # a per-sample-shaped dK where the shared one is expected
+        H._check_out(torch.zeros(2, 3, 15, 15), "dK", (3, 15, 15), torch.float32, x.device)
+    H._check_spectrum_out(torch.zeros(10, dtype=torch.complex64), 80, x.device)
+    with pytest.raises(ValueError):
+        H._check_spectrum_out(torch.zeros(9, dtype=torch.complex64), 80, x.device)
+    with pytest.raises(TypeError):
+        H._check_spectrum_out(torch.zeros(20, dtype=torch.float32), 80, x.device)
+
+
+def test_library_does_not_load_the_oracle():
+    """The product package never imports the oracle (it must fail loudly, not
+    fall back, when its HIP library is missing)."""
+    import subprocess
+    import sys
+
+    code = ("import sys; sys.path.insert(0, %r); import dimensional_fft_long_amd as H; "
+            "print('oracle' in sys.modules)") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True).stdout
+    assert out.strip() == "False"

@@ -211,3 +211,24 @@ def test_pins_reject_mutants(mutant):
     got = mutant(x, a, b, K, dy)
     want = _autograd(x, a, b, K, dy)
     assert max(_rel(g, w) for g, w in zip(got, want)) > 1e-6, "the autograd pin accepted a planted mistake"
+
+
+def test_gate_vjp_matches_autograd():
+    """oracle.gate_vjp against torch autograd (fp64) of u = sigmoid(a x + b) x:
+    the gradient of sum(u * du) with respect to x, a and b; a planted slip (the
+    derivative without the a x s (1-s) term) is rejected."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 7)).astype(np.float32)
+    du = rng.standard_normal((5, 7))
+    for a, b in [(0.7, -0.3), (-1.0, 0.5), (0.0, 0.2)]:
+        xt = torch.tensor(x.astype(np.float64), requires_grad=True)
+        at = torch.tensor(a, dtype=torch.float64, requires_grad=True)
+        bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+        (torch.sigmoid(at * xt + bt) * xt * torch.from_numpy(du)).sum().backward()
+        dx, da, db = oracle.gate_vjp(x, du, a, b)
+        assert _rel(dx, xt.grad.numpy()) < 1e-13
+        assert abs(da - float(at.grad)) <= 1e-12 * max(1.0, abs(float(at.grad)))
+        assert abs(db - float(bt.grad)) <= 1e-12 * max(1.0, abs(float(bt.grad)))
+        s = 1.0 / (1.0 + np.exp(-(a * x.astype(np.float64) + b)))
+        if a != 0.0:
+            assert _rel(du * s, xt.grad.numpy()) > 1e-3

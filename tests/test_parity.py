@@ -253,3 +253,52 @@ def test_every_chunking_gives_the_same_output(H, dims, B, C, dtype):
         outs.append(_gpu_run(H, w, workspace=ws)[0])
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+
+
+def test_two_streams_do_not_share_a_workspace(H):
+    """Same-shape calls in flight on two streams, each with the cached
+    workspace of its own stream, give the results of eager single-stream calls."""
+    dims, B, C = (128, 128), 2, 8
+    dev = torch.device("cuda:0")
+    runs = []
+    for seed in (61, 62):
+        w = synth.make(dims, B=B, C=C, seed=seed)
+        x = w["x"].to(dev)
+        al, be = torch.from_numpy(w["alpha"]).to(dev), torch.from_numpy(w["beta"]).to(dev)
+        kh = H.kernel_spectrum(w["K"].to(dev))
+        runs.append((x, al, be, kh, H.fftconv_fwd(x, al, be, kh).clone()))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = [[], []]
+    for _ in range(4):
+        for k, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                x, al, be, kh, _ = runs[k]
+                outs[k].append(H.fftconv_fwd(x, al, be, kh))
+    torch.cuda.synchronize()
+    for k in range(2):
+        for o in outs[k]:
+            assert torch.equal(o, runs[k][4])
+
+
+def test_bad_outputs_are_rejected_before_the_call(H):
+    w = synth.make((16, 16), B=1, C=2, seed=3)
+    dev = torch.device("cuda:0")
+    x = w["x"].to(dev)
+    al, be = torch.from_numpy(w["alpha"]).to(dev), torch.from_numpy(w["beta"]).to(dev)
+    kh = H.kernel_spectrum(w["K"].to(dev))
+    with pytest.raises(TypeError):
+        H.fftconv_fwd(x, al, be, kh, y=torch.empty(x.shape, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        H.fftconv_fwd(x, al, be, kh, y=torch.empty((1, 2, 16, 8), device=dev))
+    with pytest.raises(ValueError):
+        H.fftconv_fwd(x, al, be, kh, y=x)
+    with pytest.raises(ValueError):
+        H.kernel_spectrum(w["K"].to(dev), out=torch.empty(4, dtype=torch.complex64, device=dev))
+    dy = torch.randn_like(x)
+    with pytest.raises(ValueError):
+        H.fftconv_bwd(x, al, be, kh, dy, dK=torch.empty((1, 2, 31, 31), device=dev))
+    with pytest.raises(ValueError):
+        H.fftconv_bwd(x, al, be, kh, dy, dx=dy)

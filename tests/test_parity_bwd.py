@@ -148,7 +148,7 @@ def test_empty_batch_gives_zero_parameter_gradients(H):
 
 
 def test_autograd_function(H):
-    """HyenaConvolutionFunction: torch autograd through the library's forward
+    """gated_fftconv: torch autograd through the library's forward
     and backward against the oracle's gradients of sum(dy * y)."""
     dims, B, C = (16, 8), 2, 3
     w = _inputs(dims, B, C, "f32", seed=12)
@@ -157,7 +157,7 @@ def test_autograd_function(H):
     al = torch.from_numpy(w["alpha"]).to(dev).requires_grad_()
     be = torch.from_numpy(w["beta"]).to(dev).requires_grad_()
     K = w["K"].to(dev).requires_grad_()
-    y = H.HyenaConvolutionFunction.apply(x, al, be, K)
+    y = H.gated_fftconv(x, al, be, K)
     (y * w["dy"].to(dev)).sum().backward()
     ref = oracle.bwd_direct(w["x"].numpy(), w["alpha"], w["beta"], w["K"].numpy(), w["dy"].numpy())
     for t, r in zip((x.grad, al.grad, be.grad, K.grad), ref):

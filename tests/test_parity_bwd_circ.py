@@ -127,7 +127,7 @@ def test_every_chunking_gives_the_same_gradients(H, dims, B, C, dtype):
 
 
 def test_autograd_function(H):
-    """HyenaConvolutionFunction with circular=True: torch autograd through the
+    """gated_fftconv with circular=True: torch autograd through the
     library's circular forward and backward against the oracle's gradients."""
     dims, B, C = (16, 8), 2, 3
     x0, al0, be0, K0, dy0 = _inputs(dims, B, C, "f32", seed=14)
@@ -135,7 +135,7 @@ def test_autograd_function(H):
     al = torch.from_numpy(al0).cuda().requires_grad_()
     be = torch.from_numpy(be0).cuda().requires_grad_()
     K = K0.cuda().requires_grad_()
-    y = H.HyenaConvolutionFunction.apply(x, al, be, K, True)
+    y = H.gated_fftconv(x, al, be, K, True)
     (y * dy0.cuda()).sum().backward()
     ref = oracle.bwd_direct_circ(x0.numpy(), al0, be0, K0.numpy(), dy0.numpy())
     for t, r in zip((x.grad, al.grad, be.grad, K.grad), ref):

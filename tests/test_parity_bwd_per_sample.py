@@ -115,7 +115,7 @@ def test_without_kernel_gradient_and_chunking(H):
 
 
 def test_autograd_function(H):
-    """HyenaConvolutionFunction with kernels [B, C, ...]: torch autograd through
+    """gated_fftconv with kernels [B, C, ...]: torch autograd through
     the per-sample forward and backward against the oracle's gradients."""
     dims, B, C = (16, 8), 3, 2
     x0, al0, be0, K0, dy0 = _inputs(dims, B, C, "f32", seed=15)
@@ -123,7 +123,7 @@ def test_autograd_function(H):
     al = torch.from_numpy(al0).cuda().requires_grad_()
     be = torch.from_numpy(be0).cuda().requires_grad_()
     K = K0.cuda().requires_grad_()
-    y = H.HyenaConvolutionFunction.apply(x, al, be, K)
+    y = H.gated_fftconv(x, al, be, K)
     (y * dy0.cuda()).sum().backward()
     ref = oracle.bwd_direct_per_sample(x0.numpy(), al0, be0, K0.numpy(), dy0.numpy())
     for t, r in zip((x.grad, al.grad, be.grad, K.grad), ref):

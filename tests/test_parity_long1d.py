@@ -189,7 +189,7 @@ def test_bwd_workload_full_size(H, idx):
 
 
 def test_bwd_autograd_function(H):
-    """HyenaConvolutionFunction on a long 1-D signal: torch autograd through
+    """gated_fftconv on a long 1-D signal: torch autograd through
     the library's forward and backward against the oracle's gradients."""
     n, B, C = 1 << 12, 2, 2
     dev = torch.device("cuda:0")
@@ -201,8 +201,19 @@ def test_bwd_autograd_function(H):
     al = torch.from_numpy(p.alpha).to(dev).requires_grad_()
     be = torch.from_numpy(p.beta).to(dev).requires_grad_()
     K = K0.to(dev).requires_grad_()
-    y = H.HyenaConvolutionFunction.apply(x, al, be, K)
+    y = H.gated_fftconv(x, al, be, K)
     (y * dy0.to(dev)).sum().backward()
     ref = oracle.bwd_fft(x0.numpy(), p.alpha, p.beta, K0.numpy(), dy0.numpy())
     for t, r in zip((x.grad, al.grad, be.grad, K.grad), ref):
         assert _rel(t.cpu().numpy().astype(np.float64), r) <= 1e-4
+
+
+def test_bwd_fused_du_rows_with_two_channels_per_chunk(H):
+    """4096-point rows (n = 2^22, the kernel-gradient row kernel also writes the
+    du rows) with two channels in one chunk, so its channel indexing (first
+    channel of the chunk plus the row's channel) runs with more than one channel."""
+    n, B, C = 1 << 22, 1, 2
+    minb = H.bwd_workspace_bytes(B, C, (n,), torch.float32, with_dK=True, minimum=True)
+    ws = torch.empty(2 * minb, dtype=torch.uint8, device="cuda")
+    x, dy, p, K, got = _run_bwd(H, (n,), B, C, "f32", seed=29, workspace=ws)
+    _check(got, oracle.bwd_fft(x, p.alpha, p.beta, K, dy), "f32")
