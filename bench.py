@@ -87,6 +87,14 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
         by = 2 * P * g["wsp"] * 8 + nch * g["ksz"] * 8
         lines = P * g["Nm"] * g["S"]
         fl = 2 * _fft_flops(g["No"], lines, pr) + lines * g["No"] * 6
+    elif name == "fused2d":
+        # x read, y written, K_hat read once per pair (L2 serves the batch after
+        # the first); row and column transforms as in the multi-pass passes
+        by = 2 * P * g["vox"] * es + nch * g["ksz"] * 8
+        rows = g["no"]
+        lines = P * g["S"]
+        fl = (2 * _fft_flops(g["Ni"], P * rows / 2, pr) + 2 * _fft_flops(g["No"], lines, pr)
+              + lines * g["No"] * 6 + P * rows * g["S"] * 8 + P * g["vox"] * 5)
     elif name == "conv1d":
         by = 2 * P * g["vox"] * es + nch * g["ksz"] * 8
         fl = 2 * _fft_flops(g["Ni"], P / 2, pr) + P * g["S"] * (6 + 4) + P * g["vox"] * 5
@@ -172,7 +180,7 @@ KERNEL_LABEL = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_co
                 "dk_row": "k_dk_row", "conv1d_bwd": "k_conv1d", "corr1d": "k_corr1d", "lng_col_fwd": "k_lng_col_fwd",
                 "lng_row": "k_lng_row", "lng_col_inv": "k_lng_col_inv", "lng_col_fwd_dy": "k_lng_col_fwd",
                 "lng_col_fwd_u": "k_lng_col_fwd", "lng_row_dk": "k_lng_row_dk", "lng_row_du": "k_lng_row",
-                "lng_col_inv_bwd": "k_lng_col_inv", "lng_col_dk": "k_lng_col_dk"}
+                "lng_col_inv_bwd": "k_lng_col_inv", "lng_col_dk": "k_lng_col_dk", "fused2d": "k_fused2d"}
 
 
 def _src_hash():

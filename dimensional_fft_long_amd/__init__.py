@@ -293,8 +293,17 @@ PASS_NAMES = {1: ("conv1d",), 2: ("row_fwd", "col_out", "row_inv"),
               3: ("row_fwd", "col_mid_fwd", "col_out", "col_mid_inv", "row_inv")}
 
 
+def uses_fused2d(dims, circular: bool = False) -> bool:
+    """True when the forward runs the on-chip 2-D kernel (one launch, no
+    workspace): zero-padded 2-D grids with both extents in [4, 128]."""
+    return (not circular and len(dims) == 2 and all(4 <= int(n) <= 128 for n in dims)
+            and all(int(n) & (int(n) - 1) == 0 for n in dims))
+
+
 def pass_names(dims, circular: bool = False):
     """Names of the kernels one channel chunk of a forward call launches, in order."""
+    if uses_fused2d(dims, circular):
+        return ("fused2d",)
     return PASS_NAMES[len(dims)]
 
 

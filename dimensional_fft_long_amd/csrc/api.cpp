@@ -23,7 +23,7 @@ struct CallPlan {
 CallPlan plan_call(const Geom& g, int B, int C, size_t ws_bytes)
 {
     CallPlan cp{C, 1, 1};
-    if (g.d == 1 && !g.lng) return cp;
+    if ((g.d == 1 && !g.lng) || fused2d_fits(g)) return cp;  // one launch for every pair, no workspace
     int per = chunk_channels(g, B, C, ws_bytes);
     if (per > C) per = C;
     if (per < 1) per = 1;
@@ -107,6 +107,7 @@ static size_t workspace_bytes(int B, int C, int d, const int64_t* dims, int dtyp
 {
     Geom g;
     if (B <= 0 || C <= 0 || (dtype != HYENAND_F32 && dtype != HYENAND_BF16) || !make_geom(d, dims, &g, circ)) return 0;
+    if (fused2d_fits(g)) return 0;  // the on-chip 2-D forward needs none
     return minimum ? (size_t)B * (size_t)g.wsp * 8u : recommended_workspace(g, B, C);
 }
 
@@ -145,7 +146,7 @@ static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta
     if (!x || !y || !alpha || !beta || !K_hat) return HYENAND_ERR_INVALID_ARG;
     if (!aligned(x, es) || !aligned(y, es) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(K_hat, 8))
         return HYENAND_ERR_INVALID_ARG;
-    if (g.wsp > 0) {
+    if (g.wsp > 0 && !fused2d_fits(g)) {
         if (!workspace) return HYENAND_ERR_WORKSPACE;
         if (!aligned(workspace, 8)) return HYENAND_ERR_INVALID_ARG;
         if (chunk_channels(g, B, C, workspace_bytes) < 1) return HYENAND_ERR_WORKSPACE;

@@ -427,10 +427,13 @@ __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const
         const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
         const float2 Za = T[ea], Zb = T[eb];
         auto kv = [](float2 v) { return CONJ ? cconj(v) : v; };
-        const float2 Sa = kv(kc[pa * PS + (long long)o.rows[ra] * g.lt]);
-        const float2 Sb = kv(kc[pb * PS + (long long)o.rows[rb] * g.lt]);
-        const float2 Da = kv(kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]]);
-        const float2 Db = kv(kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]]);
+        // row of the ra / rb block by selection, not by indexing o.rows with a
+        // runtime value (which would put o in scratch memory)
+        const long long rwa = ra == 0 ? o.rows[0] : o.rows[1], rwb = rb == 0 ? o.rows[0] : o.rows[1];
+        const float2 Sa = kv(kc[pa * PS + rwa * g.lt]);
+        const float2 Sb = kv(kc[pb * PS + rwb * g.lt]);
+        const float2 Da = kv(kc[g.kmain + (long long)pa * g.N_mid + rwa]);
+        const float2 Db = kv(kc[g.kmain + (long long)pb * g.N_mid + rwb]);
         const float2 Wa = cadd(cmul(Za, Sa), cmul(cconj(Zb), Da));
         const float2 Wb = cadd(cmul(Zb, Sb), cmul(cconj(Za), Db));
         T[ea] = Wa;
@@ -1036,10 +1039,11 @@ __host__ __device__ __forceinline__ void spec_out_body(const Ctx& ctx, int bid, 
             const float2 Vb = csub(Zb, cconj(Za));
             const float2 Bb = make_float2(0.5f * Vb.y, -0.5f * Vb.x);
             T[ea] = cscale(cadd(Aa, Ba), 0.5f * gsc);
-            kc[g.kmain + (long long)pa * g.N_mid + o.rows[ra]] = cscale(csub(Aa, Ba), 0.5f * gsc);
+            const int rwa = ra == 0 ? o.rows[0] : o.rows[1], rwb = rb == 0 ? o.rows[0] : o.rows[1];
+            kc[g.kmain + (long long)pa * g.N_mid + rwa] = cscale(csub(Aa, Ba), 0.5f * gsc);
             if (eb != ea) {
                 T[eb] = cscale(cadd(Ab, Bb), 0.5f * gsc);
-                kc[g.kmain + (long long)pb * g.N_mid + o.rows[rb]] = cscale(csub(Ab, Bb), 0.5f * gsc);
+                kc[g.kmain + (long long)pb * g.N_mid + rwb] = cscale(csub(Ab, Bb), 0.5f * gsc);
             }
         }
     }

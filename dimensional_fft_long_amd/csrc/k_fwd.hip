@@ -15,6 +15,7 @@ hipError_t forward_chunk_padded(const ConvArgs& a, hipStream_t st, LaunchTrace* 
 hipError_t launch_forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
 {
     if (a.g.lng) return long1d_forward(a, false, st, tr);
+    if (fused2d_fits(a.g)) return a.bf16 ? fused2d_forward_bf16(a, st, tr) : fused2d_forward_f32(a, st, tr);
     return a.g.circ ? forward_chunk_circ(a, st, tr) : forward_chunk_padded(a, st, tr);
 }
 

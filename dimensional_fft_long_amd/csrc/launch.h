@@ -45,6 +45,9 @@ hipError_t backward_chunk_padded(const ConvArgs& a, bool dk, hipStream_t stream,
 hipError_t backward_chunk_circ(const ConvArgs& a, bool dk, hipStream_t stream, LaunchTrace* trace);
 hipError_t long1d_forward(const ConvArgs& a, bool spec, hipStream_t stream, LaunchTrace* trace);
 hipError_t long1d_backward(const ConvArgs& a, bool dk, hipStream_t stream, LaunchTrace* trace);
+// The on-chip 2-D forward (fused2d_fits) of every pair, fp32 / bf16 I/O.
+hipError_t fused2d_forward_f32(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace);
+hipError_t fused2d_forward_bf16(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace);
 
 // Workgroups of `kernel` (nt threads per workgroup) resident at once on the
 // current device: CUs x workgroups per CU, queried once per (kernel, nt,

@@ -192,6 +192,16 @@ inline bool make_geom(int d, const int64_t* dims, Geom* g, bool circ = false)
     return true;
 }
 
+// The on-chip 2-D forward (one workgroup per (b, c) pair, the half spectrum in
+// LDS, no workspace): zero-padded 2-D grids with both padded lengths in
+// [8, 256], i.e. n_out, n_in in [4, 128] (128 x 128: 128 KiB of half spectrum
+// plus an 18 KiB transform tile and 6 KiB of twiddles, within the 160 KiB a
+// gfx950 workgroup may hold).
+inline bool fused2d_fits(const Geom& g)
+{
+    return g.d == 2 && !g.circ && !g.lng && g.N_out >= 8 && g.N_out <= 256 && g.N_in >= 8 && g.N_in <= 256;
+}
+
 // Arguments shared by every kernel of one call (passed by value).
 struct ConvArgs {
     const void* x;          // [B][C][vox], fp32 or bf16

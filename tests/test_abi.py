@@ -116,9 +116,12 @@ def test_fwd_rejects_arguments(H):
     assert call(dt=7) == 1
     assert call(x=MISALIGNED) == 1
     assert call(k=MISALIGNED) == 1
-    assert call(w=None) == 3
-    assert call(wb=8 * 8 * 8 - 1) == 3          # one pair needs n0 * S * 8 = 512 bytes
-    assert call(w=MISALIGNED) == 1
+    # A grid that needs a workspace (an axis above 128: the multi-pass kernels).
+    dw = _dims(8, 256)
+    callw = lambda w=FAKE, wb=ws: lib.hyenand_fftconv_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 2, dw, 0, w, wb, None)
+    assert callw(w=None) == 3
+    assert callw(wb=8 * 256 * 8 - 1) == 3        # one pair needs n0 * S * 8 = 16384 bytes
+    assert callw(w=MISALIGNED) == 1
     # Empty calls succeed without touching anything.
     assert call(x=None, y=None, B=0) == 0
     assert call(x=None, y=None, C=0) == 0
