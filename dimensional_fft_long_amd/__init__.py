@@ -295,8 +295,8 @@ PASS_NAMES = {1: ("conv1d",), 2: ("row_fwd", "col_out", "row_inv"),
 
 def uses_fused2d(dims, circular: bool = False) -> bool:
     """True when the forward runs the on-chip 2-D kernel (one launch, no
-    workspace): zero-padded 2-D grids with both extents in [4, 128]."""
-    return (not circular and len(dims) == 2 and all(4 <= int(n) <= 128 for n in dims)
+    workspace): zero-padded 2-D grids with both extents in [4, 64]."""
+    return (not circular and len(dims) == 2 and all(4 <= int(n) <= 64 for n in dims)
             and all(int(n) & (int(n) - 1) == 0 for n in dims))
 
 

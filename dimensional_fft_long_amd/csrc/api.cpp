@@ -199,7 +199,8 @@ int hyenand_fftconv_launch_plan(int B, int C, int d, const int64_t* dims, int dt
     if (!make_geom(d, dims, &g)) return HYENAND_ERR_UNSUPPORTED;
     CallPlan cp{0, 0, 0};
     if (B > 0 && C > 0) {
-        if (g.wsp > 0 && chunk_channels(g, B, C, workspace_bytes) < 1) return HYENAND_ERR_WORKSPACE;
+        if (g.wsp > 0 && !fused2d_fits(g) && chunk_channels(g, B, C, workspace_bytes) < 1)
+            return HYENAND_ERR_WORKSPACE;
         cp = plan_call(g, B, C, workspace_bytes);
     }
     if (n_launches) *n_launches = cp.launches;

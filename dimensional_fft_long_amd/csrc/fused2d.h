@@ -8,7 +8,8 @@
 // gist.science summary ("Methodology", "Boundary handling") and the fusion the
 // summary's "Implementation: nSubQ" describes (fused kernels, the intermediates
 // kept in on-chip memory instead of HBM), for grids whose half spectrum fits in
-// a workgroup's LDS: n_out x n_in up to 128 x 128 (128 KiB of fp32 complex).
+// a workgroup's LDS with room for several workgroups per CU: n_out x n_in up to
+// 64 x 64 (32 KiB of fp32 complex; see fused2d_fits in plan.h).
 //
 //   phase 1  rows:    gate, pruned real FFT of two rows per complex line,
 //                     separation into two half spectra -> P[row][slot]

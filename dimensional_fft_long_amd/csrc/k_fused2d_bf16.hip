@@ -16,7 +16,7 @@ __global__ __launch_bounds__(f2_nt(LO, LI)) void k_fused2d(ConvArgs a)
                                (int)blockIdx.x, a, P, T);
 }
 
-// Calls f.template operator()<L>() for a padded length L in {8, ..., 256}.
+// Calls f.template operator()<L>() for a padded length L in {8, ..., kFused2dMaxLen}.
 template <class F>
 hipError_t with_fused_length(int L, F&& f)
 {
@@ -26,7 +26,6 @@ hipError_t with_fused_length(int L, F&& f)
     case 32: return f.template operator()<32>();
     case 64: return f.template operator()<64>();
     case 128: return f.template operator()<128>();
-    case 256: return f.template operator()<256>();
     default: return hipErrorInvalidValue;
     }
 }

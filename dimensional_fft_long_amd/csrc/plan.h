@@ -194,12 +194,17 @@ inline bool make_geom(int d, const int64_t* dims, Geom* g, bool circ = false)
 
 // The on-chip 2-D forward (one workgroup per (b, c) pair, the half spectrum in
 // LDS, no workspace): zero-padded 2-D grids with both padded lengths in
-// [8, 256], i.e. n_out, n_in in [4, 128] (128 x 128: 128 KiB of half spectrum
-// plus an 18 KiB transform tile and 6 KiB of twiddles, within the 160 KiB a
-// gfx950 workgroup may hold).
+// [8, 128], i.e. n_out, n_in in [4, 64] (64 x 64: 32 KiB of half spectrum, up
+// to four workgroups per CU).  A 128 x 128 half spectrum (128 KiB) also fits a
+// workgroup's 160 KiB, but it leaves one 4-wave workgroup per CU, whose every
+// LDS access and barrier is exposed: measured on MI355X (128^2, B = 8, C = 64)
+// 157 us per call on chip against 82 us for the three-pass path, while at 64^2
+// the on-chip kernel wins (24 against 38 us; 32^2 16 against 32 us).
+constexpr int kFused2dMaxLen = 128;
 inline bool fused2d_fits(const Geom& g)
 {
-    return g.d == 2 && !g.circ && !g.lng && g.N_out >= 8 && g.N_out <= 256 && g.N_in >= 8 && g.N_in <= 256;
+    return g.d == 2 && !g.circ && !g.lng && g.N_out >= 8 && g.N_out <= kFused2dMaxLen && g.N_in >= 8 &&
+           g.N_in <= kFused2dMaxLen;
 }
 
 // Arguments shared by every kernel of one call (passed by value).

@@ -75,9 +75,10 @@ WORKLOADS = [
     # 1024x1024x256 climate grid); the pages give no channel count
     Workload("3d_512x512x64_b1_c16_f32", (512, 512, 64), 1, 16, "f32", 1007),
     Workload("3d_1024x1024x256_b1_c2_f32", (1024, 1024, 256), 1, 2, "f32", 1008),
-    # the largest grid whose half spectrum fits one workgroup's LDS (the on-chip
-    # 2-D forward), with the 256^2 image's batch and channels
+    # smaller images with the 256^2 image's batch and channels: 128^2 (three
+    # passes) and 64^2 (the largest grid of the on-chip 2-D forward)
     Workload("2d_128x128_b8_c64_f32", (128, 128), 8, 64, "f32", 1009),
+    Workload("2d_64x64_b8_c64_f32", (64, 64), 8, 64, "f32", 1010),
 ]
 
 

@@ -308,3 +308,25 @@ def test_library_does_not_load_the_oracle():
             "print('oracle' in sys.modules)") % ROOT
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True).stdout
     assert out.strip() == "False"
+
+
+EXTENTS_FUSED = (4, 8, 16, 32, 64)
+
+
+def test_fused_shapes_take_one_launch_and_no_workspace(H):
+    """Zero-padded 2-D grids with both extents in [4, 64] run the on-chip
+    forward: one launch for every pair and no workspace."""
+    import torch
+
+    for n0 in EXTENTS_FUSED:
+        for n1 in EXTENTS_FUSED:
+            assert H.uses_fused2d((n0, n1))
+            assert H.workspace_bytes(8, 64, (n0, n1), minimum=True) == 0
+            assert H.workspace_bytes(8, 64, (n0, n1)) == 0
+            assert H.launch_plan(8, 64, (n0, n1), torch.float32, 0) == {"launches": 1, "chunk_channels": 64}
+    for dims in [(2, 8), (8, 2), (128, 128), (128, 64), (64, 128), (256, 256)]:
+        assert not H.uses_fused2d(dims)
+        assert H.workspace_bytes(2, 3, dims, minimum=True) > 0
+    # the backward and the circular mode keep their multi-pass kernels
+    assert H.bwd_workspace_bytes(2, 3, (32, 32), minimum=True) > 0
+    assert H.circ_workspace_bytes(2, 3, (32, 32), minimum=True) > 0
