@@ -53,7 +53,8 @@ EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_
            "hyenand_fftconv_fwd_per_sample", "hyenand_fftconv_fwd_per_sample_traced", "hyenand_fftconv_bwd_circ",
            "hyenand_fftconv_bwd_circ_workspace_bytes", "hyenand_fftconv_bwd_circ_workspace_min_bytes",
            "hyenand_fftconv_bwd_circ_traced", "hyenand_fftconv_bwd_per_sample",
-           "hyenand_fftconv_bwd_per_sample_traced")
+           "hyenand_fftconv_bwd_per_sample_traced", "hyenand_fftconv_fwd_noalloc",
+           "hyenand_fftconv_fwd_noalloc_max_workspace")
 
 _lib = None
 
@@ -129,6 +130,10 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_fwd_per_sample_traced.argtypes = [P, P, P, P, P, I, I, I, P, I, P, SZ, P, P, I,
                                                           ctypes.POINTER(I)]
     lib.hyenand_fftconv_fwd_per_sample_traced.restype = I
+    lib.hyenand_fftconv_fwd_noalloc.argtypes = [P, P, P, P, P, I, I, I, P, I, P]
+    lib.hyenand_fftconv_fwd_noalloc.restype = I
+    lib.hyenand_fftconv_fwd_noalloc_max_workspace.argtypes = []
+    lib.hyenand_fftconv_fwd_noalloc_max_workspace.restype = SZ
     _lib = lib
     return lib
 
@@ -637,3 +642,35 @@ def fftconv_fwd_per_sample_traced(x, alpha, beta, K_hat, y, workspace, events, s
     if rc != OK:
         raise HyenandError(rc, "fftconv_fwd_per_sample_traced")
     return int(n.value)
+
+
+# --------------------------------------------------- allocation-free forward
+
+def noalloc_max_workspace() -> int:
+    """Bytes of the static device scratch behind fftconv_fwd_noalloc."""
+    return int(get_lib().hyenand_fftconv_fwd_noalloc_max_workspace())
+
+
+def fftconv_fwd_noalloc(x, alpha, beta, K_hat, y, stream=None) -> torch.Tensor:
+    """fftconv_fwd through the allocation-free entry point: the library's static
+    device scratch serves as the workspace; the caller provides y.  Calls that
+    overlap in time on one GPU share that scratch and race."""
+    if not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous device tensor")
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    for t, nm in ((alpha, "alpha"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
+    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
+    if K_hat.numel() * 8 < spectrum_bytes(C, dims):
+        raise ValueError("K_hat is smaller than the spectrum of this shape")
+    _check_out(y, "y", x.shape, x.dtype, x.device, like=x)
+    rc = get_lib().hyenand_fftconv_fwd_noalloc(_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()),
+                                               _P(K_hat.data_ptr()), _P(y.data_ptr()), B, C, len(dims),
+                                               _dims_arr(dims), _dtype_code(x.dtype), _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd_noalloc")
+    return y
+

@@ -2,6 +2,8 @@
 // workspace sizing, chunking over channels, launch and error mapping.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/hyenand.h"
 #include "launch.h"
 #include "plan.h"
@@ -131,9 +133,12 @@ size_t hyenand_fftconv_circ_workspace_min_bytes(int B, int C, int d, const int64
     return workspace_bytes(B, C, d, dims, dtype, true, true);
 }
 
+// resolve_ws (optional): supplies the workspace once the arguments are valid
+// (the allocation-free entry point's static scratch).
 static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y, int B,
                             int C, int d, const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
-                            void* stream, LaunchTrace* trace, bool circ, bool per_sample = false)
+                            void* stream, LaunchTrace* trace, bool circ, bool per_sample = false,
+                            int (*resolve_ws)(void**, size_t*) = nullptr)
 {
     if (B < 0 || C < 0) return HYENAND_ERR_INVALID_ARG;
     if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
@@ -146,6 +151,10 @@ static int fftconv_fwd_impl(const void* x, const float* alpha, const float* beta
     if (!x || !y || !alpha || !beta || !K_hat) return HYENAND_ERR_INVALID_ARG;
     if (!aligned(x, es) || !aligned(y, es) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(K_hat, 8))
         return HYENAND_ERR_INVALID_ARG;
+    if (resolve_ws) {
+        const int rc = resolve_ws(&workspace, &workspace_bytes);
+        if (rc != HYENAND_OK) return rc;
+    }
     if (g.wsp > 0 && !fused2d_fits(g)) {
         if (!workspace) return HYENAND_ERR_WORKSPACE;
         if (!aligned(workspace, 8)) return HYENAND_ERR_INVALID_ARG;
@@ -430,6 +439,53 @@ int hyenand_fftconv_fwd_per_sample_traced(const void* x, const float* alpha, con
                                     stream, &tr, false, true);
     if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
     return rc;
+}
+
+// ------------------------------------------------------ allocation-free forward
+// For callers that cannot allocate (code under HIP graph capture, tight serving
+// loops): the forward with its workspace in a static device array instead of a
+// caller buffer.  Each GPU the library runs on holds its own copy of the array
+// (kFwdScratchBytes) until the process ends.  In host code `scratch` names a
+// host-side stand-in: its device address on the current device comes from
+// hipGetSymbolAddress, taken once per device and kept in scratch_dev.
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kFwdScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) float2 scratch[kFwdScratchBytes / sizeof(float2)];
+
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+int resolve_scratch(void** ws, size_t* bytes)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HYENAND_ERR_HIP;
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HYENAND_ERR_HIP;
+        scratch_dev[dev] = p;
+    }
+    *ws = scratch_dev[dev];
+    *bytes = kFwdScratchBytes;
+    return HYENAND_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hyenand_fftconv_fwd_noalloc_max_workspace(void) { return kFwdScratchBytes; }
+
+int hyenand_fftconv_fwd_noalloc(const void* x, const float* alpha, const float* beta, const void* K_hat, void* y,
+                                int B, int C, int d, const int64_t* dims, int dtype, void* stream)
+{
+    return fftconv_fwd_impl(x, alpha, beta, K_hat, y, B, C, d, dims, dtype, nullptr, 0, stream, nullptr, false,
+                            false, resolve_scratch);
 }
 
 }  // extern "C"

@@ -19,7 +19,9 @@
  *
  * Conventions shared by every entry point:
  *   - All array arguments are device pointers owned by the caller (e.g. torch
- *     tensors).  The library allocates nothing and keeps no state between calls.
+ *     tensors).  The library allocates nothing and keeps no state between calls
+ *     (the one exception, hyenand_fftconv_fwd_noalloc at the end, holds a
+ *     static device scratch array).
  *   - Layouts are row-major with the last grid axis contiguous:
  *       x, y   [B][C][dims[0]]..[dims[d-1]]     dtype HYENAND_F32 or HYENAND_BF16
  *       alpha, beta [C]                          fp32
@@ -312,6 +314,27 @@ int hyenand_fftconv_bwd_per_sample_traced(const void* x, const float* phi_alpha,
                                           float* dK, int B, int C, int d, const int64_t* dims, int dtype,
                                           void* workspace, size_t workspace_bytes, void* stream,
                                           void* const* events, int n_events, int* n_launches);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): hyenand_fftconv_fwd with its workspace in a static device array
+ * of hyenand_fftconv_fwd_noalloc_max_workspace() bytes (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends; the call
+ * itself allocates and frees nothing.  The caller passes inputs and outputs as
+ * for hyenand_fftconv_fwd (same layouts, errors and results).  Channels run
+ * in chunks that fit the array; a shape whose single channel (all B batch
+ * entries) needs more than the array (hyenand_fftconv_workspace_min_bytes
+ * above the maximum, e.g. the 512^3 grid) returns HYENAND_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on a GPU shares that GPU's array (which
+ * keeps the last call's contents; the forward writes every workspace value
+ * before reading it), so calls that overlap in time on one GPU (other streams,
+ * other host threads) race: serialise them.  The first call on a device looks
+ * up the array's device address (HYENAND_ERR_HIP if that fails).
+ */
+size_t hyenand_fftconv_fwd_noalloc_max_workspace(void);
+int hyenand_fftconv_fwd_noalloc(const void* x, const float* phi_alpha, const float* phi_beta, const void* K_hat,
+                                void* y, int B, int C, int d, const int64_t* dims, int dtype, void* stream);
 
 #ifdef __cplusplus
 }
