@@ -45,26 +45,46 @@ __device__ __forceinline__ void mf_split(float v0, float v1, float v2, float v3,
     lo[3] = mf_bits(v3 - mf_value(hi[3]));
 }
 
-// This lane's part of the A operand for twiddle class k (hi and lo): row
-// m = lane % 16 (output s = m / 2, part re / im), columns 4g + i (input
-// r = 2g + i / 2, part re / im) of the real form of W_64^{+-(8 s + k) r}.
-template <bool INV>
-__device__ __forceinline__ void mf_amat(int lane, int k, mf_s4& hi, mf_s4& lo)
+// bf16 bits of a float, rounded to nearest even (compile time).
+constexpr unsigned short mf_bf16_rne(float f)
 {
-    const int m = lane % 16, g = lane / 16, s = m / 2, p = m % 2;
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 2 * g + i / 2, q = i % 2;
-        const int e = ((8 * s + k) * r) & 63;
-        float sn, cs;
-        sincospif((float)e / 32.0f, &sn, &cs);   // W_64^e = cos - i sin (forward)
-        const float re = cs, im = INV ? sn : -sn;
-        // [[re, -im], [im, re]]
-        v[i] = p == 0 ? (q == 0 ? re : -im) : (q == 0 ? im : re);
-    }
-    mf_split(v[0], v[1], v[2], v[3], hi, lo);
+    const unsigned u = __builtin_bit_cast(unsigned, f);
+    return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
+constexpr float mf_bf16_float(unsigned short b) { return __builtin_bit_cast(float, (unsigned)b << 16); }
+
+// The A operands of every lane, both directions and all 8 twiddle classes:
+// lane's row m = lane % 16 (output s = m / 2, part re / im), columns 4g + i
+// (input r = 2g + i / 2, part re / im) of the real form [[re, -im], [im, re]]
+// of W_64^{+-(8 s + k) r}, split into bf16 hi and lo parts.  W_64^e comes from
+// the engine's compile-time twiddle table (W_4096^{64 e}).
+struct MfTable {
+    unsigned short hi[2][8][64][4], lo[2][8][64][4];
+};
+
+constexpr MfTable make_mf_table()
+{
+    MfTable t{};
+    for (int inv = 0; inv < 2; ++inv)
+        for (int k = 0; k < 8; ++k)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int m = lane % 16, g = lane / 16, s = m / 2, p = m % 2;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 2 * g + i / 2, q = i % 2;
+                    const int e = ((8 * s + k) * r) & 63;
+                    const float re = kTwBase.w[e * 64].x, im0 = kTwBase.w[e * 64].y;
+                    const float im = inv ? -im0 : im0;
+                    const float v = p == 0 ? (q == 0 ? re : -im) : (q == 0 ? im : re);
+                    const unsigned short h = mf_bf16_rne(v);
+                    t.hi[inv][k][lane][i] = h;
+                    t.lo[inv][k][lane][i] = mf_bf16_rne(v - mf_bf16_float(h));
+                }
+            }
+    return t;
+}
+
+template <int U>
+__constant__ const MfTable g_mf_table = make_mf_table();
 
 // Operands of the two twiddle classes a wave handles (2w, 2w + 1).
 struct MfOperands {
@@ -76,8 +96,16 @@ __device__ __forceinline__ MfOperands mf_operands(int tid)
 {
     MfOperands o;
     const int w = tid / 64, lane = tid % 64;
-    mf_amat<INV>(lane, 2 * w, o.hi[0], o.lo[0]);
-    mf_amat<INV>(lane, 2 * w + 1, o.hi[1], o.lo[1]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const unsigned short* h = g_mf_table<0>.hi[INV][2 * w + c][lane];
+        const unsigned short* l = g_mf_table<0>.lo[INV][2 * w + c][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o.hi[c][i] = (short)h[i];
+            o.lo[c][i] = (short)l[i];
+        }
+    }
     return o;
 }
 
