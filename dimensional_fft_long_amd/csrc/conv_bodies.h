@@ -28,7 +28,6 @@
 #pragma once
 
 #include "fft_core.h"
-#include "mfma_dft.h"
 #include "plan.h"
 
 #include <type_traits>
@@ -541,19 +540,9 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
             for (int r = 0; r < RL; ++r) kv[i][r] = *at(v.kt, (long long)r * (L / RL) * PS, lb);
         }
     };
-    // 512-point 2-D lines: the middle radix-8 pass of both transforms on the
-    // matrix cores (mfma_dft.h).
-    constexpr bool kMf = L == 512 && NR == 1 && NT == 256 && !CIRC && kOutMfma;
-    MfOperands AF, AI;
-    if constexpr (kMf) {
-        AF = mf_operands<false>(tid);
-        AI = mf_operands<true>(tid);
-    }
     // One item: forward from the loaded columns, product, inverse and store.
     auto run_item = [&](const OutView& v, P0& s) {
-        PL t;
-        if constexpr (kMf) t = mf_fwd_from_regs<NT, !CIRC>(ctx, T, s, AF);
-        else t = fwd_from_regs<L, NL, NT, !CIRC>(ctx, T, s);
+        auto t = fwd_from_regs<L, NL, NT, !CIRC>(ctx, T, s);
         ctx.sync();  // every LDS read of the forward transform is done: T is free
         if (v.o.t == 0) {
             pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
@@ -576,15 +565,9 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
                 t.v[i][r] = kok[i] ? m : t.v[i][r];
             }
         }
-        auto store = [&](int j, int q, int l, const float2& x) {
+        inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
             if (v.k0 + l % TW < g.S) *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
-        };
-        if constexpr (kMf) {
-            auto u = mf_inv_to_regs<NT, !CIRC>(ctx, T, t, AI);
-            pass_visit<L, pass_radix<L, false>(0), NL, NT, !CIRC>(ctx, u, store);
-        } else {
-            inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, store);
-        }
+        });
     };
     OutView v = out_view<NR, TW>(a, bid);
     const auto tw_staged = ctx.stage_load();  // oldest loads: waited for first

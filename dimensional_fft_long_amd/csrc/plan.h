@@ -79,9 +79,6 @@ constexpr int bwd_nt(int L, int NR)
     const int t = L * NR * bwd_tw(L, NR) / (NR == 1 ? 8 : 16);
     return t < 64 ? 64 : (t > 1024 ? 1024 : t);
 }
-// The middle radix-8 pass of the 512-point 2-D out-axis transforms on the
-// matrix cores (mfma_dft.h) instead of the vector ALUs.
-constexpr bool kOutMfma = true;
 constexpr bool out_looped(int L, int NR) { return NR == 1 && (long long)L * NR * out_tw(L, NR) * 8 > 80 * 1024; }
 
 struct Geom {
