@@ -60,6 +60,11 @@ def _geom(dims, circ=False):
                 prune=0 if circ else 1)
 
 
+def _long_row_len(N):
+    """Row length N2 of the long 1-D path's N1 x N2 factorisation of N = 2n."""
+    return min(N // 4, 2048) if N <= (1 << 22) else (4096 if N <= (1 << 24) else 8192)
+
+
 def _fft_flops(N, lines, prune):
     """Nominal flops of `lines` complex length-N transforms: 5 N log2 N, less
     2N for each pruned half (zero half input, or half output unused)."""
@@ -127,17 +132,17 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
     # ---- long 1-D (four-step: N = 2n = N1 x N2, complex arithmetic)
     elif name == "lng_col_fwd":
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
+        N2 = _long_row_len(N)
         by = P * g["vox"] * es + P * N * 8
         fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6 + P * g["vox"] * 5
     elif name == "lng_row":
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
+        N2 = _long_row_len(N)
         by = 2 * P * N * 8 + nch * N * 8
         fl = 2 * P * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 6
     elif name == "lng_col_inv":
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
+        N2 = _long_row_len(N)
         by = P * N * 8 + P * g["vox"] * es
         fl = P * N2 * (5.0 * (N // N2) * math.log2(N // N2) - 2.0 * (N // N2)) + P * N * 6
     elif name in ("lng_col_fwd_dy", "lng_col_fwd_u"):
@@ -150,10 +155,10 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
         # dy and u rows read, the channel's kernel-gradient rows written; with
         # 4096-point rows (N > 2^22) also the spectrum read and the du rows written
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
+        N2 = _long_row_len(N)
         by = 2 * P * N * 8 + nch * N * 8
         fl = (2 * P + nch) * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 8
-        if N2 == 4096:
+        if N2 >= 4096:
             by += P * N * 8 + nch * N * 8
             fl += P * (N // N2) * 5.0 * N2 * math.log2(N2) + P * N * 6
     elif name == "lng_col_inv_bwd":
@@ -162,7 +167,7 @@ def pass_model(name, dims, B_chunk_pairs, nch, es, circ=False):
         fl += P * g["vox"] * 14
     elif name == "lng_col_dk":
         N = 2 * g["ni"]
-        N2 = min(N // 4, 2048) if N <= (1 << 22) else 4096
+        N2 = _long_row_len(N)
         by = nch * N * 8 + nch * (2 * g["ni"] - 1) * 4
         fl = nch * N2 * 5.0 * (N // N2) * math.log2(N // N2) + nch * N * 6
     elif name == "corr1d":

@@ -49,12 +49,12 @@ __host__ __device__ __forceinline__ float2 mul_mi(float2 a)
 }
 
 // ----------------------------------------------------------- twiddle table
-// W_4096^t = exp(-2 pi i t / 4096), t in [0, 4096), evaluated at compile time
+// W_8192^t = exp(-2 pi i t / 8192), t in [0, 8192), evaluated at compile time
 // in double precision (Taylor series of sin on the first quadrant, extended by
 // the quadrant symmetries) and rounded once to float.  Any power-of-two length
-// L <= 4096 uses W_L^s = W_4096^(s * 4096 / L).  (4096-point transforms serve
-// the long 1-D path only.)
-constexpr int TW_N = 4096;
+// L <= 8192 uses W_L^s = W_8192^(s * 8192 / L).  (4096- and 8192-point
+// transforms serve the long 1-D path only.)
+constexpr int TW_N = 8192;
 
 struct TwTable {
     float2 w[TW_N];
@@ -442,7 +442,7 @@ struct LdsPasses {
 template <int L, int NL, int LP, int NT, bool INV, bool PIN, bool POUT, class Ctx>
 __host__ __device__ __forceinline__ void tile_fft(const Ctx& ctx, float2* T)
 {
-    static_assert(L >= 2 && L <= TW_N && (L & (L - 1)) == 0, "power-of-two length up to 4096");
+    static_assert(L >= 2 && L <= TW_N && (L & (L - 1)) == 0, "power-of-two length up to 8192");
     constexpr int NP = plan_passes(L);
     constexpr int R0 = pass_radix<L, false>(0);
     PassRegs<L, R0, NL, NT> s;

@@ -349,7 +349,7 @@ hipError_t forward_chunk(const ConvArgs& a, hipStream_t st, LaunchTrace* tr)
     });
 }
 
-// Transform lengths of the long 1-D path: rows N2 in {1024, 2048, 4096},
+// Transform lengths of the long 1-D path: rows N2 in {1024, 2048, 4096, 8192},
 // columns N1 in {4, ..., 4096}.
 template <class F>
 hipError_t with_row_length(int L, F&& f)
@@ -358,6 +358,7 @@ hipError_t with_row_length(int L, F&& f)
     case 1024: return f.template operator()<1024>();
     case 2048: return f.template operator()<2048>();
     case 4096: return f.template operator()<4096>();
+    case 8192: return f.template operator()<8192>();
     default: return hipErrorInvalidValue;
     }
 }

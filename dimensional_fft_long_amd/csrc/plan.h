@@ -36,8 +36,10 @@ namespace hyenand {
 // Row kernels: NP line pairs of length L per workgroup (2 <= NP <= 64),
 // tile L x row_lp(L) (line stride padded so that the transposed accesses of the
 // load and store phases spread over the LDS banks).
-constexpr int row_np(int L) { return 4096 / L < 2 ? 2 : (4096 / L > 64 ? 64 : 4096 / L); }
-constexpr int row_lp(int L) { return row_np(L) + 1; }
+// 8192-point rows (long 1-D signals beyond 2^23 samples) take one line per
+// workgroup, unpadded: a 64 KiB tile beside the 64 KiB twiddle table.
+constexpr int row_np(int L) { return L >= 8192 ? 1 : (4096 / L < 2 ? 2 : (4096 / L > 64 ? 64 : 4096 / L)); }
+constexpr int row_lp(int L) { return row_np(L) == 1 ? 1 : row_np(L) + 1; }
 // Column kernels along the middle axis / the out axis of a 2-D grid:
 // TW adjacent lines, tile L x TW of up to 128 KiB (gfx950 gives a workgroup
 // up to 160 KiB of LDS), so that even 2048-point lines read row segments of
@@ -130,7 +132,7 @@ inline bool is_pow2(long long v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Returns false for an unsupported shape: d in {1,2,3}, every n a power of two
 // in [2, 1024] ([4, 1024] in circular mode, whose transforms have length n);
-// d = 1 (zero-padded) also takes n up to 2^23 through the long 1-D path.
+// d = 1 (zero-padded) also takes n up to 2^24 through the long 1-D path.
 //
 // Circular mode (gist.science summary, "Methodology", "Boundary handling":
 // circular convolutions for periodic systems): every axis keeps N = n, the
@@ -141,14 +143,15 @@ inline bool make_geom(int d, const int64_t* dims, Geom* g, bool circ = false)
     if (d < 1 || d > 3 || !dims) return false;
     *g = Geom{};
     if (d == 1 && !circ && dims[0] > 1024) {
-        // Long 1-D: n a power of two up to 2^23.  Rows of N2 = min(N/4, 2048)
-        // points up to N = 2^22, then rows and columns of up to 4096 points.
+        // Long 1-D: n a power of two up to 2^24.  Rows of N2 = min(N/4, 2048)
+        // points up to N = 2^22, then rows and columns of up to 4096 points up
+        // to N = 2^24, then 8192-point rows (N = 2^25: 4096 x 8192).
         const long long n = dims[0];
-        if (!is_pow2(n) || n > (1ll << 23)) return false;
+        if (!is_pow2(n) || n > (1ll << 24)) return false;
         const long long N = 2 * n;
         g->d = 1;
         g->lng = 1;
-        g->N2 = (int)(N <= (1ll << 22) ? (N / 4 < 2048 ? N / 4 : 2048) : 4096);
+        g->N2 = (int)(N <= (1ll << 22) ? (N / 4 < 2048 ? N / 4 : 2048) : (N <= (1ll << 24) ? 4096 : 8192));
         g->N1 = (int)(N / g->N2);
         g->logN = 0;
         while ((1ll << g->logN) < N) ++g->logN;

@@ -30,7 +30,7 @@
  *       K_hat  library-defined complex64 layout, size from
  *              hyenand_kernel_spectrum_bytes (see below)
  *   - Supported shapes: d in {1, 2, 3}; every dims[a] a power of two in
- *     [2, 1024]; for d = 1 also n a power of two up to 2^23 (long signals, the
+ *     [2, 1024]; for d = 1 also n a power of two up to 2^24 (long signals, the
  *     summary's 1-D genomics context: see "Long 1-D signals" below).  Other
  *     shapes return HYENAND_ERR_UNSUPPORTED.
  *   - Pointers must be aligned to their element size (x, y: 4 bytes for fp32,
@@ -87,8 +87,8 @@ int hyenand_version(void);
  * block of the spectrum contiguous.
  *
  * Long 1-D signals (d = 1, n > 1024): the padded length N = 2n is transformed
- * as an N1 x N2 array, N2 = min(N/4, 2048) for N <= 2^22 and 4096 above,
- * N1 = N / N2 (sample m = N2 n1 + n2;
+ * as an N1 x N2 array, N2 = min(N/4, 2048) for N <= 2^22, 4096 up to 2^24
+ * and 8192 for N = 2^25, N1 = N / N2 (sample m = N2 n1 + n2;
  * column transforms of N1 points, twiddle W_N^(n2 k1), row transforms of N2
  * points).  K_hat holds N complex values per channel, the value of frequency
  * k = k1 + N1 k2 at [k1][k2], equal to Khat(k) / N (no Nyquist packing).  The

@@ -79,6 +79,9 @@ WORKLOADS = [
     # passes) and 64^2 (the largest grid of the on-chip 2-D forward)
     Workload("2d_128x128_b8_c64_f32", (128, 128), 8, 64, "f32", 1009),
     Workload("2d_64x64_b8_c64_f32", (64, 64), 8, 64, "f32", 1010),
+    # 2^24 tokens: the summary's 10M-token genomics context, zero-extended to a
+    # power of two (outputs below 10M are those of the 10M-token problem)
+    Workload("1d_16777216_b1_c2_bf16", (16777216,), 1, 2, "bf16", 1011),
 ]
 
 

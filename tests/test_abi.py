@@ -65,7 +65,7 @@ def test_sizes(H):
     assert rec == lib.hyenand_fftconv_workspace_bytes(8, 64, 2, _dims(256, 256), 0)
     assert lib.hyenand_fftconv_workspace_bytes(4, 4, 1, _dims(1024), 0) == 0  # 1-D needs none
     # Unsupported shapes size to 0.
-    for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(1 << 24)), (1, _dims(3 << 11)), (4, _dims(2, 2, 2, 2))]:
+    for d, dims in [(2, _dims(3, 4)), (2, _dims(1, 4)), (1, _dims(1 << 25)), (1, _dims(3 << 11)), (4, _dims(2, 2, 2, 2))]:
         assert lib.hyenand_kernel_spectrum_bytes(2, d, dims) == 0
         assert lib.hyenand_kernel_spectrum_tile(d, dims) == 0
 
@@ -153,7 +153,7 @@ def test_bwd_sizes(H):
     # 1-D: per pair S complex for the kernel gradient and one float2.
     assert lib.hyenand_fftconv_bwd_workspace_min_bytes(4, 2, 1, _dims(64), 0, 1) == 4 * 64 * 8 + 4 * 8
     assert lib.hyenand_fftconv_bwd_workspace_min_bytes(4, 2, 1, _dims(64), 0, 0) == 4 * 8
-    for d, dims in [(2, _dims(3, 4)), (1, _dims(1 << 24))]:
+    for d, dims in [(2, _dims(3, 4)), (1, _dims(1 << 25))]:
         assert lib.hyenand_fftconv_bwd_workspace_bytes(2, 2, d, dims, 0, 1) == 0
 
 
@@ -233,7 +233,7 @@ def test_per_sample_bwd_rejects(H):
     call = lambda x=FAKE, dy=FAKE, dx=FAKE, db=FAKE, B=2, C=1, d=2, dims=dd, dt=0, w=FAKE, wb=1 << 20: \
         lib.hyenand_fftconv_bwd_per_sample(x, FAKE, FAKE, FAKE, dy, dx, FAKE, db, FAKE, B, C, d, dims, dt, w, wb, None)
     assert call(x=None) == 1 and call(dy=None) == 1 and call(dx=MISALIGNED) == 1 and call(db=None) == 1
-    assert call(dims=_dims(8, 6)) == 2 and call(d=1, dims=_dims(1 << 24)) == 2 and call(w=None) == 3
+    assert call(dims=_dims(8, 6)) == 2 and call(d=1, dims=_dims(1 << 25)) == 2 and call(w=None) == 3
     # the workspace of a batch of one is enough, whatever B
     need = lib.hyenand_fftconv_bwd_workspace_min_bytes(1, 1, 2, dd, 0, 1)
     assert call(wb=need - 1) == 3
@@ -248,7 +248,8 @@ def test_long_1d_sizes(H):
     inverse-column workgroup; no circular mode."""
     lib = H.get_lib()
     # n -> partial sums per pair: N2 / TW with N2 the row length and TW the column tile
-    for n, parts in ((2048, 1024 // 16), (1 << 16, 2048 // 16), (1 << 21, 2048 // 8), (1 << 23, 4096 // 4)):
+    for n, parts in ((2048, 1024 // 16), (1 << 16, 2048 // 16), (1 << 21, 2048 // 8), (1 << 23, 4096 // 4),
+                     (1 << 24, 8192 // 4)):
         N = 2 * n
         assert lib.hyenand_kernel_spectrum_bytes(3, 1, _dims(n)) == 3 * N * 8
         assert lib.hyenand_fftconv_workspace_min_bytes(2, 3, 1, _dims(n), 0) == 2 * N * 8
@@ -262,7 +263,7 @@ def test_long_1d_sizes(H):
     bw = lib.hyenand_fftconv_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, _dims(4096), 0, FAKE,
                                  1024, None)
     assert bw == 3  # accepted shape, workspace below one channel
-    assert lib.hyenand_fftconv_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, _dims(1 << 24), 0,
+    assert lib.hyenand_fftconv_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, _dims(1 << 25), 0,
                                    FAKE, 1 << 30, None) == 2
 
 

@@ -55,7 +55,7 @@ def _run(H, dims, B, C, dtype, seed, per_sample=False, workspace=None):
 
 @pytest.mark.parametrize("n,B,C,dtype", [(2048, 2, 3, "f32"), (4096, 1, 2, "bf16"), (8192, 3, 2, "f32"),
                                          (1 << 16, 2, 2, "f32"), (1 << 18, 1, 2, "bf16"), (1 << 20, 1, 2, "f32"),
-                                         (1 << 22, 1, 1, "f32"), (1 << 23, 1, 1, "bf16")],
+                                         (1 << 22, 1, 1, "f32"), (1 << 23, 1, 1, "bf16"), (1 << 24, 1, 1, "f32")],
                          ids=lambda v: str(v))
 def test_matches_fft_oracle(H, n, B, C, dtype):
     x, p, K, y = _run(H, (n,), B, C, dtype, seed=200 + n % 97 + B)
@@ -87,6 +87,22 @@ def test_every_chunking_gives_the_same_output(H):
             for k in (1, 2, C)]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.timeout(600)
+def test_workload_16m_tokens(H):
+    """2^24 tokens (the summary's 10M-token context zero-extended to a power
+    of two; 8192-point rows), bf16, both channels against the FFT oracle, and
+    sampled outputs (corners, centre, random) against the direct sum."""
+    wl = {w.name: w for w in synth.WORKLOADS}["1d_16777216_b1_c2_bf16"]
+    x, p, K, y = _run(H, wl.dims, wl.B, wl.C, wl.dtype, seed=wl.seed)
+    assert np.all(np.isfinite(y))
+    for c in range(wl.C):
+        ref = oracle.fftconv(x[:, c:c + 1], p.alpha[c:c + 1], p.beta[c:c + 1], K[c:c + 1])
+        assert _rel(y[:, c], ref[:, 0]) <= TOL[wl.dtype], c
+    pts = synth.sample_points(wl.dims, wl.B, wl.C, [(0, 0), (0, 1)], 16, seed=wl.seed, edges=True)
+    ref = oracle.direct_points(x, p.alpha, p.beta, K, pts)
+    assert _rel(np.array([y[tuple(r)] for r in pts]), ref) <= TOL[wl.dtype]
 
 
 @pytest.mark.timeout(300)
@@ -137,7 +153,7 @@ def _check(got, ref, dtype):
 
 @pytest.mark.parametrize("n,B,C,dtype", [(2048, 2, 3, "f32"), (4096, 1, 2, "bf16"), (1 << 15, 3, 2, "f32"),
                                          (1 << 18, 1, 2, "bf16"), (1 << 20, 2, 1, "f32"), (1 << 22, 2, 1, "f32"),
-                                         (1 << 23, 1, 1, "bf16")],
+                                         (1 << 23, 1, 1, "bf16"), (1 << 24, 1, 1, "f32")],
                          ids=lambda v: str(v))
 def test_bwd_matches_fft_oracle(H, n, B, C, dtype):
     x, dy, p, K, got = _run_bwd(H, (n,), B, C, dtype, seed=300 + n % 89 + B)
