@@ -82,6 +82,7 @@ def _load():
         I = ctypes.c_int
         lib.oracle_gate.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
         lib.oracle_gate_vjp.argtypes = [P, P, I64, ctypes.c_double, ctypes.c_double, P, P]
+        lib.oracle_generate_kernels.argtypes = [P, I, I, I, P, I, I] + [P] * 10 + [ctypes.c_double, P]
         lib.oracle_direct.argtypes = [P, P, P, P, P, I, I, I, P]
         lib.oracle_direct_points.argtypes = [P, P, P, P, I, I, I, P, I64, P, P]
         lib.oracle_kernel_spectrum.argtypes = [P, I, I, P, P, P]
@@ -94,7 +95,7 @@ def _load():
         lib.oracle_bwd_direct.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, P]
         lib.oracle_bwd_direct_points.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, I64, P, P]
         lib.oracle_bwd_fft.argtypes = [P, P, P, P, P, I, I, I, P, I64, P, P, P, P, P]
-        for f in ("oracle_gate", "oracle_gate_vjp", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
+        for f in ("oracle_gate", "oracle_gate_vjp", "oracle_generate_kernels", "oracle_direct", "oracle_direct_points", "oracle_kernel_spectrum",
                   "oracle_fftconv_pairs", "oracle_num_threads", "oracle_bwd_direct", "oracle_bwd_direct_points",
                   "oracle_bwd_fft", "oracle_direct_circ", "oracle_fftconv_circ_pairs", "oracle_bwd_direct_circ",
                   "oracle_bwd_fft_circ"):
@@ -200,6 +201,32 @@ def kernel_spectrum(K, dims) -> np.ndarray:
     im = np.empty(shape, dtype=np.float64)
     _check(_load().oracle_kernel_spectrum(_ptr(K), C, d, _ptr(dd), _ptr(re), _ptr(im)), "kernel_spectrum")
     return re + 1j * im
+
+
+GEN_HIDDEN = 16
+GEN_KEYS = ("Wreg", "breg", "q", "Wgam", "Wbet", "W1", "b1", "W2", "b2", "sigma")
+
+
+def generate_kernels(x, gen) -> np.ndarray:
+    """Input-dependent kernels (summary, "Methodology": registers, a
+    softmax-weighted control z(x), a FiLM-modulated SIREN, a Gaussian window;
+    the steps are spelled out in oracle.c): x [B, C, *dims] and the generator
+    parameters ``gen`` (dict of arrays: Wreg [R, D, C], breg [R, D], q [D],
+    Wgam [16, D], Wbet [16, D], W1 [16, d], b1 [16], W2 [C, 16], b2 [C],
+    sigma [C], and the scalar omega0) -> K fp64 [B, C, *(2n-1)]."""
+    x = _f32(x)
+    B, C = x.shape[:2]
+    d = x.ndim - 2
+    dims = _dims_of(x, d)
+    arrs = {k: _f32(gen[k]) for k in GEN_KEYS}
+    R, D = arrs["Wreg"].shape[:2]
+    if arrs["Wreg"].shape != (R, D, C) or arrs["W1"].shape != (GEN_HIDDEN, d) or arrs["W2"].shape != (C, GEN_HIDDEN):
+        raise ValueError("generator parameter shapes")
+    K = np.empty((B, C) + tuple(2 * int(n) - 1 for n in dims), dtype=np.float64)
+    _check(_load().oracle_generate_kernels(_ptr(x), B, C, d, _ptr(dims), R, D,
+                                           *[_ptr(arrs[k]) for k in GEN_KEYS], float(gen["omega0"]), _ptr(K)),
+           "generate_kernels")
+    return K
 
 
 def direct_per_sample(x, alpha, beta, K) -> np.ndarray:

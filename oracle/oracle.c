@@ -863,6 +863,104 @@ int oracle_bwd_fft_circ(const float *x, const float *alpha, const float *beta, c
     return rc;
 }
 
+/* ------------------------------------------------------------------------- */
+/* Input-dependent kernel generator ([SUMM] "Methodology", "Input dependent   */
+/* kernels via registers and FiLM", "Kernel synthesis").                       */
+/* ------------------------------------------------------------------------- */
+/*
+ * For each sample b (the steps in the summary's order; the registers'
+ * processing by the network is stood in for by one layer on the sample's
+ * per-channel means):
+ *   m_b[c]      = mean over the grid of x[b,c]
+ *   a_{b,r,j}   = tanh(sum_c Wreg[r][j][c] m_b[c] + breg[r][j])     R registers, width D
+ *   pi_{b,r}    = softmax_r( sum_j q[j] a_{b,r,j} )
+ *   z_{b,j}     = sum_r pi_{b,r} a_{b,r,j}                          control variable z(x)
+ *   gam_{b,k}   = 1 + sum_j Wgam[k][j] z_{b,j},  bet_{b,k} = sum_j Wbet[k][j] z_{b,j}   FiLM
+ * and for each channel c and offset delta (delta_a in [-(n_a-1), n_a-1]):
+ *   h_k(delta)  = sin(omega0 (sum_a W1[k][a] chat_a + b1[k])),  chat_a = delta_a / (n_a - 1)
+ *   f(delta)    = sum_k W2[c][k] (gam_{b,k} h_k(delta) + bet_{b,k}) + b2[c]     (SIREN, FiLM-modulated)
+ *   w_c(delta)  = exp(-|delta|^2 / (2 sigma_c^2))                              (Gaussian window)
+ *   K_{b,c}     = w_c f                                              K(x) = w(c) (.) f(c; z(x))
+ * with 16 hidden units.  K: fp64 [B][C][(2n_0-1)..].
+ */
+#define ORC_GEN_H 16
+
+int oracle_generate_kernels(const float *x, int B, int C, int d, const int64_t *dims, int R, int D,
+                            const float *Wreg, const float *breg, const float *q, const float *Wgam,
+                            const float *Wbet, const float *W1, const float *b1, const float *W2,
+                            const float *b2, const float *sigma, double omega0, double *K)
+{
+    geom_t g;
+    if (!x || !K || !Wreg || !breg || !q || !Wgam || !Wbet || !W1 || !b1 || !W2 || !b2 || !sigma) return ORC_EINVAL;
+    if (B < 0 || C < 0 || R < 1 || D < 1 || geom_init(&g, d, dims)) return ORC_EINVAL;
+    double *m = (double *)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
+    double *a = (double *)malloc(sizeof(double) * (size_t)R * D);
+    double *z = (double *)malloc(sizeof(double) * (size_t)D);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)R);
+    if (!m || !a || !z || !sc) { free(m); free(a); free(z); free(sc); return ORC_ENOMEM; }
+    const int off = 3 - d;   /* geom axes are right-aligned: axis a of the grid is geom axis off + a */
+    for (int b = 0; b < B; ++b) {
+        for (int c = 0; c < C; ++c) {
+            const float *xs = x + ((int64_t)b * C + c) * g.L;
+            double acc = 0.0;
+            for (int64_t j = 0; j < g.L; ++j) acc += (double)xs[j];
+            m[c] = acc / (double)g.L;
+        }
+        for (int r = 0; r < R; ++r)
+            for (int j = 0; j < D; ++j) {
+                double v = breg[r * D + j];
+                for (int c = 0; c < C; ++c) v += (double)Wreg[((int64_t)r * D + j) * C + c] * m[c];
+                a[r * D + j] = tanh(v);
+            }
+        double smax = -1e300;
+        for (int r = 0; r < R; ++r) {
+            double v = 0.0;
+            for (int j = 0; j < D; ++j) v += (double)q[j] * a[r * D + j];
+            sc[r] = v;
+            if (v > smax) smax = v;
+        }
+        double ssum = 0.0;
+        for (int r = 0; r < R; ++r) { sc[r] = exp(sc[r] - smax); ssum += sc[r]; }
+        for (int j = 0; j < D; ++j) {
+            double v = 0.0;
+            for (int r = 0; r < R; ++r) v += sc[r] / ssum * a[r * D + j];
+            z[j] = v;
+        }
+        double gam[ORC_GEN_H], bet[ORC_GEN_H];
+        for (int k = 0; k < ORC_GEN_H; ++k) {
+            double vg = 1.0, vb = 0.0;
+            for (int j = 0; j < D; ++j) { vg += (double)Wgam[k * D + j] * z[j]; vb += (double)Wbet[k * D + j] * z[j]; }
+            gam[k] = vg;
+            bet[k] = vb;
+        }
+        for (int c = 0; c < C; ++c) {
+            double *Kc = K + ((int64_t)b * C + c) * g.KL;
+            const double s2 = 2.0 * (double)sigma[c] * (double)sigma[c];
+#pragma omp parallel for schedule(static)
+            for (int64_t e0 = 0; e0 < g.ke[0]; ++e0)
+                for (int64_t e1 = 0; e1 < g.ke[1]; ++e1)
+                    for (int64_t e2 = 0; e2 < g.ke[2]; ++e2) {
+                        const int64_t e[3] = {e0, e1, e2};
+                        double chat[3] = {0.0, 0.0, 0.0}, r2 = 0.0;
+                        for (int ax = 0; ax < 3; ++ax) {
+                            const double dl = (double)(e[ax] - (g.n[ax] - 1));
+                            if (g.n[ax] > 1) chat[ax] = dl / (double)(g.n[ax] - 1);
+                            r2 += dl * dl;
+                        }
+                        double f = (double)b2[c];
+                        for (int k = 0; k < ORC_GEN_H; ++k) {
+                            double arg = (double)b1[k];
+                            for (int ax = 0; ax < d; ++ax) arg += (double)W1[k * d + ax] * chat[off + ax];
+                            f += (double)W2[c * ORC_GEN_H + k] * (gam[k] * sin(omega0 * arg) + bet[k]);
+                        }
+                        Kc[(e0 * g.ke[1] + e1) * g.ke[2] + e2] = exp(-r2 / s2) * f;
+                    }
+        }
+    }
+    free(m); free(a); free(z); free(sc);
+    return ORC_OK;
+}
+
 /* Threads OpenMP will use (reported by the CPU-baseline leg). */
 int oracle_num_threads(void)
 {

@@ -214,6 +214,36 @@ def sample_points(dims, B: int, C: int, pairs, per_pair: int, seed: int, edges: 
     return np.asarray(rows, dtype=np.int64)
 
 
+def draw_generator(dims, C: int, seed: int, R: int = 4, D: int = 8) -> dict:
+    """Seeded parameters of the input-dependent kernel generator (registers,
+    softmax control, FiLM, SIREN, Gaussian window; the generator itself is the
+    library's / the oracle's, not this module's).  One
+    ``numpy.random.Generator(PCG64([seed, 4]))``, fixed order:
+      Wreg [R, D, C] ~ U(-1, 1) * 4 / sqrt(C), breg [R, D] ~ U(-1, 1),
+      q [D] ~ U(-2, 2), Wgam [16, D], Wbet [16, D] ~ U(-1/2, 1/2),
+      W1 [16, d] ~ U(-1, 1), b1 [16] ~ U(-pi, pi), W2 [C, 16] ~ U(-1/4, 1/4),
+      b2 [C] ~ U(-1/10, 1/10), sigma [C] ~ U(0.1, 0.4) * max(dims) (voxels),
+      omega0 = 10 (the static kernels' SIREN frequency).
+    All fp32 except omega0."""
+    d = len(dims)
+    rng = np.random.Generator(np.random.PCG64([seed, 4]))
+    f = np.float32
+    g = {
+        "Wreg": (rng.uniform(-1, 1, (R, D, C)) * 4.0 / math.sqrt(C)).astype(f),
+        "breg": rng.uniform(-1, 1, (R, D)).astype(f),
+        "q": rng.uniform(-2, 2, D).astype(f),
+        "Wgam": rng.uniform(-0.5, 0.5, (HIDDEN, D)).astype(f),
+        "Wbet": rng.uniform(-0.5, 0.5, (HIDDEN, D)).astype(f),
+        "W1": rng.uniform(-1, 1, (HIDDEN, d)).astype(f),
+        "b1": rng.uniform(-math.pi, math.pi, HIDDEN).astype(f),
+        "W2": rng.uniform(-0.25, 0.25, (C, HIDDEN)).astype(f),
+        "b2": rng.uniform(-0.1, 0.1, C).astype(f),
+        "sigma": (rng.uniform(0.1, 0.4, C) * max(dims)).astype(f),
+        "omega0": OMEGA0,
+    }
+    return g
+
+
 def draw_dy(dims, B: int, C: int, dtype: str, seed: int):
     """Output gradient of the backward: dy ~ N(0,1) fp32 [B, C, *dims] from its
     own stream, PCG64 seeded with [seed, 1] (x's stream is untouched); bf16 I/O
