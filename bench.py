@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "Gvoxel·channels/s of gated N-D FFT conv fwd; % of HBM roofline (1 GPU)"
 METRIC_CIRC = "Gvoxel·channels/s of gated N-D FFT conv fwd, circular mode; % of HBM roofline (1 GPU)"
 METRIC_PS = "Gvoxel·channels/s of gated N-D FFT conv fwd, one kernel per (b, c); % of HBM roofline (1 GPU)"
+METRIC_GEN = ("Gvoxel·channels/s of gated N-D FFT conv fwd with input-dependent kernels generated in the step; "
+              "% of HBM roofline (1 GPU)")
 METRIC_BWD = "Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK); % of HBM roofline (1 GPU)"
 METRIC_BWD_PS = ("Gvoxel·channels/s of gated N-D FFT conv bwd (dx, dalpha, dbeta, dK), one kernel per (b, c); "
                  "% of HBM roofline (1 GPU)")
@@ -302,7 +304,8 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
     import synth
 
     circ = boundary == "circular"
-    ps = kernel == "per-sample"
+    gen_mode = kernel == "generated"
+    ps = kernel == "per-sample" or gen_mode
     dev = torch.device("cuda:0")
     es = 2 if wl.dtype == "bf16" else 4
 
@@ -320,10 +323,19 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
         K = (K.unsqueeze(0) * gsc.reshape(shape) + gsh.reshape(shape)).contiguous()
     al = torch.from_numpy(p.alpha).to(dev)
     be = torch.from_numpy(p.beta).to(dev)
+    if gen_mode:
+        # Input-dependent kernels generated from x on the GPU at every step
+        # (registers -> control -> FiLM SIREN -> window, into the spectra).
+        gen = {k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v)
+               for k, v in synth.draw_generator(wl.dims, wl.C, wl.seed).items()}
+        kh_gen = torch.empty(H.spectrum_bytes(wl.B * wl.C, wl.dims) // 8, dtype=torch.complex64,
+                             device=dev).view(wl.B * wl.C, -1)
     torch.cuda.synchronize()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def spectrum():
+        if gen_mode:
+            return H.generate_kernel_spectrum(x, gen, out=kh_gen)
         return H.kernel_spectrum_circ(K) if circ else (H.kernel_spectrum_per_sample(K) if ps else H.kernel_spectrum(K))
 
     kh = spectrum()  # the first call also loads the spectrum kernels' code
@@ -363,6 +375,9 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
             f(x, al, be, kh, dy, *outs, workspace=ws)
         elif circ:
             H.fftconv_fwd_circ(x, al, be, kh, y=y, workspace=ws)
+        elif gen_mode:
+            H.generate_kernel_spectrum(x, gen, out=kh_gen)
+            H.fftconv_fwd_per_sample(x, al, be, kh_gen, y=y, workspace=ws)
         elif ps:
             H.fftconv_fwd_per_sample(x, al, be, kh, y=y, workspace=ws)
         else:
@@ -543,9 +558,10 @@ def main():
                     help="time the forward (default) or the backward with the kernel gradient")
     ap.add_argument("--boundary", choices=("padded", "circular"), default="padded",
                     help="zero-padded non-circular convolution (default) or the circular mode")
-    ap.add_argument("--kernel", choices=("shared", "per-sample"), default="shared",
-                    help="one kernel per channel (default) or one per (b, c): input-dependent kernels "
-                         "(zero-padded mode only)")
+    ap.add_argument("--kernel", choices=("shared", "per-sample", "generated"), default="shared",
+                    help="one kernel per channel (default), one per (b, c) (input-dependent kernels, "
+                         "zero-padded mode only), or one per (b, c) generated from x on the GPU inside every "
+                         "step (registers, FiLM SIREN, Gaussian window; the step then includes the generator)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--also", default=None,
                     help="comma-separated further workloads measured the same way and reported under "
@@ -578,18 +594,22 @@ def main():
     import dimensional_fft_long_amd as H
     import synth
 
-    if args.boundary == "circular" and args.kernel == "per-sample":
+    if args.boundary == "circular" and args.kernel != "shared":
         print("bench.py: per-sample kernels are built for the zero-padded mode only", file=sys.stderr)
+        return 2
+    if args.which == "bwd" and args.kernel == "generated":
+        print("bench.py: the generated-kernel step is timed for the forward only", file=sys.stderr)
         return 2
     torch.cuda.set_device(torch.device("cuda:0"))
     by_name = {w.name: w for w in synth.WORKLOADS}
     wl = by_name[args.workload]
     main_run = run_workload(H, wl, args.which, args.boundary, args.kernel, args.steps, args.warmup, args.settle_s,
                             args.ws_mb, with_cpu=not args.no_cpu_baseline)
-    circ, ps, bwd = args.boundary == "circular", args.kernel == "per-sample", args.which == "bwd"
+    circ, ps, bwd = args.boundary == "circular", args.kernel != "shared", args.which == "bwd"
     out = {
         "metric": ((METRIC_BWD_CIRC if circ else (METRIC_BWD_PS if ps else METRIC_BWD)) if bwd
-                   else (METRIC_CIRC if circ else (METRIC_PS if ps else METRIC))),
+                   else (METRIC_CIRC if circ else (METRIC_GEN if args.kernel == "generated"
+                                                   else (METRIC_PS if ps else METRIC)))),
         "value": main_run.pop("value"),
         "unit": UNIT,
         "n_gpus": 1,

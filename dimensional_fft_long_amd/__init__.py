@@ -53,10 +53,19 @@ EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_
            "hyenand_fftconv_fwd_per_sample", "hyenand_fftconv_fwd_per_sample_traced", "hyenand_fftconv_bwd_circ",
            "hyenand_fftconv_bwd_circ_workspace_bytes", "hyenand_fftconv_bwd_circ_workspace_min_bytes",
            "hyenand_fftconv_bwd_circ_traced", "hyenand_fftconv_bwd_per_sample",
-           "hyenand_fftconv_bwd_per_sample_traced", "hyenand_fftconv_fwd_noalloc",
+           "hyenand_fftconv_bwd_per_sample_traced", "hyenand_generate_workspace_bytes",
+           "hyenand_generate_kernel_spectrum", "hyenand_fftconv_fwd_noalloc",
            "hyenand_fftconv_fwd_noalloc_max_workspace")
 
 _lib = None
+
+
+class _Generator(ctypes.Structure):
+    """hyenand_generator (include/hyenand.h): device pointers of the
+    input-dependent kernel generator's parameters."""
+    _fields_ = [("R", ctypes.c_int), ("D", ctypes.c_int)] + \
+               [(k, ctypes.c_void_p) for k in ("Wreg", "breg", "q", "Wgam", "Wbet", "W1", "b1", "W2", "b2", "sigma")] + \
+               [("omega0", ctypes.c_float)]
 
 
 def get_lib() -> ctypes.CDLL:
@@ -134,6 +143,10 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_fftconv_fwd_noalloc.restype = I
     lib.hyenand_fftconv_fwd_noalloc_max_workspace.argtypes = []
     lib.hyenand_fftconv_fwd_noalloc_max_workspace.restype = SZ
+    lib.hyenand_generate_workspace_bytes.argtypes = [I, I, I, P]
+    lib.hyenand_generate_workspace_bytes.restype = SZ
+    lib.hyenand_generate_kernel_spectrum.argtypes = [P, ctypes.POINTER(_Generator), P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_generate_kernel_spectrum.restype = I
     _lib = lib
     return lib
 
@@ -673,4 +686,59 @@ def fftconv_fwd_noalloc(x, alpha, beta, K_hat, y, stream=None) -> torch.Tensor:
     if rc != OK:
         raise HyenandError(rc, "fftconv_fwd_noalloc")
     return y
+
+
+# ------------------------------------------------ generated per-sample kernels
+
+GEN_KEYS = ("Wreg", "breg", "q", "Wgam", "Wbet", "W1", "b1", "W2", "b2", "sigma")
+
+
+def generate_workspace_bytes(B: int, C: int, dims) -> int:
+    return int(get_lib().hyenand_generate_workspace_bytes(B, C, len(dims), _dims_arr(dims)))
+
+
+def generate_kernel_spectrum(x: torch.Tensor, gen: dict, out: torch.Tensor | None = None, workspace=None,
+                             stream=None) -> torch.Tensor:
+    """Spectra of the input-dependent kernels of x (registers -> softmax
+    control -> FiLM-modulated SIREN -> Gaussian window, hyenand.h), one per
+    (b, c), generated on the GPU without forming the kernels: K_hat [B * C, ksz]
+    for fftconv_fwd_per_sample / fftconv_bwd_per_sample.  ``gen``: fp32 device
+    tensors Wreg [R, D, C], breg [R, D], q [D], Wgam [16, D], Wbet [16, D],
+    W1 [16, d], b1 [16], W2 [C, 16], b2 [C], sigma [C], and omega0 (float)."""
+    if not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous device tensor")
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    d = len(dims)
+    shapes = {"breg": None, "q": None, "Wgam": None, "Wbet": None, "W1": (16, d), "b1": (16,), "W2": (C, 16),
+              "b2": (C,), "sigma": (C,)}
+    for k in GEN_KEYS:
+        t = gen[k]
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous():
+            raise TypeError(f"generator parameter {k} must be a contiguous float32 tensor on {x.device}")
+        if shapes.get(k) is not None and tuple(t.shape) != shapes[k]:
+            raise ValueError(f"generator parameter {k} must have shape {shapes[k]}")
+    R, D = int(gen["Wreg"].shape[0]), int(gen["Wreg"].shape[1])
+    want = {"Wreg": (R, D, C), "breg": (R, D), "q": (D,), "Wgam": (16, D), "Wbet": (16, D)}
+    for k, shp in want.items():
+        if tuple(gen[k].shape) != shp:
+            raise ValueError(f"generator parameter {k} must have shape {shp}")
+    nbytes = spectrum_bytes(B * C, dims)
+    if nbytes == 0:
+        raise HyenandError(ERR_UNSUPPORTED, "generate_kernel_spectrum")
+    if out is None:
+        out = torch.empty(nbytes // 8, dtype=torch.complex64, device=x.device).view(B * C, -1)
+    else:
+        _check_spectrum_out(out, nbytes, x.device)
+    if workspace is None:
+        workspace, ws_bytes = _cached_ws("gen", generate_workspace_bytes(B, C, dims), x.device, stream)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    g = _Generator(R, D, *[gen[k].data_ptr() for k in GEN_KEYS], float(gen["omega0"]))
+    rc = get_lib().hyenand_generate_kernel_spectrum(_P(x.data_ptr()), ctypes.byref(g), _P(out.data_ptr()), B, C, d,
+                                                    _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()),
+                                                    ws_bytes, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "generate_kernel_spectrum")
+    return out
 

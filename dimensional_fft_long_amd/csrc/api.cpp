@@ -5,6 +5,7 @@
 #include <mutex>
 
 #include "../../include/hyenand.h"
+#include "gen.h"
 #include "launch.h"
 #include "plan.h"
 
@@ -439,6 +440,87 @@ int hyenand_fftconv_fwd_per_sample_traced(const void* x, const float* alpha, con
                                     stream, &tr, false, true);
     if (n_launches) *n_launches = tr.count > 0 ? tr.count - 1 : 0;
     return rc;
+}
+
+// ------------------------------------------------- generated (per-sample) kernels
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct GenLayout {
+    size_t partial, coef, basis[3], total;
+};
+
+GenLayout gen_layout(const Geom& g, int B, int C)
+{
+    GenLayout l{};
+    size_t o = 0;
+    l.partial = o;
+    o += align256((size_t)B * C * gen_splits(g.vox) * sizeof(double));
+    l.coef = o;
+    o += align256((size_t)B * C * kGenCoef * sizeof(float));
+    const int Ns[3] = {g.N_out, g.N_mid, g.N_in};
+    for (int ax = 0; ax < 3; ++ax) {
+        l.basis[ax] = o;
+        if (Ns[ax] > 1) o += align256((size_t)C * kGenLines * Ns[ax] * 8u);
+    }
+    l.total = o;
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hyenand_generate_workspace_bytes(int B, int C, int d, const int64_t* dims)
+{
+    Geom g;
+    if (B <= 0 || C <= 0 || !make_geom(d, dims, &g) || g.lng) return 0;
+    return gen_layout(g, B, C).total;
+}
+
+int hyenand_generate_kernel_spectrum(const void* x, const hyenand_generator* gen, void* K_hat, int B, int C, int d,
+                                     const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream)
+{
+    if (B < 0 || C < 0 || !gen) return HYENAND_ERR_INVALID_ARG;
+    if (dtype != HYENAND_F32 && dtype != HYENAND_BF16) return HYENAND_ERR_INVALID_ARG;
+    if (d < 1 || d > 3) return HYENAND_ERR_UNSUPPORTED;
+    if (!dims) return HYENAND_ERR_INVALID_ARG;
+    Geom g;
+    if (!make_geom(d, dims, &g) || g.lng) return HYENAND_ERR_UNSUPPORTED;
+    if (gen->R < 1 || gen->R > 64 || gen->D < 1 || gen->D > 64 || C > 8192) return HYENAND_ERR_INVALID_ARG;
+    if (B == 0 || C == 0) return HYENAND_OK;
+    const size_t es = dtype == HYENAND_BF16 ? 2 : 4;
+    const float* ps[10] = {gen->Wreg, gen->breg, gen->q, gen->Wgam, gen->Wbet, gen->W1, gen->b1, gen->W2, gen->b2,
+                           gen->sigma};
+    for (const float* p : ps)
+        if (!p || !aligned(p, 4)) return HYENAND_ERR_INVALID_ARG;
+    if (!x || !K_hat || !aligned(x, es) || !aligned(K_hat, 8)) return HYENAND_ERR_INVALID_ARG;
+    const GenLayout lay = gen_layout(g, B, C);
+    if (!workspace || workspace_bytes < lay.total) return HYENAND_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return HYENAND_ERR_INVALID_ARG;
+    GenArgs a{};
+    a.x = x;
+    a.bf16 = dtype == HYENAND_BF16;
+    a.B = B;
+    a.C = C;
+    a.R = gen->R;
+    a.D = gen->D;
+    a.g = g;
+    a.Wreg = gen->Wreg; a.breg = gen->breg; a.q = gen->q; a.Wgam = gen->Wgam; a.Wbet = gen->Wbet;
+    a.W1 = gen->W1; a.b1 = gen->b1; a.W2 = gen->W2; a.b2 = gen->b2; a.sigma = gen->sigma;
+    a.omega0 = gen->omega0;
+    char* w = static_cast<char*>(workspace);
+    a.partial = reinterpret_cast<double*>(w + lay.partial);
+    a.splits = gen_splits(g.vox);
+    a.coef = reinterpret_cast<float*>(w + lay.coef);
+    const int Ns[3] = {g.N_out, g.N_mid, g.N_in};
+    for (int ax = 0; ax < 3; ++ax) a.basis[ax] = Ns[ax] > 1 ? reinterpret_cast<float2*>(w + lay.basis[ax]) : nullptr;
+    a.khat = static_cast<float2*>(K_hat);
+    return launch_generate_spectrum(a, static_cast<hipStream_t>(stream)) == hipSuccess ? HYENAND_OK : HYENAND_ERR_HIP;
 }
 
 // ------------------------------------------------------ allocation-free forward

@@ -49,6 +49,11 @@ hipError_t long1d_backward(const ConvArgs& a, bool dk, hipStream_t stream, Launc
 hipError_t fused2d_forward_f32(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace);
 hipError_t fused2d_forward_bf16(const ConvArgs& a, hipStream_t stream, LaunchTrace* trace);
 
+// The input-dependent kernels' spectra (gen.h): means, control / FiLM, axis
+// spectra, per-pair spectra into a.khat.
+struct GenArgs;
+hipError_t launch_generate_spectrum(const GenArgs& a, hipStream_t stream);
+
 // Workgroups of `kernel` (nt threads per workgroup) resident at once on the
 // current device: CUs x workgroups per CU, queried once per (kernel, nt,
 // device) and cached.  0 if the query fails.

@@ -316,6 +316,49 @@ int hyenand_fftconv_bwd_per_sample_traced(const void* x, const float* phi_alpha,
                                           void* const* events, int n_events, int* n_launches);
 
 /*
+ * Input-dependent kernels generated on the GPU, straight into their spectra
+ * (gist.science summary, "Methodology": R register tokens that take in the
+ * whole sample, a control variable z(x) as their softmax-weighted mean, a
+ * coordinate SIREN modulated by FiLM, and K(x) = w(c) (.) f(c; z(x)) with a
+ * Gaussian window w).  For every sample b and channel c:
+ *   m[c]   = mean of x[b,c] over the grid
+ *   a[r]   = tanh(Wreg[r] m + breg[r])            r < R, width D   (Wreg [R][D][C])
+ *   z      = sum_r softmax_r(q . a[r]) a[r]
+ *   gam    = 1 + Wgam z,  bet = Wbet z            (16 each; Wgam, Wbet [16][D])
+ *   K[b,c](delta) = exp(-|delta|^2 / (2 sigma_c^2))
+ *                   (sum_u W2[c][u] (gam_u sin(omega0 (W1[u] . chat + b1[u])) + bet_u) + b2[c])
+ * for offsets delta_a in [-(n_a-1), n_a-1], chat_a = delta_a / (n_a - 1),
+ * 16 hidden units (W1 [16][d], b1 [16], W2 [C][16], b2 [C], sigma [C]).
+ * The kernels are never formed in space: K_hat receives their spectra, B * C
+ * of them in the layout of hyenand_kernel_spectrum on [B*C] kernels, ready for
+ * hyenand_fftconv_fwd_per_sample / _bwd_per_sample.  All parameter arrays are
+ * fp32 device pointers.  Zero-padded mode, d in {1, 2, 3}, every n in
+ * [2, 1024] (not the long 1-D path: UNSUPPORTED); 1 <= R, D <= 64, C <= 8192.  Workspace:
+ * hyenand_generate_workspace_bytes (partial sums of the means, per-pair
+ * coefficients and the channels' 1-D axis spectra).  Errors as
+ * hyenand_fftconv_fwd.
+ */
+#define HYENAND_GEN_HIDDEN 16
+typedef struct hyenand_generator {
+    int R, D;           /* registers, control width                                  */
+    const float* Wreg;  /* [R][D][C]                                                 */
+    const float* breg;  /* [R][D]                                                    */
+    const float* q;     /* [D]     softmax scores q . a[r]                           */
+    const float* Wgam;  /* [16][D] FiLM scale 1 + Wgam z                             */
+    const float* Wbet;  /* [16][D] FiLM shift Wbet z                                 */
+    const float* W1;    /* [16][d] SIREN first layer on the normalised offsets       */
+    const float* b1;    /* [16]                                                      */
+    const float* W2;    /* [C][16] per-channel read-out                              */
+    const float* b2;    /* [C]                                                       */
+    const float* sigma; /* [C]     Gaussian window width (voxels)                    */
+    float omega0;       /* SIREN frequency                                           */
+} hyenand_generator;
+size_t hyenand_generate_workspace_bytes(int B, int C, int d, const int64_t* dims);
+int hyenand_generate_kernel_spectrum(const void* x, const hyenand_generator* gen, void* K_hat, int B, int C, int d,
+                                     const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
  * Allocation-free forward, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): hyenand_fftconv_fwd with its workspace in a static device array
