@@ -330,6 +330,7 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
                for k, v in synth.draw_generator(wl.dims, wl.C, wl.seed).items()}
         kh_gen = torch.empty(H.spectrum_bytes(wl.B * wl.C, wl.dims) // 8, dtype=torch.complex64,
                              device=dev).view(wl.B * wl.C, -1)
+        gws = torch.empty(H.generated_workspace_bytes(wl.B, wl.C, wl.dims, x.dtype), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -376,8 +377,7 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
         elif circ:
             H.fftconv_fwd_circ(x, al, be, kh, y=y, workspace=ws)
         elif gen_mode:
-            H.generate_kernel_spectrum(x, gen, out=kh_gen)
-            H.fftconv_fwd_per_sample(x, al, be, kh_gen, y=y, workspace=ws)
+            H.fftconv_fwd_generated(x, al, be, gen, K_hat=kh_gen, y=y, workspace=gws)
         elif ps:
             H.fftconv_fwd_per_sample(x, al, be, kh, y=y, workspace=ws)
         else:
@@ -420,6 +420,29 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / steps
+
+    gen_compare = None
+    if gen_mode:
+        # The same step as two calls (generator for every pair, then the
+        # forward), the forward alone and the generator alone, for comparison.
+        def timed(fn):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a0.record()
+            for _ in range(steps):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / steps
+
+        def sequential():
+            H.generate_kernel_spectrum(x, gen, out=kh_gen)
+            H.fftconv_fwd_per_sample(x, al, be, kh_gen, y=y, workspace=ws)
+
+        gen_compare = {"sequential_ms_per_step": timed(sequential),
+                       "forward_alone_ms_per_step": timed(lambda: H.fftconv_fwd_per_sample(x, al, be, kh_gen, y=y,
+                                                                                            workspace=ws)),
+                       "generator_alone_ms": timed(lambda: H.generate_kernel_spectrum(x, gen, out=kh_gen))}
 
     # Per-kernel durations: the same `steps` calls again through the traced
     # entry point, which records HIP events on the launch stream between kernels.
@@ -524,6 +547,8 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
         "spectrum_ms": spectrum_ms,
         "roofline": roof,
     }
+    if gen_compare:
+        out["generated"] = gen_compare
     if with_cpu:
         out["cpu_baseline"] = cpu_baseline_bwd(wl, circ) if bwd else cpu_baseline(wl, circ)
     return out

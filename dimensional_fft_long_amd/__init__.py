@@ -55,7 +55,8 @@ EXPORTS = ("hyenand_status_string", "hyenand_version", "hyenand_kernel_spectrum_
            "hyenand_fftconv_bwd_circ_traced", "hyenand_fftconv_bwd_per_sample",
            "hyenand_fftconv_bwd_per_sample_traced", "hyenand_generate_workspace_bytes",
            "hyenand_generate_kernel_spectrum", "hyenand_fftconv_fwd_noalloc",
-           "hyenand_fftconv_fwd_noalloc_max_workspace")
+           "hyenand_fftconv_fwd_noalloc_max_workspace", "hyenand_fftconv_fwd_generated",
+           "hyenand_fftconv_fwd_generated_workspace_bytes", "hyenand_fftconv_fwd_generated_workspace_min_bytes")
 
 _lib = None
 
@@ -147,6 +148,12 @@ def get_lib() -> ctypes.CDLL:
     lib.hyenand_generate_workspace_bytes.restype = SZ
     lib.hyenand_generate_kernel_spectrum.argtypes = [P, ctypes.POINTER(_Generator), P, I, I, I, P, I, P, SZ, P]
     lib.hyenand_generate_kernel_spectrum.restype = I
+    lib.hyenand_fftconv_fwd_generated.argtypes = [P, P, P, ctypes.POINTER(_Generator), P, P, I, I, I, P, I, P, SZ, P]
+    lib.hyenand_fftconv_fwd_generated.restype = I
+    lib.hyenand_fftconv_fwd_generated_workspace_bytes.argtypes = [I, I, I, P, I]
+    lib.hyenand_fftconv_fwd_generated_workspace_bytes.restype = SZ
+    lib.hyenand_fftconv_fwd_generated_workspace_min_bytes.argtypes = [I, I, I, P, I]
+    lib.hyenand_fftconv_fwd_generated_workspace_min_bytes.restype = SZ
     _lib = lib
     return lib
 
@@ -697,19 +704,12 @@ def generate_workspace_bytes(B: int, C: int, dims) -> int:
     return int(get_lib().hyenand_generate_workspace_bytes(B, C, len(dims), _dims_arr(dims)))
 
 
-def generate_kernel_spectrum(x: torch.Tensor, gen: dict, out: torch.Tensor | None = None, workspace=None,
-                             stream=None) -> torch.Tensor:
-    """Spectra of the input-dependent kernels of x (registers -> softmax
-    control -> FiLM-modulated SIREN -> Gaussian window, hyenand.h), one per
-    (b, c), generated on the GPU without forming the kernels: K_hat [B * C, ksz]
-    for fftconv_fwd_per_sample / fftconv_bwd_per_sample.  ``gen``: fp32 device
-    tensors Wreg [R, D, C], breg [R, D], q [D], Wgam [16, D], Wbet [16, D],
-    W1 [16, d], b1 [16], W2 [C, 16], b2 [C], sigma [C], and omega0 (float)."""
+def _gen_struct(x: torch.Tensor, gen: dict):
+    """Checks the generator parameters against x; returns the hyenand_generator."""
     if not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous device tensor")
-    B, C = int(x.shape[0]), int(x.shape[1])
-    dims = tuple(int(v) for v in x.shape[2:])
-    d = len(dims)
+    C = int(x.shape[1])
+    d = x.dim() - 2
     shapes = {"breg": None, "q": None, "Wgam": None, "Wbet": None, "W1": (16, d), "b1": (16,), "W2": (C, 16),
               "b2": (C,), "sigma": (C,)}
     for k in GEN_KEYS:
@@ -723,6 +723,21 @@ def generate_kernel_spectrum(x: torch.Tensor, gen: dict, out: torch.Tensor | Non
     for k, shp in want.items():
         if tuple(gen[k].shape) != shp:
             raise ValueError(f"generator parameter {k} must have shape {shp}")
+    return _Generator(R, D, *[gen[k].data_ptr() for k in GEN_KEYS], float(gen["omega0"]))
+
+
+def generate_kernel_spectrum(x: torch.Tensor, gen: dict, out: torch.Tensor | None = None, workspace=None,
+                             stream=None) -> torch.Tensor:
+    """Spectra of the input-dependent kernels of x (registers -> softmax
+    control -> FiLM-modulated SIREN -> Gaussian window, hyenand.h), one per
+    (b, c), generated on the GPU without forming the kernels: K_hat [B * C, ksz]
+    for fftconv_fwd_per_sample / fftconv_bwd_per_sample.  ``gen``: fp32 device
+    tensors Wreg [R, D, C], breg [R, D], q [D], Wgam [16, D], Wbet [16, D],
+    W1 [16, d], b1 [16], W2 [C, 16], b2 [C], sigma [C], and omega0 (float)."""
+    g = _gen_struct(x, gen)
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    d = len(dims)
     nbytes = spectrum_bytes(B * C, dims)
     if nbytes == 0:
         raise HyenandError(ERR_UNSUPPORTED, "generate_kernel_spectrum")
@@ -734,7 +749,6 @@ def generate_kernel_spectrum(x: torch.Tensor, gen: dict, out: torch.Tensor | Non
         workspace, ws_bytes = _cached_ws("gen", generate_workspace_bytes(B, C, dims), x.device, stream)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
-    g = _Generator(R, D, *[gen[k].data_ptr() for k in GEN_KEYS], float(gen["omega0"]))
     rc = get_lib().hyenand_generate_kernel_spectrum(_P(x.data_ptr()), ctypes.byref(g), _P(out.data_ptr()), B, C, d,
                                                     _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()),
                                                     ws_bytes, _stream(stream))
@@ -742,3 +756,41 @@ def generate_kernel_spectrum(x: torch.Tensor, gen: dict, out: torch.Tensor | Non
         raise HyenandError(rc, "generate_kernel_spectrum")
     return out
 
+
+def generated_workspace_bytes(B: int, C: int, dims, dtype=torch.float32, minimum: bool = False) -> int:
+    f = (get_lib().hyenand_fftconv_fwd_generated_workspace_min_bytes if minimum
+         else get_lib().hyenand_fftconv_fwd_generated_workspace_bytes)
+    return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype)))
+
+
+def fftconv_fwd_generated(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, gen: dict,
+                          K_hat: torch.Tensor | None = None, y: torch.Tensor | None = None, workspace=None,
+                          stream=None):
+    """Forward with the input-dependent kernels of x generated in the same call
+    (the generator's spectra, then the forward chains; hyenand.h).
+    Returns (y, K_hat [B * C, ksz]); K_hat feeds fftconv_bwd_per_sample."""
+    g = _gen_struct(x, gen)
+    B, C = int(x.shape[0]), int(x.shape[1])
+    dims = tuple(int(v) for v in x.shape[2:])
+    for t, nm in ((alpha, "alpha"), (beta, "beta")):
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 tensor of C elements on {x.device}")
+    nbytes = spectrum_bytes(B * C, dims)
+    if nbytes == 0:
+        raise HyenandError(ERR_UNSUPPORTED, "fftconv_fwd_generated")
+    if K_hat is None:
+        K_hat = torch.empty(nbytes // 8, dtype=torch.complex64, device=x.device).view(B * C, -1)
+    else:
+        _check_spectrum_out(K_hat, nbytes, x.device)
+    y = torch.empty_like(x) if y is None else _check_out(y, "y", x.shape, x.dtype, x.device, like=x)
+    if workspace is None:
+        workspace, ws_bytes = _cached_ws("gen_fwd", generated_workspace_bytes(B, C, dims, x.dtype), x.device, stream)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = get_lib().hyenand_fftconv_fwd_generated(_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()),
+                                                 ctypes.byref(g), _P(K_hat.data_ptr()), _P(y.data_ptr()), B, C,
+                                                 len(dims), _dims_arr(dims), _dtype_code(x.dtype),
+                                                 _P(workspace.data_ptr()), ws_bytes, _stream(stream))
+    if rc != OK:
+        raise HyenandError(rc, "fftconv_fwd_generated")
+    return y, K_hat

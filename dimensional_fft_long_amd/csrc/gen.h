@@ -59,7 +59,9 @@ struct GenArgs {
     int splits;
     float* coef;            // [B][C][17]: v_0..v_15, e
     float2* basis[3];       // per geometry axis (out, mid, in): [C][17][N_a] (NULL for absent axes)
+    float* btab;            // S >= 16: the matrix-core engine's B operands, [C][S / 16][17][64]
     float2* khat;           // [B][C][ksz]
+    int c0, nch;            // spectrum pass: the channels [c0, c0 + nch) of every batch entry
 };
 
 // ------------------------------------------------------------- gen_stats
@@ -74,9 +76,23 @@ __device__ __forceinline__ void gen_stats_body(const Ctx& ctx, int bid, const Ge
     const long long lo = (long long)sp * seg, hi = lo + seg < n ? lo + seg : n;
     const long long base = (long long)pair * n;
     double s = 0.0;
-    for (long long i = lo + tid; i < hi; i += kGenNT) {
-        if constexpr (BF16) s += (double)bf16_to_f32(static_cast<const uint16_t*>(a.x)[base + i]);
-        else s += (double)static_cast<const float*>(a.x)[base + i];
+    if (((base + lo) & 3) == 0 && ((hi - lo) & 3) == 0) {
+        // Four elements per load (segments of four-aligned elements).
+        for (long long i = lo + 4 * tid; i < hi; i += 4 * kGenNT) {
+            if constexpr (BF16) {
+                const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.x) + base + i);
+                s += (double)__builtin_bit_cast(float, v.x << 16) + (double)__builtin_bit_cast(float, v.x & 0xffff0000u) +
+                     (double)__builtin_bit_cast(float, v.y << 16) + (double)__builtin_bit_cast(float, v.y & 0xffff0000u);
+            } else {
+                const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + base + i);
+                s += (double)v.x + (double)v.y + (double)v.z + (double)v.w;
+            }
+        }
+    } else {
+        for (long long i = lo + tid; i < hi; i += kGenNT) {
+            if constexpr (BF16) s += (double)bf16_to_f32(static_cast<const uint16_t*>(a.x)[base + i]);
+            else s += (double)static_cast<const float*>(a.x)[base + i];
+        }
     }
     R[tid] = s;
     ctx.sync();
@@ -102,11 +118,15 @@ __device__ __forceinline__ void gen_film_body(const Ctx& ctx, int b, const GenAr
     float* z = score + R;           // [D]
     float* gam = z + D;             // [16]
     float* bet = gam + kGenHidden;  // [16]
-    for (int c = tid; c < C; c += kGenNT) {
+    // A wave per channel: strided partial sums, then a butterfly over the
+    // lanes (a fixed order; lane 0's total is used).
+    const int lane = tid % 64, wave = tid / 64;
+    for (int c = wave; c < C; c += kGenNT / 64) {
         const double* pp = a.partial + ((long long)b * C + c) * a.splits;
         double s = 0.0;
-        for (int k = 0; k < a.splits; ++k) s += pp[k];
-        m[c] = (float)(s / (double)a.g.vox);
+        for (int k = lane; k < a.splits; k += 64) s += pp[k];
+        for (int o = 32; o >= 1; o /= 2) s += __shfl_xor(s, o);
+        if (lane == 0) m[c] = (float)(s / (double)a.g.vox);
     }
     ctx.sync();
     for (int i = tid; i < R * D; i += kGenNT) {
@@ -210,95 +230,232 @@ __device__ __forceinline__ void gen_basis_body(const Ctx& ctx, int bid, const Ge
 
 // ---------------------------------------------------------- gen_spectrum
 // Workgroup (pair p = b C + c, block of kGenRows rows k_out N_mid + k_mid):
-// the row factors of the 33 terms into LDS, then each thread runs over its
-// k_in, holding that column's factors in registers, and sums the terms row by
-// row.  Slot 0 packs k_in = 0 and N_in / 2 (through LDS, after the row loop).
+// the row factors of the 33 terms into LDS, then the terms summed for every
+// k_in of the block's rows; slot 0 packs k_in = 0 and N_in / 2 (through LDS,
+// after the main sums).  Two engines for the main sums: the VALU one below
+// (any S), and for S >= 16 the matrix-core one, which reads the sums as the
+// complex matrix product Khat[r, s] = sum_f RC[r, f] IN[f, s] (33 terms f:
+// RC the row factors, IN the innermost axis' factors) and runs it as fp32
+// MFMA products (v_mfma_f32_16x16x4_f32: full fp32 operands, fp32 sums).
 __device__ __forceinline__ float2 gen_axis(const GenArgs& a, int ax, int c, int u, int k, int N)
 {
     return N == 1 ? make_float2(1.f, 0.f) : a.basis[ax][((long long)c * kGenLines + u) * N + k];
 }
 
-template <class Ctx>
-__device__ __forceinline__ void gen_spectrum_body(const Ctx& ctx, int bid, const GenArgs& a, float2* RC, float2* X0,
-                                                  float2* XS)
+// RC row stride: 34 complex (272 bytes, 16-byte aligned rows for float4
+// reads); entry 33 is padding.
+constexpr int kGenTerms = 2 * kGenHidden + 1, kGenRC = kGenTerms + 1;
+
+struct GenBlock {
+    int rows, r0, nr, c, p;
+    long long kbase;
+    float gsc;
+};
+
+__device__ __forceinline__ GenBlock gen_block(const GenArgs& a, int bid)
 {
     const Geom& g = a.g;
-    const int rows = g.N_out * g.N_mid, nblk = (rows + kGenRows - 1) / kGenRows;
-    const int p = bid / nblk, r0 = (bid % nblk) * kGenRows;
-    const int c = p % a.C;
-    const int tid = ctx.tid();
-    const float* cf = a.coef + (long long)p * kGenCoef;
-    const int nr = rows - r0 < kGenRows ? rows - r0 : kGenRows;
-    // Row factors: RC[r][u] = (v_u / 2i) A_out A_mid at (k_out, k_mid),
-    // RC[r][16 + u] = (v_u / 2i) conj(A_out A_mid at (-k_out, -k_mid)), RC[r][32] = e W_out W_mid.
-    // Row stride NF = 34 complex (272 bytes, 16-byte aligned rows for float4
-    // reads); entry 33 is padding.
-    constexpr int NT3 = 2 * kGenHidden + 1, NF = NT3 + 1;
-    for (int i = tid; i < nr * NT3; i += kGenNT) {
-        const int r = i / NT3, f = i % NT3, row = r0 + r;
+    GenBlock k;
+    k.rows = g.N_out * g.N_mid;
+    const int nblk = (k.rows + kGenRows - 1) / kGenRows;
+    const int q = bid / nblk;
+    k.r0 = (bid % nblk) * kGenRows;
+    k.nr = k.rows - k.r0 < kGenRows ? k.rows - k.r0 : kGenRows;
+    k.c = a.c0 + q % a.nch;
+    k.p = (q / a.nch) * a.C + k.c;
+    k.kbase = (long long)k.p * g.ksz;
+    k.gsc = 1.0f / (2.0f * (float)g.N_in * (float)g.N_out * (float)g.N_mid);
+    return k;
+}
+
+// The innermost axis' factor of term f at k_in = s: A_u(s) (f = u < 16),
+// -conj A_u(-s) (f = 16 + u), W(s) (f = 32), 0 (f = 33).
+__device__ __forceinline__ float2 gen_in_factor(const GenArgs& a, int c, int f, int s)
+{
+    const int N = a.g.N_in;
+    if (f < kGenHidden) return gen_axis(a, 2, c, f, s, N);
+    if (f < 2 * kGenHidden) {
+        const float2 v = gen_axis(a, 2, c, f - kGenHidden, (N - s) % N, N);
+        return make_float2(-v.x, v.y);
+    }
+    return f == 2 * kGenHidden ? gen_axis(a, 2, c, kGenHidden, s, N) : make_float2(0.f, 0.f);
+}
+
+// Row factors: RC[r][u] = (v_u / 2i) A_out A_mid at (k_out, k_mid),
+// RC[r][16 + u] = (v_u / 2i) conj(A_out A_mid at (-k_out, -k_mid)),
+// RC[r][32] = e W_out W_mid; RC[r][33] = 0.
+// Also the innermost axis' factors at the Nyquist bin k_in = S into XF[33]
+// (the same for every row of the block).  The fill loop has a fixed trip
+// count so that its loads are issued together.
+template <class Ctx>
+__device__ __forceinline__ void gen_row_factors(const Ctx& ctx, const GenArgs& a, const GenBlock& k, float2* RC,
+                                                float2* XF)
+{
+    const Geom& g = a.g;
+    const float* cf = a.coef + (long long)k.p * kGenCoef;
+    if (ctx.tid() < kGenTerms) XF[ctx.tid()] = gen_in_factor(a, k.c, ctx.tid(), g.S);
+    constexpr int kIters = (kGenRows * kGenRC + kGenNT - 1) / kGenNT;
+#pragma unroll
+    for (int m = 0; m < kIters; ++m) {
+        const int i = ctx.tid() + m * kGenNT;
+        if (i >= k.nr * kGenRC) break;
+        const int r = i / kGenRC, f = i % kGenRC, row = k.r0 + r;
         const int ko = row / g.N_mid, km = row % g.N_mid;
-        float2 v;
+        float2 v = make_float2(0.f, 0.f);
         if (f == 2 * kGenHidden) {
-            v = cscale(cmul(gen_axis(a, 0, c, kGenHidden, ko, g.N_out), gen_axis(a, 1, c, kGenHidden, km, g.N_mid)),
+            v = cscale(cmul(gen_axis(a, 0, k.c, kGenHidden, ko, g.N_out), gen_axis(a, 1, k.c, kGenHidden, km, g.N_mid)),
                        cf[kGenHidden]);
-        } else {
+        } else if (f < 2 * kGenHidden) {
             const int u = f % kGenHidden;
             const bool mir = f >= kGenHidden;
             const int kom = mir ? (g.N_out - ko) % g.N_out : ko, kmm = mir ? (g.N_mid - km) % g.N_mid : km;
-            float2 pr = cmul(gen_axis(a, 0, c, u, kom, g.N_out), gen_axis(a, 1, c, u, kmm, g.N_mid));
+            float2 pr = cmul(gen_axis(a, 0, k.c, u, kom, g.N_out), gen_axis(a, 1, k.c, u, kmm, g.N_mid));
             if (mir) pr = cconj(pr);
             const float h = 0.5f * cf[u];  // v / 2i = -i v / 2
             v = make_float2(h * pr.y, -h * pr.x);
         }
-        RC[r * NF + f] = v;
+        RC[r * kGenRC + f] = v;
     }
-    ctx.sync();
-    const int S = g.S, N = g.N_in;
-    const float gsc = 1.0f / (2.0f * (float)N * (float)g.N_out * (float)g.N_mid);
-    const long long kbase = (long long)p * g.ksz;
-    // Threads as (slot lane, row lane): slots k_in in [0, S) over SL lanes,
-    // rows split over kGenNT / SL row lanes (S is a power of two).
-    const int SL = S < kGenNT ? S : kGenNT, RL = kGenNT / SL;
-    const int sl = tid % SL, rl = tid / SL;
-    for (int s = sl; s < S; s += SL) {
-        float2 in[kGenHidden], inm[kGenHidden];
-#pragma unroll
-        for (int u = 0; u < kGenHidden; ++u) {
-            in[u] = gen_axis(a, 2, c, u, s, N);
-            inm[u] = cconj(gen_axis(a, 2, c, u, (N - s) % N, N));
-        }
-        const float2 win = gen_axis(a, 2, c, kGenHidden, s, N);
-        for (int r = rl; r < nr; r += RL) {
-            const float4* f4 = reinterpret_cast<const float4*>(RC + r * NF);
-            float2 acc = cmul(RC[r * NF + 2 * kGenHidden], win);
-#pragma unroll
-            for (int u = 0; u < kGenHidden; u += 2) {
-                const float4 pa = f4[u / 2], pb = f4[(kGenHidden + u) / 2];
-                acc = cadd(acc, cmul(make_float2(pa.x, pa.y), in[u]));
-                acc = cadd(acc, cmul(make_float2(pa.z, pa.w), in[u + 1]));
-                acc = csub(acc, cmul(make_float2(pb.x, pb.y), inm[u]));
-                acc = csub(acc, cmul(make_float2(pb.z, pb.w), inm[u + 1]));
-            }
-            if (s == 0) X0[r] = acc;
-            else a.khat[kbase + tm_index(g, rows, r0 + r, s)] = cscale(acc, gsc);
-        }
-    }
-    // The Nyquist bin k_in = S of every row (one row per thread).
-    if (tid < nr) {
+}
+
+// The Nyquist bin k_in = S of every row (one row per thread), then slot 0 and
+// the trailing block from X0 (k_in = 0) and XS.
+template <class Ctx>
+__device__ __forceinline__ void gen_pack_slot0(const Ctx& ctx, const GenArgs& a, const GenBlock& k, const float2* RC,
+                                               const float2* XF, const float2* X0, float2* XS)
+{
+    const Geom& g = a.g;
+    const int tid = ctx.tid();
+    if (tid < k.nr) {
         const int r = tid;
-        float2 acc = cmul(RC[r * NF + 2 * kGenHidden], gen_axis(a, 2, c, kGenHidden, S, N));
-        for (int u = 0; u < kGenHidden; ++u) {
-            acc = cadd(acc, cmul(RC[r * NF + u], gen_axis(a, 2, c, u, S, N)));
-            acc = csub(acc, cmul(RC[r * NF + kGenHidden + u], cconj(gen_axis(a, 2, c, u, (N - S) % N, N))));
-        }
+        float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int f = 0; f < kGenTerms; ++f) acc = cadd(acc, cmul(RC[r * kGenRC + f], XF[f]));
         XS[r] = acc;
     }
     ctx.sync();
-    for (int r = tid; r < nr; r += kGenNT) {
+    for (int r = tid; r < k.nr; r += kGenNT) {
         const float2 z0 = X0[r], zs = XS[r];
-        a.khat[kbase + tm_index(g, rows, r0 + r, 0)] = cscale(cadd(z0, zs), 0.5f * gsc);
-        a.khat[kbase + g.kmain + r0 + r] = cscale(csub(z0, zs), 0.5f * gsc);
+        a.khat[k.kbase + tm_index(g, k.rows, k.r0 + r, 0)] = cscale(cadd(z0, zs), 0.5f * k.gsc);
+        a.khat[k.kbase + g.kmain + k.r0 + r] = cscale(csub(z0, zs), 0.5f * k.gsc);
     }
+}
+
+// VALU engine: threads as (slot lane, row lane), slots k_in in [0, S) over SL
+// lanes holding that slot's 33 factors in registers, rows over the
+// kGenNT / SL row lanes (S is a power of two).
+template <class Ctx>
+__device__ __forceinline__ void gen_spectrum_body(const Ctx& ctx, int bid, const GenArgs& a, float2* RC, float2* XF,
+                                                  float2* X0, float2* XS)
+{
+    const Geom& g = a.g;
+    const GenBlock k = gen_block(a, bid);
+    const int tid = ctx.tid();
+    gen_row_factors(ctx, a, k, RC, XF);
+    ctx.sync();
+    const int S = g.S;
+    const int SL = S < kGenNT ? S : kGenNT, RL = kGenNT / SL;
+    const int sl = tid % SL, rl = tid / SL;
+    for (int s = sl; s < S; s += SL) {
+        float2 in[2 * kGenHidden];
+#pragma unroll
+        for (int f = 0; f < 2 * kGenHidden; ++f) in[f] = gen_in_factor(a, k.c, f, s);
+        const float2 win = gen_in_factor(a, k.c, 2 * kGenHidden, s);
+        for (int r = rl; r < k.nr; r += RL) {
+            const float4* f4 = reinterpret_cast<const float4*>(RC + r * kGenRC);
+            float2 acc = cmul(RC[r * kGenRC + 2 * kGenHidden], win);
+#pragma unroll
+            for (int f = 0; f < 2 * kGenHidden; f += 2) {
+                const float4 pa = f4[f / 2];
+                acc = cadd(acc, cmul(make_float2(pa.x, pa.y), in[f]));
+                acc = cadd(acc, cmul(make_float2(pa.z, pa.w), in[f + 1]));
+            }
+            if (s == 0) X0[r] = acc;
+            else a.khat[k.kbase + tm_index(g, k.rows, k.r0 + r, s)] = cscale(acc, k.gsc);
+        }
+    }
+    gen_pack_slot0(ctx, a, k, RC, XF, X0, XS);
+}
+
+// Matrix-core engine (S >= 16, kGenRows = 64: wave w owns rows 16 w .. 16 w + 15
+// of the block).  As real products over K = 68 (term f, part t at k = 2 f + t):
+//   Re Khat[r, s] = sum_k Are[r, k] B[k, s],  Im Khat[r, s] = sum_k Aim[r, k] B[k, s],
+//   B[2f, s] = Re IN[f, s],  B[2f + 1, s] = Im IN[f, s],
+//   Are[r, 2f] = Re RC[r, f],  Are[r, 2f + 1] = -Im RC[r, f],
+//   Aim[r, 2f] = Im RC[r, f],  Aim[r, 2f + 1] = Re RC[r, f],
+// in 17 steps of v_mfma_f32_16x16x4_f32 per part.  Operand layout of that
+// instruction: lane l holds A[l % 16][k0 + l / 16] and B[k0 + l / 16][l % 16];
+// the result D[4 (l / 16) + i][l % 16] is in element i of lane l.  The row
+// operands stay in registers; the B operands come from a per-channel table in
+// exactly that lane order (gen_btab_body: 17 coalesced loads per tile), the
+// next tile's loaded while the current tile's products run.
+typedef float gen_f4 __attribute__((ext_vector_type(4)));
+constexpr int kGenKS = (2 * kGenRC) / 4;  // 17 steps of 4
+
+// The B operand table of one (channel, 16-slot tile): [17][64] floats,
+// entry (j, l) = B[4 j + l / 16][16 tile + l % 16].
+template <class Ctx>
+__device__ __forceinline__ void gen_btab_body(const Ctx& ctx, int bid, const GenArgs& a)
+{
+    const int nst = a.g.S / 16, c = bid / nst, st = bid % nst;
+    float* out = a.btab + (long long)bid * kGenKS * 64;
+    for (int i = ctx.tid(); i < kGenKS * 64; i += kGenNT) {
+        const int j = i / 64, l = i % 64, kk = 4 * j + l / 16;
+        const float2 v = gen_in_factor(a, c, kk / 2, 16 * st + l % 16);
+        out[i] = (kk & 1) ? v.y : v.x;
+    }
+}
+
+template <class Ctx>
+__device__ __forceinline__ void gen_spectrum_mfma_body(const Ctx& ctx, int bid, const GenArgs& a, float2* RC,
+                                                       float2* XF, float2* X0, float2* XS)
+{
+    static_assert(kGenRows == 64 && kGenNT == 256, "four waves of 16 rows");
+    const Geom& g = a.g;
+    const GenBlock k = gen_block(a, bid);
+    const int tid = ctx.tid(), lane = tid % 64, w = tid / 64;
+    gen_row_factors(ctx, a, k, RC, XF);
+    ctx.sync();
+    constexpr int KS = kGenKS;
+    const int ra = 16 * w + lane % 16, kq = lane / 16;
+    float are[KS], aim[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const int kk = 4 * j + kq, f = kk / 2;
+        const float2 v = ra < k.nr ? RC[ra * kGenRC + f] : make_float2(0.f, 0.f);
+        are[j] = (kk & 1) ? -v.y : v.x;
+        aim[j] = (kk & 1) ? v.x : v.y;
+    }
+    const int S = g.S, nst = S / 16;
+    const float* bt = a.btab + (long long)k.c * nst * KS * 64 + lane;
+    float bn[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) bn[j] = bt[j * 64];
+    for (int st = 0; st < nst; ++st) {
+        float b[KS];
+#pragma unroll
+        for (int j = 0; j < KS; ++j) b[j] = bn[j];
+        if (st + 1 < nst) {
+#pragma unroll
+            for (int j = 0; j < KS; ++j) bn[j] = bt[((st + 1) * KS + j) * 64];
+        }
+        const int s = 16 * st + lane % 16;
+        gen_f4 dre = {0.f, 0.f, 0.f, 0.f}, dim = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            dre = __builtin_amdgcn_mfma_f32_16x16x4f32(are[j], b[j], dre, 0, 0, 0);
+            dim = __builtin_amdgcn_mfma_f32_16x16x4f32(aim[j], b[j], dim, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * kq + i;
+            if (r >= k.nr) continue;
+            const float2 v = make_float2(dre[i], dim[i]);
+            if (s == 0) X0[r] = v;
+            else a.khat[k.kbase + tm_index(g, k.rows, k.r0 + r, s)] = cscale(v, k.gsc);
+        }
+    }
+    gen_pack_slot0(ctx, a, k, RC, XF, X0, XS);
 }
 
 }  // namespace hyenand

@@ -359,6 +359,30 @@ int hyenand_generate_kernel_spectrum(const void* x, const hyenand_generator* gen
                                      void* stream);
 
 /*
+ * Forward with the input-dependent kernels generated in the same call (the
+ * explainer has the input-dependent parameters computed on the fly, nSubQ
+ * implementation, item on the input-dependent parameterisation overhead): the
+ * generator of hyenand_generate_kernel_spectrum writes every (b, c) spectrum
+ * into K_hat, then the forward chains read them, all on `stream`.  Results
+ * equal hyenand_generate_kernel_spectrum followed by
+ * hyenand_fftconv_fwd_per_sample, bit for bit.
+ * x, y, phi_alpha, phi_beta, dtype: as hyenand_fftconv_fwd.  gen: as
+ * hyenand_generate_kernel_spectrum (same shapes).  K_hat: device
+ * [B][C] spectra of hyenand_kernel_spectrum_bytes(B * C, d, dims) bytes,
+ * written (the per-sample backward takes it).  workspace: 256-byte aligned,
+ * at least hyenand_fftconv_fwd_generated_workspace_min_bytes (the generator's
+ * region, then the forward's); hyenand_fftconv_fwd_generated_workspace_bytes
+ * is the recommended size.  Contents unspecified on entry and exit.
+ * Errors as hyenand_generate_kernel_spectrum and hyenand_fftconv_fwd.
+ */
+size_t hyenand_fftconv_fwd_generated_workspace_bytes(int B, int C, int d, const int64_t* dims, int dtype);
+size_t hyenand_fftconv_fwd_generated_workspace_min_bytes(int B, int C, int d, const int64_t* dims, int dtype);
+int hyenand_fftconv_fwd_generated(const void* x, const float* phi_alpha, const float* phi_beta,
+                                  const hyenand_generator* gen, void* K_hat, void* y, int B, int C, int d,
+                                  const int64_t* dims, int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * Allocation-free forward, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): hyenand_fftconv_fwd with its workspace in a static device array

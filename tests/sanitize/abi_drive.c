@@ -253,6 +253,43 @@ static void run_generator(const shape_t* s, int R, int D)
     stub_set_launch_status(1);
     EXPECT(hyenand_generate_kernel_spectrum(x, &g, Kh, B, C, d, dims, dt, w, wb, NULL), HYENAND_ERR_HIP);
     stub_set_launch_status(0);
+
+    /* The generated forward with the recommended and the minimum workspace
+     * (one channel per chunk), its argument checks, and a failing launch. */
+    {
+        const size_t gr = hyenand_fftconv_fwd_generated_workspace_bytes(B, C, d, dims, dt);
+        const size_t gm = hyenand_fftconv_fwd_generated_workspace_min_bytes(B, C, d, dims, dt);
+        CHECK(gm >= wb && gr >= gm);
+        unsigned char* graw = buf(gr + 512);
+        unsigned char* gws = graw + (256 - (uintptr_t)graw % 256);
+        void* y = buf(es * B * C * vox);
+        float* al = buf(4 * (size_t)C);
+        EXPECT(hyenand_fftconv_fwd_generated(x, al, al, &g, Kh, y, B, C, d, dims, dt, gws, gr, NULL), HYENAND_OK);
+        EXPECT(hyenand_fftconv_fwd_generated(x, al, al, &g, Kh, y, B, C, d, dims, dt, gws, gm, NULL), HYENAND_OK);
+        stub_set_launch_status(1);
+        EXPECT(hyenand_fftconv_fwd_generated(x, al, al, &g, Kh, y, B, C, d, dims, dt, gws, gm, NULL), HYENAND_ERR_HIP);
+        stub_set_launch_status(0);
+        const long before = stub_launch_calls();
+        EXPECT(hyenand_fftconv_fwd_generated(x, al, al, &g, Kh, y, B, C, d, dims, dt, gws, wb - 8, NULL),
+               HYENAND_ERR_WORKSPACE);
+        if (gm > wb)
+            EXPECT(hyenand_fftconv_fwd_generated(x, al, al, &g, Kh, y, B, C, d, dims, dt, gws, gm - 8, NULL),
+                   HYENAND_ERR_WORKSPACE);
+        EXPECT(hyenand_fftconv_fwd_generated(x, NULL, al, &g, Kh, y, B, C, d, dims, dt, gws, gm, NULL),
+               HYENAND_ERR_INVALID_ARG);
+        EXPECT(hyenand_fftconv_fwd_generated(x, al, al, &g, Kh, NULL, B, C, d, dims, dt, gws, gm, NULL),
+               HYENAND_ERR_INVALID_ARG);
+        EXPECT(hyenand_fftconv_fwd_generated(x, al, al, NULL, Kh, y, B, C, d, dims, dt, gws, gm, NULL),
+               HYENAND_ERR_INVALID_ARG);
+        EXPECT(hyenand_fftconv_fwd_generated(x, al, al, &g, Kh, y, B, C, d, dims, dt, gws + 64, gm, NULL),
+               HYENAND_ERR_INVALID_ARG);
+        EXPECT(hyenand_fftconv_fwd_generated(NULL, NULL, NULL, &g, NULL, NULL, 0, C, d, dims, dt, NULL, 0, NULL),
+               HYENAND_OK);
+        CHECK(stub_launch_calls() == before);
+        free(graw);
+        free(y);
+        free(al);
+    }
     free((void*)g.Wreg); free((void*)g.breg); free((void*)g.q); free((void*)g.Wgam); free((void*)g.Wbet);
     free((void*)g.W1); free((void*)g.b1); free((void*)g.W2); free((void*)g.b2); free((void*)g.sigma);
     free(x); free(Kh); free(raw);

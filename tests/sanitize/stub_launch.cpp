@@ -154,7 +154,9 @@ hipError_t launch_spectrum(const ConvArgs& a, hipStream_t)
     return g_status;
 }
 
-hipError_t launch_generate_spectrum(const GenArgs& a, hipStream_t)
+namespace {
+
+hipError_t generate_prep(const GenArgs& a)
 {
     ++g_calls;
     const Geom& g = a.g;
@@ -177,7 +179,14 @@ hipError_t launch_generate_spectrum(const GenArgs& a, hipStream_t)
     touch_rw(a.partial, 8LL * pairs * a.splits);
     touch_rw(a.coef, 4LL * pairs * kGenCoef);
     const int Ns[3] = {g.N_out, g.N_mid, g.N_in};
-    Region r[5] = {{(const char*)a.partial, 8LL * pairs * a.splits}, {(const char*)a.coef, 4LL * pairs * kGenCoef}};
+    const long long nbt = g.S >= 16 ? 4LL * a.C * (g.S / 16) * kGenKS * 64 : 0;
+    if ((nbt > 0) != (a.btab != nullptr)) {
+        std::fprintf(stderr, "stub: operand table present %d for S = %d\n", a.btab != nullptr, g.S);
+        ++g_failures;
+    }
+    if (a.btab) touch_rw(a.btab, nbt);
+    Region r[6] = {{(const char*)a.partial, 8LL * pairs * a.splits}, {(const char*)a.coef, 4LL * pairs * kGenCoef}};
+    r[5] = {(const char*)a.btab, nbt};
     for (int ax = 0; ax < 3; ++ax) {
         const long long n = Ns[ax] > 1 ? 8LL * a.C * kGenLines * Ns[ax] : 0;
         if ((Ns[ax] > 1) != (a.basis[ax] != nullptr)) {
@@ -187,9 +196,33 @@ hipError_t launch_generate_spectrum(const GenArgs& a, hipStream_t)
         if (a.basis[ax]) touch_rw(a.basis[ax], n);
         r[2 + ax] = {(const char*)a.basis[ax], n};
     }
-    disjoint(r, 5);
-    touch_rw(a.khat, 8LL * pairs * g.ksz);
+    disjoint(r, 6);
     return g_status;
+}
+
+hipError_t generate_pairs(const GenArgs& a)
+{
+    if (a.c0 < 0 || a.nch < 0 || a.c0 + a.nch > a.C) {
+        std::fprintf(stderr, "stub: channel range [%d, %d) of %d\n", a.c0, a.c0 + a.nch, a.C);
+        ++g_failures;
+        return g_status;
+    }
+    for (int b = 0; b < a.B; ++b)
+        touch_rw(a.khat + ((long long)b * a.C + a.c0) * a.g.ksz, 8LL * a.nch * a.g.ksz);
+    return g_status;
+}
+
+}  // namespace
+
+hipError_t launch_generate_spectrum(const GenArgs& a, hipStream_t)
+{
+    const hipError_t e = generate_prep(a);
+    if (e != hipSuccess) return e;
+    if (a.c0 != 0 || a.nch != a.C) {
+        std::fprintf(stderr, "stub: spectra of channels [%d, %d) of %d\n", a.c0, a.c0 + a.nch, a.C);
+        ++g_failures;
+    }
+    return generate_pairs(a);
 }
 
 }  // namespace hyenand

@@ -104,3 +104,65 @@ def test_kernels_follow_the_input(H):
     kh = H.generate_kernel_spectrum(x.cuda(), _dev_gen(gen)).reshape(B, C, -1)
     assert torch.equal(kh[2], kh[0])
     assert (kh[1] - kh[0]).abs().max() > 1e-3 * kh[0].abs().max()
+
+
+@pytest.mark.parametrize("dims,B,C,dtype,chunked", [((256,), 3, 2, "f32", False), ((32, 32), 2, 3, "f32", False),
+                                                    ((128, 64), 2, 5, "bf16", False), ((128, 64), 2, 5, "f32", True),
+                                                    ((16, 32, 8), 2, 3, "f32", True),
+                                                    ((64, 64, 64), 1, 4, "bf16", False)],
+                         ids=lambda v: str(v))
+def test_generated_forward_equals_generate_then_forward(H, dims, B, C, dtype, chunked):
+    """hyenand_fftconv_fwd_generated gives the spectra and outputs of the two
+    calls in sequence, bit for bit, also with the minimum workspace (every
+    channel its own chunk)."""
+    x, gen, a, b = _case(dims, B, C, dtype, 120 + sum(dims))
+    dev = torch.device("cuda:0")
+    xd, al, be, gd = x.to(dev), torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev), _dev_gen(gen)
+    kh_ref = H.generate_kernel_spectrum(xd, gd)
+    y_ref = H.fftconv_fwd_per_sample(xd, al, be, kh_ref)
+    ws = None
+    if chunked:
+        ws = torch.empty(H.generated_workspace_bytes(B, C, dims, xd.dtype, minimum=True), dtype=torch.uint8,
+                         device=dev)
+    y, kh = H.fftconv_fwd_generated(xd, al, be, gd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(kh, kh_ref)
+    assert torch.equal(y, y_ref)
+    # Called again on another stream of the caller's, ordered after x is written there.
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x2 = (xd.float() * 0.5).to(xd.dtype)
+        y2, kh2 = H.fftconv_fwd_generated(x2, al, be, gd, workspace=ws)
+    s.synchronize()
+    kh2_ref = H.generate_kernel_spectrum(x2, gd)
+    assert torch.equal(kh2, kh2_ref)
+    assert torch.equal(y2, H.fftconv_fwd_per_sample(x2, al, be, kh2_ref))
+
+
+def test_generated_forward_in_a_graph(H):
+    """The generated forward captured into a HIP graph and replayed with new
+    inputs, eager work and synchronisations between the replays: every replay
+    matches the eager calls."""
+    dims, B, C = (64, 32), 2, 3
+    x, gen, a, b = _case(dims, B, C, "f32", 140)
+    dev = torch.device("cuda:0")
+    xd, al, be, gd = x.to(dev), torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev), _dev_gen(gen)
+    ws = torch.empty(H.generated_workspace_bytes(B, C, dims, xd.dtype), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(xd)
+    kh = torch.empty(H.spectrum_bytes(B * C, dims) // 8, dtype=torch.complex64, device=dev).view(B * C, -1)
+    H.fftconv_fwd_generated(xd, al, be, gd, K_hat=kh, y=y, workspace=ws)  # loads the kernels' code
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        H.fftconv_fwd_generated(xd, al, be, gd, K_hat=kh, y=y, workspace=ws)
+    for k in range(3):
+        xd.copy_(torch.from_numpy(x.numpy() * (1.0 + 0.25 * k) + 0.1 * k).to(dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        kh_ref = H.generate_kernel_spectrum(xd, gd)
+        y_ref = H.fftconv_fwd_per_sample(xd, al, be, kh_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(kh, kh_ref), f"replay {k}"
+        assert torch.equal(y, y_ref), f"replay {k}"
