@@ -190,13 +190,63 @@ KERNEL_LABEL = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_co
                 "lng_col_inv_bwd": "k_lng_col_inv", "lng_col_dk": "k_lng_col_dk", "fused2d": "k_fused2d"}
 
 
+# The sources of the zero-padded forward's kernels and of its planning (the
+# traffic record stays valid while none of them changes).
+FWD_SOURCES = ("api.cpp", "conv_bodies.h", "fft_core.h", "fused2d.h", "k_fused2d_bf16.hip", "k_fused2d_f32.hip",
+               "k_fwd.hip", "k_spec.hip", "kernels_dev.h", "launch.h", "plan.h")
+
+
 def _src_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dimensional_fft_long_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".h", ".hip", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in FWD_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def write_traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mb, workload, out_json):
+    """The HBM traffic record that `roofline.traffic` reads: FETCH_SIZE and
+    WRITE_SIZE per dispatch (KiB, from two rocprofv3 --pmc runs of the bench
+    on `workload`), each scaled by what the same counter reads for a
+    device-to-device copy of copy_mb MiB (two more runs of --copy-probe-mb),
+    averaged per kernel."""
+    import csv
+    import re
+    import statistics
+
+    import dimensional_fft_long_amd as H
+    import synth
+    import torch
+
+    def per_kernel(path):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            m = re.search(r"::(k_\w+)<", r["Kernel_Name"]) or re.search(r"(copyBuffer)", r["Kernel_Name"])
+            if m:
+                out.setdefault(m.group(1), []).append(float(r["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in out.items()}
+
+    n = copy_mb << 20
+    f_scale = n / (per_kernel(copy_fetch_csv)["copyBuffer"] * 1024)
+    w_scale = n / (per_kernel(copy_write_csv)["copyBuffer"] * 1024)
+    fe, wr = per_kernel(fetch_csv), per_kernel(write_csv)
+    wl = {w.name: w for w in synth.WORKLOADS}[workload]
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    per_ch = H.workspace_bytes(wl.B, wl.C, wl.dims, dt, minimum=True)
+    nch = wl.C
+    if per_ch:
+        nch = min(wl.C, H.workspace_bytes(wl.B, wl.C, wl.dims, dt) // per_ch)
+        nch = -(-wl.C // -(-wl.C // nch))
+    kernels = {}
+    for k in sorted(set(fe) & set(wr)):
+        rd, wt = fe[k] * 1024 * f_scale, wr[k] * 1024 * w_scale
+        kernels[k] = {"fetch_kib": fe[k], "write_kib": wr[k], "read_bytes": rd, "write_bytes": wt,
+                      "traffic_bytes_per_launch": rd + wt}
+    rec = {"source_hash": _src_hash(), "workload": workload, "chunk_channels": nch, "copy_probe_bytes": n,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
 
 
 def _traffic_from_profile(kernel_name, workload, chunk_channels):
@@ -598,7 +648,17 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=None,
                     help="only run 5 device-to-device copies of this many MiB (a kernel of known HBM "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--traffic-record", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT_JSON"),
+                    help="write the HBM traffic record of --workload from rocprofv3 counter_collection CSVs "
+                         "(the bench's FETCH_SIZE and WRITE_SIZE runs and the --copy-probe-mb runs, "
+                         "copy size --copy-probe-mb, default 256) and exit (no GPU work)")
     args = ap.parse_args()
+    if args.traffic_record:
+        fc, wc, cfc, cwc, out_json = args.traffic_record
+        rec = write_traffic_record(fc, wc, cfc, cwc, args.copy_probe_mb or 256, args.workload, out_json)
+        print(json.dumps({k: v for k, v in rec.items() if k != "kernels"}))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
               "channel with no communication, but no multi-GPU run is part of it.", file=sys.stderr)
