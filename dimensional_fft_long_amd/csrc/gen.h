@@ -39,7 +39,7 @@ namespace hyenand {
 constexpr int kGenHidden = 16;
 constexpr int kGenLines = kGenHidden + 1;       // the 16 units' axis sequences and the window's
 constexpr int kGenCoef = kGenHidden + 1;        // v_u (16) and e per pair
-constexpr int kGenRows = 64;                    // spectrum rows per gen_spectrum workgroup
+constexpr int kGenRows = 128;                   // spectrum rows per gen_spectrum workgroup
 constexpr int kGenNT = 256;
 // Workgroups per pair of the means pass: up to 256, one per 16 elements per thread.
 inline int gen_splits(long long vox)
@@ -275,7 +275,7 @@ __device__ __forceinline__ float2 gen_in_factor(const GenArgs& a, int c, int f, 
     const int N = a.g.N_in;
     if (f < kGenHidden) return gen_axis(a, 2, c, f, s, N);
     if (f < 2 * kGenHidden) {
-        const float2 v = gen_axis(a, 2, c, f - kGenHidden, (N - s) % N, N);
+        const float2 v = gen_axis(a, 2, c, f - kGenHidden, (N - s) & (N - 1), N);
         return make_float2(-v.x, v.y);
     }
     return f == 2 * kGenHidden ? gen_axis(a, 2, c, kGenHidden, s, N) : make_float2(0.f, 0.f);
@@ -285,31 +285,41 @@ __device__ __forceinline__ float2 gen_in_factor(const GenArgs& a, int c, int f, 
 // RC[r][16 + u] = (v_u / 2i) conj(A_out A_mid at (-k_out, -k_mid)),
 // RC[r][32] = e W_out W_mid; RC[r][33] = 0.
 // Also the innermost axis' factors at the Nyquist bin k_in = S into XF[33]
-// (the same for every row of the block).  The fill loop has a fixed trip
-// count so that its loads are issued together.
+// (the same for every row of the block).  TPR threads per row, each taking
+// the terms f = q, q + TPR, ... (the row's indices computed once; every
+// length is a power of two, so indices wrap by masks).
 template <class Ctx>
 __device__ __forceinline__ void gen_row_factors(const Ctx& ctx, const GenArgs& a, const GenBlock& k, float2* RC,
                                                 float2* XF)
 {
+    constexpr int TPR = kGenNT / kGenRows;
+    static_assert(TPR * kGenRows == kGenNT, "whole threads per row");
     const Geom& g = a.g;
+    const int tid = ctx.tid();
+    if (tid < kGenTerms) XF[tid] = gen_in_factor(a, k.c, tid, g.S);
+    const int r = tid / TPR, q = tid % TPR;
+    if (r >= k.nr) return;
+    const int row = k.r0 + r, lm = 31 - __builtin_clz(g.N_mid);
+    const int ko = row >> lm, km = row & (g.N_mid - 1);
+    const int kom = (g.N_out - ko) & (g.N_out - 1), kmm = (g.N_mid - km) & (g.N_mid - 1);
     const float* cf = a.coef + (long long)k.p * kGenCoef;
-    if (ctx.tid() < kGenTerms) XF[ctx.tid()] = gen_in_factor(a, k.c, ctx.tid(), g.S);
-    constexpr int kIters = (kGenRows * kGenRC + kGenNT - 1) / kGenNT;
+    // Axis sequences of channel c: A_ax[u][k] at base_ax + u * N_ax + k (absent axes: 1).
+    const float2* bo = g.N_out > 1 ? a.basis[0] + (long long)k.c * kGenLines * g.N_out : nullptr;
+    const float2* bm = g.N_mid > 1 ? a.basis[1] + (long long)k.c * kGenLines * g.N_mid : nullptr;
+    auto axis = [](const float2* b, int N, int u, int kk) {
+        return b ? b[u * N + kk] : make_float2(1.f, 0.f);
+    };
 #pragma unroll
-    for (int m = 0; m < kIters; ++m) {
-        const int i = ctx.tid() + m * kGenNT;
-        if (i >= k.nr * kGenRC) break;
-        const int r = i / kGenRC, f = i % kGenRC, row = k.r0 + r;
-        const int ko = row / g.N_mid, km = row % g.N_mid;
+    for (int j = 0; j < (kGenRC + TPR - 1) / TPR; ++j) {
+        const int f = q + TPR * j;
+        if (f >= kGenRC) break;
         float2 v = make_float2(0.f, 0.f);
         if (f == 2 * kGenHidden) {
-            v = cscale(cmul(gen_axis(a, 0, k.c, kGenHidden, ko, g.N_out), gen_axis(a, 1, k.c, kGenHidden, km, g.N_mid)),
-                       cf[kGenHidden]);
+            v = cscale(cmul(axis(bo, g.N_out, kGenHidden, ko), axis(bm, g.N_mid, kGenHidden, km)), cf[kGenHidden]);
         } else if (f < 2 * kGenHidden) {
-            const int u = f % kGenHidden;
+            const int u = f & (kGenHidden - 1);
             const bool mir = f >= kGenHidden;
-            const int kom = mir ? (g.N_out - ko) % g.N_out : ko, kmm = mir ? (g.N_mid - km) % g.N_mid : km;
-            float2 pr = cmul(gen_axis(a, 0, k.c, u, kom, g.N_out), gen_axis(a, 1, k.c, u, kmm, g.N_mid));
+            float2 pr = cmul(axis(bo, g.N_out, u, mir ? kom : ko), axis(bm, g.N_mid, u, mir ? kmm : km));
             if (mir) pr = cconj(pr);
             const float h = 0.5f * cf[u];  // v / 2i = -i v / 2
             v = make_float2(h * pr.y, -h * pr.x);
@@ -377,8 +387,9 @@ __device__ __forceinline__ void gen_spectrum_body(const Ctx& ctx, int bid, const
     gen_pack_slot0(ctx, a, k, RC, XF, X0, XS);
 }
 
-// Matrix-core engine (S >= 16, kGenRows = 64: wave w owns rows 16 w .. 16 w + 15
-// of the block).  As real products over K = 68 (term f, part t at k = 2 f + t):
+// Matrix-core engine (S >= 16; wave w owns the 16-row tiles w, w + 4, ... of
+// the block, RT = kGenRows / 64 of them).  As real products over K = 68 (term
+// f, part t at k = 2 f + t):
 //   Re Khat[r, s] = sum_k Are[r, k] B[k, s],  Im Khat[r, s] = sum_k Aim[r, k] B[k, s],
 //   B[2f, s] = Re IN[f, s],  B[2f + 1, s] = Im IN[f, s],
 //   Are[r, 2f] = Re RC[r, f],  Are[r, 2f + 1] = -Im RC[r, f],
@@ -410,21 +421,26 @@ template <class Ctx>
 __device__ __forceinline__ void gen_spectrum_mfma_body(const Ctx& ctx, int bid, const GenArgs& a, float2* RC,
                                                        float2* XF, float2* X0, float2* XS)
 {
-    static_assert(kGenRows == 64 && kGenNT == 256, "four waves of 16 rows");
+    constexpr int RT = kGenRows / 64;
+    static_assert(RT * 64 == kGenRows && kGenNT == 256, "four waves of 16-row tiles");
     const Geom& g = a.g;
     const GenBlock k = gen_block(a, bid);
     const int tid = ctx.tid(), lane = tid % 64, w = tid / 64;
     gen_row_factors(ctx, a, k, RC, XF);
     ctx.sync();
     constexpr int KS = kGenKS;
-    const int ra = 16 * w + lane % 16, kq = lane / 16;
-    float are[KS], aim[KS];
+    const int kq = lane / 16;
+    float are[RT][KS], aim[RT][KS];
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-        const int kk = 4 * j + kq, f = kk / 2;
-        const float2 v = ra < k.nr ? RC[ra * kGenRC + f] : make_float2(0.f, 0.f);
-        are[j] = (kk & 1) ? -v.y : v.x;
-        aim[j] = (kk & 1) ? v.x : v.y;
+    for (int t = 0; t < RT; ++t) {
+        const int ra = 64 * t + 16 * w + lane % 16;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int kk = 4 * j + kq, f = kk / 2;
+            const float2 v = ra < k.nr ? RC[ra * kGenRC + f] : make_float2(0.f, 0.f);
+            are[t][j] = (kk & 1) ? -v.y : v.x;
+            aim[t][j] = (kk & 1) ? v.x : v.y;
+        }
     }
     const int S = g.S, nst = S / 16;
     const float* bt = a.btab + (long long)k.c * nst * KS * 64 + lane;
@@ -440,19 +456,27 @@ __device__ __forceinline__ void gen_spectrum_mfma_body(const Ctx& ctx, int bid, 
             for (int j = 0; j < KS; ++j) bn[j] = bt[((st + 1) * KS + j) * 64];
         }
         const int s = 16 * st + lane % 16;
-        gen_f4 dre = {0.f, 0.f, 0.f, 0.f}, dim = {0.f, 0.f, 0.f, 0.f};
+        gen_f4 dre[RT], dim[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) dre[t] = dim[t] = gen_f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
-            dre = __builtin_amdgcn_mfma_f32_16x16x4f32(are[j], b[j], dre, 0, 0, 0);
-            dim = __builtin_amdgcn_mfma_f32_16x16x4f32(aim[j], b[j], dim, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                dre[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(are[t][j], b[j], dre[t], 0, 0, 0);
+                dim[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aim[t][j], b[j], dim[t], 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * kq + i;
-            if (r >= k.nr) continue;
-            const float2 v = make_float2(dre[i], dim[i]);
-            if (s == 0) X0[r] = v;
-            else a.khat[k.kbase + tm_index(g, k.rows, k.r0 + r, s)] = cscale(v, k.gsc);
+        for (int t = 0; t < RT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 64 * t + 16 * w + 4 * kq + i;
+                if (r >= k.nr) continue;
+                const float2 v = make_float2(dre[t][i], dim[t][i]);
+                if (s == 0) X0[r] = v;
+                else a.khat[k.kbase + tm_index(g, k.rows, k.r0 + r, s)] = cscale(v, k.gsc);
+            }
         }
     }
     gen_pack_slot0(ctx, a, k, RC, XF, X0, XS);
