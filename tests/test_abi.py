@@ -331,3 +331,66 @@ def test_fused_shapes_take_one_launch_and_no_workspace(H):
     # the backward and the circular mode keep their multi-pass kernels
     assert H.bwd_workspace_bytes(2, 3, (32, 32), minimum=True) > 0
     assert H.circ_workspace_bytes(2, 3, (32, 32), minimum=True) > 0
+
+
+def _gen_struct(H, R=4, D=8, p=FAKE):
+    return H._Generator(R, D, *([p.value] * 10), 10.0)
+
+
+def test_generator_sizes_and_rejects(H):
+    """The generator's entry points: workspace sizes, and every argument check
+    returns before a launch (FAKE pointers are never dereferenced)."""
+    lib = H.get_lib()
+    d2 = _dims(32, 64)
+    ws = H.generate_workspace_bytes(2, 3, (32, 64))
+    assert ws > 0 and ws % 256 == 0
+    assert lib.hyenand_generate_workspace_bytes(2, 0, 2, d2) == 0
+    assert lib.hyenand_generate_workspace_bytes(1, 1, 1, _dims(4096)) == 0  # long 1-D: not generated
+    g = _gen_struct(H)
+    call = lambda gen=ctypes.byref(g), x=FAKE, k=FAKE, B=2, C=3, d=2, dd=d2, dt=0, w=FAKE, wb=ws: \
+        lib.hyenand_generate_kernel_spectrum(x, gen, k, B, C, d, dd, dt, w, wb, None)
+    assert call(gen=None) == 1
+    assert call(x=None) == 1
+    assert call(k=None) == 1
+    assert call(x=MISALIGNED) == 1
+    assert call(dt=5) == 1
+    assert call(B=-1) == 1
+    assert call(C=8193) == 1                          # the sample's means live in LDS
+    assert call(d=4) == 2
+    assert call(d=1, dd=_dims(4096)) == 2            # the long 1-D path has no generator
+    assert call(dd=_dims(32, 48)) == 2               # not a power of two
+    assert call(w=None) == 3
+    assert call(wb=ws - 1) == 3
+    assert call(w=ctypes.c_void_p(0x10000 + 64)) == 1  # the workspace must be 256-byte aligned
+    assert call(x=None, k=None, B=0) == 0
+    for R, D in ((0, 8), (65, 8), (4, 0), (4, 65)):
+        bad = _gen_struct(H, R, D)
+        assert call(gen=ctypes.byref(bad)) == 1
+    nulls = _gen_struct(H, p=ctypes.c_void_p(0))
+    assert call(gen=ctypes.byref(nulls)) == 1
+    mis = _gen_struct(H, p=MISALIGNED)
+    assert call(gen=ctypes.byref(mis)) == 1
+
+
+def test_generated_forward_sizes_and_rejects(H):
+    lib = H.get_lib()
+    dims = (32, 256)                                   # a multi-pass shape: the forward needs its workspace
+    dd = _dims(*dims)
+    gw = H.generate_workspace_bytes(2, 3, dims)
+    rec = H.generated_workspace_bytes(2, 3, dims)
+    mn = H.generated_workspace_bytes(2, 3, dims, minimum=True)
+    fmin = H.workspace_bytes(2, 3, dims, minimum=True)
+    assert mn == gw + fmin and rec >= mn
+    # The on-chip 2-D forward needs no workspace of its own.
+    assert H.generated_workspace_bytes(2, 3, (32, 32)) == H.generate_workspace_bytes(2, 3, (32, 32))
+    g = _gen_struct(H)
+    call = lambda gen=ctypes.byref(g), a=FAKE, y=FAKE, B=2, C=3, w=FAKE, wb=rec: \
+        lib.hyenand_fftconv_fwd_generated(FAKE, a, FAKE, gen, FAKE, y, B, C, 2, dd, 0, w, wb, None)
+    assert call(gen=None) == 1
+    assert call(a=None) == 1
+    assert call(y=None) == 1
+    assert call(y=MISALIGNED) == 1
+    assert call(w=None) == 3
+    assert call(wb=gw - 8) == 3                       # not even the generator's region
+    assert call(wb=mn - 8) == 3                       # the generator's region but not one forward chunk
+    assert call(B=0, y=None) == 0

@@ -166,3 +166,32 @@ def test_generated_forward_in_a_graph(H):
         torch.cuda.synchronize()
         assert torch.equal(kh, kh_ref), f"replay {k}"
         assert torch.equal(y, y_ref), f"replay {k}"
+
+
+@pytest.mark.parametrize("dims,B,C,R,D,dtype", [((2,), 1, 1, 1, 1, "f32"), ((4, 2), 2, 3, 64, 64, "f32"),
+                                                ((2, 2, 2), 1, 2, 4, 8, "bf16"), ((1024,), 2, 3, 2, 3, "bf16"),
+                                                ((16, 8, 32), 1, 5, 8, 2, "f32"), ((8, 64), 3, 1, 3, 5, "bf16")],
+                         ids=lambda v: str(v))
+def test_generator_extremes(H, dims, B, C, R, D, dtype):
+    """The smallest grids (the VALU engine, S < 16), the largest register
+    count and control width, single channels, odd channel counts and bf16
+    inputs (the oracle reads the same bf16-rounded x)."""
+    rng = np.random.default_rng(300 + sum(dims) + R)
+    x = rng.standard_normal((B, C) + tuple(dims)).astype(np.float32)
+    x += (rng.uniform(-1, 1, (B, C)) * 2).astype(np.float32).reshape((B, C) + (1,) * len(dims))
+    xt = torch.from_numpy(x)
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    gen = synth.draw_generator(dims, C, 400 + R, R=R, D=D)
+    kh = H.generate_kernel_spectrum(xt.cuda(), _dev_gen(gen)).cpu().numpy()
+    K = oracle.generate_kernels(xt.float().numpy(), gen)
+    full = oracle.kernel_spectrum(K.reshape((B * C,) + K.shape[2:]).astype(np.float32), dims)
+    main, dblk, (No, Nm, Ni) = _layout_to_full(H, kh, dims, B * C)
+    full = full.reshape(B * C, No, Nm, Ni)
+    S = Ni // 2
+    g = 1.0 / (2 * No * Nm * Ni)
+    scale = np.abs(full).max() * g
+    assert np.all(np.isfinite(kh))
+    assert np.abs(main[..., 1:] - g * full[..., 1:S]).max() <= 1e-4 * scale
+    assert np.abs(main[..., 0] - g * (full[..., 0] + full[..., S]) / 2).max() <= 1e-4 * scale
+    assert np.abs(dblk - g * (full[..., 0] - full[..., S]) / 2).max() <= 1e-4 * scale
