@@ -496,8 +496,13 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
 
     # Per-kernel durations: the same `steps` calls again through the traced
     # entry point, which records HIP events on the launch stream between kernels.
+    # The traced calls are enqueued behind `steps` plain calls, with no host
+    # synchronisation between: the GPU stays loaded (at its steady clock; an
+    # idle gap before them, or a spin kernel, measured 10-15% slower kernels)
+    # while the host submits them.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
+    for _ in range(steps):
+        call()
     for k in range(steps):
         traced(evs[k])
     torch.cuda.synchronize()
@@ -506,6 +511,8 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
     # two markers with nothing in between, then taken off each kernel's.
     mk = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     st = torch.cuda.current_stream()
+    for _ in range(steps):
+        call()
     for k in range(steps):
         mk[2 * k].record(st)
         mk[2 * k + 1].record(st)
