@@ -518,11 +518,18 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     auto at = [](auto* p, long long q_elems, unsigned bytes) { return add_bytes(p + q_elems, bytes); };
     using P0 = PassRegs<L, R0, NL, NT>;
     using PL = PassRegs<L, RL, NL, NT>;
-    auto load_cols = [&](const OutView& v, P0& s) {
+    // FULL (wave-uniform): every line of the tile lies inside the grid (the
+    // tile's slots k0 .. k0 + TW - 1 are all below S), so the loads, products
+    // and stores need no per-lane guards; only edge tiles take the guarded code.
+    auto load_cols = [&]<bool FULL>(const OutView& v, P0& s) {
         pass_load_fn<L, R0, NL, NT, !CIRC>(ctx, [&](int j, int q, int l) -> float2 {
-            const bool ok = v.k0 + l % TW < g.S;
-            const float2 x = *at(v.base, q * PS, ok ? lane_bytes(v, j, l) : 0u);
-            return ok ? x : make_float2(0.f, 0.f);
+            if constexpr (FULL) {
+                return *at(v.base, q * PS, lane_bytes(v, j, l));
+            } else {
+                const bool ok = v.k0 + l % TW < g.S;
+                const float2 x = *at(v.base, q * PS, ok ? lane_bytes(v, j, l) : 0u);
+                return ok ? x : make_float2(0.f, 0.f);
+            }
         }, s);
     };
     // Kernel spectrum values for the positions this thread multiplies (the
@@ -530,14 +537,24 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     // whose k_in is not 0 (the k_in = 0 lines take the mirror product).
     float2 kv[PL::PER][RL];
     bool kok[PL::PER];
-    auto load_kv = [&](const OutView& v) {
+    auto load_kv = [&]<bool FULL>(const OutView& v) {
 #pragma unroll
         for (int i = 0; i < PL::PER; ++i) {
             const int gi = tid + i * NT, l = gi % NL, j = gi / NL;
-            kok[i] = bf_valid<PL::NB, NT>(gi) && v.k0 + l % TW < g.S && v.k0 + l % TW != 0;
-            const unsigned lb = kok[i] ? lane_bytes(v, j, l) : 8u;
+            kok[i] = bf_valid<PL::NB, NT>(gi) && (FULL || v.k0 + l % TW < g.S) && v.k0 + l % TW != 0;
+            const unsigned lb = (FULL && bf_valid<PL::NB, NT>(gi)) || kok[i] ? lane_bytes(v, j, l) : 8u;
 #pragma unroll
             for (int r = 0; r < RL; ++r) kv[i][r] = *at(v.kt, (long long)r * (L / RL) * PS, lb);
+        }
+    };
+    auto full_tile = [&](const OutView& v) { return v.k0 + TW <= g.S; };
+    auto load_item = [&](const OutView& v, P0& s) {
+        if (full_tile(v)) {
+            load_cols.template operator()<true>(v, s);
+            load_kv.template operator()<true>(v);
+        } else {
+            load_cols.template operator()<false>(v, s);
+            load_kv.template operator()<false>(v);
         }
     };
     // One item: forward from the loaded columns, product, inverse and store.
@@ -556,24 +573,39 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
             });
             ctx.sync();
         }
-        // Lines outside the grid and the k_in = 0 lines (final already) keep their values.
+        // Lines outside the grid and the k_in = 0 lines (final already) keep
+        // their values; tiles with neither multiply every line.
+        const bool full = full_tile(v);
+        if (full && v.o.t != 0 && (PL::NB % NT) == 0) {
 #pragma unroll
-        for (int i = 0; i < PL::PER; ++i) {
+            for (int i = 0; i < PL::PER; ++i) {
 #pragma unroll
-            for (int r = 0; r < RL; ++r) {
-                const float2 m = cmul(t.v[i][r], kv[i][r]);
-                t.v[i][r] = kok[i] ? m : t.v[i][r];
+                for (int r = 0; r < RL; ++r) t.v[i][r] = cmul(t.v[i][r], kv[i][r]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PL::PER; ++i) {
+#pragma unroll
+                for (int r = 0; r < RL; ++r) {
+                    const float2 m = cmul(t.v[i][r], kv[i][r]);
+                    t.v[i][r] = kok[i] ? m : t.v[i][r];
+                }
             }
         }
-        inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
-            if (v.k0 + l % TW < g.S) *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
-        });
+        if (full) {
+            inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+                *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
+            });
+        } else {
+            inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+                if (v.k0 + l % TW < g.S) *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
+            });
+        }
     };
     OutView v = out_view<NR, TW>(a, bid);
     const auto tw_staged = ctx.stage_load();  // oldest loads: waited for first
     P0 s;
-    load_cols(v, s);
-    load_kv(v);
+    load_item(v, s);
     ctx.stage_store(tw_staged);
     if constexpr (!kLoop) {
         run_item(v, s);
@@ -584,8 +616,7 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
             if (nxt >= W) break;
             item = nxt;
             v = out_view<NR, TW>(a, nxt);
-            load_cols(v, s);
-            load_kv(v);
+            load_item(v, s);
             ctx.sync();  // the inverse's last LDS reads are done: T is free
         }
     }
