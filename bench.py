@@ -667,7 +667,7 @@ def main():
         print(json.dumps({k: v for k, v in rec.items() if k != "kernels"}))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
               "channel with no communication, but no multi-GPU run is part of it.", file=sys.stderr)
         return 2
 

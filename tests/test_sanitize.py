@@ -57,7 +57,7 @@ def _gpu_visible() -> bool:
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANGXX)), reason="ROCm toolchain not found")
 @pytest.mark.skipif(_gpu_visible(), reason="the launcher stand-ins treat device pointers as host memory: "
-                                           "this build runs only where no GPU is visible")
+                                           "the sanitizer build runs only where no GPU is visible")
 def test_abi_host_code_under_sanitizers(tmp_path):
     inc = os.path.join(ROOT, "include")
     flags = ["-std=c++20", "-O1", "-g", "--offload-arch=gfx950", "-fPIC",
