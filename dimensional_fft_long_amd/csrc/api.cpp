@@ -500,6 +500,11 @@ int gen_setup(const void* x, const hyenand_generator* gen, void* K_hat, int B, i
     Geom g;
     if (!make_geom(d, dims, &g) || g.lng) return HYENAND_ERR_UNSUPPORTED;
     if (gen->R < 1 || gen->R > 64 || gen->D < 1 || gen->D > 64 || C > 8192) return HYENAND_ERR_INVALID_ARG;
+    // One-dimensional grids of the passes (the means pass: pairs x segments;
+    // the spectrum pass: pairs x blocks of rows) stay below 2^31 workgroups.
+    const long long pairs = (long long)B * C, rows = (long long)g.N_out * g.N_mid;
+    if (pairs * gen_splits(g.vox) >= (1LL << 31) || pairs * ((rows + kGenRows - 1) / kGenRows) >= (1LL << 31))
+        return HYENAND_ERR_UNSUPPORTED;
     if (B == 0 || C == 0) {
         *empty = true;
         return HYENAND_OK;

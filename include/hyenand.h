@@ -333,7 +333,8 @@ int hyenand_fftconv_bwd_per_sample_traced(const void* x, const float* phi_alpha,
  * of them in the layout of hyenand_kernel_spectrum on [B*C] kernels, ready for
  * hyenand_fftconv_fwd_per_sample / _bwd_per_sample.  All parameter arrays are
  * fp32 device pointers.  Zero-padded mode, d in {1, 2, 3}, every n in
- * [2, 1024] (not the long 1-D path: UNSUPPORTED); 1 <= R, D <= 64, C <= 8192.  Workspace:
+ * [2, 1024] (not the long 1-D path: UNSUPPORTED); 1 <= R, D <= 64, C <= 8192; B C
+ * (N_out N_mid / 128) below 2^31 (else UNSUPPORTED).  Workspace:
  * hyenand_generate_workspace_bytes (partial sums of the means, per-pair
  * coefficients and the channels' 1-D axis spectra).  Errors as
  * hyenand_fftconv_fwd.

@@ -394,3 +394,13 @@ def test_generated_forward_sizes_and_rejects(H):
     assert call(wb=gw - 8) == 3                       # not even the generator's region
     assert call(wb=mn - 8) == 3                       # the generator's region but not one forward chunk
     assert call(B=0, y=None) == 0
+
+
+def test_generator_rejects_grids_beyond_the_launch_limit(H):
+    """B C x (blocks of 128 spectrum rows) at 2^31 workgroups or more is refused
+    before anything is launched (3-D 1024^3: 32768 blocks per pair)."""
+    lib = H.get_lib()
+    g = _gen_struct(H)
+    d3 = _dims(1024, 1024, 1024)
+    assert lib.hyenand_generate_kernel_spectrum(FAKE, ctypes.byref(g), FAKE, 8, 8192, 3, d3, 0, FAKE, 1 << 40,
+                                                None) == 2
