@@ -557,9 +557,10 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
             load_kv.template operator()<false>(v);
         }
     };
-    // One item: forward from the loaded columns, product, inverse and store.
-    auto run_item = [&](const OutView& v, P0& s) {
-        auto t = fwd_from_regs<L, NL, NT, !CIRC>(ctx, T, s);
+    // One item: forward from the loaded columns, product, inverse and store
+    // (c: the context whose passes run the transforms).
+    auto run_item = [&](const auto& c, const OutView& v, P0& s) {
+        auto t = fwd_from_regs<L, NL, NT, !CIRC>(c, T, s);
         ctx.sync();  // every LDS read of the forward transform is done: T is free
         if (v.o.t == 0) {
             pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
@@ -593,11 +594,11 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
             }
         }
         if (full) {
-            inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+            inv_to_fn<L, NL, NT, !CIRC>(c, T, t, [&](int j, int q, int l, const float2& x) {
                 *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
             });
         } else {
-            inv_to_fn<L, NL, NT, !CIRC>(ctx, T, t, [&](int j, int q, int l, const float2& x) {
+            inv_to_fn<L, NL, NT, !CIRC>(c, T, t, [&](int j, int q, int l, const float2& x) {
                 if (v.k0 + l % TW < g.S) *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
             });
         }
@@ -607,12 +608,21 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     P0 s;
     load_item(v, s);
     ctx.stage_store(tw_staged);
-    if constexpr (!kLoop) {
-        run_item(v, s);
+    if constexpr (out_tw_regs(L, NR) > 0 && !kLoop) {
+        // The first twiddled pass's factors in registers for the forward and
+        // the (same-plan) inverse transform: one barrier after staging, then
+        // one LDS read per factor instead of one per factor and transform.
+        using Cache = TwCache<L, NL, NT, 1 + out_tw_regs(L, NR)>;
+        Cache twc;
+        ctx.sync();
+        twc.load(ctx, [&](int e) { return ctx.twl[e]; });
+        run_item(TwCachedCtx<Ctx, Cache>{ctx, &twc}, v, s);
+    } else if constexpr (!kLoop) {
+        run_item(ctx, v, s);
     } else {
         for (int item = bid;;) {
             const int nxt = item + nblk;
-            run_item(v, s);
+            run_item(ctx, v, s);
             if (nxt >= W) break;
             item = nxt;
             v = out_view<NR, TW>(a, nxt);

@@ -19,7 +19,9 @@
 // the thread index (tid()), the workgroup barrier (sync()), the LDS twiddle
 // tables (twl, reversed-plan tables at kRevBase; stage() fills them and must
 // precede a barrier that precedes the first transform pass with twiddles) and
-// the gate (gate()); the device context is in kernels_dev.h.
+// the gate (gate()); the device context is in kernels_dev.h.  A context
+// wrapped in TwCachedCtx also carries register copies of some passes'
+// twiddles (TwCache below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -371,19 +373,107 @@ __host__ __device__ __forceinline__ void pass_load_fn(const Ctx& ctx, const F& f
     }
 }
 
+// Twiddles of one pass for the butterflies a thread owns:
+// W_{NS R}^{(j mod NS) r}, r in [1, R).  When NT/NL is a multiple of NS the
+// butterflies g = t + i*NT of a thread share j mod NS and one set serves all
+// of them (U = 1); passes without twiddles (NS = 1) hold none.
+template <int L, int R, int NS, int NL, int NT>
+struct PassTw {
+    static constexpr int PER = PassRegs<L, R, NL, NT>::PER;
+    static constexpr bool kShared = NT % NL == 0 && (NT / NL) % NS == 0;
+    static constexpr int U = NS == 1 ? 0 : (kShared ? 1 : PER);
+    float2 w[U > 0 ? U : 1][R - 1];
+};
+
+// Register copies of the twiddles of passes [1, PEND) of the forward plan of
+// length L for NL lines on NT threads.  A kernel that runs several transforms
+// of one shape loads them once (TwCache::load) and hands them to the passes
+// through its context (TwCachedCtx); a pass takes the copy whose radix,
+// stride and shape match its own (a twiddle's value depends on nothing else:
+// the reversed plan of a symmetric radix sequence reuses every copy, an
+// inverse conjugates it), else it reads the LDS table.  Each copy costs
+// 2 (R-1) U registers per thread.
+template <int L, int NL, int NT, int PEND, int P = 1, bool END = (P >= PEND || P >= plan_passes(L))>
+struct TwCache {
+    static constexpr int R = pass_radix<L, false>(P), NS = pass_ns<L, false>(P);
+    PassTw<L, R, NS, NL, NT> here;
+    TwCache<L, NL, NT, PEND, P + 1> rest;
+    template <int R2, int NS2, int NL2, int NT2>
+    __host__ __device__ static constexpr bool has()
+    {
+        return (R2 == R && NS2 == NS && NL2 == NL && NT2 == NT) ||
+               TwCache<L, NL, NT, PEND, P + 1>::template has<R2, NS2, NL2, NT2>();
+    }
+    template <int R2, int NS2>
+    __host__ __device__ __forceinline__ const PassTw<L, R2, NS2, NL, NT>& get() const
+    {
+        if constexpr (R2 == R && NS2 == NS) return here;
+        else return rest.template get<R2, NS2>();
+    }
+    // rd(e): entry e of the context's tables, whose forward-plan tables come
+    // first (the LDS copy, once it is staged and a barrier has passed).
+    template <class Ctx, class Rd>
+    __host__ __device__ __forceinline__ void load(const Ctx& ctx, const Rd& rd)
+    {
+        const int tid = ctx.tid();
+#pragma unroll
+        for (int u = 0; u < PassTw<L, R, NS, NL, NT>::U; ++u) {
+            const int e = tw_local_off<L, false>(P) + ((tid + u * NT) / NL % NS) * (R - 1);
+#pragma unroll
+            for (int r = 1; r < R; ++r) here.w[u][r - 1] = rd(e + r - 1);
+        }
+        rest.load(ctx, rd);
+    }
+};
+
+template <int L, int NL, int NT, int PEND, int P>
+struct TwCache<L, NL, NT, PEND, P, true> {
+    template <int, int, int, int>
+    __host__ __device__ static constexpr bool has() { return false; }
+    template <class Ctx, class Rd>
+    __host__ __device__ __forceinline__ void load(const Ctx&, const Rd&) {}
+};
+
+// A context whose passes take their twiddles from a TwCache where it has them.
+template <class Base, class Cache>
+struct TwCachedCtx : Base {
+    const Cache* twc;
+};
+
+// Whether the context Ctx holds the factors of a pass (radix R, stride NS,
+// NL lines, NT threads) in registers.
+template <class Ctx>
+struct TwCacheOf {
+    template <int, int, int, int>
+    __host__ __device__ static constexpr bool has() { return false; }
+};
+
+template <class Base, class Cache>
+struct TwCacheOf<TwCachedCtx<Base, Cache>> : Cache {};
+
 // Twiddle W_{NS R}^{(j mod NS) r} and radix-R DFT on every owned butterfly.
-// TOFF: offset of this pass's twiddle table in the context's LDS tables.
+// The factors come from the context's TwCache when it holds this pass, else
+// from its LDS tables (TOFF: offset of this pass's table there).
 template <int L, int R, int NS, int NL, int NT, bool INV, bool PIN, bool POUT, int TOFF, class Ctx>
 __host__ __device__ __forceinline__ void pass_compute(const Ctx& ctx, PassRegs<L, R, NL, NT>& s)
 {
     using PR = PassRegs<L, R, NL, NT>;
+    constexpr bool kCached = TwCacheOf<Ctx>::template has<R, NS, NL, NT>();
     const int tid = ctx.tid();
 #pragma unroll
     for (int i = 0; i < PR::PER; ++i) {
         const int g = tid + i * NT;
         if (bf_valid<PR::NB, NT>(g)) {
             const int j = g / NL;
-            if constexpr (NS > 1) {
+            if constexpr (NS > 1 && kCached) {
+                const auto& tw = ctx.twc->template get<R, NS>();
+                const int u = tw.kShared ? 0 : i;
+#pragma unroll
+                for (int r = 1; r < (PIN ? R / 2 : R); ++r) {
+                    const float2 w = tw.w[u][r - 1];
+                    s.v[i][r] = INV ? cmulc(s.v[i][r], w) : cmul(s.v[i][r], w);
+                }
+            } else if constexpr (NS > 1) {
                 const float2* tw = ctx.twl + TOFF + (j % NS) * (R - 1) - 1;
 #pragma unroll
                 for (int r = 1; r < (PIN ? R / 2 : R); ++r) {

@@ -82,6 +82,12 @@ constexpr int bwd_nt(int L, int NR)
     return t < 64 ? 64 : (t > 1024 ? 1024 : t);
 }
 constexpr bool out_looped(int L, int NR) { return NR == 1 && (long long)L * NR * out_tw(L, NR) * 8 > 80 * 1024; }
+// Twiddled passes whose factors the forward out-axis kernel keeps in registers
+// for both of its transforms (fft_core.h TwCache).  512-point 2-D lines keep
+// the first (7 factors, shared by a thread's two butterflies; 106 -> 126
+// VGPRs, four workgroups per CU still): 256^2 k_col_out 145 -> 141 us.  Both
+// twiddled passes (140 VGPRs, three workgroups per CU) took 155 us.
+constexpr int out_tw_regs(int L, int NR) { return (NR == 1 && L == 512) ? 1 : 0; }
 
 struct Geom {
     int d;
