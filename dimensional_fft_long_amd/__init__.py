@@ -201,6 +201,16 @@ def workspace_bytes(B: int, C: int, dims, dtype=torch.float32, minimum: bool = F
     return int(f(B, C, len(dims), _dims_arr(dims), _dtype_code(dtype)))
 
 
+def _ws_bytes(workspace, device) -> int:
+    """A caller's workspace: a contiguous tensor on ``device`` (the kernels
+    write it as device memory); its size in bytes."""
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch tensor")
+    if workspace.device != torch.device(device) or not workspace.is_contiguous():
+        raise TypeError(f"workspace must be a contiguous tensor on {device}")
+    return workspace.numel() * workspace.element_size()
+
+
 def _check_spectrum_out(out, nbytes, device):
     if not isinstance(out, torch.Tensor) or out.dtype != torch.complex64:
         raise TypeError("out must be a complex64 tensor")
@@ -285,9 +295,9 @@ def fftconv_fwd(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, K_hat:
     B, C = int(x.shape[0]), int(x.shape[1])
     dims = tuple(int(v) for v in x.shape[2:])
     for t, nm in ((alpha, "alpha"), (beta, "beta")):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
-            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
-    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 tensor of C elements on {x.device}")
+    if K_hat.dtype != torch.complex64 or K_hat.device != x.device or not K_hat.is_contiguous():
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
     if K_hat.numel() * 8 < spectrum_bytes(C, dims):
         raise ValueError("K_hat is smaller than the spectrum of this shape")
@@ -295,7 +305,7 @@ def fftconv_fwd(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, K_hat:
     if workspace is None:
         workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device, stream)
     else:
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = _ws_bytes(workspace, x.device)
     rc = get_lib().hyenand_fftconv_fwd(_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()),
                                  _P(y.data_ptr()), B, C, len(dims), _dims_arr(dims), dt,
                                  _P(workspace.data_ptr()), ws_bytes, _stream(stream))
@@ -343,7 +353,7 @@ def fftconv_fwd_traced(x, alpha, beta, K_hat, y, workspace, events, stream=None)
             e.record(st)
     arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     n = ctypes.c_int(0)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace, x.device)
     rc = get_lib().hyenand_fftconv_fwd_traced(
         _P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
         B, C, len(dims), _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()), ws_bytes,
@@ -372,14 +382,14 @@ def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspa
               per_sample=False, stream=None):
     if not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous device tensor")
-    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_cuda or not dy.is_contiguous():
+    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
         raise TypeError("dy must be a contiguous device tensor with the shape and dtype of x")
     B, C = int(x.shape[0]), int(x.shape[1])
     dims = tuple(int(v) for v in x.shape[2:])
     for t, nm in ((alpha, "alpha"), (beta, "beta")):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
-            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
-    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 tensor of C elements on {x.device}")
+    if K_hat.dtype != torch.complex64 or K_hat.device != x.device or not K_hat.is_contiguous():
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
     need = spectrum_circ_bytes(C, dims) if circular else spectrum_bytes(C, dims) * (B if per_sample else 1)
     if K_hat.numel() * 8 < need:
@@ -402,7 +412,7 @@ def _bwd_args(x, alpha, beta, K_hat, dy, dx, dalpha, dbeta, dK, with_dK, workspa
         workspace, ws_bytes = _bwd_workspace(1 if per_sample else B, C, dims, x.dtype, dK is not None, dev,
                                              circular, stream)
     else:
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = _ws_bytes(workspace, x.device)
     args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(dy.data_ptr()),
             _P(dx.data_ptr()), _P(dalpha.data_ptr()), _P(dbeta.data_ptr()),
             _P(dK.data_ptr()) if dK is not None else None, B, C, len(dims), _dims_arr(dims),
@@ -557,9 +567,9 @@ def _circ_args(x, alpha, beta, K_hat, y, workspace, stream=None):
     B, C = int(x.shape[0]), int(x.shape[1])
     dims = tuple(int(v) for v in x.shape[2:])
     for t, nm in ((alpha, "alpha"), (beta, "beta")):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
-            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
-    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 tensor of C elements on {x.device}")
+    if K_hat.dtype != torch.complex64 or K_hat.device != x.device or not K_hat.is_contiguous():
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum_circ")
     if K_hat.numel() * 8 < spectrum_circ_bytes(C, dims):
         raise ValueError("K_hat is smaller than the circular spectrum of this shape")
@@ -567,7 +577,7 @@ def _circ_args(x, alpha, beta, K_hat, y, workspace, stream=None):
     if workspace is None:
         workspace, ws_bytes = _cached_ws("circ", circ_workspace_bytes(B, C, dims, x.dtype), x.device, stream)
     else:
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = _ws_bytes(workspace, x.device)
     args = [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
             B, C, len(dims), _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()), ws_bytes]
     return args, y
@@ -612,9 +622,9 @@ def _ps_args(x, alpha, beta, K_hat, y, workspace, stream=None):
     B, C = int(x.shape[0]), int(x.shape[1])
     dims = tuple(int(v) for v in x.shape[2:])
     for t, nm in ((alpha, "alpha"), (beta, "beta")):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
-            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
-    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 tensor of C elements on {x.device}")
+    if K_hat.dtype != torch.complex64 or K_hat.device != x.device or not K_hat.is_contiguous():
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum_per_sample")
     if K_hat.numel() * 8 < spectrum_bytes(B * C, dims):
         raise ValueError("K_hat must hold B * C spectra of this shape")
@@ -622,7 +632,7 @@ def _ps_args(x, alpha, beta, K_hat, y, workspace, stream=None):
     if workspace is None:
         workspace, ws_bytes = _workspace(B, C, dims, x.dtype, x.device, stream)
     else:
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = _ws_bytes(workspace, x.device)
     return [_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()), _P(K_hat.data_ptr()), _P(y.data_ptr()),
             B, C, len(dims), _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()), ws_bytes], y
 
@@ -680,9 +690,9 @@ def fftconv_fwd_noalloc(x, alpha, beta, K_hat, y, stream=None) -> torch.Tensor:
     B, C = int(x.shape[0]), int(x.shape[1])
     dims = tuple(int(v) for v in x.shape[2:])
     for t, nm in ((alpha, "alpha"), (beta, "beta")):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != C:
-            raise TypeError(f"{nm} must be a contiguous float32 device tensor of C elements")
-    if K_hat.dtype != torch.complex64 or not K_hat.is_cuda or not K_hat.is_contiguous():
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous() or t.numel() != C:
+            raise TypeError(f"{nm} must be a contiguous float32 tensor of C elements on {x.device}")
+    if K_hat.dtype != torch.complex64 or K_hat.device != x.device or not K_hat.is_contiguous():
         raise TypeError("K_hat must be the contiguous complex64 output of kernel_spectrum")
     if K_hat.numel() * 8 < spectrum_bytes(C, dims):
         raise ValueError("K_hat is smaller than the spectrum of this shape")
@@ -748,7 +758,7 @@ def generate_kernel_spectrum(x: torch.Tensor, gen: dict, out: torch.Tensor | Non
     if workspace is None:
         workspace, ws_bytes = _cached_ws("gen", generate_workspace_bytes(B, C, dims), x.device, stream)
     else:
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = _ws_bytes(workspace, x.device)
     rc = get_lib().hyenand_generate_kernel_spectrum(_P(x.data_ptr()), ctypes.byref(g), _P(out.data_ptr()), B, C, d,
                                                     _dims_arr(dims), _dtype_code(x.dtype), _P(workspace.data_ptr()),
                                                     ws_bytes, _stream(stream))
@@ -786,7 +796,7 @@ def fftconv_fwd_generated(x: torch.Tensor, alpha: torch.Tensor, beta: torch.Tens
     if workspace is None:
         workspace, ws_bytes = _cached_ws("gen_fwd", generated_workspace_bytes(B, C, dims, x.dtype), x.device, stream)
     else:
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = _ws_bytes(workspace, x.device)
     rc = get_lib().hyenand_fftconv_fwd_generated(_P(x.data_ptr()), _P(alpha.data_ptr()), _P(beta.data_ptr()),
                                                  ctypes.byref(g), _P(K_hat.data_ptr()), _P(y.data_ptr()), B, C,
                                                  len(dims), _dims_arr(dims), _dtype_code(x.dtype),

@@ -268,9 +268,10 @@ def test_long_1d_sizes(H):
 
 
 def test_output_checks_reject_bad_outputs(H):
-    """Caller-provided outputs are checked before any call: dtype, device,
-    contiguity, exact shape, and no overlap with the input they must not alias
-    (host tensors here; the GPU entry points run the same checks)."""
+    """Caller-provided outputs and workspaces are checked before any call:
+    dtype, device, contiguity, exact shape, and no overlap with the input they
+    must not alias (host tensors here; the GPU entry points run the same
+    checks)."""
     import torch
 
     x = torch.zeros(2, 3, 8, 8)
@@ -292,6 +293,14 @@ def test_output_checks_reject_bad_outputs(H):
         H._check_out(torch.zeros(3, dtype=torch.float64), "dalpha", (3,), torch.float32, x.device)
     with pytest.raises(ValueError):   # a per-sample-shaped dK where the shared one is expected
         H._check_out(torch.zeros(2, 3, 15, 15), "dK", (3, 15, 15), torch.float32, x.device)
+    assert H._ws_bytes(torch.zeros(16, dtype=torch.uint8), x.device) == 16
+    assert H._ws_bytes(torch.zeros(4, dtype=torch.float64), x.device) == 32
+    with pytest.raises(TypeError):   # a workspace on another device
+        H._ws_bytes(torch.zeros(16, dtype=torch.uint8, device="meta"), x.device)
+    with pytest.raises(TypeError):
+        H._ws_bytes(torch.zeros(32, dtype=torch.uint8)[::2], x.device)
+    with pytest.raises(TypeError):
+        H._ws_bytes(bytearray(16), x.device)
     H._check_spectrum_out(torch.zeros(10, dtype=torch.complex64), 80, x.device)
     with pytest.raises(ValueError):
         H._check_spectrum_out(torch.zeros(9, dtype=torch.complex64), 80, x.device)

@@ -297,6 +297,10 @@ def test_bad_outputs_are_rejected_before_the_call(H):
         H.fftconv_fwd(x, al, be, kh, y=x)
     with pytest.raises(ValueError):
         H.kernel_spectrum(w["K"].to(dev), out=torch.empty(4, dtype=torch.complex64, device=dev))
+    with pytest.raises(TypeError):   # a host workspace would reach the kernels as a device pointer
+        H.fftconv_fwd(x, al, be, kh, workspace=torch.empty(H.workspace_bytes(1, 2, (16, 16)), dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        H.fftconv_fwd(x, al.cpu(), be, kh)
     dy = torch.randn_like(x)
     with pytest.raises(ValueError):
         H.fftconv_bwd(x, al, be, kh, dy, dK=torch.empty((1, 2, 31, 31), device=dev))
