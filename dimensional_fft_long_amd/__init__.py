@@ -28,6 +28,14 @@ zero outside the grid.  Entry points mirror ``include/hyenand.h``:
   ``fftconv_bwd_circ(...)`` -- the circular mode (gist.science summary,
   "Boundary handling": periodic grids, no padding; K is [C, *dims] indexed by
   offset mod n)
+* ``generate_kernel_spectrum(x, gen)`` / ``fftconv_fwd_generated(...)`` -- the
+  input-dependent kernels generated on the GPU from x, alone or ahead of the
+  forward in one call
+* ``fftconv_fwd_noalloc(...)`` -- the forward with the library's static
+  workspace (for callers that cannot allocate)
+
+Calls without a ``workspace`` argument take one from a cache keyed by kind,
+device, size and stream; ``release_workspaces()`` frees it.
 """
 from __future__ import annotations
 
@@ -261,6 +269,16 @@ def _cached_ws(kind: str, nbytes: int, device, stream):
         buf = torch.empty(max(int(nbytes), 8), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf, int(nbytes)
+
+
+def release_workspaces() -> None:
+    """Free the workspaces the calls above cached (one per shape and stream;
+    a long-running program that meets many shapes calls this now and then).
+    Each buffer's device is synchronised first, so no call in flight still
+    uses it; the next call allocates afresh."""
+    for dev in {buf.device for buf in _ws_cache.values()}:
+        torch.cuda.synchronize(dev)
+    _ws_cache.clear()
 
 
 def _workspace(B, C, dims, dtype, device, stream=None):

@@ -294,6 +294,7 @@ def test_output_checks_reject_bad_outputs(H):
     with pytest.raises(ValueError):   # a per-sample-shaped dK where the shared one is expected
         H._check_out(torch.zeros(2, 3, 15, 15), "dK", (3, 15, 15), torch.float32, x.device)
     assert H._ws_bytes(torch.zeros(16, dtype=torch.uint8), x.device) == 16
+    H.release_workspaces()   # an empty cache: nothing to synchronise
     assert H._ws_bytes(torch.zeros(4, dtype=torch.float64), x.device) == 32
     with pytest.raises(TypeError):   # a workspace on another device
         H._ws_bytes(torch.zeros(16, dtype=torch.uint8, device="meta"), x.device)

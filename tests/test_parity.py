@@ -283,6 +283,23 @@ def test_two_streams_do_not_share_a_workspace(H):
             assert torch.equal(o, runs[k][4])
 
 
+def test_released_workspaces_are_reallocated(H):
+    """release_workspaces() empties the binding's workspace cache; the next
+    call allocates a new buffer and gives the same result."""
+    w = synth.make((128, 64), B=2, C=3, seed=41)
+    dev = torch.device("cuda:0")
+    x = w["x"].to(dev)
+    al, be = torch.from_numpy(w["alpha"]).to(dev), torch.from_numpy(w["beta"]).to(dev)
+    kh = H.kernel_spectrum(w["K"].to(dev))
+    y0 = H.fftconv_fwd(x, al, be, kh)
+    assert H._ws_cache
+    H.release_workspaces()
+    assert not H._ws_cache
+    y1 = H.fftconv_fwd(x, al, be, kh)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
 def test_bad_outputs_are_rejected_before_the_call(H):
     w = synth.make((16, 16), B=1, C=2, seed=3)
     dev = torch.device("cuda:0")
