@@ -1436,6 +1436,64 @@ __host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, c
     }
 }
 
+// Long 1-D product rows with the transforms' ends in registers (rows of
+// N2 <= 4096 points; the 8192-point rows keep lng_row_body, whose forward
+// and reversed twiddle tables would not fit one workgroup's LDS together):
+// the forward's first pass reads the row from the workspace, its last pass
+// leaves each thread holding the positions the inverse's first pass takes
+// (the reversed plan), the product with the kernel spectrum happens there,
+// and the inverse's last pass writes the row back.  Two LDS round trips per
+// transform instead of a load into the tile, four in-place passes, the
+// product and a read back out; one line of L points per workgroup (two of
+// 2048, four of 1024), 8 points per thread per pass, so that two or more
+// workgroups share a CU.
+template <int L, bool CONJ, class Ctx>
+__host__ __device__ __forceinline__ void lng_prod_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr int NL = lngp_nl(L), NT = lngp_nt(L);
+    constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
+    using PL = PassRegs<L, RL, NL, NT>;
+    const Geom& g = a.g;
+    const int N1 = g.N1;
+    const int H = a.nch * a.B * N1;
+    const int tid = ctx.tid();
+    // Row h = bid*NL + l: signal q = h / N1 of the chunk (channel c0 + q / B,
+    // batch entry q % B), row k1 = h % N1 of its N1 x L array.
+    auto row_off = [&](int l) -> long long {
+        const int h = bid * NL + l;
+        return (long long)(h / N1) * g.wsp + (long long)(h % N1) * L;
+    };
+    auto khat_off = [&](int l) -> long long {
+        const int h = bid * NL + l, q = h / N1, k1 = h % N1;
+        const int c = a.c0 + q / a.B, b = q % a.B;
+        return (long long)c * g.ksz + (long long)b * a.khat_bstride + (long long)k1 * L;
+    };
+    auto live = [&](int l) { return bid * NL + l < H; };
+    float2 kv[PL::PER][RL];
+    auto after_load = [&]() {
+        ctx.stage();
+#pragma unroll
+        for (int i = 0; i < PL::PER; ++i) {
+            const int gi = tid + i * NT, l = gi % NL, j = gi / NL;
+            const bool ok = bf_valid<PL::NB, NT>(gi) && live(l);
+            const long long base = ok ? khat_off(l) + j : 0;
+#pragma unroll
+            for (int r = 0; r < RL; ++r) kv[i][r] = ok ? a.khat[base + r * (L / RL)] : make_float2(0.f, 0.f);
+        }
+    };
+    auto t = fwd_from_fn<L, NL, NT, false>(ctx, T, [&](int pos, int l) -> float2 {
+        return live(l) ? a.ws[row_off(l) + pos] : make_float2(0.f, 0.f);
+    }, after_load);
+#pragma unroll
+    for (int i = 0; i < PL::PER; ++i)
+#pragma unroll
+        for (int r = 0; r < RL; ++r) t.v[i][r] = cmul(t.v[i][r], CONJ ? cconj(kv[i][r]) : kv[i][r]);
+    ctx.sync();  // every LDS read of the forward transform is done: T is free
+    inv_to_fn<L, NL, NT, false>(ctx, T, t, [&](int pos, int l, const float2& x) {
+        if (live(l)) a.ws[row_off(l) + pos] = x;
+    });
+}
+
 // Backward, kernel gradient, step 2: NP rows (channel, k1) per workgroup; for
 // each batch entry the forward row transforms of the column-transformed dy
 // and u, P += DY conj(U) (registers, batch entries in order), and, where
@@ -1522,6 +1580,75 @@ __host__ __device__ __forceinline__ void lng_row_dk_body(const Ctx& ctx, int bid
         const int idx = tid + i * NT, lp = idx / L, pos = idx % L, h = bid * NP + lp;
         if (h < H) a.dkw[(long long)(h / N1) * g.kmain + (long long)(h % N1) * L + pos] = T[pos * LP + lp];
     }
+}
+
+// Kernel-gradient row pass with the transforms' ends in registers (rows of
+// N2 <= 4096 points, as lng_prod_body): for each batch entry the forward row
+// transforms of dy and u end in registers, P += DY conj(U) there, and, where
+// lng_dk_fuses_du, the du row DY conj(Khat) is inverse-transformed straight
+// back to the workspace; then the inverse of P goes to the kernel-gradient
+// plane dkw.
+template <int L, class Ctx>
+__host__ __device__ __forceinline__ void lng_prod_dk_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+{
+    constexpr bool DU = lng_dk_fuses_du(L);
+    constexpr int NL = lngp_nl(L), NT = lngp_nt(L);
+    constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
+    using PL = PassRegs<L, RL, NL, NT>;
+    const Geom& g = a.g;
+    const int N1 = g.N1;
+    const int H = a.nch * N1;
+    const int tid = ctx.tid();
+    auto live = [&](int l) { return bid * NL + l < H; };
+    auto row_off = [&](int l, int b) -> long long {  // row k1 of pair (channel, b) in the workspace
+        const int h = bid * NL + l;
+        return ((long long)(h / N1) * a.B + b) * g.wsp + (long long)(h % N1) * L;
+    };
+    auto none = []() {};
+    auto fwd_rows = [&](const float2* ws, int b) {
+        return fwd_from_fn<L, NL, NT, false>(ctx, T, [&](int pos, int l) -> float2 {
+            return live(l) ? ws[row_off(l, b) + pos] : make_float2(0.f, 0.f);
+        }, none);
+    };
+    ctx.stage();
+    PL P;
+    float2 kv[PL::PER][DU ? RL : 1];
+#pragma unroll
+    for (int i = 0; i < PL::PER; ++i) {
+        const int gi = tid + i * NT, l = gi % NL, j = gi / NL, h = bid * NL + l;
+        const bool ok = bf_valid<PL::NB, NT>(gi) && live(l);
+#pragma unroll
+        for (int r = 0; r < RL; ++r) {
+            P.v[i][r] = make_float2(0.f, 0.f);
+            if constexpr (DU)
+                kv[i][r] = ok ? a.khat[(long long)(a.c0 + h / N1) * g.ksz + (long long)(h % N1) * L + j + r * (L / RL)]
+                              : make_float2(0.f, 0.f);
+        }
+    }
+    for (int b = 0; b < a.B; ++b) {
+        auto DY = fwd_rows(a.ws, b);
+        ctx.sync();  // T is free for the next transform
+        auto U = fwd_rows(a.ws_u, b);
+        ctx.sync();
+#pragma unroll
+        for (int i = 0; i < PL::PER; ++i)
+#pragma unroll
+            for (int r = 0; r < RL; ++r) P.v[i][r] = cadd(P.v[i][r], cmulc(DY.v[i][r], U.v[i][r]));
+        if constexpr (DU) {
+#pragma unroll
+            for (int i = 0; i < PL::PER; ++i)
+#pragma unroll
+                for (int r = 0; r < RL; ++r) DY.v[i][r] = cmulc(DY.v[i][r], kv[i][r]);
+            inv_to_fn<L, NL, NT, false>(ctx, T, DY, [&](int pos, int l, const float2& x) {
+                if (live(l)) a.ws[row_off(l, b) + pos] = x;
+            });
+            ctx.sync();  // T is free for the next transform
+        }
+    }
+    inv_to_fn<L, NL, NT, false>(ctx, T, P, [&](int pos, int l, const float2& x) {
+        const int h = bid * NL + l;
+        if (live(l)) a.dkw[(long long)(h / N1) * g.kmain + (long long)(h % N1) * L + pos] = x;
+    });
 }
 
 // Step 3: TW adjacent columns per workgroup: conjugate twiddle, inverse

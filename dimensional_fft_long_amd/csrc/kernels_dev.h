@@ -174,6 +174,24 @@ __global__ __launch_bounds__(row_nt(L)) void k_lng_row(ConvArgs a)
     lng_row_body<L, SPEC, CONJ>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
+template <int L, bool CONJ>
+__global__ __launch_bounds__(lngp_nt(L)) void k_lng_prod(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
+    __shared__ float2 T[L * lngp_nl(L)];
+    lng_prod_body<L, CONJ>(make_ctx<L, lngp_nt(L), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
+}
+
+// Two workgroups per CU (at most 128 VGPRs): the dy, u, P and kernel spectrum
+// registers otherwise take 135 and leave room for one.
+template <int L>
+__global__ __launch_bounds__(lngp_nt(L), 2 * lngp_nt(L) / 64 / 4) void k_lng_prod_dk(ConvArgs a)
+{
+    __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
+    __shared__ float2 T[L * lngp_nl(L)];
+    lng_prod_dk_body<L>(make_ctx<L, lngp_nt(L), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
+}
+
 template <int L>
 __global__ __launch_bounds__(row_nt(L)) void k_lng_row_dk(ConvArgs a)
 {

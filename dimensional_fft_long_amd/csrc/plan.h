@@ -288,6 +288,12 @@ inline size_t recommended_workspace(const Geom& g, int B, int C)
 // (2M tokens, 2048-point rows: 1.28 ms separate against 1.44 fused; 8M tokens,
 // 4096-point rows: 3.05 against 2.81).
 constexpr bool lng_dk_fuses_du(int N2) { return N2 >= 4096; }
+// Long 1-D product rows in registers (lng_prod_body) for rows up to 4096
+// points: lines per workgroup (4096 points each) and threads (8 points per
+// thread per pass).
+constexpr bool lng_prod_regs(int N2) { return N2 <= 4096; }
+constexpr int lngp_nl(int L) { return L >= 4096 ? 1 : 4096 / L; }
+constexpr int lngp_nt(int L) { return L * lngp_nl(L) / 8; }
 
 // Backward partial sums of dalpha / dbeta per (b, c) pair: one per line pair
 // of the row kernels (d >= 2), one per pair (d = 1), one per inverse-column

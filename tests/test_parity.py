@@ -50,6 +50,9 @@ SMALL = [
     ((16, 64), 2, 2, "f32"), ((64, 16), 1, 3, "bf16"), ((2, 512), 1, 2, "f32"), ((512, 2), 1, 2, "f32"),
     ((2, 2, 2), 1, 1, "f32"), ((4, 8, 16), 2, 3, "f32"), ((16, 4, 8), 1, 2, "f32"), ((8, 8, 8), 3, 1, "f32"),
     ((2, 2, 64), 1, 2, "f32"), ((64, 2, 2), 1, 2, "f32"), ((8, 16, 8), 2, 3, "bf16"),
+    # 512-point out-axis lines (registers hold the first twiddled pass) with
+    # fewer slots than a tile, and with two whole tiles
+    ((256, 4), 2, 3, "f32"), ((256, 2), 1, 2, "bf16"), ((256, 32), 1, 2, "f32"),
     # maximum extents: 2048-point transforms on every axis position
     ((1024, 2), 2, 2, "f32"), ((2, 1024), 1, 3, "bf16"), ((1024, 2, 2), 1, 2, "f32"), ((2, 1024, 2), 2, 1, "f32"),
     ((2, 2, 1024), 1, 2, "bf16"),

@@ -185,6 +185,16 @@ def test_bwd_without_kernel_gradient_and_chunking(H):
             assert np.array_equal(g, r)
 
 
+@pytest.mark.parametrize("n,B,C,dtype", [(1 << 14, 2, 2, "f32"), (1 << 22, 1, 1, "f32")], ids=lambda v: str(v))
+def test_bwd_without_kernel_gradient_matches_fft_oracle(H, n, B, C, dtype):
+    """Without dK the du rows take the row pass of their own (the correlation
+    with the kernel spectrum): 2048- and 4096-point rows against the oracle."""
+    x, dy, p, K, got = _run_bwd(H, (n,), B, C, dtype, seed=23 + n % 31, with_dK=False)
+    assert got[3] is None
+    ref = oracle.bwd_fft(x, p.alpha, p.beta, K, dy)
+    _check(got[:3], ref[:3], dtype)
+
+
 def test_bwd_per_sample_kernels(H):
     n = 1 << 13
     x, dy, p, Kb, got = _run_bwd(H, (n,), 3, 2, "f32", seed=21, per_sample=True)
