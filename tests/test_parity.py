@@ -53,6 +53,8 @@ SMALL = [
     # 512-point out-axis lines (registers hold the first twiddled pass) with
     # fewer slots than a tile, and with two whole tiles
     ((256, 4), 2, 3, "f32"), ((256, 2), 1, 2, "bf16"), ((256, 32), 1, 2, "f32"),
+    # 1024-point out-axis lines of a volume (4-line tiles, two mirrored rows)
+    ((512, 2, 4), 1, 2, "f32"), ((512, 4, 16), 1, 1, "bf16"),
     # maximum extents: 2048-point transforms on every axis position
     ((1024, 2), 2, 2, "f32"), ((2, 1024), 1, 3, "bf16"), ((1024, 2, 2), 1, 2, "f32"), ((2, 1024, 2), 2, 1, "f32"),
     ((2, 2, 1024), 1, 2, "bf16"),
