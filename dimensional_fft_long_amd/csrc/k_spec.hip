@@ -23,13 +23,13 @@ hipError_t launch_spectrum(const ConvArgs& a, hipStream_t st)
         });
         if (e != hipSuccess) return e;
         return with_length(g.N_out, [&]<int L>() {
-            const long long grid = (long long)a.C * (g.N_mid / 2) * ceil_div(g.S, mul3_tw(L));
+            const long long grid = (long long)a.C * (g.N_mid / 2) * ceil_div(g.S, out_tw(L, 2));
             hipLaunchKernelGGL((k_spec_out<L, 2>), dim3((unsigned)grid), dim3(out_nt(L, 2)), 0, st, a);
             return last_error();
         });
     }
     return with_length(g.N_out, [&]<int L>() {
-        const long long grid = (long long)a.C * ceil_div(g.S, col_tw(L));
+        const long long grid = (long long)a.C * ceil_div(g.S, out_tw(L, 1));
         hipLaunchKernelGGL((k_spec_out<L, 1>), dim3((unsigned)grid), dim3(out_nt(L, 1)), 0, st, a);
         return last_error();
     });

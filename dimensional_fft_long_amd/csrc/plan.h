@@ -59,7 +59,11 @@ constexpr int mul3_tw(int L) { return L == 1024 ? 4 : (8192 / L > 16 ? 16 : (819
 constexpr int tile_threads(int points) { return points / 16 < 64 ? 64 : (points / 16 > 1024 ? 1024 : points / 16); }
 constexpr int row_nt(int L) { return tile_threads(2 * L * row_np(L)); }
 constexpr int col_nt(int L) { return tile_threads(L * col_tw(L)); }
-constexpr int out_tw(int L, int NR) { return NR == 1 ? col_tw(L) : mul3_tw(L); }
+// 2-D out-axis lines of 1024 points take 8 (64 KiB: two workgroups per CU
+// that run one item each, instead of one looping workgroup; 512^2, B = 8,
+// C = 16: k_col_out 260 -> 201 us per call).  The middle-axis kernel keeps 16
+// for them (with 8, 512^3 k_col_mid 730 -> 840 us per call).
+constexpr int out_tw(int L, int NR) { return NR == 1 ? (L == 1024 ? 8 : col_tw(L)) : mul3_tw(L); }
 constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
 // 2-D out-axis tiles above 80 KiB leave room for one workgroup per CU: such
 // kernels run one workgroup per CU that loops over the work items (1024^2:

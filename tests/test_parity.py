@@ -71,7 +71,7 @@ def test_small_grids_match_direct_sum(H, dims, B, C, dtype):
     assert _rel(got, ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 1, 2), ((32, 64, 16), 1, 2)])
+@pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 1, 2), ((32, 64, 16), 1, 2), ((512, 64), 1, 3)])
 def test_medium_grids_match_fft_oracle(H, dims, B, C):
     w = synth.make(dims, B=B, C=C, dtype="f32", seed=5)
     y, _ = _gpu_run(H, w)
