@@ -185,22 +185,9 @@ KERNEL_LABEL = {"row_fwd": "k_row_fwd", "row_inv": "k_row_inv", "col_out": "k_co
                 "col_mid_fwd_dy": "k_col_mid", "col_mid_fwd_u": "k_col_mid", "col_out_bwd": "k_col_out_bwd",
                 "row_inv_bwd": "k_row_inv", "gate_reduce": "k_gate_reduce", "mid_inv_dk": "k_plane_mid_inv",
                 "dk_row": "k_dk_row", "conv1d_bwd": "k_conv1d", "corr1d": "k_corr1d", "lng_col_fwd": "k_lng_col_fwd",
-                "lng_row": "k_lng_row", "lng_col_inv": "k_lng_col_inv", "lng_col_fwd_dy": "k_lng_col_fwd",
-                "lng_col_fwd_u": "k_lng_col_fwd", "lng_row_dk": "k_lng_row_dk", "lng_row_du": "k_lng_row",
+                "lng_row": "k_lng_prod", "lng_col_inv": "k_lng_col_inv", "lng_col_fwd_dy": "k_lng_col_fwd",
+                "lng_col_fwd_u": "k_lng_col_fwd", "lng_row_dk": "k_lng_prod_dk", "lng_row_du": "k_lng_prod",
                 "lng_col_inv_bwd": "k_lng_col_inv", "lng_col_dk": "k_lng_col_dk", "fused2d": "k_fused2d"}
-
-
-def _kernel_label(name, dims):
-    """The kernel that runs pass `name`: long 1-D rows of up to 4096 points
-    (N = 2n split into N1 x N2 as plan.h make_geom does) take the register-flow
-    row kernels k_lng_prod / k_lng_prod_dk."""
-    label = KERNEL_LABEL[name]
-    if name in ("lng_row", "lng_row_du", "lng_row_dk"):
-        N = 2 * dims[0]
-        rows = min(N // 4, 2048) if N <= 1 << 22 else (4096 if N <= 1 << 24 else 8192)
-        if rows <= 4096:
-            label = "k_lng_prod_dk" if name == "lng_row_dk" else "k_lng_prod"
-    return label
 
 
 # The sources of the zero-padded forward's kernels and of its planning (the
@@ -585,7 +572,7 @@ def run_workload(H, wl, which="fwd", boundary="padded", kernel="shared", steps=5
         P_l, nk_l = nch * wl.B, nch * (wl.B if ps else 1)
     moved, fl = pass_model(dominant, wl.dims, P_l, nk_l, es, circ)
     alg = _alg_bytes(dominant, wl, P_l, nk_l, es, circ, ps)
-    kernel_label = _kernel_label(dominant, wl.dims)
+    kernel_label = KERNEL_LABEL[dominant]
     hbm = {"bound": "hbm", "achieved": alg / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     alu = {"bound": "alu", "achieved": fl / dom_s / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s"}
     for r in (hbm, alu):

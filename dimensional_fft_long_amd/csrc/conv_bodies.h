@@ -1369,26 +1369,23 @@ __host__ __device__ __forceinline__ void lng_col_fwd_body(const Ctx& ctx, int bi
     fwd_fn_to_fn<L, TW, NT, !SPEC>(ctx, T, ld, st, after_load);
 }
 
-// Step 2: NP rows k1 per workgroup, N2 points each.  Forward: forward
-// transform, product with the spectrum row, inverse transform, in place.
-// SPEC: forward transform scaled by 1/N, in place in the spectrum.
-// CONJ (backward, du): the product takes the conjugate spectrum (a
-// correlation with K).
-template <int L, bool SPEC, bool CONJ = false, class Ctx>
-__host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
+// Spectrum, step 2: NP rows k1 per workgroup, N2 points each: the forward
+// row transform scaled by 1/N, in place in the spectrum (the convolution's row
+// passes are lng_prod_body and lng_prod_dk_body below).
+template <int L, class Ctx>
+__host__ __device__ __forceinline__ void lng_spec_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
     constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
     constexpr int ITER = NP * L / NT;
     static_assert(NP * L % NT == 0, "whole element loops");
     const Geom& g = a.g;
     const int N1 = g.N1;
-    const int H = (SPEC ? a.C : a.nch * a.B) * N1;
+    const int H = a.C * N1;
     const int tid = ctx.tid();
     ctx.stage();
     auto row_base = [&](int lp) -> float2* {
         const int h = bid * NP + lp, q = h / N1, k1 = h % N1;
-        return (SPEC ? const_cast<float2*>(a.khat) + (long long)q * g.ksz : a.ws + (long long)q * g.wsp) +
-               (long long)k1 * L;
+        return const_cast<float2*>(a.khat) + (long long)q * g.ksz + (long long)k1 * L;
     };
     float2 v[ITER];
 #pragma unroll
@@ -1403,50 +1400,25 @@ __host__ __device__ __forceinline__ void lng_row_body(const Ctx& ctx, int bid, c
     }
     ctx.sync();
     tile_fft<L, NP, LP, NT, false, false, false>(ctx, T);
-    if constexpr (SPEC) {
-        const float sc = 1.0f / (float)(1ll << g.logN);
+    const float sc = 1.0f / (float)(1ll << g.logN);
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-            if (bid * NP + lp < H) row_base(lp)[pos] = cscale(T[pos * LP + lp], sc);
-        }
-    } else {
-        // The spectrum row of this (b, c) pair: channel c, batch entry b (per-sample spectra: b * bstride).
-        float2 kv[ITER];
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int idx = tid + i * NT, lp = idx / L, pos = idx % L, h = bid * NP + lp;
-            const int q = h / N1, k1 = h % N1;
-            const int c = a.c0 + q / a.B, b = q % a.B;
-            kv[i] = h < H ? a.khat[(long long)c * g.ksz + (long long)b * a.khat_bstride + (long long)k1 * L + pos]
-                          : make_float2(0.f, 0.f);
-        }
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-            T[pos * LP + lp] = cmul(T[pos * LP + lp], CONJ ? cconj(kv[i]) : kv[i]);
-        }
-        ctx.sync();
-        tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-            if (bid * NP + lp < H) row_base(lp)[pos] = T[pos * LP + lp];
-        }
+    for (int i = 0; i < ITER; ++i) {
+        const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
+        if (bid * NP + lp < H) row_base(lp)[pos] = cscale(T[pos * LP + lp], sc);
     }
 }
 
-// Long 1-D product rows with the transforms' ends in registers (rows of
-// N2 <= 4096 points; the 8192-point rows keep lng_row_body, whose forward
-// and reversed twiddle tables would not fit one workgroup's LDS together):
+// Long 1-D, step 2: the product rows, with the transforms' ends in registers:
 // the forward's first pass reads the row from the workspace, its last pass
 // leaves each thread holding the positions the inverse's first pass takes
 // (the reversed plan), the product with the kernel spectrum happens there,
-// and the inverse's last pass writes the row back.  Two LDS round trips per
-// transform instead of a load into the tile, four in-place passes, the
-// product and a read back out; one line of L points per workgroup (two of
-// 2048, four of 1024), 8 points per thread per pass, so that two or more
-// workgroups share a CU.
+// and the inverse's last pass writes the row back (two LDS round trips per
+// transform of 4096 points).  One line of L points per workgroup (two of
+// 2048, four of 1024), 8 points per thread per pass, so that two workgroups
+// share a CU below 8192 points (the 8192-point plan is a palindrome: its
+// forward and reversed plans share 64 KiB of tables beside the 64 KiB line).
+// CONJ (backward, du): the product takes the conjugate spectrum (a
+// correlation with K).
 template <int L, bool CONJ, class Ctx>
 __host__ __device__ __forceinline__ void lng_prod_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
@@ -1494,96 +1466,8 @@ __host__ __device__ __forceinline__ void lng_prod_body(const Ctx& ctx, int bid, 
     });
 }
 
-// Backward, kernel gradient, step 2: NP rows (channel, k1) per workgroup; for
-// each batch entry the forward row transforms of the column-transformed dy
-// and u, P += DY conj(U) (registers, batch entries in order), and, where
-// lng_dk_fuses_du, the du row DY conj(Khat) inverse-transformed in place of
-// the dy row (the dy rows read once; elsewhere the du row pass follows); then
-// the inverse row transform of P into the channel's kernel-gradient plane dkw.
-template <int L, class Ctx>
-__host__ __device__ __forceinline__ void lng_row_dk_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
-{
-    constexpr bool DU = lng_dk_fuses_du(L);
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
-    constexpr int ITER = NP * L / NT;
-    static_assert(NP * L % NT == 0, "whole element loops");
-    const Geom& g = a.g;
-    const int N1 = g.N1;
-    const int H = a.nch * N1;
-    const int tid = ctx.tid();
-    ctx.stage();
-    auto row_off = [&](int lp, int b) -> long long {  // workspace offset of row k1 of pair (channel, b)
-        const int h = bid * NP + lp;
-        return ((long long)(h / N1) * a.B + b) * g.wsp + (long long)(h % N1) * L;
-    };
-    // forward row transform of the rows at workspace base `ws` of batch entry b, into registers
-    auto fwd_rows = [&](const float2* ws, int b, float2* out) {
-        float2 v[ITER];
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-            v[i] = bid * NP + lp < H ? ws[row_off(lp, b) + pos] : make_float2(0.f, 0.f);
-        }
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-            T[pos * LP + lp] = v[i];
-        }
-        ctx.sync();
-        tile_fft<L, NP, LP, NT, false, false, false>(ctx, T);
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-            out[i] = T[pos * LP + lp];
-        }
-        ctx.sync();  // T is free for the next transform
-    };
-    float2 P[ITER], DY[ITER], U[ITER], kv[DU ? ITER : 1];
-#pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT, lp = idx / L, pos = idx % L, h = bid * NP + lp;
-        P[i] = make_float2(0.f, 0.f);
-        if constexpr (DU)
-            kv[i] = h < H ? a.khat[(long long)(a.c0 + h / N1) * g.ksz + (long long)(h % N1) * L + pos]
-                          : make_float2(0.f, 0.f);
-    }
-    for (int b = 0; b < a.B; ++b) {
-        fwd_rows(a.ws, b, DY);
-        fwd_rows(a.ws_u, b, U);
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) P[i] = cadd(P[i], cmulc(DY[i], U[i]));
-        if constexpr (DU) {
-#pragma unroll
-            for (int i = 0; i < ITER; ++i) {
-                const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-                T[pos * LP + lp] = cmulc(DY[i], kv[i]);
-            }
-            ctx.sync();
-            tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
-#pragma unroll
-            for (int i = 0; i < ITER; ++i) {
-                const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-                if (bid * NP + lp < H) a.ws[row_off(lp, b) + pos] = T[pos * LP + lp];
-            }
-            ctx.sync();  // T is free for the next transform
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT, lp = idx / L, pos = idx % L;
-        T[pos * LP + lp] = P[i];
-    }
-    ctx.sync();
-    tile_fft<L, NP, LP, NT, true, false, false>(ctx, T);
-#pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int idx = tid + i * NT, lp = idx / L, pos = idx % L, h = bid * NP + lp;
-        if (h < H) a.dkw[(long long)(h / N1) * g.kmain + (long long)(h % N1) * L + pos] = T[pos * LP + lp];
-    }
-}
-
-// Kernel-gradient row pass with the transforms' ends in registers (rows of
-// N2 <= 4096 points, as lng_prod_body): for each batch entry the forward row
+// Backward, kernel gradient, step 2, with the transforms' ends in registers
+// (as lng_prod_body): for each batch entry the forward row
 // transforms of dy and u end in registers, P += DY conj(U) there, and, where
 // lng_dk_fuses_du, the du row DY conj(Khat) is inverse-transformed straight
 // back to the workspace; then the inverse of P goes to the kernel-gradient

@@ -183,7 +183,10 @@ __host__ __device__ constexpr int plan_radix(int L, int p)
     const int k = ilog2(L);
     // k: passes
     // 1: 2 | 2: 4 | 3: 8 | 4: 4 4 | 5: 8 4 | 6: 8 8 | 7: 8 4 4 | 8: 8 8 4
-    // 9: 8 8 8 | 10: 8 8 4 4 | 11: 8 8 8 4
+    // 9: 8 8 8 | 10: 8 8 4 4 | 11: 8 8 8 4 | 12: 8 8 8 8 | 13: 8 4 8 4 8
+    // The 8192-point plan (long 1-D rows only) is a palindrome, so that the
+    // forward and reversed plans share one 64 KiB set of twiddle tables.
+    if (k == 13) return p < 5 ? (p % 2 == 0 ? 8 : 4) : 0;
     const int r8 = (k % 3 == 1 && k >= 4) ? (k - 4) / 3 : k / 3;
     const int r4 = (k % 3 == 1 && k >= 4) ? 2 : (k % 3 == 2 ? 1 : 0);
     const int r2 = (k == 1) ? 1 : 0;

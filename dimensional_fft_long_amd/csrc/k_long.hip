@@ -22,14 +22,11 @@ hipError_t long1d_chunk(const ConvArgs& a, bool spec, hipStream_t st, LaunchTrac
     if (e != hipSuccess) return e;
     e = with_row_length(g.N2, [&]<int L>() {
         mark();
-        if (spec) {
-            hipLaunchKernelGGL((k_lng_row<L, true>), dim3(ceil_div(sigs * g.N1, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        } else if constexpr (lng_prod_regs(L)) {
+        if (spec)
+            hipLaunchKernelGGL((k_lng_spec_row<L>), dim3(ceil_div(sigs * g.N1, row_np(L))), dim3(row_nt(L)), 0, st, a);
+        else
             hipLaunchKernelGGL((k_lng_prod<L, false>), dim3(ceil_div(sigs * g.N1, lngp_nl(L))), dim3(lngp_nt(L)), 0,
                                st, a);
-        } else {
-            hipLaunchKernelGGL((k_lng_row<L, false>), dim3(ceil_div(sigs * g.N1, row_np(L))), dim3(row_nt(L)), 0, st, a);
-        }
         return last_error();
     });
     if (e != hipSuccess || spec) return e;
@@ -75,23 +72,15 @@ hipError_t long1d_bwd_chunk(const ConvArgs& a, bool dk, hipStream_t st, LaunchTr
     if (e == hipSuccess && dk)
         e = with_row_length(g.N2, [&]<int L>() {
             mark();
-            if constexpr (lng_prod_regs(L))
-                hipLaunchKernelGGL((k_lng_prod_dk<L>), dim3(ceil_div((long long)a.nch * g.N1, lngp_nl(L))),
-                                   dim3(lngp_nt(L)), 0, st, a);
-            else
-                hipLaunchKernelGGL((k_lng_row_dk<L>), dim3(ceil_div((long long)a.nch * g.N1, row_np(L))),
-                                   dim3(row_nt(L)), 0, st, a);
+            hipLaunchKernelGGL((k_lng_prod_dk<L>), dim3(ceil_div((long long)a.nch * g.N1, lngp_nl(L))),
+                               dim3(lngp_nt(L)), 0, st, a);
             return last_error();
         });
     if (e == hipSuccess && !(dk && lng_dk_fuses_du(g.N2)))  // else the kernel-gradient row pass wrote du
         e = with_row_length(g.N2, [&]<int L>() {
             mark();
-            if constexpr (lng_prod_regs(L))
-                hipLaunchKernelGGL((k_lng_prod<L, true>), dim3(ceil_div(sigs * g.N1, lngp_nl(L))), dim3(lngp_nt(L)), 0,
-                                   st, a);
-            else
-                hipLaunchKernelGGL((k_lng_row<L, false, true>), dim3(ceil_div(sigs * g.N1, row_np(L))),
-                                   dim3(row_nt(L)), 0, st, a);
+            hipLaunchKernelGGL((k_lng_prod<L, true>), dim3(ceil_div(sigs * g.N1, lngp_nl(L))), dim3(lngp_nt(L)), 0,
+                               st, a);
             return last_error();
         });
     if (e == hipSuccess)

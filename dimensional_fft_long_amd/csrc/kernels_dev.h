@@ -166,12 +166,12 @@ __global__ __launch_bounds__(col_nt(L)) void k_lng_col_fwd(ConvArgs a)
     lng_col_fwd_body<L, SPEC, BF16, GATE>(make_ctx<L, col_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
-template <int L, bool SPEC, bool CONJ = false>
-__global__ __launch_bounds__(row_nt(L)) void k_lng_row(ConvArgs a)
+template <int L>
+__global__ __launch_bounds__(row_nt(L)) void k_lng_spec_row(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
     __shared__ float2 T[L * row_lp(L)];
-    lng_row_body<L, SPEC, CONJ>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
+    lng_spec_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L, bool CONJ>
@@ -182,22 +182,15 @@ __global__ __launch_bounds__(lngp_nt(L)) void k_lng_prod(ConvArgs a)
     lng_prod_body<L, CONJ>(make_ctx<L, lngp_nt(L), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
 }
 
-// Two workgroups per CU (at most 128 VGPRs): the dy, u, P and kernel spectrum
-// registers otherwise take 135 and leave room for one.
+// Two workgroups per CU below 8192 points (at most 128 VGPRs): the dy, u, P and
+// kernel spectrum registers otherwise take 135 and leave room for one.  8192
+// points: one workgroup per CU (its LDS), 128 VGPRs too.
 template <int L>
-__global__ __launch_bounds__(lngp_nt(L), 2 * lngp_nt(L) / 64 / 4) void k_lng_prod_dk(ConvArgs a)
+__global__ __launch_bounds__(lngp_nt(L), lngp_wgs(L) * lngp_nt(L) / 64 / 4) void k_lng_prod_dk(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
     __shared__ float2 T[L * lngp_nl(L)];
     lng_prod_dk_body<L>(make_ctx<L, lngp_nt(L), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
-}
-
-template <int L>
-__global__ __launch_bounds__(row_nt(L)) void k_lng_row_dk(ConvArgs a)
-{
-    __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * row_lp(L)];
-    lng_row_dk_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T);
 }
 
 template <int L, bool BF16, bool BWD = false>

@@ -288,18 +288,17 @@ inline size_t recommended_workspace(const Geom& g, int B, int C)
 }
 
 // Long 1-D backward with dK: the kernel-gradient row kernel also writes the du
-// rows (the du row pass fused) for 4096-point rows, whose 96 KiB tile leaves
-// one workgroup per CU whatever the registers; shorter rows run three
-// workgroups per CU, which the fused kernel's extra registers would cost
-// (2M tokens, 2048-point rows: 1.28 ms separate against 1.44 fused; 8M tokens,
-// 4096-point rows: 3.05 against 2.81).
+// rows (the du row pass fused) for rows of 4096 and 8192 points (one line per
+// workgroup); with 1024- and 2048-point rows, four or two lines per
+// workgroup, the fused product's registers would spill 94-108 VGPRs.
 constexpr bool lng_dk_fuses_du(int N2) { return N2 >= 4096; }
-// Long 1-D product rows in registers (lng_prod_body) for rows up to 4096
-// points: lines per workgroup (4096 points each) and threads (8 points per
-// thread per pass).
-constexpr bool lng_prod_regs(int N2) { return N2 <= 4096; }
+// Long 1-D product rows in registers (lng_prod_body): lines per workgroup
+// (4096 points each, one line of 8192) and threads (8 points per thread per
+// pass); workgroups per CU the kernel-gradient row kernel is held to (a line
+// of 8192 points and its 64 KiB of twiddles leave room for one).
 constexpr int lngp_nl(int L) { return L >= 4096 ? 1 : 4096 / L; }
 constexpr int lngp_nt(int L) { return L * lngp_nl(L) / 8; }
+constexpr int lngp_wgs(int L) { return L >= 8192 ? 1 : 2; }
 
 // Backward partial sums of dalpha / dbeta per (b, c) pair: one per line pair
 // of the row kernels (d >= 2), one per pair (d = 1), one per inverse-column
