@@ -250,21 +250,21 @@ def write_traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, c
 
 
 def _traffic_from_profile(kernel_name, workload, chunk_channels):
-    """HBM bytes per launch of `kernel_name` from the committed rocprofv3 PMC
-    summary (FETCH_SIZE and WRITE_SIZE scaled by what they read for a copy of
-    known size), if it was taken on the current kernel sources and the same
-    workload; else None."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    if not os.path.exists(path):
-        return None
-    try:
-        rec = json.load(open(path))
-    except ValueError:
-        return None
-    if (rec.get("source_hash") != _src_hash() or rec.get("workload") != workload
-            or rec.get("chunk_channels") != chunk_channels):
-        return None
-    return rec.get("kernels", {}).get(kernel_name, {}).get("traffic_bytes_per_launch")
+    """HBM bytes per launch of `kernel_name` from a committed rocprofv3 PMC
+    record (profiles/pmc_traffic*.json, one per workload: FETCH_SIZE and
+    WRITE_SIZE scaled by what they read for a copy of known size), if it was
+    taken on the current kernel sources and the same workload; else None."""
+    import glob
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_traffic*.json"))):
+        try:
+            rec = json.load(open(path))
+        except ValueError:
+            continue
+        if (rec.get("source_hash") == _src_hash() and rec.get("workload") == workload
+                and rec.get("chunk_channels") == chunk_channels):
+            return rec.get("kernels", {}).get(kernel_name, {}).get("traffic_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(wl, circ=False, max_seconds=20.0):
