@@ -394,12 +394,24 @@ __host__ __device__ __forceinline__ OutTile out_tile(const Geom& g, int B, int n
     // one whole run of the tile-major plane) take the row pairs fastest, so
     // that the workgroups one XCD runs together read adjacent runs (rows rp,
     // rp + 1, ... and their mirrors) at every out-axis position: 128^3
-    // k_col_out 251.5 -> 225.6 us per launch.  Narrower tiles share their
-    // slot tile with their neighbours and keep the slot tiles fastest (512^3:
+    // k_col_out 251.5 -> 225.6 us per launch.  Tiles of half a slot tile
+    // (the backward's 8-slot tiles of 16-slot runs) keep the two halves of a
+    // run together, then take the row pairs (128^3 k_col_out_bwd 194.7 ->
+    // 187.0 us against the slot tiles fastest).  Narrower tiles share their
+    // slot tile with more neighbours and keep the slot tiles fastest (512^3:
     // 2.77 ms, against 2.97 with the row pairs fastest).
-    const bool rows_fast = NR == 2 && TW >= g.lt;
-    const int rp = rows_fast ? r2 % nrp : r2 / ct;
-    o.t = rows_fast ? r2 / nrp : r2 % ct;
+    int rp;
+    if (NR == 2 && TW >= g.lt) {
+        rp = r2 % nrp;
+        o.t = r2 / nrp;
+    } else if (NR == 2 && 2 * TW == g.lt && ct % 2 == 0) {
+        const int hi = r2 / (2 * nrp), rem = r2 % (2 * nrp);
+        rp = rem / 2;
+        o.t = 2 * hi + rem % 2;
+    } else {
+        rp = r2 / ct;
+        o.t = r2 % ct;
+    }
     if (NR == 1) {
         o.rows[0] = 0; o.rows[1] = 0; o.self_mirror = true;
     } else {

@@ -76,9 +76,13 @@ constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)
 // would fill a CU's whole 512 KiB register file: 1024^2 22.8 -> 10.9 ms,
 // 512^3 104.6 -> 79.9 ms per call).  Points per thread per pass: 8 for 2-D
 // lines (256^2: 0.88 -> 0.80 ms against 16), 16 for the two-row 3-D tiles
-// (128^3: 6.7 against 7.8 ms with 8).
+// (128^3: 6.7 against 7.8 ms with 8).  The two-row tiles of 256-point lines
+// take 8 slots (32 KiB; the kernel spectrum's slot tiles stay 16 wide for the
+// forward): 128^3 k_col_out_bwd 238 -> 187 us per launch, backward 6.73 ->
+// 6.16 ms.
 constexpr int bwd_tw(int L, int NR)
 {
+    if (NR == 2 && L == 256) return 8;
     const int cap = 65536 / (8 * L * NR);
     return out_tw(L, NR) < cap ? out_tw(L, NR) : (cap < 4 ? 4 : cap);
 }
