@@ -71,7 +71,11 @@ def test_small_grids_match_direct_sum(H, dims, B, C, dtype):
     assert _rel(got, ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 1, 2), ((32, 64, 16), 1, 2), ((512, 64), 1, 3)])
+# (128, 8, 32) and (256, 4, 16): 256- and 512-point out-axis lines whose tiles
+# take the row pairs fastest in the work-item order, with several row pairs
+# and slot tiles per channel
+@pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 1, 2), ((32, 64, 16), 1, 2), ((512, 64), 1, 3),
+                                      ((128, 8, 32), 2, 2), ((256, 4, 16), 1, 2)])
 def test_medium_grids_match_fft_oracle(H, dims, B, C):
     w = synth.make(dims, B=B, C=C, dtype="f32", seed=5)
     y, _ = _gpu_run(H, w)

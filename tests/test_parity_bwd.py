@@ -77,8 +77,10 @@ def test_small_grids_match_direct_sums(H, dims, B, C, dtype):
         assert _rel(g, r) <= TOL_PARAM[dtype]
 
 
+# (128, 8, 32) and (256, 4, 16): the backward's 8-slot tiles of 16-slot runs
+# (two tiles of a run together, then the row pairs, in the work-item order)
 @pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 3, 2), ((32, 64, 16), 2, 2),
-                                      ((1024,), 3, 2)])
+                                      ((1024,), 3, 2), ((128, 8, 32), 2, 2), ((256, 4, 16), 1, 2)])
 def test_medium_grids_match_fft_oracle(H, dims, B, C):
     w = _inputs(dims, B, C, "f32", seed=6)
     got = _gpu_bwd(H, w)

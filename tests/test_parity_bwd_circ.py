@@ -77,8 +77,10 @@ def test_small_grids_match_direct_sums(H, dims, B, C, dtype):
         assert _rel(g, r) <= TOL_PARAM[dtype]
 
 
+# (256, 4, 32): 256-point circular out-axis lines, the backward's 8-slot tiles
+# of 16-slot runs in the work-item order
 @pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 3, 2), ((32, 64, 16), 2, 2),
-                                      ((1024,), 3, 2)])
+                                      ((1024,), 3, 2), ((256, 4, 32), 2, 2)])
 def test_medium_grids_match_fft_oracle(H, dims, B, C):
     x, al, be, K, dy = _inputs(dims, B, C, "f32", seed=12)
     got = _gpu_bwd(H, x, al, be, K, dy)

@@ -68,8 +68,9 @@ def test_small_grids_match_direct_sum(H, dims, B, C, dtype):
     assert _rel(got, ref) <= TOL[dtype]
 
 
+# (256, 4, 32): 256-point circular out-axis lines, row pairs fastest
 @pytest.mark.parametrize("dims,B,C", [((128, 128), 2, 2), ((64, 256), 1, 2), ((32, 64, 16), 1, 2),
-                                      ((1024, 1024), 1, 1)])
+                                      ((1024, 1024), 1, 1), ((256, 4, 32), 2, 2)])
 def test_medium_grids_match_fft_oracle(H, dims, B, C):
     x, al, be, K = _inputs(dims, B, C, "f32", seed=9)
     got = _gpu(H, x, al, be, K)
