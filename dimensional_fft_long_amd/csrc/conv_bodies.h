@@ -120,7 +120,7 @@ template <int L, bool BF16, bool GATE, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lay(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
     constexpr int ITER = NP * n / NT, ITS = NP * S / NT;  // element loops over samples / slots
     static_assert(NP * n % NT == 0 && NP * S % NT == 0, "whole element loops");
     const int tid = ctx.tid();
@@ -141,7 +141,7 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
         float2 z = GATE ? make_float2(ctx.gate(xa[i], md.al0, md.be0), ctx.gate(xb[i], md.al1, md.be1))
                         : make_float2(xa[i], xb[i]);
         if (!md.valid) z = make_float2(0.f, 0.f);
-        T[m * LP + lp] = z;
+        T[tile_idx<LP>(m, lp)] = z;
     }
     ctx.sync();
     tile_fft<L, NP, LP, NT, false, !CIRC, false>(ctx, T);
@@ -157,8 +157,8 @@ __host__ __device__ __forceinline__ void row_fwd_body(const Ctx& ctx, int bid, c
         const int lp = rest % NP, k = ((rest / NP) << a.g.lt_log) + u;
         const long long wo = (long long)(k >> a.g.lt_log) * tstride + u;
         const RowMeta& md = M[lp];
-        const float2 Z = T[k * LP + lp];
-        const float2 Zm = T[(k == 0 ? S : L - k) * LP + lp];
+        const float2 Z = T[tile_idx<LP>(k, lp)];
+        const float2 Zm = T[tile_idx<LP>(k == 0 ? S : L - k, lp)];
         float2 oa, ob;
         if (k == 0) {
             oa = make_float2(2.f * Z.x, 2.f * Zm.x);
@@ -196,18 +196,18 @@ __host__ __device__ __forceinline__ float gate_vjp(const Ctx& ctx, float du, flo
 // belong to one (b, c) pair), one per signal for d = 1 (part[2h], part[2h+1]).
 // xa, xb: the x values of the thread's elements, loaded before the transform.
 // n: samples per line (L / 2 zero-padded, L circular).
-template <int L, int n, bool BF16, int ITER, class Ctx>
+template <int L, int n, bool BF16, int ITER, int LP, int TSZ, class Ctx>
 __host__ __device__ __forceinline__ void bwd_epilogue(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       const RowMeta* M, const float* xa, const float* xb)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L);
+    constexpr int NP = row_np(L), NT = row_nt(L);
     const int tid = ctx.tid();
     float2 ea[ITER], eb[ITER];
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
         const int idx = tid + i * NT, lp = idx / n, m = idx % n;
         const RowMeta& md = M[lp];
-        const float2 z = T[m * LP + lp];
+        const float2 z = T[tile_idx<LP>(m, lp)];
         ea[i] = make_float2(0.f, 0.f);
         eb[i] = make_float2(0.f, 0.f);
         if (md.valid) {
@@ -218,7 +218,7 @@ __host__ __device__ __forceinline__ void bwd_epilogue(const Ctx& ctx, int bid, c
     ctx.sync();  // every read of du in T is done
     // The two rows' terms sit side by side in T when they fit (n = L/2);
     // circular lines (n = L) take them one row after the other.
-    constexpr int NH = 2 * NP * n <= L * LP ? 2 : 1;
+    constexpr int NH = 2 * NP * n <= TSZ ? 2 : 1;
     for (int r0 = 0; r0 < 2; r0 += NH) {
 #pragma unroll
         for (int i = 0; i < ITER; ++i) {
@@ -262,7 +262,7 @@ template <int L, bool BF16, bool BWD, bool CIRC, class Ctx>
 __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                       RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lay(L), NT = row_nt(L), n = CIRC ? L : L / 2, S = L / 2;
     constexpr int ITER = NP * S / NT, ITO = NP * n / NT;
     static_assert(NP * S % NT == 0 && NP * n % NT == 0, "whole element loops");
     const int tid = ctx.tid();
@@ -293,11 +293,11 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
         int lp;
         const int k = slot(tid + i * NT, lp);
         if (k == 0) {
-            T[lp] = make_float2(ya[i].x, yb[i].x);
-            T[S * LP + lp] = make_float2(ya[i].y, yb[i].y);
+            T[tile_idx<LP>(0, lp)] = make_float2(ya[i].x, yb[i].x);
+            T[tile_idx<LP>(S, lp)] = make_float2(ya[i].y, yb[i].y);
         } else {
-            T[k * LP + lp] = make_float2(ya[i].x - yb[i].y, ya[i].y + yb[i].x);
-            T[(L - k) * LP + lp] = make_float2(ya[i].x + yb[i].y, yb[i].x - ya[i].y);
+            T[tile_idx<LP>(k, lp)] = make_float2(ya[i].x - yb[i].y, ya[i].y + yb[i].x);
+            T[tile_idx<LP>(L - k, lp)] = make_float2(ya[i].x + yb[i].y, yb[i].x - ya[i].y);
         }
     }
     float xa[BWD ? ITO : 1], xb[BWD ? ITO : 1];
@@ -312,13 +312,13 @@ __host__ __device__ __forceinline__ void row_inv_body(const Ctx& ctx, int bid, c
     ctx.sync();
     tile_fft<L, NP, LP, NT, true, false, !CIRC>(ctx, T);
     if constexpr (BWD) {
-        bwd_epilogue<L, n, BF16, ITO>(ctx, bid, a, T, M, xa, xb);
+        bwd_epilogue<L, n, BF16, ITO, LP, lay_elems(L, NP, LP)>(ctx, bid, a, T, M, xa, xb);
     } else {
 #pragma unroll
         for (int i = 0; i < ITO; ++i) {
             const int idx = tid + i * NT, lp = idx / n, m = idx % n;
             const RowMeta& md = M[lp];
-            const float2 z = T[m * LP + lp];
+            const float2 z = T[tile_idx<LP>(m, lp)];
             if (md.valid) {
                 store_y<BF16>(a, md.o0 + m, z.x);
                 store_y<BF16>(a, md.o1 + m, z.y);
@@ -903,7 +903,7 @@ __host__ __device__ __forceinline__ void conv1d_body(const Ctx& ctx, int bid, co
     ctx.sync();
     tile_fft<L, NP, LP, NT, true, false, !CIRC>(ctx, T);
     if constexpr (BWD) {
-        bwd_epilogue<L, n, BF16, ITER>(ctx, bid, a, T, M, xa, xb);
+        bwd_epilogue<L, n, BF16, ITER, LP, L * LP>(ctx, bid, a, T, M, xa, xb);
     } else {
         for (int idx = tid; idx < NP * n; idx += NT) {
             const int lp = idx / n, m = idx % n;

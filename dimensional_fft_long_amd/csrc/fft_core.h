@@ -305,6 +305,27 @@ constexpr PlanTwiddles<L, PLANS> make_plan_twiddles()
     return t;
 }
 
+// Element (pos, line) of a tile of layout code LP (plan.h row_lay): pos * P +
+// line + D * (pos >> SH); with D = 0 the plain stride LP.  The split form
+// takes pos = a + c, c a constant of the unrolled loop (so that it folds into
+// the instruction's offset), and is exact when a or c is a multiple of 2^SH:
+// for the passes of the padded row layouts (512, 1024 and 2048 points, SH <= 3)
+// c = r L/R on loads, c = r NS on stores, and a = R j with R = 8 when NS = 1
+// (tests/host/row_layout.cpp checks every access against the plain form).
+template <int LP>
+__host__ __device__ __forceinline__ int tile_idx(int pos, int line)
+{
+    constexpr int P = LP & 255, D = (LP >> 8) & 15, SH = (LP >> 12) & 15;
+    return pos * P + line + (D ? D * (pos >> SH) : 0);
+}
+template <int LP>
+__host__ __device__ __forceinline__ int tile_idx_split(int a, int c, int line)
+{
+    constexpr int P = LP & 255, D = (LP >> 8) & 15, SH = (LP >> 12) & 15;
+    if constexpr (D == 0) return (a + c) * P + line;
+    else return a * P + D * (a >> SH) + line + (c * P + D * (c >> SH));
+}
+
 // Registers of one Stockham pass over NL lines: butterfly g in [0, NL*L/R),
 // line l = g % NL, j = g / NL; thread t owns g = t + i*NT.
 //   inputs:  positions j + r*L/R
@@ -334,7 +355,7 @@ __host__ __device__ __forceinline__ void pass_load_lds(const Ctx& ctx, const flo
         if (bf_valid<PR::NB, NT>(g)) {
             const int l = g % NL, j = g / NL;
 #pragma unroll
-            for (int r = 0; r < (PIN ? R / 2 : R); ++r) s.v[i][r] = T[(j + r * (L / R)) * LP + l];
+            for (int r = 0; r < (PIN ? R / 2 : R); ++r) s.v[i][r] = T[tile_idx_split<LP>(j, r * (L / R), l)];
         }
     }
 }
@@ -502,7 +523,7 @@ __host__ __device__ __forceinline__ void pass_store_lds(const Ctx& ctx, float2* 
             const int l = g % NL, j = g / NL;
             const int base = (j / NS) * NS * R + (j % NS);
 #pragma unroll
-            for (int r = 0; r < (POUT ? R / 2 : R); ++r) T[(base + r * NS) * LP + l] = s.v[i][r];
+            for (int r = 0; r < (POUT ? R / 2 : R); ++r) T[tile_idx_split<LP>(base, r * NS, l)] = s.v[i][r];
         }
     }
 }

@@ -95,7 +95,7 @@ template <int L, bool BF16, bool GATE, bool CIRC = false>
 __global__ __launch_bounds__(row_nt(L)) void k_row_fwd(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * row_lp(L)];
+    __shared__ float2 T[lay_elems(L, row_np(L), row_lay(L))];
     __shared__ RowMeta M[row_np(L)];
     row_fwd_body<L, BF16, GATE, CIRC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
@@ -104,7 +104,7 @@ template <int L, bool BF16, bool BWD, bool CIRC = false>
 __global__ __launch_bounds__(row_nt(L)) void k_row_inv(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * row_lp(L)];
+    __shared__ float2 T[lay_elems(L, row_np(L), row_lay(L))];
     __shared__ RowMeta M[row_np(L)];
     row_inv_body<L, BF16, BWD, CIRC>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }

@@ -40,6 +40,25 @@ namespace hyenand {
 // workgroup, unpadded: a 64 KiB tile beside the 64 KiB twiddle table.
 constexpr int row_np(int L) { return L >= 8192 ? 1 : (4096 / L < 2 ? 2 : (4096 / L > 64 ? 64 : 4096 / L)); }
 constexpr int row_lp(int L) { return row_np(L) == 1 ? 1 : row_np(L) + 1; }
+// Layout code of the tiles of the forward / inverse row kernels: element
+// (pos, lp) at pos * P + lp + D * (pos >> SH), the code P | D << 8 | SH << 12
+// (a plain line stride when D = 0).  512-, 1024- and 2048-point rows take
+// D extra slots after every 2^SH positions instead of a padded line stride:
+// fewer bank conflicts on the strided Stockham stores (2048-point rows 4.2 ->
+// about 0.6 conflict cycles per LDS instruction in a 32-bank model that
+// reproduces the measured counts) and smaller tiles (2048 points: 49 -> 34
+// KiB, three workgroups per CU instead of two; 512 points: four instead of
+// three).  1024^2 forward 4.12 -> 3.59 ms, 256^2 0.318 -> 0.303 ms.
+constexpr int row_lay(int L)
+{
+    return L == 2048 ? (2 | 1 << 8 | 3 << 12) : L == 1024 ? (4 | 1 << 8 | 2 << 12)
+         : L == 512 ? (8 | 2 << 8 | 2 << 12) : row_lp(L);
+}
+constexpr int lay_p(int lay) { return lay & 255; }
+constexpr int lay_d(int lay) { return (lay >> 8) & 15; }
+constexpr int lay_sh(int lay) { return (lay >> 12) & 15; }
+// Elements of an L-position tile of layout lay with NL lines.
+constexpr int lay_elems(int L, int NL, int lay) { return (L - 1) * lay_p(lay) + NL + lay_d(lay) * ((L - 1) >> lay_sh(lay)); }
 // Column kernels along the middle axis / the out axis of a 2-D grid:
 // TW adjacent lines, tile L x TW of up to 128 KiB (gfx950 gives a workgroup
 // up to 160 KiB of LDS), so that even 2048-point lines read row segments of

@@ -1,4 +1,6 @@
-"""Out-axis work-item order (CPU only).
+"""Index maps of the kernels, checked on the host (CPU only).
+
+Out-axis work-item order:
 
 The out-axis kernels map each workgroup id to a (channel, slot tile, row
 pair, batch entry) item through ``out_tile`` (XCD-blocked ids; row pairs or
@@ -24,6 +26,21 @@ def test_out_axis_items_are_a_permutation(tmp_path):
     r = subprocess.run([HIPCC, "-std=c++20", "-O1", "-x", "hip", "--offload-host-only",
                         "-I", os.path.join(ROOT, "include"),
                         os.path.join(ROOT, "tests", "host", "item_order.cpp"), "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("all ok"), r.stdout[-4000:]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_row_tile_layouts_are_exact(tmp_path):
+    """tests/host/row_layout.cpp: every row length's tile layout places each
+    element at a distinct index inside the tile, and the split index the LDS
+    passes use equals the plain index for every access of the radix plan."""
+    exe = str(tmp_path / "row_layout")
+    r = subprocess.run([HIPCC, "-std=c++20", "-O1", "-x", "hip", "--offload-host-only",
+                        "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "host", "row_layout.cpp"), "-o", exe],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
