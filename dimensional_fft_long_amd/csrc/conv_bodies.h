@@ -429,7 +429,7 @@ __host__ __device__ __forceinline__ OutTile out_tile(const Geom& g, int B, int n
 // its mirror, so no two threads touch the same element.
 // CONJ multiplies by the conjugate spectrum (the backward's correlation with
 // K): Sv, Dv of a real kernel conjugate like the spectrum itself.
-template <int L, int NR, int TW, int NT, bool CONJ = false, class Ctx>
+template <int L, int NR, int TW, int NT, bool CONJ = false, int LP = NR * TW, class Ctx>
 __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const Geom& g, const OutTile& o,
                                                            const float2* kc, float2* T)
 {
@@ -444,7 +444,7 @@ __host__ __device__ __forceinline__ void out_slot0_product(const Ctx& ctx, const
         } else {
             ra = 0; rb = 1; pa = job; pb = (L - job) % L;
         }
-        const int ea = pa * NL + ra * TW, eb = pb * NL + rb * TW;
+        const int ea = tile_idx<LP>(pa, ra * TW), eb = tile_idx<LP>(pb, rb * TW);
         const float2 Za = T[ea], Zb = T[eb];
         auto kv = [](float2 v) { return CONJ ? cconj(v) : v; };
         // row of the ra / rb block by selection, not by indexing o.rows with a
@@ -519,7 +519,7 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
                                                       float2* T)
 {
     constexpr int TW = out_tw(L, NR);
-    constexpr int NL = NR * TW, NT = out_nt(L, NR);
+    constexpr int NL = NR * TW, NT = out_nt(L, NR), LP = out_lay(L, NR);
     constexpr int R0 = pass_radix<L, false>(0);
     constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
     constexpr bool kLoop = out_looped(L, NR);
@@ -580,17 +580,17 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
     // One item: forward from the loaded columns, product, inverse and store
     // (c: the context whose passes run the transforms).
     auto run_item = [&](const auto& c, const OutView& v, P0& s) {
-        auto t = fwd_from_regs<L, NL, NT, !CIRC>(c, T, s);
+        auto t = fwd_from_regs<L, NL, NT, !CIRC, LP>(c, T, s);
         ctx.sync();  // every LDS read of the forward transform is done: T is free
         if (v.o.t == 0) {
             pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
-                if (l % TW == 0) T[pos * NL + l] = x;
+                if (l % TW == 0) T[tile_idx<LP>(pos, l)] = x;
             });
             ctx.sync();
-            out_slot0_product<L, NR, TW, NT>(ctx, g, v.o, v.kc, T);
+            out_slot0_product<L, NR, TW, NT, false, LP>(ctx, g, v.o, v.kc, T);
             ctx.sync();
             pass_visit<L, RL, NL, NT, false>(ctx, t, [&](int pos, int l, float2& x) {
-                if (l % TW == 0) x = T[pos * NL + l];
+                if (l % TW == 0) x = T[tile_idx<LP>(pos, l)];
             });
             ctx.sync();
         }
@@ -614,11 +614,11 @@ __host__ __device__ __forceinline__ void col_out_body(const Ctx& ctx, int bid, i
             }
         }
         if (full) {
-            inv_to_fn<L, NL, NT, !CIRC>(c, T, t, [&](int j, int q, int l, const float2& x) {
+            inv_to_fn<L, NL, NT, !CIRC, LP>(c, T, t, [&](int j, int q, int l, const float2& x) {
                 *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
             });
         } else {
-            inv_to_fn<L, NL, NT, !CIRC>(c, T, t, [&](int j, int q, int l, const float2& x) {
+            inv_to_fn<L, NL, NT, !CIRC, LP>(c, T, t, [&](int j, int q, int l, const float2& x) {
                 if (v.k0 + l % TW < g.S) *at(v.base, q * PS, lane_bytes(v, j, l)) = x;
             });
         }

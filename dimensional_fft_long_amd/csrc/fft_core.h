@@ -603,7 +603,7 @@ __host__ __device__ __forceinline__ void tile_fft(const Ctx& ctx, float2* T)
 // are non-zero) and whose last pass is left in registers (positions
 // j + r*L/R_last).  The tile T is scratch; the caller must not touch it
 // before a barrier.
-template <int L, int NL, int NT, bool PIN, class Ctx>
+template <int L, int NL, int NT, bool PIN, int LP = NL, class Ctx>
 __host__ __device__ __forceinline__ auto fwd_from_regs(const Ctx& ctx, float2* T,
                                                        PassRegs<L, pass_radix<L, false>(0), NL, NT>& s)
 {
@@ -613,12 +613,12 @@ __host__ __device__ __forceinline__ auto fwd_from_regs(const Ctx& ctx, float2* T
     if constexpr (NP == 1) {
         return s;
     } else {
-        pass_store_lds<L, R0, 1, NL, NL, NT, false>(ctx, T, s);
+        pass_store_lds<L, R0, 1, NL, LP, NT, false>(ctx, T, s);
         ctx.sync();
-        LdsPasses<L, false, 1, NP - 1, NL, NL, NT, false>::run(ctx, T);
+        LdsPasses<L, false, 1, NP - 1, NL, LP, NT, false>::run(ctx, T);
         constexpr int RL = pass_radix<L, false>(NP - 1), NSL = pass_ns<L, false>(NP - 1);
         PassRegs<L, RL, NL, NT> t;
-        pass_load_lds<L, RL, NL, NL, NT, false>(ctx, T, t);
+        pass_load_lds<L, RL, NL, LP, NT, false>(ctx, T, t);
         pass_compute<L, RL, NSL, NL, NT, false, false, false, tw_local_off<L, false>(NP - 1)>(ctx, t);
         return t;
     }
@@ -641,7 +641,7 @@ __host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, 
 // last pass's registers (positions j + r*L/R0 in natural order, R0 the
 // forward plan's first radix; POUT: only positions < L/2 are valid).  The
 // tile T must be free for writing (a barrier after its last read).
-template <int L, int NL, int NT, bool POUT, class Ctx, class S>
+template <int L, int NL, int NT, bool POUT, int LP = NL, class Ctx, class S>
 __host__ __device__ __forceinline__ auto inv_to_regs(const Ctx& ctx, float2* T, S& s)
 {
     constexpr int NP = plan_passes(L);
@@ -650,22 +650,22 @@ __host__ __device__ __forceinline__ auto inv_to_regs(const Ctx& ctx, float2* T, 
     if constexpr (NP == 1) {
         return s;
     } else {
-        pass_store_lds<L, R0, 1, NL, NL, NT, false>(ctx, T, s);
+        pass_store_lds<L, R0, 1, NL, LP, NT, false>(ctx, T, s);
         ctx.sync();
-        LdsPasses<L, true, 1, NP - 1, NL, NL, NT, true>::run(ctx, T);
+        LdsPasses<L, true, 1, NP - 1, NL, LP, NT, true>::run(ctx, T);
         constexpr int RL = pass_radix<L, true>(NP - 1), NSL = pass_ns<L, true>(NP - 1);
         PassRegs<L, RL, NL, NT> t;
-        pass_load_lds<L, RL, NL, NL, NT, false>(ctx, T, t);
+        pass_load_lds<L, RL, NL, LP, NT, false>(ctx, T, t);
         pass_compute<L, RL, NSL, NL, NT, true, false, POUT, Ctx::kRevBase + tw_local_off<L, true>(NP - 1)>(ctx, t);
         return t;
     }
 }
 
 // Inverse transform whose last pass writes through gfn (see pass_visit).
-template <int L, int NL, int NT, bool POUT, class Ctx, class S, class G>
+template <int L, int NL, int NT, bool POUT, int LP = NL, class Ctx, class S, class G>
 __host__ __device__ __forceinline__ void inv_to_fn(const Ctx& ctx, float2* T, S& s, const G& gfn)
 {
-    auto t = inv_to_regs<L, NL, NT, POUT>(ctx, T, s);
+    auto t = inv_to_regs<L, NL, NT, POUT, LP>(ctx, T, s);
     pass_visit<L, pass_radix<L, false>(0), NL, NT, POUT>(ctx, t, gfn);
 }
 

@@ -237,7 +237,7 @@ template <int L, int NR, bool CIRC = false>
 __global__ __launch_bounds__(out_nt(L, NR)) void k_col_out(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
-    __shared__ float2 T[L * NR * out_tw(L, NR)];
+    __shared__ float2 T[lay_elems(L, NR * out_tw(L, NR), out_lay(L, NR))];
     col_out_body<L, NR, CIRC>(make_ctx<L, out_nt(L, NR), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, (int)gridDim.x, a, T);
 }
 

@@ -84,6 +84,12 @@ constexpr int col_nt(int L) { return tile_threads(L * col_tw(L)); }
 // for them (with 8, 512^3 k_col_mid 730 -> 840 us per call).
 constexpr int out_tw(int L, int NR) { return NR == 1 ? (L == 1024 ? 8 : col_tw(L)) : mul3_tw(L); }
 constexpr int out_nt(int L, int NR) { return tile_threads(L * NR * out_tw(L, NR)); }
+// Layout code (row_lay) of the forward out-axis kernel's tile: 512-point 2-D
+// lines take two extra slots after every two positions (no bank conflicts on
+// the strided stores in the 32-bank model, 1.0 cycle per instruction before;
+// 40,880 bytes with the twiddles, still four workgroups per CU): 256^2
+// k_col_out 148-154 -> 144-146 us per launch.
+constexpr int out_lay(int L, int NR) { return (NR == 1 && L == 512) ? (8 | 2 << 8 | 1 << 12) : NR * out_tw(L, NR); }
 // 2-D out-axis tiles above 80 KiB leave room for one workgroup per CU: such
 // kernels run one workgroup per CU that loops over the work items (1024^2:
 // 4.29 -> 4.08 ms per call).  The 3-D kernel of the same tile size lost with

@@ -1,6 +1,7 @@
-// Host check of the row kernels' tile layouts: for every row length, the
-// layout code row_lay(L) must place the L x row_np(L) elements of a tile at
-// distinct indices below lay_elems(L, row_np(L), row_lay(L)), and the split
+// Host check of the padded tile layouts: for every row length, the layout
+// code row_lay(L) must place the L x row_np(L) elements of a tile at distinct
+// indices below lay_elems(L, row_np(L), row_lay(L)) (the same for the 2-D
+// out-axis tiles of out_lay(L, 1) with their out_tw(L, 1) lines), and the split
 // index used by the LDS passes (lane part + loop constant) must equal the
 // plain index for every access of every pass of the length's radix plan
 // (loads at j + r L/R, stores at (j / NS) NS R + j % NS + r NS).  Prints one
@@ -13,10 +14,10 @@
 
 using namespace hyenand;
 
-template <int L>
+template <int L, int NP = row_np(L), int LP = row_lay(L)>
 static bool check()
 {
-    constexpr int NP = row_np(L), LP = row_lay(L), E = lay_elems(L, NP, LP);
+    constexpr int E = lay_elems(L, NP, LP);
     std::vector<unsigned char> seen(E, 0);
     for (int pos = 0; pos < L; ++pos)
         for (int l = 0; l < NP; ++l) {
@@ -47,7 +48,9 @@ static bool check()
 int main()
 {
     const bool ok = check<4>() && check<8>() && check<16>() && check<32>() && check<64>() && check<128>() &&
-                    check<256>() && check<512>() && check<1024>() && check<2048>() && check<4096>();
+                    check<256>() && check<512>() && check<1024>() && check<2048>() && check<4096>() &&
+                    check<256, out_tw(256, 1), out_lay(256, 1)>() && check<512, out_tw(512, 1), out_lay(512, 1)>() &&
+                    check<1024, out_tw(1024, 1), out_lay(1024, 1)>();
     std::printf(ok ? "all ok\n" : "failed\n");
     return ok ? 0 : 1;
 }
