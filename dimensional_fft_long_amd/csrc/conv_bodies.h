@@ -1442,7 +1442,7 @@ __host__ __device__ __forceinline__ void lng_spec_row_body(const Ctx& ctx, int b
 template <int L, bool CONJ, class Ctx>
 __host__ __device__ __forceinline__ void lng_prod_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
-    constexpr int NL = lngp_nl(L), NT = lngp_nt(L);
+    constexpr int NL = lngp_nl(L), NT = lngp_nt(L), LP = lngp_lay(L);
     constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
     using PL = PassRegs<L, RL, NL, NT>;
     const Geom& g = a.g;
@@ -1473,7 +1473,7 @@ __host__ __device__ __forceinline__ void lng_prod_body(const Ctx& ctx, int bid, 
             for (int r = 0; r < RL; ++r) kv[i][r] = ok ? a.khat[base + r * (L / RL)] : make_float2(0.f, 0.f);
         }
     };
-    auto t = fwd_from_fn<L, NL, NT, false>(ctx, T, [&](int pos, int l) -> float2 {
+    auto t = fwd_from_fn<L, NL, NT, false, LP>(ctx, T, [&](int pos, int l) -> float2 {
         return live(l) ? a.ws[row_off(l) + pos] : make_float2(0.f, 0.f);
     }, after_load);
 #pragma unroll
@@ -1481,7 +1481,7 @@ __host__ __device__ __forceinline__ void lng_prod_body(const Ctx& ctx, int bid, 
 #pragma unroll
         for (int r = 0; r < RL; ++r) t.v[i][r] = cmul(t.v[i][r], CONJ ? cconj(kv[i][r]) : kv[i][r]);
     ctx.sync();  // every LDS read of the forward transform is done: T is free
-    inv_to_fn<L, NL, NT, false>(ctx, T, t, [&](int pos, int l, const float2& x) {
+    inv_to_fn<L, NL, NT, false, LP>(ctx, T, t, [&](int pos, int l, const float2& x) {
         if (live(l)) a.ws[row_off(l) + pos] = x;
     });
 }
@@ -1496,7 +1496,7 @@ template <int L, class Ctx>
 __host__ __device__ __forceinline__ void lng_prod_dk_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T)
 {
     constexpr bool DU = lng_dk_fuses_du(L);
-    constexpr int NL = lngp_nl(L), NT = lngp_nt(L);
+    constexpr int NL = lngp_nl(L), NT = lngp_nt(L), LP = lngp_lay(L);
     constexpr int RL = pass_radix<L, false>(plan_passes(L) - 1);
     using PL = PassRegs<L, RL, NL, NT>;
     const Geom& g = a.g;
@@ -1510,7 +1510,7 @@ __host__ __device__ __forceinline__ void lng_prod_dk_body(const Ctx& ctx, int bi
     };
     auto none = []() {};
     auto fwd_rows = [&](const float2* ws, int b) {
-        return fwd_from_fn<L, NL, NT, false>(ctx, T, [&](int pos, int l) -> float2 {
+        return fwd_from_fn<L, NL, NT, false, LP>(ctx, T, [&](int pos, int l) -> float2 {
             return live(l) ? ws[row_off(l, b) + pos] : make_float2(0.f, 0.f);
         }, none);
     };
@@ -1543,13 +1543,13 @@ __host__ __device__ __forceinline__ void lng_prod_dk_body(const Ctx& ctx, int bi
             for (int i = 0; i < PL::PER; ++i)
 #pragma unroll
                 for (int r = 0; r < RL; ++r) DY.v[i][r] = cmulc(DY.v[i][r], kv[i][r]);
-            inv_to_fn<L, NL, NT, false>(ctx, T, DY, [&](int pos, int l, const float2& x) {
+            inv_to_fn<L, NL, NT, false, LP>(ctx, T, DY, [&](int pos, int l, const float2& x) {
                 if (live(l)) a.ws[row_off(l, b) + pos] = x;
             });
             ctx.sync();  // T is free for the next transform
         }
     }
-    inv_to_fn<L, NL, NT, false>(ctx, T, P, [&](int pos, int l, const float2& x) {
+    inv_to_fn<L, NL, NT, false, LP>(ctx, T, P, [&](int pos, int l, const float2& x) {
         const int h = bid * NL + l;
         if (live(l)) a.dkw[(long long)(h / N1) * g.kmain + (long long)(h % N1) * L + pos] = x;
     });

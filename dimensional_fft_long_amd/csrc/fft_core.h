@@ -627,13 +627,13 @@ __host__ __device__ __forceinline__ auto fwd_from_regs(const Ctx& ctx, float2* T
 // Forward transform whose first pass reads through the accessor f (see
 // pass_load_fn).  `after_load()` runs once the first pass's loads are issued
 // and before they are used (a place to issue more independent loads).
-template <int L, int NL, int NT, bool PIN, class Ctx, class F, class H>
+template <int L, int NL, int NT, bool PIN, int LP = NL, class Ctx, class F, class H>
 __host__ __device__ __forceinline__ auto fwd_from_fn(const Ctx& ctx, float2* T, const F& f, const H& after_load)
 {
     PassRegs<L, pass_radix<L, false>(0), NL, NT> s;
     pass_load_fn<L, pass_radix<L, false>(0), NL, NT, PIN>(ctx, f, s);
     after_load();
-    return fwd_from_regs<L, NL, NT, PIN>(ctx, T, s);
+    return fwd_from_regs<L, NL, NT, PIN, LP>(ctx, T, s);
 }
 
 // Inverse transform (reversed plan) whose first-pass inputs are the registers

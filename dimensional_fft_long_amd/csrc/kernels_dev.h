@@ -178,7 +178,7 @@ template <int L, bool CONJ>
 __global__ __launch_bounds__(lngp_nt(L)) void k_lng_prod(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
-    __shared__ float2 T[L * lngp_nl(L)];
+    __shared__ float2 T[lay_elems(L, lngp_nl(L), lngp_lay(L))];
     lng_prod_body<L, CONJ>(make_ctx<L, lngp_nt(L), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
 }
 
@@ -189,7 +189,7 @@ template <int L>
 __global__ __launch_bounds__(lngp_nt(L), lngp_wgs(L) * lngp_nt(L) / 64 / 4) void k_lng_prod_dk(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, (kPlanF | kPlanR)>()];
-    __shared__ float2 T[L * lngp_nl(L)];
+    __shared__ float2 T[lay_elems(L, lngp_nl(L), lngp_lay(L))];
     lng_prod_dk_body<L>(make_ctx<L, lngp_nt(L), (kPlanF | kPlanR)>(TWL), (int)blockIdx.x, a, T);
 }
 

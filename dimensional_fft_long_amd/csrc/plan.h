@@ -328,6 +328,17 @@ constexpr bool lng_dk_fuses_du(int N2) { return N2 >= 4096; }
 constexpr int lngp_nl(int L) { return L >= 4096 ? 1 : 4096 / L; }
 constexpr int lngp_nt(int L) { return L * lngp_nl(L) / 8; }
 constexpr int lngp_wgs(int L) { return L >= 8192 ? 1 : 2; }
+// Layout code (row_lay) of the register-flow row kernels' tiles: one extra
+// slot after every 16 positions for one-line tiles of 4096 and 8192 points,
+// two after every 8 for 2048-point tiles of two lines, two after every 4 for
+// 1024-point tiles of four lines (LDS conflict cycles per instruction of
+// k_lng_prod 2.7 and 4.4 on the plain tiles; 2^24 tokens: row pass 262 ->
+// 252 us, 2^21 tokens: 179 -> 168 us).
+constexpr int lngp_lay(int L)
+{
+    return L >= 4096 ? (1 | 1 << 8 | 4 << 12) : L == 2048 ? (2 | 2 << 8 | 3 << 12)
+         : L == 1024 ? (4 | 2 << 8 | 2 << 12) : lngp_nl(L);
+}
 
 // Backward partial sums of dalpha / dbeta per (b, c) pair: one per line pair
 // of the row kernels (d >= 2), one per pair (d = 1), one per inverse-column

@@ -1,9 +1,11 @@
 // Host check of the padded tile layouts: for every row length, the layout
 // code row_lay(L) must place the L x row_np(L) elements of a tile at distinct
 // indices below lay_elems(L, row_np(L), row_lay(L)) (the same for the 2-D
-// out-axis tiles of out_lay(L, 1) with their out_tw(L, 1) lines), and the split
+// out-axis tiles of out_lay(L, 1) with their out_tw(L, 1) lines and the
+// register-flow row tiles of lngp_lay(L) with lngp_nl(L) lines), and the split
 // index used by the LDS passes (lane part + loop constant) must equal the
-// plain index for every access of every pass of the length's radix plan
+// plain index for every access of every pass of the length's radix plan and
+// of the reversed plan
 // (loads at j + r L/R, stores at (j / NS) NS R + j % NS + r NS).  Prints one
 // line per length; exits non-zero on the first failure.
 #include <cstdio>
@@ -27,7 +29,11 @@ static bool check()
                 return false;
             }
         }
-    for (int p = 0, ns = 1; p < plan_passes(L); ++p) {
+    // the forward plan, then the reversed plan (the inverse transforms of
+    // the out-axis and register-flow row kernels)
+    for (int q = 0, ns = 1; q < 2 * plan_passes(L); ++q) {
+        const int p = q < plan_passes(L) ? q : 2 * plan_passes(L) - 1 - q;
+        if (q == plan_passes(L)) ns = 1;
         const int R = plan_radix(L, p);
         for (int j = 0; j < L / R; ++j)
             for (int r = 0; r < R; ++r)
@@ -50,7 +56,9 @@ int main()
     const bool ok = check<4>() && check<8>() && check<16>() && check<32>() && check<64>() && check<128>() &&
                     check<256>() && check<512>() && check<1024>() && check<2048>() && check<4096>() &&
                     check<256, out_tw(256, 1), out_lay(256, 1)>() && check<512, out_tw(512, 1), out_lay(512, 1)>() &&
-                    check<1024, out_tw(1024, 1), out_lay(1024, 1)>();
+                    check<1024, out_tw(1024, 1), out_lay(1024, 1)>() &&
+                    check<1024, lngp_nl(1024), lngp_lay(1024)>() && check<2048, lngp_nl(2048), lngp_lay(2048)>() &&
+                    check<4096, lngp_nl(4096), lngp_lay(4096)>() && check<8192, lngp_nl(8192), lngp_lay(8192)>();
     std::printf(ok ? "all ok\n" : "failed\n");
     return ok ? 0 : 1;
 }
