@@ -1239,7 +1239,7 @@ template <int L, class Ctx>
 __host__ __device__ __forceinline__ void dk_row_body(const Ctx& ctx, int bid, const ConvArgs& a, float2* T,
                                                      RowMeta* M)
 {
-    constexpr int NP = row_np(L), LP = row_lp(L), NT = row_nt(L), S = L / 2;
+    constexpr int NP = row_np(L), LP = row_lay(L), NT = row_nt(L), S = L / 2;
     const Geom& g = a.g;
     const bool one_d = g.d == 1;
     const int rc = g.N_out * g.N_mid;
@@ -1283,11 +1283,11 @@ __host__ __device__ __forceinline__ void dk_row_body(const Ctx& ctx, int bid, co
             }
         }
         if (k == 0) {
-            T[lp] = make_float2(ya.x, yb.x);
-            T[S * LP + lp] = make_float2(ya.y, yb.y);
+            T[tile_idx<LP>(0, lp)] = make_float2(ya.x, yb.x);
+            T[tile_idx<LP>(S, lp)] = make_float2(ya.y, yb.y);
         } else {
-            T[k * LP + lp] = make_float2(ya.x - yb.y, ya.y + yb.x);
-            T[(L - k) * LP + lp] = make_float2(ya.x + yb.y, yb.x - ya.y);
+            T[tile_idx<LP>(k, lp)] = make_float2(ya.x - yb.y, ya.y + yb.x);
+            T[tile_idx<LP>(L - k, lp)] = make_float2(ya.x + yb.y, yb.x - ya.y);
         }
     }
     ctx.sync();
@@ -1305,7 +1305,7 @@ __host__ __device__ __forceinline__ void dk_row_body(const Ctx& ctx, int bid, co
         };
         const int e2 = kidx(t, g.n_in, g.N_in);
         if (!md.valid || e2 == kEmpty) continue;
-        const float2 z = T[t * LP + lp];
+        const float2 z = T[tile_idx<LP>(t, lp)];
         for (int s2 = 0; s2 < 2; ++s2) {
             if (s2 == 1 && !md.valid1) break;
             const long long c = s2 ? md.w1 : md.w0;

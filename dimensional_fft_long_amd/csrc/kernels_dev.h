@@ -153,7 +153,7 @@ template <int L>
 __global__ __launch_bounds__(row_nt(L)) void k_dk_row(ConvArgs a)
 {
     __shared__ float2 TWL[twl_size<L, kPlanF>()];
-    __shared__ float2 T[L * row_lp(L)];
+    __shared__ float2 T[lay_elems(L, row_np(L), row_lay(L))];
     __shared__ RowMeta M[row_np(L)];
     dk_row_body<L>(make_ctx<L, row_nt(L), kPlanF>(TWL), (int)blockIdx.x, a, T, M);
 }
